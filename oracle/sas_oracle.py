@@ -1,0 +1,297 @@
+"""Oracle: a plain, slow CPU implementation of SAS log-gated block-sparse attention.
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module. The product path
+(``learned_context_ranking_amd``) never imports it, and this module imports nothing
+from the product: the two share only the seeded input generator, which carries none of
+the method's arithmetic.
+
+Everything here is NumPy in float64, applied to inputs that are exactly representable
+(bf16-rounded draws, fp32 scores), one query block at a time, with a matrix product as
+the only library step. It follows the pages' notation: block size ``b``, history blocks
+``m < j`` of query block ``j``, scores ``s``, gates ``g = softmax(s)`` with the current
+block's gate fixed at 1, the Top-K set ``I`` and the key set ``S = B_j U (U_{m in I} B_m)``.
+
+Sources, cited by page title and section:
+
+* [SAS-ja] "論文解説: SAS — 疎注意の「どのブロックを読むか」を言語モデル損失で端から端まで学習する"
+  (ta-paperlens.web.app). Section "前提" restates the paper's section 3 (n tokens in
+  C = n/b blocks, selector scores s in R^C, the Top-K union S, per-query cost |S|).
+  Section "仕組み" restates section 4.1 (positive gates g = phi(s), current block gate 1,
+  one gate per block broadcast to its tokens), section 4.3 eq. (9) (log g added to the
+  logits inside the softmax; exp(z + log g) = g exp(z)) and Algorithm 2 / section 5.1
+  (inference: Top-K on s, no gates, plain sparse attention).
+* [SAS-ko] "SAS는 언어모델 손실로 문맥 순위를 직접 학습하는 사후 어텐션 희소화다"
+  (onedev.kr/papers/5). Section "어떻게 동작하나" gives o = softmax(q K_S^T + log g_S) V_S.
+  Section "무엇과 다른가" gives the four design choices: (1) the gate inside the softmax and
+  its gradient dg_m = sum_{i in B_m} (p~_i / g_m) dO^T (v_i - o); (2) g = softmax(s), so
+  log g_m = s_m - LSE(s), invariant to a global shift of s; (4) sparse training scope.
+
+Readings taken where the pages are silent (each also stated where it is used):
+
+* R1 scale: logits are ``scale * q.k`` (the pages drop the scale); ``log g`` is added
+  unscaled so that exp(z + log g) = g exp(z) holds exactly.
+* R2 the gate softmax normalises over every valid history block m < j of the row, not
+  only the selected ones.
+* R3 s, I and g are shared by the b queries of a query block and by the G query heads
+  of a KV head; dg sums over those G*b rows.
+* R4 query block j sees history blocks 0..j-1 and its own block with a causal mask.
+* R5 ties in s go to the lowest block index; -0 equals +0; NaN ranks as -inf.
+* R6 selected indices are reported in ascending order, padded with -1 (logg with 0).
+* R7 decode: the query is the last of kv_len tokens; its current block holds tokens
+  [b*floor((L-1)/b), L); history is the blocks before it; attention is ungated unless
+  log-gates are supplied.
+* R8 dg is the derivative with respect to g itself, reported per selected slot.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------- gates and selection
+
+def _rank_keys(s_row):
+    """Scores as the selection compares them (R5): NaN -> -inf, -0 -> +0."""
+    s = np.array(s_row, dtype=np.float64)
+    s[np.isnan(s)] = NEG_INF
+    s[s == 0.0] = 0.0
+    return s
+
+
+def row_log_gates(s_row):
+    """Log-gates of one row of history scores.
+
+    [SAS-ko] "무엇과 다른가", choice 2: g = softmax(s), so log g_m = s_m - LSE(s).
+    [SAS-ja] "仕組み": the current block's gate is 1 (log-gate 0) and is not part of s.
+    Returns (LSE, log g) with LSE = -inf and an empty vector for a row with no history.
+    A NaN score is read as -inf (R5), so its gate is 0.
+    """
+    s = _rank_keys(s_row)
+    if s.size == 0:
+        return NEG_INF, s
+    mx = s.max()
+    if mx == NEG_INF:
+        return NEG_INF, np.full_like(s, NEG_INF)
+    lse = mx + np.log(np.sum(np.exp(s - mx)))
+    return lse, s - lse
+
+
+def row_topk(s_row, k):
+    """The k highest-scoring history blocks of one row, ties to the lowest index (R5),
+    reported in ascending block order (R6).
+
+    [SAS-ja] "前提": the selector's Top-K blocks form the attended set.
+    """
+    s = _rank_keys(s_row)
+    k = min(int(k), s.size)
+    order = np.lexsort((np.arange(s.size), -s))   # primary key -s, then the block index
+    return np.sort(order[:k])
+
+
+def select(s, valid, topk, full_scope=False, kcap=None):
+    """Gates plus Top-K selection for a stack of score rows.
+
+    s: [R, ld] fp32 scores; row r has ``valid[r]`` history blocks (columns 0..valid-1).
+    Sparse scope keeps min(topk, valid) blocks; full scope keeps all of them
+    ([SAS-ko] "무엇과 다른가", choice 4).
+    Returns idx [R, kcap] int32 (ascending, -1 pad), cnt [R] int32, lse [R] float64,
+    logg [R, kcap] float64 (log g of each selected block, 0 pad).
+    """
+    s = np.asarray(s)
+    R = s.shape[0]
+    valid = np.broadcast_to(np.asarray(valid, dtype=np.int64), (R,))
+    if kcap is None:
+        kcap = int(valid.max()) if full_scope else int(topk)
+    idx = np.full((R, kcap), -1, dtype=np.int32)
+    cnt = np.zeros(R, dtype=np.int32)
+    lse = np.full(R, NEG_INF, dtype=np.float64)
+    logg = np.zeros((R, kcap), dtype=np.float64)
+    for r in range(R):
+        row = s[r, : valid[r]]
+        lse[r], lg = row_log_gates(row)
+        k = row.size if full_scope else min(int(topk), row.size)
+        if k > kcap:
+            raise ValueError("kcap smaller than the number of selected blocks")
+        sel = row_topk(row, k)
+        idx[r, :k] = sel
+        cnt[r] = k
+        logg[r, :k] = lg[sel]
+    return idx, cnt, lse, logg
+
+
+def select_prefill(s, topk, full_scope=False, kcap=None):
+    """Selection for prefill/training score tensors s [B, H, NB, NB]: row j has j valid
+    history blocks (R4). Returns tensors shaped [B, H, NB, kcap] / [B, H, NB]."""
+    B, H, NB, ld = s.shape
+    valid = np.tile(np.arange(NB), B * H)
+    idx, cnt, lse, logg = select(s.reshape(B * H * NB, ld), valid, topk, full_scope, kcap)
+    kc = idx.shape[1]
+    return (idx.reshape(B, H, NB, kc), cnt.reshape(B, H, NB), lse.reshape(B, H, NB),
+            logg.reshape(B, H, NB, kc))
+
+
+# ---------------------------------------------------------------- training forward/backward
+
+def _key_set(j, idx_row, cnt_j, logg_row, block):
+    """Token indices of S_j = B_j U (U_{m in I_j} B_m) and the additive log-gate of each
+    ([SAS-ja] "仕組み": each block's gate is broadcast to all of its tokens; the current
+    block's gate is 1)."""
+    toks = [np.arange(j * block, (j + 1) * block)]
+    ell = [np.zeros(block)]
+    for t in range(int(cnt_j)):
+        m = int(idx_row[t])
+        toks.append(np.arange(m * block, (m + 1) * block))
+        ell.append(np.full(block, float(logg_row[t])))
+    return np.concatenate(toks), np.concatenate(ell)
+
+
+def _block_logits(q, Kb, keys, ell, j, block, scale):
+    """Logits of one query block over S_j: z_ti = scale * q_t.k_i + log g_{m(i)}
+    ([SAS-ko] "어떻게 동작하나": softmax(q K_S^T + log g_S); R1), -inf above the diagonal
+    of the current block (R4). Returns (z, zu) where zu is z before the gate is added."""
+    zu = scale * (q @ Kb.T)
+    qpos = j * block + np.arange(q.shape[0])
+    zu = np.where(keys[None, :] > qpos[:, None], NEG_INF, zu)
+    return zu + ell[None, :], zu
+
+
+def attn_fwd(Q, K, V, idx, cnt, logg, scale, block=64):
+    """Gated block-sparse attention forward, eq. (9) of [SAS-ja] "仕組み".
+
+    Q [B, Hq, n, d]; K, V [B, Hkv, n, d]; idx/logg [B, Hkv, NB, kcap]; cnt [B, Hkv, NB].
+    Returns O [B, Hq, n, d] and the natural-log row sums LSE [B, Hq, n].
+    """
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    NB = n // block
+    O = np.zeros_like(Q)
+    LSE = np.zeros((B, Hq, n))
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(NB):
+                keys, ell = _key_set(j, idx[b, h, j], cnt[b, h, j], logg[b, h, j], block)
+                Kb, Vb = K[b, h, keys], V[b, h, keys]
+                rows = slice(j * block, (j + 1) * block)
+                for g in range(G):
+                    hq = h * G + g
+                    z, _ = _block_logits(Q[b, hq, rows], Kb, keys, ell, j, block, scale)
+                    mx = z.max(axis=1, keepdims=True)
+                    e = np.exp(z - mx)
+                    Z = e.sum(axis=1, keepdims=True)
+                    O[b, hq, rows] = (e / Z) @ Vb
+                    LSE[b, hq, rows] = (mx + np.log(Z))[:, 0]
+    return O, LSE
+
+
+def attn_bwd(Q, K, V, dO, idx, cnt, logg, scale, block=64):
+    """Backward of :func:`attn_fwd` with the gate gradient.
+
+    Content gradients are those of softmax attention over S_j; gradients reach only the
+    attended keys (sparse scope, [SAS-ko] "무엇과 다른가", choice 4). The gate gradient of
+    selected block m of query block j follows choice 1 of the same section:
+    dg_jm = sum over the G*b query rows t of the group (R3) and keys i in B_m of
+    (p~_ti / g_jm) * dO_t^T (v_i - o_t). By eq. (9) p~_ti / g_jm = exp(z_ti - LSE_t) with
+    z_ti the logit before the gate is added, which is what is evaluated (it stays
+    defined when g_jm = 0).
+    Returns dQ, dK, dV (float64, shapes of Q, K, V) and dg [B, Hkv, NB, kcap] (0 pad).
+    """
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64)
+    V = np.asarray(V, np.float64); dO = np.asarray(dO, np.float64)
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    G = Hq // Hkv
+    NB = n // block
+    kcap = idx.shape[-1]
+    dQ = np.zeros_like(Q); dK = np.zeros_like(K); dV = np.zeros_like(V)
+    dg = np.zeros((B, Hkv, NB, kcap))
+    for b in range(B):
+        for h in range(Hkv):
+            for j in range(NB):
+                keys, ell = _key_set(j, idx[b, h, j], cnt[b, h, j], logg[b, h, j], block)
+                Kb, Vb = K[b, h, keys], V[b, h, keys]
+                rows = slice(j * block, (j + 1) * block)
+                for g in range(G):
+                    hq = h * G + g
+                    q = Q[b, hq, rows]
+                    z, zu = _block_logits(q, Kb, keys, ell, j, block, scale)
+                    mx = z.max(axis=1, keepdims=True)
+                    e = np.exp(z - mx)
+                    Z = e.sum(axis=1, keepdims=True)
+                    P = e / Z
+                    lse = mx + np.log(Z)
+                    o = P @ Vb
+                    do = dO[b, hq, rows]
+                    dP = do @ Vb.T                      # dO_t^T v_i
+                    delta = np.sum(do * o, axis=1, keepdims=True)   # dO_t^T o_t
+                    dS = P * (dP - delta)
+                    dQ[b, hq, rows] += scale * (dS @ Kb)
+                    np.add.at(dK[b, h], keys, scale * (dS.T @ q))
+                    np.add.at(dV[b, h], keys, P.T @ do)
+                    # gate gradient, one selected block at a time
+                    ratio = np.exp(zu - lse)             # = p~ / g
+                    for t in range(int(cnt[b, h, j])):
+                        cols = slice(block * (t + 1), block * (t + 2))
+                        dg[b, h, j, t] += np.sum(ratio[:, cols] * (dP[:, cols] - delta))
+    return dQ, dK, dV, dg
+
+
+def dense_causal(Q, K, V, scale):
+    """Ordinary causal softmax attention over every earlier token ([SAS-ja] "前提": the
+    dense attention the sparse form replaces). Used to pin the full-scope, ungated case."""
+    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
+    B, Hq, n, d = Q.shape
+    G = Hq // K.shape[1]
+    O = np.zeros_like(Q)
+    mask = np.triu(np.ones((n, n), dtype=bool), 1)
+    for b in range(B):
+        for hq in range(Hq):
+            z = scale * Q[b, hq] @ K[b, hq // G].T
+            z[mask] = NEG_INF
+            e = np.exp(z - z.max(axis=1, keepdims=True))
+            O[b, hq] = (e / e.sum(axis=1, keepdims=True)) @ V[b, hq // G]
+    return O
+
+
+# ---------------------------------------------------------------- decode (Algorithm 2)
+
+def decode_rows_valid(kv_len, block=64):
+    """History blocks of each decode sequence: the blocks before the one holding token
+    kv_len - 1 (R7)."""
+    return (np.asarray(kv_len, dtype=np.int64) - 1) // block
+
+
+def decode(q, Kc, Vc, kv_len, idx, cnt, scale, block=64, logg=None):
+    """Inference form, [SAS-ja] "仕組み", Algorithm 2 / section 5.1: Top-K on s, then plain
+    (ungated) sparse attention over the current block plus the selected blocks.
+
+    q [B, Hq, d]; Kc, Vc [B, Hkv, Lmax, d]; kv_len [B]; idx [B, Hkv, kcap]; cnt [B, Hkv].
+    With ``logg`` ([B, Hkv, kcap]) the log-gates are added as in training (a check only).
+    Returns o [B, Hq, d].
+    """
+    q = np.asarray(q, np.float64); Kc = np.asarray(Kc, np.float64); Vc = np.asarray(Vc, np.float64)
+    B, Hq, d = q.shape
+    Hkv = Kc.shape[1]
+    G = Hq // Hkv
+    o = np.zeros_like(q)
+    for b in range(B):
+        L = int(kv_len[b])
+        c = (L - 1) // block
+        for h in range(Hkv):
+            toks = [np.arange(c * block, L)]
+            ell = [np.zeros(L - c * block)]
+            for t in range(int(cnt[b, h])):
+                m = int(idx[b, h, t])
+                toks.append(np.arange(m * block, (m + 1) * block))
+                ell.append(np.full(block, 0.0 if logg is None else float(logg[b, h, t])))
+            keys = np.concatenate(toks)
+            ell = np.concatenate(ell)
+            Kb, Vb = Kc[b, h, keys], Vc[b, h, keys]
+            for g in range(G):
+                z = scale * (Kb @ q[b, h * G + g]) + ell
+                e = np.exp(z - z.max())
+                o[b, h * G + g] = (e / e.sum()) @ Vb
+    return o

@@ -1,0 +1,375 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+None of the SAS pages prints a worked numerical example, so no stored value comes from
+them. The pins are identities, closed forms, textbook routines (torch SDPA and autograd
+in float64), brute force on tiny inputs and finite differences. Each is chosen so that a
+plausible mistake in the oracle (a dropped gate term, a wrong sign, a wrong causal index,
+a transposed operand, a gate normalised over the wrong set) fails at least one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from learned_context_ranking_amd import synth
+
+RTOL = 1e-10
+
+
+def _rand_case(B=1, Hq=2, Hkv=1, n=128, d=16, block=16, topk=2, seed=0, full=False):
+    g = np.random.default_rng(seed)
+    Q = g.standard_normal((B, Hq, n, d))
+    K = g.standard_normal((B, Hkv, n, d))
+    V = g.standard_normal((B, Hkv, n, d))
+    dO = g.standard_normal((B, Hq, n, d))
+    NB = n // block
+    s = g.standard_normal((B, Hkv, NB, NB)).astype(np.float32)
+    idx, cnt, lse, logg = oracle.select_prefill(s, topk, full_scope=full)
+    return dict(Q=Q, K=K, V=V, dO=dO, s=s, idx=idx, cnt=cnt, lse=lse, logg=logg,
+                scale=1.0 / math.sqrt(d), block=block)
+
+
+# ------------------------------------------------------------------ P-a: eq. (9) identity
+
+def test_pa_log_gate_equals_multiplicative_gate():
+    """exp(z + log g) = g exp(z): the log-add forward equals gating the exponentials
+    and renormalising (SAS explainer, section 仕組み, eq. (9))."""
+    c = _rand_case(Hq=3, Hkv=1, n=96, d=8, block=16, topk=3, seed=1)
+    O, LSE = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], c["logg"], c["scale"], c["block"])
+    b, blk = 0, c["block"]
+    for hq in range(3):
+        for t in range(96):
+            j = t // blk
+            num = np.zeros(8)
+            den = 0.0
+            for i in range(96):
+                mi = i // blk
+                if mi == j:
+                    if i > t:
+                        continue
+                    gate = 1.0
+                else:
+                    sel = list(c["idx"][b, 0, j, : c["cnt"][b, 0, j]])
+                    if mi not in sel:
+                        continue
+                    gate = math.exp(c["logg"][b, 0, j, sel.index(mi)])
+                w = gate * math.exp(c["scale"] * float(c["Q"][b, hq, t] @ c["K"][b, 0, i]))
+                num += w * c["V"][b, 0, i]
+                den += w
+            np.testing.assert_allclose(O[b, hq, t], num / den, rtol=1e-12, atol=1e-13)
+            assert abs(LSE[b, hq, t] - math.log(den)) < 1e-12
+
+
+# ------------------------------------------------------------------ P-b: textbook reduction
+
+def test_pb_full_scope_ungated_is_dense_causal():
+    """Full scope with every log-gate 0 is ordinary causal attention: the oracle matches
+    torch SDPA (is_causal) and torch autograd gradients in float64."""
+    c = _rand_case(B=1, Hq=4, Hkv=2, n=128, d=16, block=16, full=True, seed=2)
+    zero = np.zeros_like(c["logg"])
+    O, _ = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], zero, c["scale"], c["block"])
+    Qt = torch.tensor(c["Q"], requires_grad=True)
+    Kt = torch.tensor(c["K"], requires_grad=True)
+    Vt = torch.tensor(c["V"], requires_grad=True)
+    G = 2
+    Ot = torch.nn.functional.scaled_dot_product_attention(
+        Qt, Kt.repeat_interleave(G, 1), Vt.repeat_interleave(G, 1), is_causal=True, scale=c["scale"])
+    np.testing.assert_allclose(O, Ot.detach().numpy(), rtol=RTOL, atol=1e-12)
+    np.testing.assert_allclose(O, oracle.dense_causal(c["Q"], c["K"], c["V"], c["scale"]), rtol=RTOL, atol=1e-12)
+    (Ot * torch.tensor(c["dO"])).sum().backward()
+    dQ, dK, dV, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], zero,
+                                     c["scale"], c["block"])
+    np.testing.assert_allclose(dQ, Qt.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dK, Kt.grad.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dV, Vt.grad.numpy(), rtol=1e-9, atol=1e-11)
+
+
+def _autograd_gated(c):
+    """Gated block-sparse attention written as dense attention with an additive mask
+    built from leaf log-gate tensors; torch autograd returns every gradient."""
+    B, Hq, n, d = c["Q"].shape
+    Hkv = c["K"].shape[1]
+    G = Hq // Hkv
+    blk = c["block"]
+    NB = n // blk
+    Qt = torch.tensor(c["Q"], requires_grad=True)
+    Kt = torch.tensor(c["K"], requires_grad=True)
+    Vt = torch.tensor(c["V"], requires_grad=True)
+    lg = torch.tensor(c["logg"], requires_grad=True)            # [B,Hkv,NB,kcap]
+    l0 = torch.zeros((B, Hkv, NB), dtype=torch.float64, requires_grad=True)
+    rows = []
+    for b in range(B):
+        per_h = []
+        for h in range(Hkv):
+            blocks = []
+            for j in range(NB):
+                cols = [torch.full((blk,), float("-inf"), dtype=torch.float64) for _ in range(NB)]
+                for t in range(int(c["cnt"][b, h, j])):
+                    m = int(c["idx"][b, h, j, t])
+                    cols[m] = lg[b, h, j, t].expand(blk)
+                cols[j] = l0[b, h, j].expand(blk)
+                blocks.append(torch.cat(cols).unsqueeze(0).expand(blk, n))
+            M = torch.cat(blocks, 0)
+            causal = torch.triu(torch.ones(n, n, dtype=torch.bool), 1)
+            M = M.masked_fill(causal, float("-inf"))
+            per_h.append(M)
+        rows.append(torch.stack(per_h))
+    M = torch.stack(rows).repeat_interleave(G, 1)
+    z = c["scale"] * Qt @ Kt.repeat_interleave(G, 1).transpose(-1, -2) + M
+    P = torch.softmax(z, -1)
+    Ot = P @ Vt.repeat_interleave(G, 1)
+    (Ot * torch.tensor(c["dO"])).sum().backward()
+    return Ot.detach().numpy(), Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy(), lg.grad.numpy(), l0.grad.numpy()
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_pb_gated_matches_autograd(full):
+    """The oracle's forward and its hand-written backward (content gradients and the
+    inside-softmax gate gradient) agree with torch autograd through a dense masked
+    formulation; dg = (dL/dlog g) / g."""
+    c = _rand_case(B=1, Hq=4, Hkv=2, n=128, d=16, block=16, topk=3, full=full, seed=3)
+    O, LSE = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], c["logg"], c["scale"], c["block"])
+    dQ, dK, dV, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], c["logg"],
+                                     c["scale"], c["block"])
+    Oa, dQa, dKa, dVa, dlg, _ = _autograd_gated(c)
+    np.testing.assert_allclose(O, Oa, rtol=RTOL, atol=1e-12)
+    np.testing.assert_allclose(dQ, dQa, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dK, dKa, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dV, dVa, rtol=1e-9, atol=1e-11)
+    valid = np.arange(c["idx"].shape[-1])[None, None, None, :] < c["cnt"][..., None]
+    ref_dg = np.where(valid, dlg / np.exp(c["logg"]), 0.0)
+    np.testing.assert_allclose(dg, ref_dg, rtol=1e-9, atol=1e-11)
+
+
+# ------------------------------------------------------------------ P-c: shift invariance
+
+def test_pc_global_shift_of_scores():
+    """g = softmax(s) is invariant to a global shift of s (SAS summary, section
+    무엇과 다른가, choice 2). Scores on a dyadic grid make s + 8 exact in fp32."""
+    g = np.random.default_rng(4)
+    s = (np.round(g.standard_normal((1, 2, 12, 12)) * 1024) / 1024).astype(np.float32)
+    s2 = (s + np.float32(8.0)).astype(np.float32)
+    assert np.all((s2 - np.float32(8.0)) == s)
+    a = oracle.select_prefill(s, 4)
+    b = oracle.select_prefill(s2, 4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    np.testing.assert_allclose(a[3], b[3], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(a[2] + 8.0, b[2], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P-d: finite differences
+
+def test_pd_finite_differences():
+    """Central differences of L = sum(dO * O) in float64 against the analytic dQ, dK, dV
+    and dg of the oracle (dg is the derivative with respect to g itself)."""
+    c = _rand_case(B=1, Hq=2, Hkv=1, n=64, d=8, block=8, topk=2, seed=5)
+    args = (c["idx"], c["cnt"])
+
+    def loss(Q, K, V, logg):
+        O, _ = oracle.attn_fwd(Q, K, V, *args, logg, c["scale"], c["block"])
+        return float(np.sum(c["dO"] * O))
+
+    dQ, dK, dV, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], *args, c["logg"], c["scale"], c["block"])
+    h = 1e-6
+    g = np.random.default_rng(6)
+    for name, X, dX in (("Q", c["Q"], dQ), ("K", c["K"], dK), ("V", c["V"], dV)):
+        for _ in range(12):
+            pos = tuple(int(g.integers(0, s)) for s in X.shape)
+            Xp = X.copy(); Xp[pos] += h
+            Xm = X.copy(); Xm[pos] -= h
+            kw = dict(Q=c["Q"], K=c["K"], V=c["V"], logg=c["logg"])
+            kw[name] = Xp
+            lp = loss(**kw)
+            kw[name] = Xm
+            lm = loss(**kw)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - dX[pos]) <= 1e-6 * max(1.0, abs(dX[pos])), (name, pos, fd, dX[pos])
+    NB = c["idx"].shape[2]
+    for j in range(1, NB):
+        for t in range(int(c["cnt"][0, 0, j])):
+            gv = math.exp(c["logg"][0, 0, j, t])
+            lp_ = c["logg"].copy(); lp_[0, 0, j, t] = math.log(gv + h)
+            lm_ = c["logg"].copy(); lm_[0, 0, j, t] = math.log(gv - h)
+            fd = (loss(c["Q"], c["K"], c["V"], lp_) - loss(c["Q"], c["K"], c["V"], lm_)) / (2 * h)
+            assert abs(fd - dg[0, 0, j, t]) <= 1e-6 * max(1.0, abs(fd)), (j, t, fd, dg[0, 0, j, t])
+
+
+# ------------------------------------------------------------------ P-e: brute-force Top-K
+
+def _brute_topk(s, k):
+    """Enumerate every k-subset; the Top-K set is the one whose members, ordered by
+    (score descending, index ascending), form the lexicographically smallest key list."""
+    s = [(-math.inf if math.isnan(x) else float(x)) for x in s]
+    best, best_key = None, None
+    for sub in itertools.combinations(range(len(s)), k):
+        key = sorted((-s[m], m) for m in sub)
+        if best_key is None or key < best_key:
+            best, best_key = sub, key
+    return list(sub if best is None else best)
+
+
+def test_pe_bruteforce_topk():
+    g = np.random.default_rng(7)
+    rows = []
+    for _ in range(60):
+        C = int(g.integers(0, 10))
+        rows.append(g.standard_normal(C).astype(np.float32))
+    for _ in range(60):     # heavy ties pin the lowest-index rule
+        C = int(g.integers(1, 10))
+        rows.append(g.integers(-2, 3, C).astype(np.float32))
+    rows.append(np.array([0.0, -0.0, 0.0, -0.0, 1.0], np.float32))
+    rows.append(np.array([-np.inf, np.nan, -np.inf, 2.0, np.nan], np.float32))
+    rows.append(np.array([np.nan, np.nan, np.nan], np.float32))
+    rows.append(np.array([-np.inf, -np.inf, 0.5, -np.inf], np.float32))
+    for row in rows:
+        for k in range(0, len(row) + 2):
+            got = list(oracle.row_topk(row, k))
+            want = sorted(_brute_topk(row, min(k, len(row))))
+            assert got == want, (row, k, got, want)
+
+
+def test_pe_select_padding_and_counts():
+    s = np.random.default_rng(8).standard_normal((1, 1, 8, 8)).astype(np.float32)
+    idx, cnt, lse, logg = oracle.select_prefill(s, 3)
+    assert list(cnt[0, 0]) == [0, 1, 2, 3, 3, 3, 3, 3]
+    for j in range(8):
+        k = cnt[0, 0, j]
+        assert np.all(idx[0, 0, j, k:] == -1) and np.all(logg[0, 0, j, k:] == 0)
+        assert np.all(np.diff(idx[0, 0, j, :k]) > 0)
+        assert np.all(idx[0, 0, j, :k] < j)
+
+
+# ------------------------------------------------------------------ P-f: invariants
+
+def test_pf_gate_and_current_block_balance():
+    """Scaling every gate of a row, the current block's included, adds one constant to
+    all of that row's logits and leaves the output unchanged, so
+    sum_m g_m dg_m + dL/d(log g0) = 0 per (KV head, query block)."""
+    c = _rand_case(B=1, Hq=4, Hkv=2, n=96, d=8, block=16, topk=2, seed=9)
+    _, _, _, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], c["logg"],
+                                  c["scale"], c["block"])
+    *_, dl0 = _autograd_gated(c)
+    tot = np.sum(np.exp(c["logg"]) * dg * (np.arange(dg.shape[-1]) < c["cnt"][..., None]), -1) + dl0
+    assert np.max(np.abs(tot)) < 1e-11
+
+
+def test_pf_observable_sums():
+    """Invariants usable on full-size outputs: shifting all keys of a KV head by one
+    vector leaves every row's softmax unchanged (sum_i dK_i = 0); shifting all values by c
+    shifts every output by c (sum_i dV_i = sum over the group's rows of dO)."""
+    c = _rand_case(B=1, Hq=4, Hkv=2, n=128, d=8, block=16, topk=2, seed=10)
+    dQ, dK, dV, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], c["logg"],
+                                     c["scale"], c["block"])
+    np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-11)
+    np.testing.assert_allclose(dV.sum(axis=2), c["dO"].reshape(1, 2, 2, 128, 8).sum(axis=(2, 3)), atol=1e-11)
+
+
+# ------------------------------------------------------------------ P-g: closed forms
+
+def test_pg_gate_closed_forms():
+    s = np.zeros((1, 1, 9, 9), np.float32)
+    idx, cnt, lse, logg = oracle.select_prefill(s, 9, full_scope=True)
+    for j in range(1, 9):
+        np.testing.assert_allclose(logg[0, 0, j, :j], -math.log(j), atol=1e-15)
+        assert abs(lse[0, 0, j] - math.log(j)) < 1e-15
+    assert lse[0, 0, 0] == -np.inf and cnt[0, 0, 0] == 0
+    # sparse scope: the gate softmax still runs over every history block (uniform
+    # scores give log g = -log j however few blocks are kept)
+    idx, cnt, lse, logg = oracle.select_prefill(s, 2)
+    for j in range(2, 9):
+        np.testing.assert_allclose(logg[0, 0, j, :2], -math.log(j), atol=1e-15)
+        assert list(idx[0, 0, j, :2]) == [0, 1]
+    g = np.random.default_rng(11)
+    s = g.standard_normal((1, 1, 20, 20)).astype(np.float32)
+    _, _, _, logg = oracle.select_prefill(s, 19, full_scope=True)
+    for j in range(1, 20):
+        assert abs(np.exp(logg[0, 0, j, :j]).sum() - 1.0) < 1e-14
+    assert logg[0, 0, 1, 0] == 0.0        # a single history block has gate 1
+
+
+def test_pg_zero_query_closed_form():
+    """With q = 0 every logit is its log-gate, so the output is the gate-weighted mean
+    of the attended values: o_t = (sum_{i<=t in B_j} v_i + sum_m g_m sum_{i in B_m} v_i)
+    / ((t - j b + 1) + b sum_m g_m), and LSE_t is the log of that denominator."""
+    c = _rand_case(B=1, Hq=1, Hkv=1, n=64, d=4, block=8, topk=3, seed=12)
+    Q0 = np.zeros_like(c["Q"])
+    O, LSE = oracle.attn_fwd(Q0, c["K"], c["V"], c["idx"], c["cnt"], c["logg"], c["scale"], 8)
+    V = c["V"][0, 0]
+    for t in range(64):
+        j = t // 8
+        gs = np.exp(c["logg"][0, 0, j, : c["cnt"][0, 0, j]])
+        ms = c["idx"][0, 0, j, : c["cnt"][0, 0, j]]
+        num = V[j * 8: t + 1].sum(0) + sum(gm * V[m * 8: (m + 1) * 8].sum(0) for gm, m in zip(gs, ms))
+        den = (t - j * 8 + 1) + 8 * gs.sum()
+        np.testing.assert_allclose(O[0, 0, t], num / den, rtol=1e-13, atol=1e-14)
+        assert abs(LSE[0, 0, t] - math.log(den)) < 1e-13
+
+
+def test_pg_first_block_is_plain_causal():
+    c = _rand_case(B=1, Hq=2, Hkv=1, n=64, d=8, block=16, topk=2, seed=13)
+    O, _ = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], c["logg"], c["scale"], 16)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(c["Q"][:, :, :16]), torch.tensor(c["K"][:, :, :16]).expand(1, 2, 16, 8),
+        torch.tensor(c["V"][:, :, :16]).expand(1, 2, 16, 8), is_causal=True, scale=c["scale"])
+    np.testing.assert_allclose(O[:, :, :16], ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ P-h: decode consistency
+
+def test_ph_decode_ungated_is_sdpa_over_gathered_keys():
+    g = np.random.default_rng(14)
+    B, Hq, Hkv, d, blk, Lmax = 3, 4, 2, 8, 8, 80
+    q = g.standard_normal((B, Hq, d))
+    Kc = g.standard_normal((B, Hkv, Lmax, d))
+    Vc = g.standard_normal((B, Hkv, Lmax, d))
+    kv_len = np.array([80, 41, 9])
+    C = oracle.decode_rows_valid(kv_len, blk)
+    s = g.standard_normal((B, Hkv, Lmax // blk)).astype(np.float32)
+    valid = np.repeat(C, Hkv)
+    idx, cnt, _, logg = oracle.select(s.reshape(B * Hkv, -1), valid, 3, kcap=3)
+    idx = idx.reshape(B, Hkv, 3); cnt = cnt.reshape(B, Hkv)
+    o = oracle.decode(q, Kc, Vc, kv_len, idx, cnt, 1 / math.sqrt(d), blk)
+    for b in range(B):
+        L = kv_len[b]
+        for h in range(Hkv):
+            toks = list(range(((L - 1) // blk) * blk, L))
+            for t in range(cnt[b, h]):
+                toks += list(range(idx[b, h, t] * blk, (idx[b, h, t] + 1) * blk))
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.tensor(q[b, h * 2: h * 2 + 2, None]), torch.tensor(Kc[b, h, toks]).expand(2, -1, -1),
+                torch.tensor(Vc[b, h, toks]).expand(2, -1, -1), scale=1 / math.sqrt(d))
+            np.testing.assert_allclose(o[b, h * 2: h * 2 + 2], ref.numpy()[:, 0], rtol=1e-12, atol=1e-13)
+
+
+def test_ph_gated_decode_equals_training_row():
+    """Gated decode at kv_len = L reproduces the training forward's output at position
+    L - 1 when both use the same selection and log-gates."""
+    c = _rand_case(B=1, Hq=2, Hkv=1, n=64, d=8, block=8, topk=3, seed=15)
+    O, _ = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], c["logg"], c["scale"], 8)
+    for L in (64, 57, 41):
+        j = (L - 1) // 8
+        q = c["Q"][:, :, L - 1]
+        o = oracle.decode(q, c["K"], c["V"], np.array([L]), c["idx"][:, :, j], c["cnt"][:, :, j],
+                          c["scale"], 8, logg=c["logg"][:, :, j])
+        # the training row at L-1 attends causally up to L-1 in its own block
+        np.testing.assert_allclose(o, O[:, :, L - 1], rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------------ generator sanity
+
+def test_synth_bf16_rounding_and_determinism():
+    x = np.array([1.0, 1.00390625, 1.005859375, -2.5, 3.0e38, 1e-40], np.float32)
+    b = synth.f32_to_bf16_bits(x)
+    back = synth.bf16_bits_to_f32(b)
+    ref = torch.tensor(x).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(back, ref)
+    a1 = synth.normal_bf16((1, 2, 8, 4), 0, synth.TID_Q)
+    a2 = synth.normal_bf16((1, 2, 8, 4), 0, synth.TID_Q)
+    assert np.array_equal(a1, a2)
+    assert np.array_equal(synth.normal_bf16_slice((1, 2, 8, 4), 0, synth.TID_Q, 0, 1), a1[0, 1])
+    z = synth.scores_zipf(1, 2, 16, 0)
+    p = synth.scores_planted(1, 2, 16, 0)
+    assert z.shape == p.shape == (1, 2, 16, 16) and z.dtype == np.float32
