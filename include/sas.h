@@ -1,0 +1,194 @@
+/*
+ * sas.h - C ABI of the MI355X (gfx950) library for SAS log-gated block-sparse attention.
+ *
+ * The method (sources are cited by page title and section):
+ *   [SAS-ja] "論文解説: SAS — 疎注意の「どのブロックを読むか」を言語モデル損失で端から端まで学習する"
+ *            (ta-paperlens.web.app), sections "前提" (paper section 3) and "仕組み"
+ *            (paper sections 4.1, 4.3 eq. (9), Algorithm 2 / section 5.1).
+ *   [SAS-ko] "SAS는 언어모델 손실로 문맥 순위를 직접 학습하는 사후 어텐션 희소화다"
+ *            (onedev.kr/papers/5), sections "어떻게 동작하나" and "무엇과 다른가" (choices 1, 2, 4).
+ *
+ * A sequence of n tokens is cut into NB = n / 64 blocks. For query block j the history is
+ * blocks 0..j-1, scored by s[j][m]. Gates g = softmax(s) over that history; the current
+ * block j has gate 1 and a causal mask. The K highest scores pick the history blocks
+ * attended; log g of each picked block is added to every logit of its tokens, and the
+ * softmax runs over the current block plus the picked blocks. Inference (decode) uses the
+ * same Top-K but no gates.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library never
+ *     allocates, frees or synchronises. Work is enqueued on `stream` (a hipStream_t passed
+ *     as void*, NULL = the null stream) and the call returns without waiting.
+ *   - Layouts are row-major and contiguous: Q/O/dO [B][Hq][n][d], K/V [B][Hkv][n][d]
+ *     (d innermost), so one 64-token block of one KV head is one contiguous run.
+ *     Query head hq uses KV head hq / (Hq / Hkv).
+ *   - bf16 tensors are passed as void*; they hold IEEE bfloat16 bit patterns.
+ *   - Arguments are checked on the host before anything is enqueued. A failed check
+ *     returns a status code with nothing enqueued; sas_last_error() then describes it.
+ *     A launch failure returns SAS_ERR_HIP. Faults inside kernels are asynchronous and
+ *     surface at the caller's next synchronisation.
+ *   - Supported: block == 64, d in {64, 128}, Hq % Hkv == 0, pointers 16-byte aligned.
+ *   - Entry points are thread-safe; the library keeps no state between calls except a
+ *     thread-local error string.
+ */
+#ifndef SAS_H
+#define SAS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SAS_OK = 0,
+    SAS_ERR_INVALID_ARG = 1,   /* a pointer, size or value is out of its documented range */
+    SAS_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels implement            */
+    SAS_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the size query says   */
+    SAS_ERR_HIP = 4            /* a HIP runtime call or launch failed                      */
+} sas_status;
+
+typedef enum {
+    SAS_SCOPE_SPARSE = 0,      /* keep min(topk, C_j) blocks ([SAS-ko] choice 4, sparse)  */
+    SAS_SCOPE_FULL = 1         /* keep every history block ([SAS-ko] choice 4, full)      */
+} sas_scope;
+
+typedef enum {
+    SAS_ROWS_PREFILL = 0,      /* s[B][H][rows][ld]; row j (query block j) has j valid
+                                  history scores in columns 0..j-1                         */
+    SAS_ROWS_DECODE = 1        /* s[B][H][rows][ld]; every row of batch entry b has
+                                  row_valid[b] valid history scores                       */
+} sas_rows;
+
+/* Library version string, e.g. "sas-mi355x 0.1.0 gfx950". */
+const char* sas_version(void);
+
+/* Human-readable name of a status code. */
+const char* sas_status_string(sas_status status);
+
+/* Detail of the last failed call on this thread ("" if none). */
+const char* sas_last_error(void);
+
+/*
+ * sas_gates - gate normalisation of history scores.
+ * [SAS-ko] "무엇과 다른가", choice 2: g = softmax(s), log g_m = s_m - LSE(s) over every valid
+ * history block of the row; [SAS-ja] "仕組み": the current block's gate is fixed at 1 and is
+ * not part of s.
+ *
+ *   s          fp32 [B][H][rows][ld], device; only the valid columns of each row are read.
+ *   B, H, rows number of batch entries, heads and score rows per head (rows >= 1).
+ *   cols       columns per row that may be valid (1 <= cols <= ld, cols <= 8192).
+ *              PREFILL requires cols >= rows - 1.
+ *   mode       sas_rows; PREFILL: row j has j valid scores. DECODE: row_valid[b] valid
+ *              scores for every row of batch entry b (values are clamped to [0, cols]).
+ *   row_valid  int32 [B], device; required for DECODE, must be NULL for PREFILL.
+ *   lse        fp32 [B][H][rows], device, out: LSE of the valid scores (-inf if none).
+ *   g          fp32 [B][H][rows][ld], device, out, nullable: g_m = exp(s_m - LSE) for valid
+ *              columns, 0 for columns valid..cols-1; columns >= cols are not written.
+ * NaN scores are read as -inf (gate 0).
+ */
+sas_status sas_gates(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                     const int32_t* row_valid, float* lse, float* g, void* stream);
+
+/*
+ * sas_topk_select - softmax gates plus Top-K history-block selection, one row per
+ * (batch, head, query block).
+ * [SAS-ja] "前提": the selector's K best blocks form the attended set S = B_0 U (U_{m in I} B_m);
+ * "仕組み" (Algorithm 2): inference takes the Top-K of s itself; [SAS-ko] choice 2 for the
+ * log-gates; choice 4 for the scope.
+ *
+ * Same s/B/H/rows/cols/ld/mode/row_valid arguments as sas_gates, and:
+ *   topk   budget K >= 0 in blocks (ignored for SAS_SCOPE_FULL).
+ *   scope  sas_scope. A row keeps k = min(topk, valid) blocks (SPARSE) or valid (FULL).
+ *   kcap   row stride of idx/logg; must be >= min(topk, V) (SPARSE) or >= V (FULL), where
+ *          V = min(cols, rows - 1) in PREFILL mode and V = cols in DECODE mode.
+ *   idx    int32 [B][H][rows][kcap], out: the kept block indices in ascending order,
+ *          padded with -1. Ties in s go to the lower block index; -0 equals +0; NaN ranks
+ *          as -inf. The comparison uses the fp32 scores, so the result is exact.
+ *   cnt    int32 [B][H][rows], out: k.
+ *   lse    fp32 [B][H][rows], out, nullable: LSE of the row's valid scores.
+ *   logg   fp32 [B][H][rows][kcap], out, nullable: s_m - LSE for each kept block, 0 pad.
+ */
+sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                           const int32_t* row_valid, int topk, int scope, int kcap,
+                           int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream);
+
+/*
+ * sas_attn_fwd - log-gated block-sparse attention forward.
+ * [SAS-ja] "仕組み", eq. (9) / [SAS-ko] "어떻게 동작하나": o = softmax(scale q K_S^T + log g_S) V_S
+ * with S = the current block (causal, gate 1) plus the blocks in idx, log g broadcast to
+ * every token of its block. scale multiplies q.k only; log g is added unscaled.
+ *
+ *   Q        bf16 [B][Hq][n][d]; K, V bf16 [B][Hkv][n][d].
+ *   idx, cnt, logg  as written by sas_topk_select with rows = n / 64, laid out
+ *            [B][Hkv][n/64][kcap] and [B][Hkv][n/64]. Rows must hold distinct blocks < j;
+ *            entries outside [0, j) are ignored. cnt is clamped to [0, min(kcap, j)].
+ *            logg may be NULL: every kept block then has gate 1 (ungated sparse attention).
+ *   n        multiple of 64.  d in {64, 128}.  block must be 64.  kcap >= 0.
+ *   scale    finite, > 0 (typically 1/sqrt(d)).
+ *   O        bf16 [B][Hq][n][d], out.
+ *   lse_rows fp32 [B][Hq][n], out: natural-log softmax normaliser of each query row (the
+ *            backward needs it).
+ */
+sas_status sas_attn_fwd(const void* Q, const void* K, const void* V, const int32_t* idx,
+                        const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
+                        int d, int block, int kcap, float scale, void* O, float* lse_rows,
+                        void* stream);
+
+/* Bytes of device workspace sas_attn_bwd needs for these sizes (0 on invalid sizes). */
+size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int block, int kcap);
+
+/*
+ * sas_attn_bwd - backward of sas_attn_fwd, with the gate gradient.
+ * Content gradients are those of softmax attention over S (only attended keys receive
+ * gradient: [SAS-ko] choice 4, sparse scope). The gate gradient follows [SAS-ko] choice 1:
+ * dg_jm = sum over the G*64 query rows t of KV head h's group in block j and keys i of
+ * block m of (p~_ti / g_jm) dO_t.(v_i - o_t), i.e. the derivative with respect to g_jm.
+ *
+ *   Q, K, V, idx, cnt, logg, sizes, scale: exactly as passed to sas_attn_fwd.
+ *   O, lse_rows  the forward's outputs. dO bf16 [B][Hq][n][d].
+ *   idx rows must be ascending (as sas_topk_select writes them).
+ *   dQ fp32 [B][Hq][n][d], dK, dV fp32 [B][Hkv][n][d], out (overwritten, not accumulated).
+ *   dg fp32 [B][Hkv][n/64][kcap], out: aligned with idx, 0 on padding slots.
+ *   ws, ws_bytes  device workspace of at least sas_attn_bwd_workspace_size() bytes,
+ *            16-byte aligned; its contents need no initialisation.
+ */
+sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* lse_rows, const int32_t* idx,
+                        const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
+                        int d, int block, int kcap, float scale, float* dQ, float* dK,
+                        float* dV, float* dg, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace sas_decode needs for these sizes (0 on invalid sizes). */
+size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap);
+
+/*
+ * sas_decode - one decode step in the inference form ([SAS-ja] "仕組み", Algorithm 2 /
+ * section 5.1): ungated sparse attention of each new query token over its current block
+ * plus the Top-K blocks chosen by sas_topk_select (mode DECODE, rows = 1,
+ * row_valid[b] = (kv_len[b] - 1) / 64).
+ *
+ *   q        bf16 [B][Hq][d]: the new token's queries.
+ *   Kc, Vc   bf16 [B][Hkv][Lmax][d]: the caches, already holding the new token's K/V.
+ *   kv_len   int32 [B], device: tokens in each cache (1 <= kv_len <= Lmax, clamped). The
+ *            query is token kv_len - 1; its current block is tokens
+ *            [64 * floor((kv_len - 1) / 64), kv_len).
+ *   idx, cnt int32 [B][Hkv][kcap] and [B][Hkv] from sas_topk_select; entries outside
+ *            [0, (kv_len - 1) / 64) are ignored.
+ *   logg     fp32 [B][Hkv][kcap] or NULL. NULL is the inference form (no gates); a non-NULL
+ *            pointer adds the log-gates as in training (useful to check decode against the
+ *            training forward).
+ *   o        bf16 [B][Hq][d], out.
+ *   ws       workspace of sas_decode_workspace_size() bytes, 16-byte aligned.
+ */
+sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                      int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
+                      int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
+                      void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAS_H */

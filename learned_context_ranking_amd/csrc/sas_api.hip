@@ -1,0 +1,210 @@
+// C ABI host layer: argument checks, workspace carving and kernel launches.
+// Every check runs before any HIP call, so a rejected call enqueues nothing and touches
+// no device state (the checks also run on machines without a GPU).
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/sas.h"
+#include "sas_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sas_status fail(sas_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sas_status ok() {
+  g_last_error.clear();
+  return SAS_OK;
+}
+
+sas_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SAS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...)                   \
+  do {                                             \
+    if (!(cond)) return fail(code, __VA_ARGS__);   \
+  } while (0)
+
+sas_status check_rows(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                      const int32_t* row_valid) {
+  REQUIRE(s != nullptr, SAS_ERR_INVALID_ARG, "s is NULL");
+  REQUIRE(B > 0 && H > 0 && rows > 0, SAS_ERR_INVALID_ARG, "B, H, rows must be > 0 (got %d, %d, %d)", B, H, rows);
+  REQUIRE(cols > 0 && cols <= ld, SAS_ERR_INVALID_ARG, "need 0 < cols <= ld (got cols=%d ld=%d)", cols, ld);
+  REQUIRE(cols <= 8192, SAS_ERR_UNSUPPORTED, "cols=%d exceeds 8192", cols);
+  REQUIRE(mode == SAS_ROWS_PREFILL || mode == SAS_ROWS_DECODE, SAS_ERR_INVALID_ARG, "bad mode %d", mode);
+  if (mode == SAS_ROWS_PREFILL) {
+    REQUIRE(row_valid == nullptr, SAS_ERR_INVALID_ARG, "row_valid must be NULL in PREFILL mode");
+    REQUIRE(cols >= rows - 1, SAS_ERR_INVALID_ARG, "PREFILL needs cols >= rows - 1 (cols=%d rows=%d)", cols, rows);
+  } else {
+    REQUIRE(row_valid != nullptr, SAS_ERR_INVALID_ARG, "row_valid is required in DECODE mode");
+  }
+  REQUIRE((long long)B * H * rows < (1ll << 31), SAS_ERR_UNSUPPORTED, "too many rows");
+  return SAS_OK;
+}
+
+sas_status check_attn(const void* Q, const void* K, const void* V, const int32_t* idx,
+                      const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
+                      int d, int block, int kcap, float scale) {
+  REQUIRE(Q && K && V, SAS_ERR_INVALID_ARG, "Q, K and V must be non-NULL");
+  REQUIRE(cnt != nullptr, SAS_ERR_INVALID_ARG, "cnt is NULL");
+  REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
+  REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && n > 0, SAS_ERR_INVALID_ARG, "B, Hq, Hkv, n must be > 0");
+  REQUIRE(Hq % Hkv == 0, SAS_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  REQUIRE(block == 64, SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+  REQUIRE(n % 64 == 0, SAS_ERR_INVALID_ARG, "n=%d is not a multiple of 64", n);
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);
+  REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  REQUIRE(aligned16(Q) && aligned16(K) && aligned16(V), SAS_ERR_INVALID_ARG, "Q, K, V must be 16-byte aligned");
+  REQUIRE((long long)B * Hq * n * d < (1ll << 40), SAS_ERR_UNSUPPORTED, "tensor too large");
+  REQUIRE((long long)B * Hkv * (n / 64) < (1ll << 31) / 4, SAS_ERR_UNSUPPORTED, "too many blocks");
+  REQUIRE((long long)(n / 64) * (kcap > 0 ? kcap : 1) < (1ll << 31), SAS_ERR_UNSUPPORTED, "n/64 * kcap too large");
+  (void)logg;
+  return SAS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sas_version(void) { return "sas-mi355x 0.1.0 gfx950"; }
+
+const char* sas_status_string(sas_status st) {
+  switch (st) {
+    case SAS_OK: return "SAS_OK";
+    case SAS_ERR_INVALID_ARG: return "SAS_ERR_INVALID_ARG";
+    case SAS_ERR_UNSUPPORTED: return "SAS_ERR_UNSUPPORTED";
+    case SAS_ERR_WORKSPACE: return "SAS_ERR_WORKSPACE";
+    case SAS_ERR_HIP: return "SAS_ERR_HIP";
+  }
+  return "SAS_ERR_UNKNOWN";
+}
+
+const char* sas_last_error(void) { return g_last_error.c_str(); }
+
+sas_status sas_gates(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                     const int32_t* row_valid, float* lse, float* g, void* stream) {
+  sas_status st = check_rows(s, B, H, rows, cols, ld, mode, row_valid);
+  if (st != SAS_OK) return st;
+  REQUIRE(lse != nullptr, SAS_ERR_INVALID_ARG, "lse is NULL");
+  sas::SelectArgs a{};
+  a.s = s; a.R = (long long)B * H * rows; a.H = H; a.rows = rows; a.cols = cols; a.ld = ld;
+  a.mode = mode; a.row_valid = row_valid; a.do_select = 0; a.lse = lse; a.g = g;
+  return hip_result(sas::launch_select(a, (hipStream_t)stream), "sas_gates launch");
+}
+
+sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                           const int32_t* row_valid, int topk, int scope, int kcap,
+                           int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream) {
+  sas_status st = check_rows(s, B, H, rows, cols, ld, mode, row_valid);
+  if (st != SAS_OK) return st;
+  REQUIRE(scope == SAS_SCOPE_SPARSE || scope == SAS_SCOPE_FULL, SAS_ERR_INVALID_ARG, "bad scope %d", scope);
+  REQUIRE(topk >= 0, SAS_ERR_INVALID_ARG, "topk=%d < 0", topk);
+  REQUIRE(cnt != nullptr, SAS_ERR_INVALID_ARG, "cnt is NULL");
+  // most history blocks any row can have: rows - 1 in PREFILL (row j has j), cols in DECODE
+  const int maxvalid = mode == SAS_ROWS_PREFILL ? (rows - 1 < cols ? rows - 1 : cols) : cols;
+  const int need = scope == SAS_SCOPE_FULL ? maxvalid : (topk < maxvalid ? topk : maxvalid);
+  REQUIRE(kcap >= need, SAS_ERR_INVALID_ARG, "kcap=%d < %d blocks a row may keep", kcap, need);
+  REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
+  sas::SelectArgs a{};
+  a.s = s; a.R = (long long)B * H * rows; a.H = H; a.rows = rows; a.cols = cols; a.ld = ld;
+  a.mode = mode; a.row_valid = row_valid; a.topk = topk; a.full = scope == SAS_SCOPE_FULL;
+  a.kcap = kcap; a.do_select = 1; a.idx = idx; a.cnt = cnt; a.lse = lse; a.logg = logg;
+  return hip_result(sas::launch_select(a, (hipStream_t)stream), "sas_topk_select launch");
+}
+
+sas_status sas_attn_fwd(const void* Q, const void* K, const void* V, const int32_t* idx,
+                        const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
+                        int d, int block, int kcap, float scale, void* O, float* lse_rows,
+                        void* stream) {
+  sas_status st = check_attn(Q, K, V, idx, cnt, logg, B, Hq, Hkv, n, d, block, kcap, scale);
+  if (st != SAS_OK) return st;
+  REQUIRE(O != nullptr && lse_rows != nullptr, SAS_ERR_INVALID_ARG, "O and lse_rows must be non-NULL");
+  REQUIRE(aligned16(O), SAS_ERR_INVALID_ARG, "O must be 16-byte aligned");
+  sas::AttnArgs a{};
+  a.Q = (const uint16_t*)Q; a.K = (const uint16_t*)K; a.V = (const uint16_t*)V;
+  a.idx = idx; a.cnt = cnt; a.logg = logg;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.Oout = (uint16_t*)O; a.lse_rows = lse_rows;
+  return hip_result(sas::launch_fwd(a, (hipStream_t)stream), "sas_attn_fwd launch");
+}
+
+size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int block, int kcap) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || n <= 0 || block != 64 || n % 64 != 0 || kcap < 0) return 0;
+  if (Hq % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  return sas::bwd_workspace_bytes(B, Hq, Hkv, n, d, kcap);
+}
+
+sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* lse_rows, const int32_t* idx,
+                        const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
+                        int d, int block, int kcap, float scale, float* dQ, float* dK,
+                        float* dV, float* dg, void* ws, size_t ws_bytes, void* stream) {
+  sas_status st = check_attn(Q, K, V, idx, cnt, logg, B, Hq, Hkv, n, d, block, kcap, scale);
+  if (st != SAS_OK) return st;
+  REQUIRE(O && dO && lse_rows, SAS_ERR_INVALID_ARG, "O, dO and lse_rows must be non-NULL");
+  REQUIRE(dQ && dK && dV, SAS_ERR_INVALID_ARG, "dQ, dK and dV must be non-NULL");
+  REQUIRE(kcap == 0 || dg != nullptr, SAS_ERR_INVALID_ARG, "dg is NULL");
+  REQUIRE(aligned16(O) && aligned16(dO) && aligned16(dQ) && aligned16(dK) && aligned16(dV),
+          SAS_ERR_INVALID_ARG, "O, dO, dQ, dK, dV must be 16-byte aligned");
+  const size_t need = sas::bwd_workspace_bytes(B, Hq, Hkv, n, d, kcap);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  sas::AttnArgs a{};
+  a.Q = (const uint16_t*)Q; a.K = (const uint16_t*)K; a.V = (const uint16_t*)V;
+  a.O = (const uint16_t*)O; a.dO = (const uint16_t*)dO;
+  a.idx = idx; a.cnt = cnt; a.logg = logg;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.lse_rows = (float*)lse_rows; a.dQ = dQ; a.dK = dK; a.dV = dV; a.dg = dg;
+  return hip_result(sas::launch_bwd(a, ws, (hipStream_t)stream), "sas_attn_bwd launch");
+}
+
+size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || kcap < 0 || Hq % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  return sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
+}
+
+sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                      int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
+                      int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
+                      void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(q && Kc && Vc && kv_len && cnt && o, SAS_ERR_INVALID_ARG, "q, Kc, Vc, kv_len, cnt, o must be non-NULL");
+  REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
+  REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && Lmax > 0, SAS_ERR_INVALID_ARG, "B, Hq, Hkv, Lmax must be > 0");
+  REQUIRE(Hq % Hkv == 0, SAS_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  REQUIRE(G == 1 || G == 2 || G == 4 || G == 5 || G == 8, SAS_ERR_UNSUPPORTED, "decode supports Hq/Hkv in {1,2,4,5,8} (got %d)", G);
+  REQUIRE(block == 64, SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);
+  REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  REQUIRE(aligned16(q) && aligned16(Kc) && aligned16(Vc) && aligned16(o), SAS_ERR_INVALID_ARG,
+          "q, Kc, Vc, o must be 16-byte aligned");
+  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  sas::DecodeArgs a{};
+  a.q = (const uint16_t*)q; a.Kc = (const uint16_t*)Kc; a.Vc = (const uint16_t*)Vc;
+  a.kv_len = kv_len; a.Lmax = Lmax; a.idx = idx; a.cnt = cnt; a.logg = logg;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.o = (uint16_t*)o; a.part = (float*)ws;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal launch interface between the C ABI host layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sas {
+
+struct SelectArgs {
+  const float* s;
+  long long R;          // rows in total = B * H * rows
+  int H, rows, cols;
+  long long ld;
+  int mode;             // 0 prefill, 1 decode
+  const int32_t* row_valid;
+  int topk, full, kcap, do_select;
+  int32_t* idx;
+  int32_t* cnt;
+  float* lse;
+  float* logg;
+  float* g;
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t st);
+
+struct AttnArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  const uint16_t* O;     // backward only
+  const uint16_t* dO;    // backward only
+  const int32_t* idx;
+  const int32_t* cnt;
+  const float* logg;     // may be null
+  int B, Hq, Hkv, n, d, kcap;
+  float scale;
+  uint16_t* Oout;        // forward output
+  float* lse_rows;       // forward output / backward input
+  float* dQ;
+  float* dK;
+  float* dV;
+  float* dg;
+  // backward workspace pieces
+  float* delta;
+  int32_t* inv_cnt;
+  int32_t* inv_off;
+  int32_t* inv_list;
+};
+hipError_t launch_fwd(const AttnArgs& a, hipStream_t st);
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap);
+hipError_t launch_bwd(AttnArgs a, void* ws, hipStream_t st);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* Kc;
+  const uint16_t* Vc;
+  const int32_t* kv_len;
+  long long Lmax;
+  const int32_t* idx;
+  const int32_t* cnt;
+  const float* logg;
+  int B, Hq, Hkv, d, kcap;
+  float scale;
+  uint16_t* o;
+  float* part;           // workspace: partial (m, l, acc) per chunk
+  int bpc;               // blocks per chunk
+  int nchunk;            // chunks per (b, h_kv) = ceil((kcap + 1) / bpc)
+};
+size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap);
+hipError_t launch_decode(DecodeArgs a, hipStream_t st);
+
+}  // namespace sas

@@ -1,0 +1,136 @@
+// Gate normalisation and Top-K block selection, one wavefront per score row.
+//
+// [SAS-ko] "무엇과 다른가", choice 2: g = softmax(s) over the row's valid history blocks,
+// log g_m = s_m - LSE(s). [SAS-ja] "前提" / "仕組み" (Algorithm 2): the K best-scoring
+// history blocks are attended. Selection compares the fp32 scores themselves; ties go to
+// the lower block index, -0 equals +0 and NaN ranks as -inf.
+//
+// Each lane holds PL scores (element m = lane + 64 i, so loads are coalesced). The K-th
+// largest order-preserving key is found by fixing its 32 bits from the top: a candidate
+// bit stays set when at least K keys are >= the candidate, counted with one ballot per
+// register. Blocks strictly above the threshold are kept; among the blocks equal to it the
+// lowest indices fill the remaining places. A ballot prefix count writes the kept indices
+// in ascending order without any sort.
+#include "sas_common.h"
+#include "sas_kernels.h"
+
+namespace sas {
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int PL>
+__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.R) return;  // uniform per wave
+  int valid;
+  if (a.mode == 0) {
+    valid = (int)(row % a.rows);
+  } else {
+    const long long b = row / ((long long)a.H * a.rows);
+    valid = a.row_valid[b];
+  }
+  valid = min(max(valid, 0), a.cols);
+  const float* srow = a.s + row * a.ld;
+
+  float x[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int m = lane + 64 * i;
+    float v = -INFINITY;
+    if (m < valid) {
+      v = srow[m];
+      if (v != v) v = -INFINITY;  // NaN ranks as -inf
+      if (v == 0.0f) v = 0.0f;    // -0 -> +0
+    }
+    x[i] = v;
+  }
+
+  // LSE over the valid scores.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) mx = fmaxf(mx, x[i]);
+  mx = wave_max(mx);
+  float lse = -INFINITY;
+  if (mx != -INFINITY) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) sum += expf(x[i] - mx);
+    sum = wave_sum(sum);
+    lse = mx + logf(sum);
+  }
+  if (a.lse != nullptr && lane == 0) a.lse[row] = lse;
+  if (a.g != nullptr) {
+    float* grow = a.g + row * a.ld;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int m = lane + 64 * i;
+      if (m < a.cols) grow[m] = (m < valid && lse != -INFINITY) ? expf(x[i] - lse) : 0.0f;
+    }
+  }
+  if (!a.do_select) return;
+
+  const int k = a.full ? valid : min(a.topk, valid);
+  int32_t* idx_row = a.idx + row * a.kcap;
+  float* lg_row = a.logg != nullptr ? a.logg + row * a.kcap : nullptr;
+  if (k > 0) {
+    uint32_t key[PL];
+#pragma unroll
+    for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i < valid) ? order_key(x[i]) : 0u;
+    // Valid keys are >= order_key(-inf) = 0x007FFFFF > 0, so padding (key 0) never reaches
+    // the threshold.
+    uint32_t T = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) c += __popcll(__ballot(key[i] >= cand));
+      if (c >= k) T = cand;
+    }
+    int n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) n_gt += __popcll(__ballot(key[i] > T));
+    const int need_eq = k - n_gt;
+    const unsigned long long lt = (1ull << lane) - 1ull;
+    int base = 0, eq_before = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const bool eq = key[i] == T;
+      const unsigned long long beq = __ballot(eq);
+      const int eq_rank = eq_before + __popcll(beq & lt);
+      const bool sel = key[i] > T || (eq && eq_rank < need_eq);
+      const unsigned long long bsel = __ballot(sel);
+      if (sel) {
+        const int pos = base + __popcll(bsel & lt);
+        idx_row[pos] = lane + 64 * i;
+        if (lg_row != nullptr) lg_row[pos] = (lse == -INFINITY) ? -INFINITY : x[i] - lse;
+      }
+      base += __popcll(bsel);
+      eq_before += __popcll(beq);
+    }
+  }
+  for (int p = k + lane; p < a.kcap; p += 64) {
+    idx_row[p] = -1;
+    if (lg_row != nullptr) lg_row[p] = 0.0f;
+  }
+  if (lane == 0) a.cnt[row] = k;
+}
+
+hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)((a.R + 3) / 4)), block(256);
+  const int c = a.cols;
+  if (c <= 64) hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, st, a);
+  else if (c <= 128) hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, st, a);
+  else if (c <= 256) hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, st, a);
+  else if (c <= 512) hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, st, a);
+  else if (c <= 1024) hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, st, a);
+  else if (c <= 2048) hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, st, a);
+  else if (c <= 4096) hipLaunchKernelGGL(select_kernel<64>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(select_kernel<128>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace sas

@@ -1,0 +1,206 @@
+"""ctypes binding of libsas.so (the C ABI declared in include/sas.h).
+
+Argument marshalling only: every computation runs in the library's HIP kernels. torch
+supplies device memory and the current HIP stream. Each function carries the name of
+the C entry point it calls, returns the output tensors, and raises SasError when the
+library rejects the call. There is no fallback: if libsas.so is missing or fails to load,
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsas.so")
+
+SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
+SCOPE = {"sparse": 0, "full": 1}
+ROWS = {"prefill": 0, "decode": 1}
+BLOCK = 64
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+SIGNATURES = {
+    "sas_version": ([], ctypes.c_char_p),
+    "sas_status_string": ([_I], ctypes.c_char_p),
+    "sas_last_error": ([], ctypes.c_char_p),
+    "sas_gates": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
+    "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
+    "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "sas_attn_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
+    "sas_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                      _P, _P, _P, _P, _P, _SZ, _P], _I),
+    "sas_decode_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
+    "sas_decode": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
+}
+
+
+class SasError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{status_string(status)}: {detail}")
+
+
+def lib():
+    """Load libsas.so once and declare the C signatures."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python -m learned_context_ranking_amd.build_lib)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return lib().sas_status_string(int(st)).decode()
+
+
+def version() -> str:
+    return lib().sas_version().decode()
+
+
+def _check(st):
+    if st != SAS_OK:
+        raise SasError(st, lib().sas_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ entry points
+
+def sas_gates(s, mode="prefill", row_valid=None, cols=None, want_g=False):
+    """s: fp32 [B, H, rows, ld]. Returns (lse [B, H, rows], g or None)."""
+    _need(s, torch.float32, "s")
+    B, H, rows, ld = s.shape
+    cols = ld if cols is None else cols
+    lse = torch.empty((B, H, rows), dtype=torch.float32, device=s.device)
+    g = torch.empty_like(s) if want_g else None
+    if row_valid is not None:
+        _need(row_valid, torch.int32, "row_valid")
+    _check(lib().sas_gates(_ptr(s), B, H, rows, cols, ld, ROWS[mode], _ptr(row_valid), _ptr(lse),
+                           _ptr(g), _stream(s.device)))
+    return lse, g
+
+
+def sas_topk_select(s, topk, scope="sparse", mode="prefill", row_valid=None, kcap=None, cols=None):
+    """s: fp32 [B, H, rows, ld]. Returns idx int32 [B, H, rows, kcap], cnt int32 [B, H, rows],
+    lse fp32 [B, H, rows], logg fp32 [B, H, rows, kcap]."""
+    _need(s, torch.float32, "s")
+    B, H, rows, ld = s.shape
+    cols = ld if cols is None else cols
+    if kcap is None:
+        kcap = cols if scope == "full" else min(topk, cols)
+    dev = s.device
+    idx = torch.empty((B, H, rows, kcap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, H, rows), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, H, rows), dtype=torch.float32, device=dev)
+    logg = torch.empty((B, H, rows, kcap), dtype=torch.float32, device=dev)
+    if row_valid is not None:
+        _need(row_valid, torch.int32, "row_valid")
+    _check(lib().sas_topk_select(_ptr(s), B, H, rows, cols, ld, ROWS[mode], _ptr(row_valid), int(topk),
+                                 SCOPE[scope], kcap, _ptr(idx), _ptr(cnt), _ptr(lse), _ptr(logg),
+                                 _stream(dev)))
+    return idx, cnt, lse, logg
+
+
+def sas_attn_fwd(Q, K, V, idx, cnt, logg, scale, out=None, lse_out=None):
+    """Q bf16 [B, Hq, n, d]; K, V bf16 [B, Hkv, n, d]; idx/cnt/logg from sas_topk_select.
+    Returns (O bf16 [B, Hq, n, d], lse_rows fp32 [B, Hq, n])."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
+        _need(t, torch.bfloat16, nm)
+    _need(idx, torch.int32, "idx")
+    _need(cnt, torch.int32, "cnt")
+    if logg is not None:
+        _need(logg, torch.float32, "logg")
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    kcap = idx.shape[-1]
+    O = torch.empty_like(Q) if out is None else out
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=Q.device) if lse_out is None else lse_out
+    _check(lib().sas_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(cnt), _ptr(logg), B, Hq, Hkv, n,
+                              d, BLOCK, kcap, float(scale), _ptr(O), _ptr(lse), _stream(Q.device)))
+    return O, lse
+
+
+def bwd_workspace(B, Hq, Hkv, n, d, kcap, device):
+    nbytes = lib().sas_attn_bwd_workspace_size(B, Hq, Hkv, n, d, BLOCK, kcap)
+    if nbytes == 0:
+        raise SasError(SAS_ERR_INVALID_ARG, "invalid sizes for sas_attn_bwd_workspace_size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def sas_attn_bwd(Q, K, V, O, dO, lse_rows, idx, cnt, logg, scale, ws=None, outs=None):
+    """Returns (dQ fp32, dK fp32, dV fp32, dg fp32 [B, Hkv, n/64, kcap])."""
+    for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O"), (dO, "dO")):
+        _need(t, torch.bfloat16, nm)
+    _need(lse_rows, torch.float32, "lse_rows")
+    B, Hq, n, d = Q.shape
+    Hkv = K.shape[1]
+    kcap = idx.shape[-1]
+    dev = Q.device
+    if ws is None:
+        ws = bwd_workspace(B, Hq, Hkv, n, d, kcap, dev)
+    if outs is None:
+        dQ = torch.empty(Q.shape, dtype=torch.float32, device=dev)
+        dK = torch.empty(K.shape, dtype=torch.float32, device=dev)
+        dV = torch.empty(V.shape, dtype=torch.float32, device=dev)
+        dg = torch.empty((B, Hkv, n // BLOCK, kcap), dtype=torch.float32, device=dev)
+    else:
+        dQ, dK, dV, dg = outs
+    _check(lib().sas_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(lse_rows), _ptr(idx),
+                              _ptr(cnt), _ptr(logg), B, Hq, Hkv, n, d, BLOCK, kcap, float(scale),
+                              _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(ws), ws.numel(), _stream(dev)))
+    return dQ, dK, dV, dg
+
+
+def decode_workspace(B, Hq, Hkv, d, kcap, device):
+    nbytes = lib().sas_decode_workspace_size(B, Hq, Hkv, d, kcap)
+    if nbytes == 0:
+        raise SasError(SAS_ERR_INVALID_ARG, "invalid sizes for sas_decode_workspace_size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None):
+    """q bf16 [B, Hq, d]; Kc, Vc bf16 [B, Hkv, Lmax, d]; kv_len int32 [B];
+    idx int32 [B, Hkv, kcap] (or [B, Hkv, 1, kcap]); cnt int32 [B, Hkv(, 1)]. Returns o bf16."""
+    for t, nm in ((q, "q"), (Kc, "Kc"), (Vc, "Vc")):
+        _need(t, torch.bfloat16, nm)
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hq, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    kcap = idx.shape[-1]
+    if ws is None:
+        ws = decode_workspace(B, Hq, Hkv, d, kcap, q.device)
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().sas_decode(_ptr(q), _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, _ptr(idx), _ptr(cnt), _ptr(logg),
+                            B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
+                            _stream(q.device)))
+    return o

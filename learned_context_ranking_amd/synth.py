@@ -18,6 +18,9 @@ on onedev.kr, sections "어떻게 쓰나" and "전제와 한계"). Head counts f
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_PLANT, TID_QDEC = 0, 1, 2, 3, 4, 5, 6
@@ -29,8 +32,9 @@ def rng(seed: int, tensor_id: int, chunk: int = 0) -> np.random.Generator:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 with round-to-nearest-even; returns the raw uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u >> 16) & 1) + 0x7FFF
+    # Finite values and infinities cannot carry past bit 31 (NaN is patched below).
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
     b = ((u + r) >> 16).astype(np.uint16)
     nan = np.isnan(np.asarray(x, dtype=np.float32))
     if nan.any():
@@ -42,17 +46,28 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
 
 
-def normal_bf16(shape, seed: int, tensor_id: int) -> np.ndarray:
+def normal_bf16(shape, seed: int, tensor_id: int, threads: int | None = None) -> np.ndarray:
     """N(0,1) draws in fp32, rounded to bf16; returned as uint16 bit patterns.
 
-    ``shape`` is (B, H, rows, d); one generator per (b, h) slice.
+    ``shape`` is (B, H, rows, d); one generator per (b, h) slice, so the result does not
+    depend on how many threads fill it.
     """
     B, H = shape[0], shape[1]
     out = np.empty(shape, dtype=np.uint16)
-    for b in range(B):
-        for h in range(H):
-            g = rng(seed, tensor_id, b * H + h)
-            out[b, h] = f32_to_bf16_bits(g.standard_normal(shape[2:], dtype=np.float32))
+
+    def fill(k):
+        b, h = divmod(k, H)
+        g = rng(seed, tensor_id, k)
+        out[b, h] = f32_to_bf16_bits(g.standard_normal(shape[2:], dtype=np.float32))
+
+    n = B * H
+    threads = threads or min(16, os.cpu_count() or 1)
+    if threads <= 1 or n <= 1:
+        for k in range(n):
+            fill(k)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(n)))
     return out
 
 

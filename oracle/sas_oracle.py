@@ -157,85 +157,118 @@ def _block_logits(q, Kb, keys, ell, j, block, scale):
     return zu + ell[None, :], zu
 
 
+def fwd_query_block(Q, K, V, b, h, j, idx_row, cnt_j, logg_row, scale, block=64):
+    """One query block of the forward for every query head of KV head h: returns
+    O [G, block, d] and LSE [G, block] (eq. (9) of [SAS-ja] "仕組み")."""
+    Hq, Hkv = Q.shape[1], K.shape[1]
+    G = Hq // Hkv
+    keys, ell = _key_set(j, idx_row, cnt_j, logg_row, block)
+    Kb = np.asarray(K[b, h, keys], np.float64)
+    Vb = np.asarray(V[b, h, keys], np.float64)
+    rows = slice(j * block, (j + 1) * block)
+    O = np.zeros((G, block, Q.shape[-1]))
+    LSE = np.zeros((G, block))
+    for g in range(G):
+        q = np.asarray(Q[b, h * G + g, rows], np.float64)
+        z, _ = _block_logits(q, Kb, keys, ell, j, block, scale)
+        mx = z.max(axis=1, keepdims=True)
+        e = np.exp(z - mx)
+        Z = e.sum(axis=1, keepdims=True)
+        O[g] = (e / Z) @ Vb
+        LSE[g] = (mx + np.log(Z))[:, 0]
+    return O, LSE
+
+
 def attn_fwd(Q, K, V, idx, cnt, logg, scale, block=64):
     """Gated block-sparse attention forward, eq. (9) of [SAS-ja] "仕組み".
 
     Q [B, Hq, n, d]; K, V [B, Hkv, n, d]; idx/logg [B, Hkv, NB, kcap]; cnt [B, Hkv, NB].
     Returns O [B, Hq, n, d] and the natural-log row sums LSE [B, Hq, n].
     """
-    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64); V = np.asarray(V, np.float64)
     B, Hq, n, d = Q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
     NB = n // block
-    O = np.zeros_like(Q)
+    O = np.zeros((B, Hq, n, d))
     LSE = np.zeros((B, Hq, n))
     for b in range(B):
         for h in range(Hkv):
             for j in range(NB):
-                keys, ell = _key_set(j, idx[b, h, j], cnt[b, h, j], logg[b, h, j], block)
-                Kb, Vb = K[b, h, keys], V[b, h, keys]
+                o, l = fwd_query_block(Q, K, V, b, h, j, idx[b, h, j], cnt[b, h, j], logg[b, h, j],
+                                       scale, block)
                 rows = slice(j * block, (j + 1) * block)
-                for g in range(G):
-                    hq = h * G + g
-                    z, _ = _block_logits(Q[b, hq, rows], Kb, keys, ell, j, block, scale)
-                    mx = z.max(axis=1, keepdims=True)
-                    e = np.exp(z - mx)
-                    Z = e.sum(axis=1, keepdims=True)
-                    O[b, hq, rows] = (e / Z) @ Vb
-                    LSE[b, hq, rows] = (mx + np.log(Z))[:, 0]
+                O[b, h * G:(h + 1) * G, rows] = o
+                LSE[b, h * G:(h + 1) * G, rows] = l
     return O, LSE
 
 
-def attn_bwd(Q, K, V, dO, idx, cnt, logg, scale, block=64):
-    """Backward of :func:`attn_fwd` with the gate gradient.
+def bwd_query_block(Q, K, V, dO, b, h, j, idx_row, cnt_j, logg_row, scale, block=64):
+    """Backward contributions of one query block (all G query heads of KV head h).
 
     Content gradients are those of softmax attention over S_j; gradients reach only the
     attended keys (sparse scope, [SAS-ko] "무엇과 다른가", choice 4). The gate gradient of
-    selected block m of query block j follows choice 1 of the same section:
+    selected block m follows choice 1 of the same section:
     dg_jm = sum over the G*b query rows t of the group (R3) and keys i in B_m of
     (p~_ti / g_jm) * dO_t^T (v_i - o_t). By eq. (9) p~_ti / g_jm = exp(z_ti - LSE_t) with
     z_ti the logit before the gate is added, which is what is evaluated (it stays
     defined when g_jm = 0).
-    Returns dQ, dK, dV (float64, shapes of Q, K, V) and dg [B, Hkv, NB, kcap] (0 pad).
+    Returns dQ [G, block, d], the key token indices of S_j, dK and dV over those keys
+    ([len(keys), d], summed over the G heads) and dg [cnt_j].
     """
-    Q = np.asarray(Q, np.float64); K = np.asarray(K, np.float64)
-    V = np.asarray(V, np.float64); dO = np.asarray(dO, np.float64)
+    Hq, Hkv = Q.shape[1], K.shape[1]
+    G = Hq // Hkv
+    keys, ell = _key_set(j, idx_row, cnt_j, logg_row, block)
+    Kb = np.asarray(K[b, h, keys], np.float64)
+    Vb = np.asarray(V[b, h, keys], np.float64)
+    rows = slice(j * block, (j + 1) * block)
+    d = Q.shape[-1]
+    dQ = np.zeros((G, block, d))
+    dKs = np.zeros((len(keys), d))
+    dVs = np.zeros((len(keys), d))
+    dg = np.zeros(int(cnt_j))
+    for g in range(G):
+        q = np.asarray(Q[b, h * G + g, rows], np.float64)
+        z, zu = _block_logits(q, Kb, keys, ell, j, block, scale)
+        mx = z.max(axis=1, keepdims=True)
+        e = np.exp(z - mx)
+        Z = e.sum(axis=1, keepdims=True)
+        P = e / Z
+        lse = mx + np.log(Z)
+        o = P @ Vb
+        do = np.asarray(dO[b, h * G + g, rows], np.float64)
+        dP = do @ Vb.T                                   # dO_t^T v_i
+        delta = np.sum(do * o, axis=1, keepdims=True)    # dO_t^T o_t
+        dS = P * (dP - delta)
+        dQ[g] = scale * (dS @ Kb)
+        dKs += scale * (dS.T @ q)
+        dVs += P.T @ do
+        ratio = np.exp(zu - lse)                         # = p~ / g
+        for t in range(int(cnt_j)):
+            cols = slice(block * (t + 1), block * (t + 2))
+            dg[t] += np.sum(ratio[:, cols] * (dP[:, cols] - delta))
+    return dQ, keys, dKs, dVs, dg
+
+
+def attn_bwd(Q, K, V, dO, idx, cnt, logg, scale, block=64):
+    """Backward of :func:`attn_fwd` with the gate gradient (see :func:`bwd_query_block`).
+    Returns dQ, dK, dV (float64, shapes of Q, K, V) and dg [B, Hkv, NB, kcap] (0 pad)."""
     B, Hq, n, d = Q.shape
     Hkv = K.shape[1]
     G = Hq // Hkv
     NB = n // block
     kcap = idx.shape[-1]
-    dQ = np.zeros_like(Q); dK = np.zeros_like(K); dV = np.zeros_like(V)
+    dQ = np.zeros((B, Hq, n, d)); dK = np.zeros((B, Hkv, n, d)); dV = np.zeros((B, Hkv, n, d))
     dg = np.zeros((B, Hkv, NB, kcap))
     for b in range(B):
         for h in range(Hkv):
             for j in range(NB):
-                keys, ell = _key_set(j, idx[b, h, j], cnt[b, h, j], logg[b, h, j], block)
-                Kb, Vb = K[b, h, keys], V[b, h, keys]
-                rows = slice(j * block, (j + 1) * block)
-                for g in range(G):
-                    hq = h * G + g
-                    q = Q[b, hq, rows]
-                    z, zu = _block_logits(q, Kb, keys, ell, j, block, scale)
-                    mx = z.max(axis=1, keepdims=True)
-                    e = np.exp(z - mx)
-                    Z = e.sum(axis=1, keepdims=True)
-                    P = e / Z
-                    lse = mx + np.log(Z)
-                    o = P @ Vb
-                    do = dO[b, hq, rows]
-                    dP = do @ Vb.T                      # dO_t^T v_i
-                    delta = np.sum(do * o, axis=1, keepdims=True)   # dO_t^T o_t
-                    dS = P * (dP - delta)
-                    dQ[b, hq, rows] += scale * (dS @ Kb)
-                    np.add.at(dK[b, h], keys, scale * (dS.T @ q))
-                    np.add.at(dV[b, h], keys, P.T @ do)
-                    # gate gradient, one selected block at a time
-                    ratio = np.exp(zu - lse)             # = p~ / g
-                    for t in range(int(cnt[b, h, j])):
-                        cols = slice(block * (t + 1), block * (t + 2))
-                        dg[b, h, j, t] += np.sum(ratio[:, cols] * (dP[:, cols] - delta))
+                c = int(cnt[b, h, j])
+                dq, keys, dks, dvs, dgj = bwd_query_block(Q, K, V, dO, b, h, j, idx[b, h, j], c,
+                                                          logg[b, h, j], scale, block)
+                dQ[b, h * G:(h + 1) * G, j * block:(j + 1) * block] = dq
+                np.add.at(dK[b, h], keys, dks)
+                np.add.at(dV[b, h], keys, dvs)
+                dg[b, h, j, :c] = dgj
     return dQ, dK, dV, dg
 
 

@@ -1,0 +1,84 @@
+"""Helpers for the GPU parity tests: seeded inputs, device copies and the tolerance rule.
+
+Tolerance (floating outputs, bf16 GPU path against the fp64 oracle on the same
+bf16-rounded inputs), applied per tensor; both parts must hold:
+  * max |got - ref| <= 2e-2 * max(1, max |ref|)      (scale-aware max-abs)
+  * sum |got - ref| / sum |ref| <= 1e-2               (mean relative error)
+Indices and counts are compared bit for bit.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+from learned_context_ranking_amd import synth
+
+MAX_ABS = 2e-2
+MEAN_REL = 1e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy().astype(np.float64)
+    return t.cpu().numpy()
+
+
+def assert_close(name, got, ref, max_abs=MAX_ABS, mean_rel=MEAN_REL):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite output"
+    diff = np.abs(got - ref)
+    bound = max_abs * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
+    mx = float(diff.max()) if diff.size else 0.0
+    den = float(np.abs(ref).sum())
+    rel = float(diff.sum()) / den if den > 0 else float(diff.sum())
+    log(f"  {name}: max|d|={mx:.3e} (bound {bound:.3e}) mean-rel={rel:.3e}")
+    assert mx <= bound, f"{name}: max abs error {mx} > {bound}"
+    assert rel <= mean_rel, f"{name}: mean relative error {rel} > {mean_rel}"
+
+
+class Prefill:
+    """Seeded prefill/training inputs: bf16 bit patterns, their exact fp32 values, and
+    scores. ``scores`` is one of normal / planted / zipf."""
+
+    def __init__(self, B, Hq, Hkv, n, d, seed=0, scores="normal", backward=True):
+        self.B, self.Hq, self.Hkv, self.n, self.d = B, Hq, Hkv, n, d
+        self.NB = n // 64
+        self.scale = 1.0 / math.sqrt(d)
+        self.q_bits = synth.normal_bf16((B, Hq, n, d), seed, synth.TID_Q)
+        self.k_bits = synth.normal_bf16((B, Hkv, n, d), seed, synth.TID_K)
+        self.v_bits = synth.normal_bf16((B, Hkv, n, d), seed, synth.TID_V)
+        self.do_bits = synth.normal_bf16((B, Hq, n, d), seed, synth.TID_DO) if backward else None
+        if scores == "normal":
+            self.s = synth.scores_normal((B, Hkv, self.NB, self.NB), seed)
+        elif scores == "planted":
+            self.s = synth.scores_planted(B, Hkv, self.NB, seed)
+        else:
+            self.s = synth.scores_zipf(B, Hkv, self.NB, seed)
+
+    def f32(self, name):
+        return synth.bf16_bits_to_f32(getattr(self, name + "_bits"))
+
+    def device(self):
+        out = dict(Q=dev_bf16(self.q_bits), K=dev_bf16(self.k_bits), V=dev_bf16(self.v_bits),
+                   s=dev(self.s))
+        if self.do_bits is not None:
+            out["dO"] = dev_bf16(self.do_bits)
+        return out

@@ -1,0 +1,126 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point declared in
+include/sas.h, and rejects bad arguments with a status code before touching the device.
+
+No call here passes valid arguments, so no kernel is ever launched: every rejected call
+returns from the host-side checks, which run before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from learned_context_ranking_amd import sas
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sas.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(sas.LIB_PATH), reason="libsas.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sas_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) == 10, names
+    L = ctypes.CDLL(sas.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(sas.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    assert "gfx950" in sas.version()
+    assert sas.status_string(0) == "SAS_OK"
+    assert sas.status_string(3) == "SAS_ERR_WORKSPACE"
+
+
+FAKE = ctypes.c_void_p(0x10000)      # 16-byte aligned, never dereferenced
+MIS = ctypes.c_void_p(0x10002)       # misaligned
+NULL = None
+
+
+def _fwd(**kw):
+    a = dict(Q=FAKE, K=FAKE, V=FAKE, idx=FAKE, cnt=FAKE, logg=FAKE, B=1, Hq=4, Hkv=2, n=256, d=128,
+             block=64, kcap=4, scale=0.125, O=FAKE, lse=FAKE, stream=NULL)
+    a.update(kw)
+    return sas.lib().sas_attn_fwd(a["Q"], a["K"], a["V"], a["idx"], a["cnt"], a["logg"], a["B"], a["Hq"],
+                                  a["Hkv"], a["n"], a["d"], a["block"], a["kcap"], a["scale"], a["O"],
+                                  a["lse"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=NULL), sas.SAS_ERR_INVALID_ARG),
+    (dict(cnt=NULL), sas.SAS_ERR_INVALID_ARG),
+    (dict(Hq=3), sas.SAS_ERR_INVALID_ARG),
+    (dict(block=32), sas.SAS_ERR_UNSUPPORTED),
+    (dict(n=100), sas.SAS_ERR_INVALID_ARG),
+    (dict(d=96), sas.SAS_ERR_UNSUPPORTED),
+    (dict(kcap=-1), sas.SAS_ERR_INVALID_ARG),
+    (dict(scale=0.0), sas.SAS_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), sas.SAS_ERR_INVALID_ARG),
+    (dict(K=MIS), sas.SAS_ERR_INVALID_ARG),
+    (dict(O=NULL), sas.SAS_ERR_INVALID_ARG),
+    (dict(B=0), sas.SAS_ERR_INVALID_ARG),
+])
+def test_fwd_rejects(kw, code):
+    assert _fwd(**kw) == code
+    assert sas.lib().sas_last_error().decode() != ""
+
+
+def test_select_rejects():
+    L = sas.lib()
+    args = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, 4, 0, 4, FAKE, FAKE, FAKE, FAKE, NULL]
+    bad = list(args); bad[0] = NULL
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[10] = 3          # kcap < topk
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[9] = 1           # full scope needs kcap >= rows - 1 = 15
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[6] = sas.ROWS["decode"]   # decode needs row_valid
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[7] = FAKE        # prefill forbids row_valid
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[4] = 10          # prefill: cols >= rows - 1
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[4] = 9000; bad[5] = 9000
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_UNSUPPORTED
+    bad = list(args); bad[8] = -1
+    assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    g = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, NULL, NULL, NULL]
+    assert L.sas_gates(*g) == sas.SAS_ERR_INVALID_ARG   # lse NULL
+
+
+def test_bwd_workspace_and_rejects():
+    L = sas.lib()
+    assert L.sas_attn_bwd_workspace_size(1, 4, 2, 256, 128, 64, 4) > 0
+    assert L.sas_attn_bwd_workspace_size(1, 4, 2, 250, 128, 64, 4) == 0
+    assert L.sas_attn_bwd_workspace_size(1, 3, 2, 256, 128, 64, 4) == 0
+    need = L.sas_attn_bwd_workspace_size(1, 4, 2, 256, 128, 64, 4)
+    args = [FAKE] * 9 + [1, 4, 2, 256, 128, 64, 4, 0.125] + [FAKE] * 4 + [FAKE, need - 1, NULL]
+    assert L.sas_attn_bwd(*args) == sas.SAS_ERR_WORKSPACE
+    args[-3] = NULL
+    args[-2] = need
+    assert L.sas_attn_bwd(*args) == sas.SAS_ERR_WORKSPACE
+    args[-3] = FAKE
+    args[4] = NULL                          # dO
+    assert L.sas_attn_bwd(*args) == sas.SAS_ERR_INVALID_ARG
+
+
+def test_decode_rejects():
+    L = sas.lib()
+    need = L.sas_decode_workspace_size(2, 8, 2, 128, 4)
+    assert need > 0
+    args = [FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, NULL, 2, 8, 2, 128, 64, 4, 0.1, FAKE, FAKE, need, NULL]
+    bad = list(args); bad[-2] = need - 1
+    assert L.sas_decode(*bad) == sas.SAS_ERR_WORKSPACE
+    bad = list(args); bad[9] = 6; bad[10] = 2     # G = 3 not instantiated
+    assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED
+    bad = list(args); bad[3] = NULL               # kv_len
+    assert L.sas_decode(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[12] = 128               # block
+    assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED

@@ -1,0 +1,144 @@
+"""GPU parity of sas_attn_fwd / sas_attn_bwd against the oracle.
+
+Small cases are compared element by element on every output (O, LSE, dQ, dK, dV, dg);
+they span several query blocks, GQA groups of 1, 3, 4, 5 and 8 heads, d = 64 and 128,
+full and sparse scope, ungated attention, rows whose budget exceeds their history and
+the first block (no history). Full-size cases sample query blocks (O, LSE, dQ, dg are
+local to a query block) and key blocks (dK, dV through the oracle's inverse map), and
+check gradient invariants on every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from learned_context_ranking_amd import sas
+from gpu_util import Prefill, assert_close, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # B, Hq, Hkv, n, d, topk, scope, gated, scores
+    (1, 1, 1, 1024, 64, 4, "sparse", True, "normal"),      # the tiny oracle workload
+    (1, 8, 2, 1024, 128, 4, "sparse", True, "normal"),
+    (2, 8, 2, 512, 64, 3, "sparse", True, "normal"),
+    (1, 10, 2, 768, 128, 6, "sparse", True, "zipf"),        # G = 5 (head split 3 + 2)
+    (1, 8, 1, 512, 64, 5, "sparse", True, "planted"),       # G = 8 (two workgroups of 4)
+    (1, 3, 1, 640, 128, 4, "sparse", True, "normal"),       # G = 3
+    (1, 4, 1, 512, 128, 0, "full", True, "normal"),         # full scope
+    (1, 4, 2, 512, 128, 4, "sparse", False, "normal"),      # ungated (logg = NULL)
+]
+
+
+def _run(case, seed=0):
+    B, Hq, Hkv, n, d, topk, scope, gated, scores = case
+    P = Prefill(B, Hq, Hkv, n, d, seed=seed, scores=scores)
+    t = P.device()
+    NB = P.NB
+    kcap = NB - 1 if scope == "full" else topk
+    idx, cnt, _, logg = sas.sas_topk_select(t["s"], topk, scope=scope, kcap=kcap, cols=NB)
+    lg = logg if gated else None
+    O, lse = sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx, cnt, lg, P.scale)
+    dQ, dK, dV, dg = sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx, cnt, lg, P.scale)
+    torch.cuda.synchronize()
+    return P, dict(idx=idx, cnt=cnt, logg=logg, O=O, lse=lse, dQ=dQ, dK=dK, dV=dV, dg=dg), gated, scope, topk
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}-{c[2]}n{c[3]}d{c[4]}K{c[5]}{c[6]}{'' if c[7] else '-ungated'}"
+                                             for c in CASES])
+def test_fwd_bwd_parity(case):
+    log(f"fwd/bwd parity {case}")
+    P, g, gated, scope, topk = _run(case)
+    idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk, full_scope=scope == "full",
+                                                    kcap=g["idx"].shape[-1])
+    assert np.array_equal(host(g["idx"]), idx_r) and np.array_equal(host(g["cnt"]), cnt_r)
+    lg = logg_r if gated else np.zeros_like(logg_r)
+    Q, K, V, dO = P.f32("q"), P.f32("k"), P.f32("v"), P.f32("do")
+    O_r, lse_r = oracle.attn_fwd(Q, K, V, idx_r, cnt_r, lg, P.scale)
+    assert_close("O", host(g["O"]), O_r)
+    assert_close("LSE", host(g["lse"]), lse_r)
+    dQ_r, dK_r, dV_r, dg_r = oracle.attn_bwd(Q, K, V, dO, idx_r, cnt_r, lg, P.scale)
+    assert_close("dQ", host(g["dQ"]), dQ_r)
+    assert_close("dK", host(g["dK"]), dK_r)
+    assert_close("dV", host(g["dV"]), dV_r)
+    assert_close("dg", host(g["dg"]), dg_r)
+
+
+def test_deterministic_reruns():
+    case = (1, 10, 2, 512, 128, 4, "sparse", True, "normal")
+    _, a, *_ = _run(case)
+    _, b, *_ = _run(case)
+    for k in ("idx", "cnt", "O", "lse", "dQ", "dK", "dV"):
+        assert torch.equal(a[k], b[k]), k
+    # dg of a 5-head group is reduced across two workgroups with atomics: compare loosely
+    assert float((a["dg"] - b["dg"]).abs().max()) <= 1e-3 * max(1.0, float(a["dg"].abs().max()))
+
+
+def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backward=True):
+    log(f"full size B={B} Hq={Hq} Hkv={Hkv} n={n} d={d} K={topk} scores={scores}")
+    P = Prefill(B, Hq, Hkv, n, d, seed=0, scores=scores, backward=backward)
+    t = P.device()
+    NB, G = P.NB, Hq // Hkv
+    idx, cnt, _, logg = sas.sas_topk_select(t["s"], topk, cols=NB)
+    O, lse = sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx, cnt, logg, P.scale)
+    if backward:
+        dQ, dK, dV, dg = sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx, cnt, logg, P.scale)
+    torch.cuda.synchronize()
+    log("  GPU done; oracle selection")
+    idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk)
+    assert np.array_equal(host(idx), idx_r) and np.array_equal(host(cnt), cnt_r)
+    Q, K, V = P.f32("q"), P.f32("k"), P.f32("v")
+    dO = P.f32("do") if backward else None
+    g = np.random.default_rng(1)
+    js = sorted(set([0, 1, NB - 1] + list(g.integers(2, NB - 1, nsample_j))))
+    Oh = host(O)
+    lseh = host(lse)
+    if backward:
+        dQh, dgh = host(dQ), host(dg)
+    for j in js:
+        h = int(g.integers(0, Hkv))
+        rows = slice(j * 64, (j + 1) * 64)
+        o_r, l_r = oracle.fwd_query_block(Q, K, V, 0, h, j, idx_r[0, h, j], cnt_r[0, h, j], logg_r[0, h, j], P.scale)
+        assert_close(f"O[j={j},h={h}]", Oh[0, h * G:(h + 1) * G, rows], o_r)
+        assert_close(f"LSE[j={j},h={h}]", lseh[0, h * G:(h + 1) * G, rows], l_r)
+        if backward:
+            dq_r, _, _, _, dg_r = oracle.bwd_query_block(Q, K, V, dO, 0, h, j, idx_r[0, h, j], cnt_r[0, h, j],
+                                                         logg_r[0, h, j], P.scale)
+            assert_close(f"dQ[j={j},h={h}]", dQh[0, h * G:(h + 1) * G, rows], dq_r)
+            if cnt_r[0, h, j] > 0:
+                assert_close(f"dg[j={j},h={h}]", dgh[0, h, j, :cnt_r[0, h, j]], dg_r)
+    if not backward:
+        return
+    dKh, dVh = host(dK), host(dV)
+    for m in [0] + list(g.integers(1, NB, nsample_m)):
+        h = int(g.integers(0, Hkv))
+        users = [j for j in range(m + 1, NB) if m in idx_r[0, h, j, :cnt_r[0, h, j]]]
+        dk_r = np.zeros((64, d)); dv_r = np.zeros((64, d))
+        for j in [m] + users:
+            _, keys, dks, dvs, _ = oracle.bwd_query_block(Q, K, V, dO, 0, h, j, idx_r[0, h, j], cnt_r[0, h, j],
+                                                          logg_r[0, h, j], P.scale)
+            sel = (keys >= m * 64) & (keys < (m + 1) * 64)
+            dk_r[keys[sel] - m * 64] += dks[sel]
+            dv_r[keys[sel] - m * 64] += dvs[sel]
+        log(f"  key block m={m} h={h}: {len(users)} selecting query blocks")
+        assert_close(f"dK[m={m},h={h}]", dKh[0, h, m * 64:(m + 1) * 64], dk_r)
+        assert_close(f"dV[m={m},h={h}]", dVh[0, h, m * 64:(m + 1) * 64], dv_r)
+    # invariants over every element: sum_i dK_i = 0, sum_i dV_i = sum of the group's dO rows
+    sk = dK.double().sum(dim=2).abs()
+    sa = dK.double().abs().sum(dim=2)
+    assert bool((sk <= 1e-2 * sa).all()), float((sk / sa).max())
+    sv = host(dV.double().sum(dim=2))
+    sdo = dO.reshape(B, Hkv, G, n, d).sum(axis=(2, 3))
+    assert_close("sum dV", sv, sdo)
+
+
+def test_full_size_qwen3_4b_train():
+    _full_size(1, 32, 8, 32768, 128, 32, "normal")
+
+
+def test_full_size_qwen3_14b_k32():
+    _full_size(1, 40, 8, 32768, 128, 32, "zipf", nsample_j=4, nsample_m=2)
+
+
+def test_full_size_long_prefill_fwd():
+    _full_size(1, 32, 8, 131072, 128, 64, "planted", nsample_j=4, backward=False)

@@ -1,0 +1,129 @@
+"""GPU parity of sas_gates / sas_topk_select against the oracle: selected indices and
+counts bit-exact, log-gates and LSE within float tolerance. Score entries that no row
+may read (m >= j in prefill, m >= row_valid in decode) are set to NaN to show that the
+kernel never reads them."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from learned_context_ranking_amd import sas, synth
+from gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _poison_prefill(s):
+    s = s.copy()
+    NB = s.shape[2]
+    inval = np.triu(np.ones((NB, s.shape[3]), dtype=bool), 0)[:NB]
+    s[..., inval] = np.nan
+    return s
+
+
+def _check_prefill(s, topk, scope="sparse", kcap=None):
+    B, H, NB, ld = s.shape
+    full = scope == "full"
+    idx_r, cnt_r, lse_r, logg_r = oracle.select_prefill(s, topk, full_scope=full, kcap=kcap)
+    sd = dev(_poison_prefill(s))
+    idx, cnt, lse, logg = sas.sas_topk_select(sd, topk, scope=scope, kcap=idx_r.shape[-1], cols=NB)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(cnt), cnt_r)
+    assert np.array_equal(host(idx), idx_r)
+    fin = np.isfinite(lse_r)
+    assert np.array_equal(np.isfinite(host(lse)), fin)
+    np.testing.assert_allclose(host(lse)[fin], lse_r[fin], rtol=0, atol=2e-5)
+    np.testing.assert_allclose(host(logg), logg_r, rtol=0, atol=2e-5)
+    return idx, cnt, lse, logg
+
+
+@pytest.mark.parametrize("NB,topk", [(16, 4), (100, 7), (129, 32), (512, 32), (300, 0)])
+def test_select_prefill_normal(NB, topk):
+    log(f"select prefill NB={NB} K={topk}")
+    s = synth.scores_normal((2, 3, NB, NB), seed=NB)
+    _check_prefill(s, topk)
+
+
+def test_select_prefill_full_scope():
+    s = synth.scores_normal((1, 2, 70, 70), seed=5)
+    _check_prefill(s, 0, scope="full", kcap=69)
+
+
+def test_select_ties_signed_zero_nan_inf():
+    """Integer-valued scores (many ties), +-0, -inf and NaN in valid positions."""
+    g = np.random.default_rng(3)
+    NB = 200
+    s = g.integers(-2, 3, size=(1, 2, NB, NB)).astype(np.float32)
+    s[0, 0, :, ::7] = -0.0
+    s[0, 1, :, ::11] = -np.inf
+    s[0, 1, :, 5::13] = np.nan
+    _check_prefill(s, 16)
+    _check_prefill(s, 70)
+
+
+def test_select_planted_and_zipf_rows():
+    _check_prefill(synth.scores_planted(1, 2, 256, 0), 64)
+    _check_prefill(synth.scores_zipf(1, 2, 256, 0), 32)
+
+
+@pytest.mark.parametrize("cols", [1, 63, 64, 65, 511, 1024, 2047, 2048, 4000, 8191])
+def test_select_decode_rows(cols):
+    """DECODE mode: one row per (sequence, KV head) with row_valid[b] valid scores;
+    covers every per-lane register count of the kernel."""
+    log(f"select decode cols={cols}")
+    B, H = 5, 3
+    g = np.random.default_rng(cols)
+    s = g.standard_normal((B, H, 1, cols)).astype(np.float32)
+    valid = np.array([cols, 0, cols // 2, min(cols, 3), max(cols - 1, 0)], np.int32)
+    sp = s.copy()
+    for b in range(B):
+        sp[b, :, :, valid[b]:] = np.nan
+    topk = 16
+    kcap = min(topk, cols)
+    idx_r, cnt_r, lse_r, logg_r = oracle.select(s.reshape(B * H, cols), np.repeat(valid, H), topk, kcap=kcap)
+    idx, cnt, lse, logg = sas.sas_topk_select(dev(sp), topk, mode="decode", row_valid=dev(valid), kcap=kcap)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).reshape(B * H, kcap), idx_r)
+    assert np.array_equal(host(cnt).reshape(-1), cnt_r)
+    np.testing.assert_allclose(host(logg).reshape(B * H, kcap), logg_r, rtol=0, atol=3e-5)
+
+
+def test_gates_dense():
+    s = synth.scores_normal((1, 2, 40, 40), seed=9)
+    lse, g = sas.sas_gates(dev(_poison_prefill(s)), want_g=True)
+    torch.cuda.synchronize()
+    g = host(g)
+    for h in range(2):
+        for j in range(40):
+            l, lg = oracle.row_log_gates(s[0, h, j, :j])
+            if j == 0:
+                assert host(lse)[0, h, 0] == -np.inf
+            else:
+                assert abs(host(lse)[0, h, j] - l) < 2e-5
+                np.testing.assert_allclose(g[0, h, j, :j], np.exp(lg), rtol=0, atol=1e-6)
+            assert np.all(g[0, h, j, j:] == 0)
+
+
+def test_select_shift_invariance():
+    """Scores on a dyadic grid shifted by 8 (exact in fp32) give identical indices and
+    log-gates on the GPU as well."""
+    g = np.random.default_rng(4)
+    s = (np.round(g.standard_normal((1, 2, 64, 64)) * 1024) / 1024).astype(np.float32)
+    a = sas.sas_topk_select(dev(s), 8, cols=64)
+    b = sas.sas_topk_select(dev((s + np.float32(8)).astype(np.float32)), 8, cols=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert float((a[3] - b[3]).abs().max()) < 1e-5
+
+
+def test_select_full_size_long_prefill():
+    """Long-prefill scores (8 KV heads x 2048 query blocks, 8 planted blocks per row),
+    K = 64: every row bit-exact."""
+    log("select full size: 8 x 2048 x 2048 planted, K=64")
+    s = synth.scores_planted(1, 8, 2048, 0)
+    idx_r, cnt_r, _, logg_r = oracle.select_prefill(s, 64)
+    idx, cnt, _, logg = sas.sas_topk_select(dev(s), 64, cols=2048)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx), idx_r)
+    assert np.array_equal(host(cnt), cnt_r)
+    np.testing.assert_allclose(host(logg), logg_r, rtol=0, atol=3e-5)
