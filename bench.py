@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the SAS log-gated block-sparse attention hot path on one MI355X.
+
+A step is one pass of the training hot path over the Qwen3-4B-shaped single-layer
+workload (batch 1, 32 query / 8 KV heads, head_dim 128, n = 32,768, block 64, Top-K 32,
+bf16 Q/K/V/dO ~ N(0,1), fp32 scores ~ N(0,1)): gate + Top-K selection, gated forward,
+backward with dQ, dK, dV and dg. Inputs are resident in HBM before timing starts.
+
+value = algorithmic FLOPs / step time, counting only attended (query, key) pairs:
+4*d per pair forward (q.k, p.v) and 8*d backward (dO.v, p^T dO, dS k, dS^T q); the
+backward's recomputation of q.k is not counted. The decode workload (64 sequences,
+32,768 cached tokens, 16 blocks + the current block per KV head) is reported alongside
+as HBM GB/s of the decode kernel with the caches flushed from L2 / Infinity Cache.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pair_count(cnt: np.ndarray, G: int, block: int = 64) -> int:
+    """Attended (query row, key) pairs: causal current block plus cnt_j full history
+    blocks for every query block, times the G query heads of each KV head."""
+    per_block = block * (block + 1) // 2 + cnt.astype(np.int64) * block * block
+    return int(per_block.sum()) * G
+
+
+def bf16_device(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def train_inputs(w, torch):
+    from learned_context_ranking_amd import synth
+    q = synth.normal_bf16((w.B, w.Hq, w.n, w.d), w.seed, synth.TID_Q)
+    k = synth.normal_bf16((w.B, w.Hkv, w.n, w.d), w.seed, synth.TID_K)
+    v = synth.normal_bf16((w.B, w.Hkv, w.n, w.d), w.seed, synth.TID_V)
+    do = synth.normal_bf16((w.B, w.Hq, w.n, w.d), w.seed, synth.TID_DO)
+    s = synth.prefill_scores(w)
+    host = dict(q=q, k=k, v=v, do=do, s=s)
+    dev = dict(Q=bf16_device(q, torch), K=bf16_device(k, torch), V=bf16_device(v, torch),
+               dO=bf16_device(do, torch), s=torch.from_numpy(s).cuda())
+    return host, dev
+
+
+def run_train(w, steps, warmup, torch):
+    from learned_context_ranking_amd import sas
+    log(f"[bench] generating {w.name} inputs")
+    host, t = train_inputs(w, torch)
+    scale = 1.0 / math.sqrt(w.d)
+    NB = w.NB
+    dev = t["Q"].device
+    idx = torch.empty((w.B, w.Hkv, NB, w.topk), dtype=torch.int32, device=dev)
+    # outputs and workspace allocated once, outside the timed region
+    O = torch.empty_like(t["Q"])
+    lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
+    dQ = torch.empty(t["Q"].shape, dtype=torch.float32, device=dev)
+    dK = torch.empty(t["K"].shape, dtype=torch.float32, device=dev)
+    dV = torch.empty(t["V"].shape, dtype=torch.float32, device=dev)
+    dg = torch.empty((w.B, w.Hkv, NB, w.topk), dtype=torch.float32, device=dev)
+    ws = sas.bwd_workspace(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dev)
+    stream = torch.cuda.current_stream()
+    ev = {k: [] for k in ("sel", "fwd", "bwd")}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            marks[0].record(stream)
+        idx_, cnt_, _, logg_ = sas.sas_topk_select(t["s"], w.topk, kcap=w.topk, cols=NB)
+        if record:
+            marks[1].record(stream)
+        sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx_, cnt_, logg_, scale, out=O, lse_out=lse)
+        if record:
+            marks[2].record(stream)
+        sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx_, cnt_, logg_, scale, ws=ws,
+                         outs=(dQ, dK, dV, dg))
+        if record:
+            marks[3].record(stream)
+            ev["sel"].append((marks[0], marks[1]))
+            ev["fwd"].append((marks[1], marks[2]))
+            ev["bwd"].append((marks[2], marks[3]))
+        return cnt_
+
+    log(f"[bench] warmup {warmup}")
+    for _ in range(warmup):
+        cnt = step(False)
+    torch.cuda.synchronize()
+    cnt = step(False)
+    torch.cuda.synchronize()
+    cnt_h = cnt.cpu().numpy()
+    pairs = pair_count(cnt_h, w.G)
+    flop_fwd = 4.0 * w.d * pairs
+    flop_bwd = 8.0 * w.d * pairs
+    log(f"[bench] timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
+    return dict(ms_step=ms_step, ms=ms, pairs=pairs, flop_fwd=flop_fwd, flop_bwd=flop_bwd,
+                host=host, cnt=cnt_h)
+
+
+def run_decode(steps, torch):
+    """Decode workload: one new token per sequence over a 32,768-token cache."""
+    from learned_context_ranking_amd import sas, synth
+    w = synth.WORKLOADS["decode"]
+    B, Hq, Hkv, d, L, K = w.B, w.Hq, w.Hkv, w.d, w.n, w.topk
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1234)
+    log("[bench] generating decode caches on device (seeded)")
+    Kc = torch.randn((B, Hkv, L, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, L, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    C = L // 64
+    s = torch.from_numpy(synth.scores_normal((B, Hkv, 1, C), w.seed)).to(dev)
+    kv_len = torch.full((B,), L, dtype=torch.int32, device=dev)
+    row_valid = ((kv_len - 1) // 64).to(torch.int32)
+    idx, cnt, _, _ = sas.sas_topk_select(s, K, mode="decode", row_valid=row_valid, kcap=K)
+    ws = sas.decode_workspace(B, Hq, Hkv, d, K, dev)
+    o = torch.empty_like(q)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # > L2 + Infinity Cache
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(d)
+    for _ in range(3):
+        sas.sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, ws=ws, out=o)
+    torch.cuda.synchronize()
+    times, sel_times = [], []
+    for _ in range(steps):
+        flush.zero_()
+        a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        sas.sas_topk_select(s, K, mode="decode", row_valid=row_valid, kcap=K)
+        b.record(stream)
+        sas.sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, ws=ws, out=o)
+        c.record(stream)
+        times.append((b, c))
+        sel_times.append((a, b))
+    torch.cuda.synchronize()
+    ms = float(np.median([x.elapsed_time(y) for x, y in times]))
+    ms_sel = float(np.median([x.elapsed_time(y) for x, y in sel_times]))
+    cnt_h = cnt.cpu().numpy()
+    # algorithmic bytes: the selected K/V blocks plus the current block, q and o
+    blocks = int(cnt_h.sum()) + B * Hkv
+    nbytes = blocks * 64 * d * 2 * 2 + 2 * B * Hq * d * 2
+    return dict(ms=ms, ms_select=ms_sel, bytes=nbytes, gbs=nbytes / ms / 1e6,
+                workload=f"decode: B={B} sequences, Hq={Hq}, Hkv={Hkv}, d={d}, kv_len={L}, block=64, "
+                         f"K={K} blocks + current block, ungated (Algorithm 2)")
+
+
+def cpu_baseline(w, host, cnt, budget_s=20.0):
+    """The oracle (NumPy, float64) on a sample of query blocks of the same workload; FLOPs
+    of the sampled blocks over their wall time. Threads = the BLAS pool's size."""
+    import oracle
+    from learned_context_ranking_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:   # threadpoolctl missing: report the affinity mask
+        cores = len(os.sched_getaffinity(0))
+    f = synth.bf16_bits_to_f32
+    Q, K, V, dO = f(host["q"]), f(host["k"]), f(host["v"]), f(host["do"])
+    idx_r, cnt_r, _, logg_r = oracle.select_prefill(host["s"], w.topk)
+    scale = 1.0 / math.sqrt(w.d)
+    rng = np.random.default_rng(7)
+    t0 = time.perf_counter()
+    flops = 0.0
+    nblk = 0
+    while time.perf_counter() - t0 < budget_s:
+        h = int(rng.integers(0, w.Hkv))
+        j = int(rng.integers(0, w.NB))
+        c = int(cnt_r[0, h, j])
+        oracle.fwd_query_block(Q, K, V, 0, h, j, idx_r[0, h, j], c, logg_r[0, h, j], scale)
+        oracle.bwd_query_block(Q, K, V, dO, 0, h, j, idx_r[0, h, j], c, logg_r[0, h, j], scale)
+        pairs = (64 * 65 // 2 + c * 64 * 64) * w.G
+        flops += 12.0 * w.d * pairs
+        nblk += 1
+    dt = time.perf_counter() - t0
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"{nblk} random (KV head, query block) tiles of the training workload, fwd+bwd "
+                       f"with dg, float64 NumPy, {dt:.1f} s wall")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the SAS hot path here is a single-GPU library "
+              "(heads and batch shard with no communication); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from learned_context_ranking_amd import sas, synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sas.lib()
+    w = synth.WORKLOADS["qwen3_4b_train"]
+    tr = run_train(w, args.steps, args.warmup, torch)
+    flop_step = tr["flop_fwd"] + tr["flop_bwd"]
+    value = flop_step / (tr["ms_step"] * 1e-3) / 1e12
+    ms = tr["ms"]
+    kern = {
+        "select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"],
+    }
+    # dominant launch of the step
+    fwd_tf = tr["flop_fwd"] / (ms["fwd"] * 1e-3) / 1e12
+    bwd_tf = tr["flop_bwd"] / (ms["bwd"] * 1e-3) / 1e12
+    roof = {"kernel": "sas_attn_bwd" if ms["bwd"] >= ms["fwd"] else "sas_attn_fwd",
+            "bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "traffic": None}
+    roof["achieved"] = bwd_tf if ms["bwd"] >= ms["fwd"] else fwd_tf
+    roof["frac"] = roof["achieved"] / PEAK_BF16_TFLOPS
+    out = {
+        "metric": "gated block-sparse attn TFLOP/s fwd+bwd @n=32K,K=32; decode KV GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(tr["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen3_4b_train: B=1, Hq=32, Hkv=8, d=128, n=32768, block=64, Top-K=32, "
+                        "sparse scope, select+fwd+bwd with dg",
+            "global_batch": w.B, "seq_len": w.n, "parallelism": "single GPU",
+            "attended_pairs": tr["pairs"], "flop_per_step": flop_step,
+        },
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "fwd_tflops": round(fwd_tf, 2),
+        "bwd_tflops": round(bwd_tf, 2),
+        "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
+    }
+    if not args.no_decode:
+        dec = run_decode(max(args.steps, 20), torch)
+        out["decode"] = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms": round(dec["ms"], 5),
+                         "select_ms": round(dec["ms_select"], 5), "bytes": dec["bytes"],
+                         "workload": dec["workload"],
+                         "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": PEAK_HBM_GBS,
+                                      "unit": "GB/s", "frac": round(dec["gbs"] / PEAK_HBM_GBS, 4),
+                                      "traffic": None}}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(w, tr["host"], tr["cnt"], args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
