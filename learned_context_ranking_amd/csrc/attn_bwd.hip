@@ -8,20 +8,26 @@
 // u_ti * (dP_ti - delta_t) with u the ungated weight; this stays exact when g is tiny.
 //
 // Passes (no atomics, deterministic):
-//   1. delta_t = dO_t . o_t                                  (HBM-bound row dots)
-//   2. inverse index: for every key block m, the ascending list of (j, slot) with
+//   1. inverse index: for every key block m, the ascending list of (j, slot) with
 //      idx[j][slot] = m, found by binary search in the ascending idx rows; the lists of
 //      one (b, KV head) live in its own NB * kcap slice of the list buffer
-//   3. query-major pass, one workgroup per (b, KV head, j): dQ and dg. dg_jm has exactly
-//      one owner (the workgroup of j), reduced over its waves through LDS
-//   4. key-major pass, one workgroup per (b, KV head, m): dK and dV over the current block
-//      m itself plus every query block that selected m, all G heads
+//   2. query-major pass, one workgroup per (b, KV head, j, pair of query heads): delta_t =
+//      dO_t . o_t for its rows, dQ, and the workgroup's share of dg. Each dg_jm is owned by
+//      the workgroups of query block j; their per-split partials are summed in a fixed
+//      order by a small reduction kernel
+//   3. key-major pass, one workgroup per (b, KV head, m): dK and dV over the current block
+//      m itself plus every query block that selected m, for all G heads
+//
+// All 64-row operand tiles live in LDS in the swizzled layout of Tile<D>, copied straight
+// from global memory (global_load_lds) one block ahead of use. Operands whose contraction
+// runs along the rows of a tile (K^T for dQ, Q^T and dO^T for dK and dV) are read with the
+// transposing ds_read_b64_tr_b16 from the same natural tile.
+#include <algorithm>
+
 #include "sas_common.h"
 #include "sas_kernels.h"
 
 namespace sas {
-
-void head_split(int G, int* nsplit, int* hpw, int* nw);
 
 // ---------------------------------------------------------------- small kernels
 
@@ -29,25 +35,6 @@ __global__ void fill_f32_kernel(float* p, long long n, float v) {
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (long long)gridDim.x * blockDim.x)
     p[i] = v;
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void delta_kernel(const uint16_t* O, const uint16_t* dO,
-                                                    float* delta, long long rows) {
-  constexpr int LPR = D / 8;  // lanes per row
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = gid / LPR;
-  const int c = (int)(gid % LPR);
-  float acc = 0.0f;
-  if (row < rows) {
-    const u16x8 o = ld16(O + row * D + c * 8);
-    const u16x8 g = ld16(dO + row * D + c * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc += bf2f(o[e]) * bf2f(g[e]);
-  }
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (row < rows && c == 0) delta[row] = acc;
 }
 
 // Number of the valid selection entries of rows j > m that name block m.
@@ -121,319 +108,369 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, in
 
 template <int D>
 struct DqSmem {
-  static constexpr int KP = D + 8, TP = 64 + 8;
-  uint16_t k[64 * KP];    // K natural (A operand of S^T = K Q^T)
-  uint16_t kt[D * TP];    // K^T, keys permuted (A operand of dQ^T = K^T dS^T)
-  uint16_t v[64 * KP];    // V natural (A operand of dP^T = V dO^T)
-  float dgp[4];
+  uint16_t k[2][Tile<D>::ELEMS];   // K blocks: rows for S^T = K Q^T, transposed for dQ^T = K^T dS^T
+  uint16_t v[2][Tile<D>::ELEMS];   // V blocks: rows for dP^T = V dO^T
+  float dgp[2][4];                 // per-wave dg partials of the last two blocks
 };
 
-template <int D, int NW>
-__global__ __launch_bounds__(64 * NW) void dq_kernel(const AttnArgs a, int nsplit, int hpw) {
-  constexpr int NT = 64 * NW, CH = D / 8;
-  using SM = DqSmem<D>;
-  __shared__ __attribute__((aligned(16))) SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// 4 waves: 2 query heads x 2 halves of the 64 query rows (32 rows per wave).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(const AttnArgs a, int nsplit) {
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
-  const int per_j = a.B * a.Hkv * nsplit;
+  const int BH = a.B * a.Hkv;
+  const int per_j = BH * nsplit;
   const int j = NB - 1 - (int)(blockIdx.x / per_j);
-  int r = blockIdx.x % per_j;
-  const int split = r % nsplit;
-  r /= nsplit;
-  const int h = r % a.Hkv, b = r / a.Hkv;
-  const int head0 = split * hpw;
-  const int nheads = min(hpw, G - head0);
-  const bool active = wave < nheads;
-  const int hq = h * G + head0 + (active ? wave : 0);
+  const int r = blockIdx.x % per_j;
+  const int split = r / BH;
+  const int h = (r % BH) % a.Hkv, b = (r % BH) / a.Hkv;
+  const int head0 = split * 2;
+  const int nheads = min(2, G - head0);
+  const int whead = wave >> 1, wrow0 = (wave & 1) * 32;
+  const bool active = whead < nheads;
+  const int hq = h * G + head0 + (active ? whead : 0);
 
   const size_t kv_off = ((size_t)(b * a.Hkv + h) * a.n) * D;
-  const size_t q_off = ((size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock) * D;
-  const size_t row_off = (size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock;
+  const size_t row_off = (size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock + wrow0;
+  const size_t q_off = row_off * D;
   const size_t sel_row = (size_t)(b * a.Hkv + h) * NB + j;
   const int cnt_j = min(max(a.cnt[sel_row], 0), min(a.kcap, j));
   const int32_t* idx_row = a.idx + sel_row * a.kcap;
   const float* lg_row = a.logg != nullptr ? a.logg + sel_row * a.kcap : nullptr;
-  float* dg_row = a.dg + sel_row * a.kcap;
+  float* dg_out = (nsplit == 1 ? a.dg : a.dg_part + (size_t)split * BH * NB * a.kcap) + sel_row * a.kcap;
 
-  bf16x8 qf[2][D / 16], dof[2][D / 16];
+  // Q and dO as B operands (query ql, d = 16 ks + 8 hl + e); delta = dO . O for the same rows
+  bf16x8 qf[D / 16], dof[D / 16];
+  float dlt = 0.0f;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const size_t o = q_off + ql * D + 16 * ks + 8 * hl;
+    if (active) {
+      qf[ks] = as_bf16x8(ld16(a.Q + o));
+      dof[ks] = as_bf16x8(ld16(a.dO + o));
+      const u16x8 ov = ld16(a.O + o);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const size_t o = q_off + (32 * nt + ql) * D + 16 * ks + 8 * hl;
-      qf[nt][ks] = active ? as_bf16x8(ld16(a.Q + o)) : bf16x8{};
-      dof[nt][ks] = active ? as_bf16x8(ld16(a.dO + o)) : bf16x8{};
+      for (int e = 0; e < 8; ++e) dlt += bf2f(ov[e]) * (float)dof[ks][e];
+    } else {
+      qf[ks] = bf16x8{};
+      dof[ks] = bf16x8{};
     }
-  float lse2[2], dl[2];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    lse2[nt] = active ? a.lse_rows[row_off + 32 * nt + ql] * kLog2e : 0.0f;
-    dl[nt] = active ? a.delta[row_off + 32 * nt + ql] : 0.0f;
   }
-  f32x16 dqacc[D / 32][2];
+  dlt += __shfl_xor(dlt, 32, 64);
+  float lse2 = 0.0f;
+  if (active) {
+    if (hl == 0) a.delta[row_off + ql] = dlt;
+    lse2 = a.lse_rows[row_off + ql] * kLog2e;
+  }
+
+  const TileLoader<D, NW> loader(wave, lane);
+  auto block_of = [&](int t, int& m, float& lg2, bool& ok) {
+    m = j; lg2 = 0.0f; ok = true;
+    if (t > 0) {
+      m = __builtin_amdgcn_readfirstlane(idx_row[t - 1]);
+      lg2 = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
+      if (m < 0 || m >= j) { m = 0; lg2 = -INFINITY; ok = false; }
+    }
+  };
+  auto fetch = [&](int m, int buf) {
+    loader.load(sm.k[buf], a.K + kv_off + (size_t)m * kBlock * D);
+    loader.load(sm.v[buf], a.V + kv_off + (size_t)m * kBlock * D);
+  };
+
+  f32x16 dq[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dqacc[dt][nt][i] = 0.0f;
+    for (int i = 0; i < 16; ++i) dq[dt][i] = 0.0f;
   const float c2 = a.scale * kLog2e;
+  const int g16 = lane >> 4, lp = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
+
+  int m_cur;
+  float lg_next;
+  bool ok_next;
+  block_of(0, m_cur, lg_next, ok_next);
+  fetch(m_cur, 0);
+  wait_vm();
+  __syncthreads();
 
   for (int t = 0; t <= cnt_j; ++t) {
-    int m = j;
-    float lg2 = 0.0f;
-    bool ok = true;
-    if (t > 0) {
-      m = idx_row[t - 1];
-      lg2 = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
-      if (m < 0 || m >= j) {
-        m = 0;
-        lg2 = -INFINITY;
-        ok = false;
-      }
+    const int buf = t & 1;
+    const float lg2 = lg_next;
+    const bool ok = ok_next;
+    if (t < cnt_j) {
+      int mn;
+      block_of(t + 1, mn, lg_next, ok_next);
+      fetch(mn, buf ^ 1);
     }
-    __syncthreads();
-    if (t >= 2 && tid == 0) {  // dg of the previous block, reduced over the waves
-      float s = 0.0f;
-      for (int w = 0; w < nheads; ++w) s += sm.dgp[w];
-      if (nsplit == 1) dg_row[t - 2] = s; else atomicAdd(&dg_row[t - 2], s);
+    // dg of the previous block: sum of the four waves' partials
+    if (t >= 2 && tid == 0) {
+      const float* pp = sm.dgp[(t - 1) & 1];
+      dg_out[t - 2] = (pp[0] + pp[1]) + (pp[2] + pp[3]);
     }
-    {
-      const uint16_t* Kb = a.K + kv_off + (size_t)m * kBlock * D;
-      const uint16_t* Vb = a.V + kv_off + (size_t)m * kBlock * D;
+    float dgacc = 0.0f;
+    if (active) {
+      f32x16 st[2], dpt[2];
 #pragma unroll
-      for (int c = tid; c < 64 * CH; c += NT) {
-        const int key = c & 63, col = c >> 6;
-        const u16x8 kv = ld16(Kb + key * D + col * 8);
-        st16(&sm.k[key * SM::KP + col * 8], kv);
-        const int p = perm32(key);
+      for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sm.kt[(col * 8 + e) * SM::TP + p] = kv[e];
-        const int row = c / CH, cc = c % CH;
-        st16(&sm.v[row * SM::KP + cc * 8], ld16(Vb + row * D + cc * 8));
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
-
-    f32x16 st[2][2], dpt[2][2];
+        for (int i = 0; i < 16; ++i) { st[mt][i] = 0.0f; dpt[mt][i] = 0.0f; }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { st[mt][nt][i] = 0.0f; dpt[mt][nt][i] = 0.0f; }
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+        for (int mt = 0; mt < 2; ++mt) {
+          const int o = Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl);
+          st[mt] = mfma32(as_bf16x8(ld16(&sm.k[buf][o])), qf[ks], st[mt]);
+          dpt[mt] = mfma32(as_bf16x8(ld16(&sm.v[buf][o])), dof[ks], dpt[mt]);
+        }
+      const float g = fast_exp2(lg2);
+      bf16x8 dsf[2][2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ka = as_bf16x8(ld16(&sm.k[(32 * mt + ql) * SM::KP + 16 * ks + 8 * hl]));
-        const bf16x8 va = as_bf16x8(ld16(&sm.v[(32 * mt + ql) * SM::KP + 16 * ks + 8 * hl]));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          st[mt][nt] = mfma32(ka, qf[nt][ks], st[mt][nt]);
-          dpt[mt][nt] = mfma32(va, dof[nt][ks], dpt[mt][nt]);
-        }
-      }
-    const float gblk = exp2f(lg2);
-    float dgacc = 0.0f;
-    bf16x8 dsf[2][2][2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
         float ds[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float zu = st[mt][nt][i] * c2;
+          float u = fast_exp2(st[mt][i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
           if (t == 0) {
             const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (key > 32 * nt + ql) zu = -INFINITY;
+            if (key > wrow0 + ql) u = 0.0f;
           }
-          const float u = exp2f(zu - lse2[nt]);
-          const float dd = dpt[mt][nt][i] - dl[nt];
-          dgacc += u * dd;
-          ds[i] = u * gblk * dd;
+          const float w = u * (dpt[mt][i] - dlt);
+          dgacc += w;
+          ds[i] = w * g;
         }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           const int o = 8 * hh;
-          dsf[mt][nt][hh] = pack8(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5], ds[o + 6], ds[o + 7]);
+          dsf[mt][hh] = pack8(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5], ds[o + 6], ds[o + 7]);
         }
       }
-    if (t > 0) {
+      // dQ^T += K^T dS^T (K^T read transposed from the natural K tile)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r0 = 32 * mt + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
+            const bf16x8 ka = join_tr16(lds_tr16(&sm.k[buf][Tile<D>::off(r0, d0)]),
+                                        lds_tr16(&sm.k[buf][Tile<D>::off(r0 + 8, d0)]));
+            dq[dt] = mfma32(ka, dsf[mt][hh], dq[dt]);
+          }
       dgacc = ok ? wave_sum(dgacc) : 0.0f;
-      if (lane == 0) sm.dgp[wave] = dgacc;
     }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 ka = as_bf16x8(ld16(&sm.kt[(32 * dt + ql) * SM::TP + 16 * (2 * mt + hh) + 8 * hl]));
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) dqacc[dt][nt] = mfma32(ka, dsf[mt][nt][hh], dqacc[dt][nt]);
-        }
+    if (lane == 0) sm.dgp[t & 1][wave] = (t > 0 && active) ? dgacc : 0.0f;
+    if (t < cnt_j) wait_vm();
+    __syncthreads();
   }
-  __syncthreads();
   if (tid == 0) {
     if (cnt_j >= 1) {
-      float s = 0.0f;
-      for (int w = 0; w < nheads; ++w) s += sm.dgp[w];
-      if (nsplit == 1) dg_row[cnt_j - 1] = s; else atomicAdd(&dg_row[cnt_j - 1], s);
+      const float* pp = sm.dgp[cnt_j & 1];
+      dg_out[cnt_j - 1] = (pp[0] + pp[1]) + (pp[2] + pp[3]);
     }
+    for (int p = cnt_j; p < a.kcap; ++p) dg_out[p] = 0.0f;
   }
-  if (split == 0)
-    for (int p = cnt_j + tid; p < a.kcap; p += NT) dg_row[p] = 0.0f;
   if (!active) return;
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-        f32x4 v;
-        v[0] = dqacc[dt][nt][4 * g4 + 0] * a.scale;
-        v[1] = dqacc[dt][nt][4 * g4 + 1] * a.scale;
-        v[2] = dqacc[dt][nt][4 * g4 + 2] * a.scale;
-        v[3] = dqacc[dt][nt][4 * g4 + 3] * a.scale;
-        *reinterpret_cast<f32x4*>(a.dQ + q_off + (32 * nt + ql) * D + d0) = v;
-      }
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+      f32x4 v;
+      v[0] = dq[dt][4 * g4 + 0] * a.scale;
+      v[1] = dq[dt][4 * g4 + 1] * a.scale;
+      v[2] = dq[dt][4 * g4 + 2] * a.scale;
+      v[3] = dq[dt][4 * g4 + 3] * a.scale;
+      *reinterpret_cast<f32x4*>(a.dQ + q_off + ql * D + d0) = v;
+    }
+}
+
+// Sum of the per-split dg partials in split order (deterministic).
+__global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int nsplit) {
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x) {
+    float s = 0.0f;
+    for (int k = 0; k < nsplit; ++k) s += part[(long long)k * n + i];
+    dg[i] = s;
+  }
 }
 
 // ---------------------------------------------------------------- key-major: dK, dV
 
 template <int D>
 struct DkvSmem {
-  static constexpr int QP = D + 8, TP = 64 + 8;
-  uint16_t q[64 * QP];    // Q_j natural   (A operand of S = Q K^T)
-  uint16_t dob[64 * QP];  // dO_j natural  (A operand of dP = dO V^T)
-  uint16_t qt[D * TP];    // Q_j^T, queries permuted (A operand of dK^T = Q^T dS)
-  uint16_t dot[D * TP];   // dO_j^T        (A operand of dV^T = dO^T P)
-  float lse2[64];
-  float delta[64];
+  uint16_t q[2][Tile<D>::ELEMS];    // Q_j rows (S = Q K^T) and Q_j^T (dK^T = Q^T dS)
+  uint16_t dob[2][Tile<D>::ELEMS];  // dO_j rows (dP = dO V^T) and dO_j^T (dV^T = dO^T P)
+  float lse2[2][64];
+  float dlt[2][64];
 };
 
-// Workgroup of 4 waves per (b, h, m); wave w owns keys 16w..16w+15 of block m with
-// 16x16x32 MFMAs, so K and V of its keys stay in registers for the whole list.
+// 4 waves per (b, KV head, key block m): wave w owns keys 32 (w & 1) .. + 31 and query rows
+// 32 (w >> 1) .. + 31 of every (query block, head) item; K and V of its keys stay in
+// registers for the whole list. The two query halves are summed through LDS at the end.
 template <int D>
-__global__ __launch_bounds__(256) void dkv_kernel(const AttnArgs a) {
-  using SM = DkvSmem<D>;
-  constexpr int CH = D / 8;
-  __shared__ __attribute__((aligned(16))) SM sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g16 = lane >> 4;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void dkv_kernel(const AttnArgs a) {
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  const int kh = wave & 1, qh = wave >> 1;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
   // Early key blocks are selected most often: launch them first.
   const int per_m = a.B * a.Hkv;
   const int m = (int)(blockIdx.x / per_m);
-  const int r = blockIdx.x % per_m;
-  const int h = r % a.Hkv, b = r / a.Hkv;
+  const int rr = blockIdx.x % per_m;
+  const int h = rr % a.Hkv, b = rr / a.Hkv;
   const long long bh = (long long)b * a.Hkv + h;
 
   const size_t kv_off = ((size_t)bh * a.n + (size_t)m * kBlock) * D;
-  const int key = 16 * wave + l16;  // this lane's key column within block m
-  bf16x8 kf[D / 32], vf[D / 32];
+  const int key = 32 * kh + ql;  // this lane's key column within block m
+  // K and V as B operands of S = Q K^T and dP = dO V^T: key column, d = 16 ks + 8 hl + e
+  bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks) {
-    kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 32 * ks + 8 * g16));
-    vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 32 * ks + 8 * g16));
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 16 * ks + 8 * hl));
+    vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 16 * ks + 8 * hl));
   }
-  f32x4 dk[D / 16], dv[D / 16];
+  f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
   const float c2 = a.scale * kLog2e;
+  const int g16 = lane >> 4, lp = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
   const int off0 = a.inv_off[bh * (NB + 1) + m];
   const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
+  const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
+  const int nitems = (nlist + 1) * G;
+  const TileLoader<D, NW> loader(wave, lane);
 
-  for (int e = 0; e <= nlist; ++e) {
-    int j = m;
-    float lg2 = 0.0f;
+  // item it -> (query block j, head g, base-2 log-gate); entry 0 is the diagonal block
+  auto item_of = [&](int it, int& jj, int& g, float& lg2) {
+    const int e = it / G;
+    g = it - e * G;
+    jj = m;
+    lg2 = 0.0f;
     if (e > 0) {
-      const int p = a.inv_list[bh * NB * a.kcap + off0 + e - 1];
-      j = p / a.kcap;
-      const int slot = p - j * a.kcap;
-      lg2 = a.logg != nullptr ? a.logg[((size_t)bh * NB + j) * a.kcap + slot] * kLog2e : 0.0f;
+      const int p = __builtin_amdgcn_readfirstlane(list[e - 1]);
+      jj = p / a.kcap;
+      const int slot = p - jj * a.kcap;
+      lg2 = a.logg != nullptr ? a.logg[((size_t)bh * NB + jj) * a.kcap + slot] * kLog2e : 0.0f;
     }
-    for (int g = 0; g < G; ++g) {
-      const int hq = h * G + g;
-      const size_t row0 = (size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock;
-      __syncthreads();
-#pragma unroll
-      for (int c = tid; c < 64 * CH; c += 256) {
-        const int row = c & 63, col = c >> 6;
-        const u16x8 qv = ld16(a.Q + (row0 + row) * D + col * 8);
-        const u16x8 gv = ld16(a.dO + (row0 + row) * D + col * 8);
-        st16(&sm.q[row * SM::QP + col * 8], qv);
-        st16(&sm.dob[row * SM::QP + col * 8], gv);
-        const int p = perm16(row);
-#pragma unroll
-        for (int x = 0; x < 8; ++x) {
-          sm.qt[(col * 8 + x) * SM::TP + p] = qv[x];
-          sm.dot[(col * 8 + x) * SM::TP + p] = gv[x];
-        }
-      }
-      if (tid < 64) {
-        sm.lse2[tid] = a.lse_rows[row0 + tid] * kLog2e;
-        sm.delta[tid] = a.delta[row0 + tid];
-      }
-      __syncthreads();
+  };
+  auto fetch = [&](int jj, int g, int buf) {
+    const size_t row0 = (size_t)(b * a.Hq + h * G + g) * a.n + (size_t)jj * kBlock;
+    loader.load(sm.q[buf], a.Q + row0 * D);
+    loader.load(sm.dob[buf], a.dO + row0 * D);
+    if (wave == 0) {
+      __builtin_amdgcn_global_load_lds((const void*)(a.lse_rows + row0 + lane),
+                                       (__attribute__((address_space(3))) void*)sm.lse2[buf], 4, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(a.delta + row0 + lane),
+                                       (__attribute__((address_space(3))) void*)sm.dlt[buf], 4, 0, 0);
+    }
+  };
 
-      f32x4 s[4], dp[4];
+  int j_next, g_next;
+  float lg_next;
+  item_of(0, j_next, g_next, lg_next);
+  fetch(j_next, g_next, 0);
+  wait_vm();
+  __syncthreads();
+
+  for (int it = 0; it < nitems; ++it) {
+    const int buf = it & 1;
+    const int jj = j_next;
+    const float lg2 = lg_next;
+    if (it + 1 < nitems) {
+      item_of(it + 1, j_next, g_next, lg_next);
+      fetch(j_next, g_next, buf ^ 1);
+    }
+    f32x16 s = {}, dp = {};
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int o = Tile<D>::off(32 * qh + ql, 16 * ks + 8 * hl);
+      s = mfma32(as_bf16x8(ld16(&sm.q[buf][o])), kf[ks], s);
+      dp = mfma32(as_bf16x8(ld16(&sm.dob[buf][o])), vf[ks], dp);
+    }
+    // lane holds key column `key`, query rows 32 qh + 8 (i/4) + 4 hl + i%4
+    bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { s[qt][i] = 0.0f; dp[qt][i] = 0.0f; }
+    for (int hh = 0; hh < 2; ++hh) {
+      float pv[8], dsv[8];
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
+      for (int q4 = 0; q4 < 2; ++q4) {
+        const int qb = 32 * qh + 16 * hh + 8 * q4 + 4 * hl;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][qb]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][qb]);
 #pragma unroll
-        for (int qt = 0; qt < 4; ++qt) {
-          const bf16x8 qa = as_bf16x8(ld16(&sm.q[(16 * qt + l16) * SM::QP + 32 * ks + 8 * g16]));
-          const bf16x8 ga = as_bf16x8(ld16(&sm.dob[(16 * qt + l16) * SM::QP + 32 * ks + 8 * g16]));
-          s[qt] = mfma16(qa, kf[ks], s[qt]);
-          dp[qt] = mfma16(ga, vf[ks], dp[qt]);
-        }
-      float pv[4][4], dsv[4][4];
-#pragma unroll
-      for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int q = 16 * qt + 4 * g16 + i;
-          float z = s[qt][i] * c2 + lg2;
-          if (e == 0 && key > q) z = -INFINITY;
-          const float p = exp2f(z - sm.lse2[q]);
-          pv[qt][i] = p;
-          dsv[qt][i] = p * (dp[qt][i] - sm.delta[q]);
-        }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8 pb = pack8(pv[2 * kk][0], pv[2 * kk][1], pv[2 * kk][2], pv[2 * kk][3],
-                                pv[2 * kk + 1][0], pv[2 * kk + 1][1], pv[2 * kk + 1][2], pv[2 * kk + 1][3]);
-        const bf16x8 sb = pack8(dsv[2 * kk][0], dsv[2 * kk][1], dsv[2 * kk][2], dsv[2 * kk][3],
-                                dsv[2 * kk + 1][0], dsv[2 * kk + 1][1], dsv[2 * kk + 1][2], dsv[2 * kk + 1][3]);
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16x8 da = as_bf16x8(ld16(&sm.dot[(16 * dt + l16) * SM::TP + 32 * kk + 8 * g16]));
-          const bf16x8 qa = as_bf16x8(ld16(&sm.qt[(16 * dt + l16) * SM::TP + 32 * kk + 8 * g16]));
-          dv[dt] = mfma16(da, pb, dv[dt]);
-          dk[dt] = mfma16(qa, sb, dk[dt]);
+        for (int x = 0; x < 4; ++x) {
+          const int i = 8 * hh + 4 * q4 + x;
+          float p = fast_exp2(s[i] * c2 + (lg2 - l4[x] * kLog2e));
+          if (jj == m && key > qb + x) p = 0.0f;
+          pv[4 * q4 + x] = p;
+          dsv[4 * q4 + x] = p * (dp[i] - d4[x]);
         }
       }
+      pb[hh] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      sb[hh] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
     }
-  }
-  float* dKp = a.dK + kv_off + key * D;
-  float* dVp = a.dV + kv_off + key * D;
+    // dV^T += dO^T P and dK^T += Q^T dS; the transposed operands come from tr16 reads
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt) {
-    const int d0 = 16 * dt + 4 * g16;
-    f32x4 kv = dk[dt] * a.scale;
-    *reinterpret_cast<f32x4*>(dKp + d0) = kv;
-    *reinterpret_cast<f32x4*>(dVp + d0) = dv[dt];
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r0 = 32 * qh + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
+        const bf16x8 da = join_tr16(lds_tr16(&sm.dob[buf][Tile<D>::off(r0, d0)]),
+                                    lds_tr16(&sm.dob[buf][Tile<D>::off(r0 + 8, d0)]));
+        const bf16x8 qa = join_tr16(lds_tr16(&sm.q[buf][Tile<D>::off(r0, d0)]),
+                                    lds_tr16(&sm.q[buf][Tile<D>::off(r0 + 8, d0)]));
+        dv[dt] = mfma32(da, pb[hh], dv[dt]);
+        dk[dt] = mfma32(qa, sb[hh], dk[dt]);
+      }
+    if (it + 1 < nitems) wait_vm();
+    __syncthreads();
+  }
+
+  // Sum the two query halves: waves with qh = 1 hand their partials over through LDS.
+  float* red = reinterpret_cast<float*>(&sm.q[0][0]);   // 2 key halves x 2 x (D/32 x 16 x 64) floats
+  constexpr int PER = (D / 32) * 16 * 64;
+  __syncthreads();
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[(kh * 2 + 0) * PER + (dt * 16 + i) * 64 + lane] = dk[dt][i];
+        red[(kh * 2 + 1) * PER + (dt * 16 + i) * 64 + lane] = dv[dt][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    float* dKp = a.dK + kv_off + key * D;
+    float* dVp = a.dV + kv_off + key * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+        f32x4 kv, vv;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 4 * g4 + x;
+          kv[x] = (dk[dt][i] + red[(kh * 2 + 0) * PER + (dt * 16 + i) * 64 + lane]) * a.scale;
+          vv[x] = dv[dt][i] + red[(kh * 2 + 1) * PER + (dt * 16 + i) * 64 + lane];
+        }
+        *reinterpret_cast<f32x4*>(dKp + d0) = kv;
+        *reinterpret_cast<f32x4*>(dVp + d0) = vv;
+      }
   }
 }
 
@@ -441,42 +478,38 @@ __global__ __launch_bounds__(256) void dkv_kernel(const AttnArgs a) {
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+static int dq_splits(int G) { return (G + 1) / 2; }
+
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap) {
   (void)d;
   const size_t NB = (size_t)n / kBlock;
   const size_t bh = (size_t)B * Hkv;
+  const size_t kc = (size_t)(kcap > 0 ? kcap : 1);
+  const int ns = dq_splits(Hq / Hkv);
   return al256((size_t)B * Hq * n * sizeof(float))            // delta
          + al256(bh * NB * sizeof(int32_t))                    // counts
          + al256(bh * (NB + 1) * sizeof(int32_t))              // offsets
-         + al256(bh * NB * (size_t)(kcap > 0 ? kcap : 1) * sizeof(int32_t));  // lists
+         + al256(bh * NB * kc * sizeof(int32_t))               // lists
+         + (ns > 1 ? al256((size_t)ns * bh * NB * kc * sizeof(float)) : 0);  // dg partials
 }
 
 template <int D>
 static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   const int NB = a.n / kBlock;
   const long long nrows = (long long)a.B * a.Hkv * NB;
-  const long long qrows = (long long)a.B * a.Hq * a.n;
-  {
-    const long long threads = qrows * (D / 8);
-    hipLaunchKernelGGL(delta_kernel<D>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
-                       a.Oout != nullptr ? a.Oout : a.O, a.dO, a.delta, qrows);
-  }
   hipLaunchKernelGGL(inv_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, a.idx, a.cnt,
                      NB, a.kcap, nrows, a.inv_cnt, (const int32_t*)nullptr, (int32_t*)nullptr);
   hipLaunchKernelGGL(inv_scan_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, st, a.inv_cnt, NB,
                      a.inv_off);
   hipLaunchKernelGGL(inv_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, a.idx, a.cnt,
                      NB, a.kcap, nrows, a.inv_cnt, (const int32_t*)a.inv_off, a.inv_list);
-  int nsplit, hpw, nw;
-  head_split(a.Hq / a.Hkv, &nsplit, &hpw, &nw);
-  if (nsplit > 1) {
-    const long long ndg = nrows * a.kcap;
-    hipLaunchKernelGGL(fill_f32_kernel, dim3(1024), dim3(256), 0, st, a.dg, ndg, 0.0f);
+  const int nsplit = dq_splits(a.Hq / a.Hkv);
+  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+  if (nsplit > 1 && a.kcap > 0) {
+    const long long n = nrows * a.kcap;
+    hipLaunchKernelGGL(dg_reduce_kernel, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)),
+                       dim3(256), 0, st, (const float*)a.dg_part, a.dg, n, nsplit);
   }
-  const unsigned grid = (unsigned)nrows * nsplit;
-  if (nw == 1) hipLaunchKernelGGL((dq_kernel<D, 1>), dim3(grid), dim3(64), 0, st, a, nsplit, hpw);
-  else if (nw == 2) hipLaunchKernelGGL((dq_kernel<D, 2>), dim3(grid), dim3(128), 0, st, a, nsplit, hpw);
-  else hipLaunchKernelGGL((dq_kernel<D, 4>), dim3(grid), dim3(256), 0, st, a, nsplit, hpw);
   hipLaunchKernelGGL(dkv_kernel<D>, dim3((unsigned)nrows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -484,6 +517,7 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
 hipError_t launch_bwd(AttnArgs a, void* ws, hipStream_t st) {
   const size_t NB = (size_t)a.n / kBlock;
   const size_t bh = (size_t)a.B * a.Hkv;
+  const size_t kc = (size_t)(a.kcap > 0 ? a.kcap : 1);
   char* p = (char*)ws;
   a.delta = (float*)p;
   p += al256((size_t)a.B * a.Hq * a.n * sizeof(float));
@@ -492,6 +526,8 @@ hipError_t launch_bwd(AttnArgs a, void* ws, hipStream_t st) {
   a.inv_off = (int32_t*)p;
   p += al256(bh * (NB + 1) * sizeof(int32_t));
   a.inv_list = (int32_t*)p;
+  p += al256(bh * NB * kc * sizeof(int32_t));
+  a.dg_part = (float*)p;
   if (a.d == 128) return launch_bwd_d<128>(a, st);
   return launch_bwd_d<64>(a, st);
 }

@@ -48,13 +48,85 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
+// Eight fp32 values to bf16 (round-to-nearest-even); pairs compile to v_cvt_pk_bf16_f32.
 __device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4,
                                          float a5, float a6, float a7) {
-  u16x8 v;
-  v[0] = f2bf(a0); v[1] = f2bf(a1); v[2] = f2bf(a2); v[3] = f2bf(a3);
-  v[4] = f2bf(a4); v[5] = f2bf(a5); v[6] = f2bf(a6); v[7] = f2bf(a7);
-  return as_bf16x8(v);
+  bf16x8 v;
+  v[0] = (__bf16)a0; v[1] = (__bf16)a1; v[2] = (__bf16)a2; v[3] = (__bf16)a3;
+  v[4] = (__bf16)a4; v[5] = (__bf16)a5; v[6] = (__bf16)a6; v[7] = (__bf16)a7;
+  return v;
 }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes, lane l'
+// receives element l'%4 of the 8-byte chunk addressed by lane 4e + l'/4, for e = 0..3.
+// Used to read MFMA operands whose k-dimension is strided in LDS (V^T, K^T, Q^T, dO^T)
+// from tiles stored in their natural row-major layout.
+__device__ __forceinline__ i16x4 lds_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)((__attribute__((address_space(3))) uint16_t*)p));
+}
+__device__ __forceinline__ bf16x8 join_tr16(i16x4 lo, i16x4 hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// A 64-row tile of bf16 rows of D elements in LDS, unpadded (D*2 bytes per row) with the
+// 16-byte chunks of row r stored at chunk position c ^ swz(r). The swizzle makes both
+//  - row reads (16 lanes read the same chunk of 16 consecutive rows, ds_read_b128) and
+//  - transposing reads (8 consecutive rows x 4 consecutive chunks, ds_read_b64_tr_b16)
+// touch every LDS bank at most once / exactly twice, i.e. run without bank conflicts.
+// Tiles are filled with global_load_lds (lane i of an instruction writes bytes
+// [16 i, 16 i + 16) of a 1 KB window), so the swizzle is applied on the global side.
+template <int D>
+struct Tile {
+  static constexpr int CPR = D / 8;          // 16-byte chunks per row
+  static constexpr int ELEMS = 64 * D;
+  __device__ static __forceinline__ int swz(int r) {
+    return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  // element offset of (row r, element d)
+  __device__ static __forceinline__ int off(int r, int d) {
+    return r * D + ((((d >> 3) ^ swz(r))) << 3) + (d & 7);
+  }
+};
+
+// Asynchronous global -> LDS copy of a 64-row tile whose rows are D elements apart in
+// global memory. Wave w issues the 1 KB windows w, w + NW, ...; the per-lane source
+// offsets depend only on (wave, lane), so they are computed once (TileLoader) and each
+// copy adds a wave-uniform base. Completion is awaited with wait_vm() before the barrier
+// that publishes the tile.
+template <int D, int NW>
+struct TileLoader {
+  static constexpr int CPR = Tile<D>::CPR;
+  static constexpr int N = CPR / NW;           // 1 KB windows per wave
+  static_assert(CPR % NW == 0, "tile windows must split evenly over the waves");
+  uint32_t off[N];                             // byte offset of this lane's 16 B in global memory
+  int wave;
+  __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int s = 64 * (wave + NW * i) + lane;
+      const int r = s / CPR, p = s % CPR;
+      off[i] = (uint32_t)(r * D + ((p ^ Tile<D>::swz(r)) << 3)) * 2u;
+    }
+  }
+  __device__ __forceinline__ void load(uint16_t* lds_tile, const uint16_t* g) const {
+    const char* gb = (const char*)g;
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(gb + off[i]),
+                                       (__attribute__((address_space(3))) void*)(lds_tile + 512 * (wave + NW * i)),
+                                       16, 0, 0);
+  }
+};
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 2^x with the hardware v_exp_f32 (no denormal range reduction: results below 2^-126
+// flush to zero, which is harmless for softmax weights relative to a maximum >= 1/256).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -42,6 +42,7 @@ struct AttnArgs {
   float* dg;
   // backward workspace pieces
   float* delta;
+  float* dg_part;        // [nsplit][rows][kcap] per-split gate-gradient partials
   int32_t* inv_cnt;
   int32_t* inv_off;
   int32_t* inv_list;
