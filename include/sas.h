@@ -153,6 +153,8 @@ size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int blo
  *   dg fp32 [B][Hkv][n/64][kcap], out: aligned with idx, 0 on padding slots.
  *   ws, ws_bytes  device workspace of at least sas_attn_bwd_workspace_size() bytes,
  *            16-byte aligned; its contents need no initialisation.
+ * Returns SAS_ERR_UNSUPPORTED when (Hq / Hkv) * n * d * 2 >= 2^31 (the key-major pass
+ * addresses the query rows of one KV group with 31-bit offsets).
  */
 sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                         const void* dO, const float* lse_rows, const int32_t* idx,

@@ -27,6 +27,17 @@
 #include "sas_common.h"
 #include "sas_kernels.h"
 
+// Build-time tuning knobs (defaults are the measured best on gfx950)
+#ifndef SAS_DQ_WPE
+#define SAS_DQ_WPE 2
+#endif
+#ifndef SAS_DKV_NBUF
+#define SAS_DKV_NBUF 3   // ring depth of the key-major pass
+#endif
+#ifndef SAS_DKV_WPE
+#define SAS_DKV_WPE 1    // waves per SIMD the key-major pass is built for
+#endif
+
 namespace sas {
 
 // ---------------------------------------------------------------- small kernels
@@ -106,19 +117,17 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, in
 
 // ---------------------------------------------------------------- query-major: dQ, dg
 
-template <int D>
-struct DqSmem {
-  uint16_t k[2][Tile<D>::ELEMS];   // K blocks: rows for S^T = K Q^T, transposed for dQ^T = K^T dS^T
-  uint16_t v[2][Tile<D>::ELEMS];   // V blocks: rows for dP^T = V dO^T
-  float dgp[2][4];                 // per-wave dg partials of the last two blocks
-};
-
 // 4 waves: 2 query heads x 2 halves of the 64 query rows (32 rows per wave).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SAS_DQ_WPE, SAS_DQ_WPE)))
 void dq_kernel(const AttnArgs a, int nsplit) {
   constexpr int NW = 4;
-  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
+  // K/V double buffers as distinct LDS objects selected at compile time (see fwd_kernel)
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[Tile<D>::ELEMS];
+  __shared__ float dgp[2][4];   // per-wave dg partials of the last two blocks
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
@@ -169,17 +178,23 @@ void dq_kernel(const AttnArgs a, int nsplit) {
   }
 
   const TileLoader<D, NW> loader(wave, lane);
+  LaneList sel;   // the selection row, one entry per lane
+  auto load_sel = [&](int i, int& v, float& g) {
+    v = i < cnt_j ? idx_row[i] : 0;
+    g = (i < cnt_j && lg_row != nullptr) ? lg_row[i] * kLog2e : 0.0f;
+  };
   auto block_of = [&](int t, int& m, float& lg2, bool& ok) {
     m = j; lg2 = 0.0f; ok = true;
     if (t > 0) {
-      m = __builtin_amdgcn_readfirstlane(idx_row[t - 1]);
-      lg2 = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
+      sel.ensure(t - 1, lane, load_sel);
+      m = sel.at(t - 1);
+      lg2 = sel.gat(t - 1);
       if (m < 0 || m >= j) { m = 0; lg2 = -INFINITY; ok = false; }
     }
   };
-  auto fetch = [&](int m, int buf) {
-    loader.load(sm.k[buf], a.K + kv_off + (size_t)m * kBlock * D);
-    loader.load(sm.v[buf], a.V + kv_off + (size_t)m * kBlock * D);
+  auto fetch = [&](int m, uint16_t* kb, uint16_t* vb) {
+    loader.load(kb, a.K + kv_off + (size_t)m * kBlock * D);
+    loader.load(vb, a.V + kv_off + (size_t)m * kBlock * D);
   };
 
   f32x16 dq[D / 32];
@@ -195,82 +210,81 @@ void dq_kernel(const AttnArgs a, int nsplit) {
   float lg_next;
   bool ok_next;
   block_of(0, m_cur, lg_next, ok_next);
-  fetch(m_cur, 0);
+  fetch(m_cur, sk0, sv0);
   wait_vm();
   __syncthreads();
 
-  for (int t = 0; t <= cnt_j; ++t) {
-    const int buf = t & 1;
+  // one block: prefetch block t+1 into (kn, vn), compute block t from (kc, vc)
+  auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     const float lg2 = lg_next;
     const bool ok = ok_next;
     if (t < cnt_j) {
       int mn;
       block_of(t + 1, mn, lg_next, ok_next);
-      fetch(mn, buf ^ 1);
+      fetch(mn, kn, vn);
     }
     // dg of the previous block: sum of the four waves' partials
     if (t >= 2 && tid == 0) {
-      const float* pp = sm.dgp[(t - 1) & 1];
+      const float* pp = dgp[(t - 1) & 1];
       dg_out[t - 2] = (pp[0] + pp[1]) + (pp[2] + pp[3]);
     }
     float dgacc = 0.0f;
     if (active) {
-      f32x16 st[2], dpt[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { st[mt][i] = 0.0f; dpt[mt][i] = 0.0f; }
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const int o = Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl);
-          st[mt] = mfma32(as_bf16x8(ld16(&sm.k[buf][o])), qf[ks], st[mt]);
-          dpt[mt] = mfma32(as_bf16x8(ld16(&sm.v[buf][o])), dof[ks], dpt[mt]);
-        }
       const float g = fast_exp2(lg2);
-      bf16x8 dsf[2][2];
+      // The two 32-key halves of the block one after the other; the scheduling barrier keeps
+      // the second half from being hoisted into the first (which would overflow 256 VGPRs).
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        float ds[16];
+        if (mt == 1) __builtin_amdgcn_sched_barrier(0);
+        f32x16 st = {}, dpt = {};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float u = fast_exp2(st[mt][i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
-          if (t == 0) {
-            const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (key > wrow0 + ql) u = 0.0f;
-          }
-          const float w = u * (dpt[mt][i] - dlt);
-          dgacc += w;
-          ds[i] = w * g;
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const int o = Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl);
+          st = mfma32(as_bf16x8(ld16(&kc[o])), qf[ks], st);
+          dpt = mfma32(as_bf16x8(ld16(&vc[o])), dof[ks], dpt);
         }
+        bf16x8 dsf[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int o = 8 * hh;
-          dsf[mt][hh] = pack8(ds[o], ds[o + 1], ds[o + 2], ds[o + 3], ds[o + 4], ds[o + 5], ds[o + 6], ds[o + 7]);
+          float ds[8];
+#pragma unroll
+          for (int x = 0; x < 8; ++x) {
+            const int i = 8 * hh + x;
+            float u = fast_exp2(st[i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
+            if (t == 0) {
+              const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+              if (key > wrow0 + ql) u = 0.0f;
+            }
+            const float w = u * (dpt[i] - dlt);
+            dgacc += w;
+            ds[x] = w * g;
+          }
+          dsf[hh] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
         }
-      }
-      // dQ^T += K^T dS^T (K^T read transposed from the natural K tile)
+        // dQ^T += K^T dS^T over these 32 keys (K^T read transposed from the natural K tile)
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int r0 = 32 * mt + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
-            const bf16x8 ka = join_tr16(lds_tr16(&sm.k[buf][Tile<D>::off(r0, d0)]),
-                                        lds_tr16(&sm.k[buf][Tile<D>::off(r0 + 8, d0)]));
-            dq[dt] = mfma32(ka, dsf[mt][hh], dq[dt]);
+            const bf16x8 ka = join_tr16(lds_tr16(&kc[Tile<D>::off(r0, d0)]),
+                                        lds_tr16(&kc[Tile<D>::off(r0 + 8, d0)]));
+            dq[dt] = mfma32(ka, dsf[hh], dq[dt]);
           }
+      }
       dgacc = ok ? wave_sum(dgacc) : 0.0f;
     }
-    if (lane == 0) sm.dgp[t & 1][wave] = (t > 0 && active) ? dgacc : 0.0f;
+    if (lane == 0) dgp[t & 1][wave] = (t > 0 && active) ? dgacc : 0.0f;
     if (t < cnt_j) wait_vm();
     __syncthreads();
+  };
+  for (int t = 0; t <= cnt_j; t += 2) {
+    step(t, sk0, sv0, sk1, sv1);
+    if (t + 1 <= cnt_j) step(t + 1, sk1, sv1, sk0, sv0);
   }
   if (tid == 0) {
     if (cnt_j >= 1) {
-      const float* pp = sm.dgp[cnt_j & 1];
+      const float* pp = dgp[cnt_j & 1];
       dg_out[cnt_j - 1] = (pp[0] + pp[1]) + (pp[2] + pp[3]);
     }
     for (int p = cnt_j; p < a.kcap; ++p) dg_out[p] = 0.0f;
@@ -302,28 +316,43 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 
 // ---------------------------------------------------------------- key-major: dK, dV
 
-template <int D>
-struct DkvSmem {
-  uint16_t q[2][Tile<D>::ELEMS];    // Q_j rows (S = Q K^T) and Q_j^T (dK^T = Q^T dS)
-  uint16_t dob[2][Tile<D>::ELEMS];  // dO_j rows (dP = dO V^T) and dO_j^T (dV^T = dO^T P)
-  float lse2[2][64];
-  float dlt[2][64];
-};
-
 // 4 waves per (b, KV head, key block m): wave w owns keys 32 (w & 1) .. + 31 and query rows
 // 32 (w >> 1) .. + 31 of every (query block, head) item; K and V of its keys stay in
 // registers for the whole list. The two query halves are summed through LDS at the end.
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Items stream through a ring of NBUF buffer sets (distinct LDS objects, selected at compile
+// time, so the compiler never waits for a copy in flight before computing): item it+NBUF-1
+// is copied in while item it is computed. The copies are buffer loads into LDS addressed
+// by a per-lane constant offset plus a scalar per-item offset, so they cost no vector
+// instructions. Operand reads are issued in two batches (row reads before S and dP, the
+// transposed reads before the softmax); in the swizzled Tile layout each read address is
+// one of two lane base offsets XORed with a constant plus an immediate. WPE is the number
+// of waves per SIMD the kernel is built for (1: 512 registers, 2: 256).
+template <int D, int NBUF, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void dkv_kernel(const AttnArgs a) {
+  static_assert(NBUF == 2 || NBUF == 3, "ring depth");
   constexpr int NW = 4;
-  __shared__ __attribute__((aligned(16))) DkvSmem<D> sm;
+  constexpr int TE = Tile<D>::ELEMS;
+  // Each Q buffer carries the item's lse and delta rows behind the tile: every wave copies
+  // one 64-float row (waves 0 / 1: lse / delta, waves 2 / 3 a spare copy of lse) into its
+  // own slot, without a branch, so the copies target only 2 * NBUF distinct LDS objects,
+  // which the compiler tracks apart and waits for one at a time.
+  constexpr int TQ = TE + 4 * 128;
+  constexpr int E2 = NBUF >= 3 ? TQ : 8, F2 = NBUF >= 3 ? TE : 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sq2[E2];
+  __shared__ __attribute__((aligned(16))) uint16_t so0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t so1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t so2[F2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
   const int kh = wave & 1, qh = wave >> 1;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
-  // Early key blocks are selected most often: launch them first.
+  // Early key blocks are selected most often: launch them first; consecutive workgroups
+  // differ in (batch, KV head), so each KV head stays on one XCD (one L2) when B * Hkv is a
+  // multiple of 8.
   const int per_m = a.B * a.Hkv;
   const int m = (int)(blockIdx.x / per_m);
   const int rr = blockIdx.x % per_m;
@@ -347,109 +376,192 @@ void dkv_kernel(const AttnArgs a) {
   const float c2 = a.scale * kLog2e;
   const int g16 = lane >> 4, lp = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
+  // Lane base offsets (elements) in the Tile layout. Row read ks of row r = 32 qh + ql at
+  // d = 16 ks + 8 hl sits at rx ^ (ks << 4); the transposing read of rows r0 + tr_row
+  // (r0 = 32 qh + 16 hh + 8 half) at d = 32 dt + tr_d sits at r0 D + (tx ^ ((4 dt ^ 2 half) << 3)):
+  // the swizzle of row r0 + tr_row is swz(tr_row) ^ 2 half because r0 is a multiple of 8.
+  const int rrow = 32 * qh + ql;
+  const int rx0 = rrow * D + ((hl ^ Tile<D>::swz(rrow)) << 3);
+  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
   const int off0 = a.inv_off[bh * (NB + 1) + m];
   const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
   const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
   const int nitems = (nlist + 1) * G;
-  const TileLoader<D, NW> loader(wave, lane);
 
-  // item it -> (query block j, head g, base-2 log-gate); entry 0 is the diagonal block
-  auto item_of = [&](int it, int& jj, int& g, float& lg2) {
-    const int e = it / G;
-    g = it - e * G;
-    jj = m;
-    lg2 = 0.0f;
-    if (e > 0) {
-      const int p = __builtin_amdgcn_readfirstlane(list[e - 1]);
-      jj = p / a.kcap;
-      const int slot = p - jj * a.kcap;
-      lg2 = a.logg != nullptr ? a.logg[((size_t)bh * NB + jj) * a.kcap + slot] * kLog2e : 0.0f;
-    }
-  };
-  auto fetch = [&](int jj, int g, int buf) {
-    const size_t row0 = (size_t)(b * a.Hq + h * G + g) * a.n + (size_t)jj * kBlock;
-    loader.load(sm.q[buf], a.Q + row0 * D);
-    loader.load(sm.dob[buf], a.dO + row0 * D);
-    if (wave == 0) {
-      __builtin_amdgcn_global_load_lds((const void*)(a.lse_rows + row0 + lane),
-                                       (__attribute__((address_space(3))) void*)sm.lse2[buf], 4, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(a.delta + row0 + lane),
-                                       (__attribute__((address_space(3))) void*)sm.dlt[buf], 4, 0, 0);
-    }
-  };
-
-  int j_next, g_next;
-  float lg_next;
-  item_of(0, j_next, g_next, lg_next);
-  fetch(j_next, g_next, 0);
-  wait_vm();
-  __syncthreads();
-
-  for (int it = 0; it < nitems; ++it) {
-    const int buf = it & 1;
-    const int jj = j_next;
-    const float lg2 = lg_next;
-    if (it + 1 < nitems) {
-      item_of(it + 1, j_next, g_next, lg_next);
-      fetch(j_next, g_next, buf ^ 1);
-    }
-    f32x16 s = {}, dp = {};
+  // Buffer resources over the G query heads of this (b, KV head): Q and dO rows, lse and
+  // delta rows. Sizes were checked on the host to fit 31 bits.
+  const size_t head0 = (size_t)(b * a.Hq + h * G) * a.n;
+  const int qbytes = G * a.n * D * 2, rbytes = G * a.n * 4;
+  const uint16_t* qbase = a.Q + head0 * D;
+  const uint16_t* obase = a.dO + head0 * D;
+  const float* rbase = (wave == 1 ? a.delta : a.lse_rows) + head0;
+  // per-lane byte offsets of this wave's 16-byte slots within a 64-row tile
+  constexpr int NWIN = Tile<D>::CPR / NW;
+  uint32_t voff[NWIN];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const int o = Tile<D>::off(32 * qh + ql, 16 * ks + 8 * hl);
-      s = mfma32(as_bf16x8(ld16(&sm.q[buf][o])), kf[ks], s);
-      dp = mfma32(as_bf16x8(ld16(&sm.dob[buf][o])), vf[ks], dp);
+  for (int i = 0; i < NWIN; ++i) {
+    const int sidx = 64 * (wave + NW * i) + lane;
+    const int r = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
+    voff[i] = (uint32_t)(r * D + ((c ^ Tile<D>::swz(r)) << 3)) * 2u;
+  }
+
+  // Entries are visited in descending j with the diagonal block j = m last; each list is
+  // held one entry per lane (one window for the item being computed, one for the copies).
+  auto load_lst = [&](int e, int& v, float& g) {
+    v = m;
+    g = 0.0f;
+    if (e < nlist) {
+      const int p = list[nlist - 1 - e];
+      v = p / a.kcap;
+      const int slot = p - v * a.kcap;
+      g = a.logg != nullptr ? a.logg[((size_t)bh * NB + v) * a.kcap + slot] * kLog2e : 0.0f;
     }
-    // lane holds key column `key`, query rows 32 qh + 8 (i/4) + 4 hl + i%4
-    bf16x8 pb[2], sb[2];
+  };
+  LaneList lst_c, lst_f;
+  // (ec, gc): entry and head of the item being computed; (ef, gf): the next item to copy,
+  // which stays at the last item once reached (copies past the end repeat it)
+  int ec = 0, gc = 0, ef = 0, gf = 0;
+  auto fetch = [&](uint16_t* qb, uint16_t* ob) {
+    int jj = m;
+    if (ef < nlist) {
+      lst_f.ensure(ef, lane, load_lst);
+      jj = lst_f.at(ef);
+    }
+    const uint32_t row = (uint32_t)(gf * a.n + jj * kBlock);
+    const uint32_t so = row * (uint32_t)(D * 2);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(qbase, qbytes, qb + 512 * (wave + NW * i), voff[i], so);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(obase, qbytes, ob + 512 * (wave + NW * i), voff[i], so);
+    buffer_load_lds4(rbase, rbytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
+    if (!(ef == nlist && gf == G - 1)) {
+      if (++gf == G) { gf = 0; ++ef; }
+    }
+  };
+  // per item each wave issues 2 * NWIN tile copies and one row copy
+  constexpr int PER = 2 * NWIN + 1;
+  static_assert(PER < 64, "copies in flight exceed the vmcnt range");
+
+  // softmax of the item in (qc, oc) from its S^T and dP^T, then dV^T += dO^T P, dK^T += Q^T dS
+  // (one code path for both cases: a branch here would make the compiler copy the
+  // accumulators at the merge)
+  auto finish = [&](bool diag, float lg2, const uint16_t* qc, const uint16_t* oc,
+                    const f32x16& s, const f32x16& dp, const bf16x8 (&da)[D / 32][2],
+                    const bf16x8 (&qa)[D / 32][2]) {
+    const float* lc = reinterpret_cast<const float*>(qc + TE);
+    const float* dc = reinterpret_cast<const float*>(qc + TE + 128);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       float pv[8], dsv[8];
 #pragma unroll
       for (int q4 = 0; q4 < 2; ++q4) {
         const int qb = 32 * qh + 16 * hh + 8 * q4 + 4 * hl;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[buf][qb]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[buf][qb]);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lc[qb]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dc[qb]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = 8 * hh + 4 * q4 + x;
           float p = fast_exp2(s[i] * c2 + (lg2 - l4[x] * kLog2e));
-          if (jj == m && key > qb + x) p = 0.0f;
+          if (diag && key > qb + x) p = 0.0f;   // causal mask of the diagonal block
           pv[4 * q4 + x] = p;
           dsv[4 * q4 + x] = p * (dp[i] - d4[x]);
         }
       }
-      pb[hh] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      sb[hh] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+      const bf16x8 pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      const bf16x8 sb = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dv[dt] = mfma32(da[dt][hh], pb, dv[dt]);
+        dk[dt] = mfma32(qa[dt][hh], sb, dk[dt]);
+      }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS; the transposed operands come from tr16 reads
+  };
+
+  // one item: copy the next item into (qn, on), compute the current one from (qc, oc). A
+  // copy is issued on every step (past the end of the list it repeats the last item into a
+  // buffer that is not read again), so every step has the same number of copies in flight
+  // and the compiler's wait tracking stays exact across iterations.
+  auto step = [&](const uint16_t* qc, const uint16_t* oc, uint16_t* qn, uint16_t* on) {
+    if (NBUF == 3) wait_vm_n<PER>(); else wait_vm();
+    barrier_lds();
+    int jj = m;
+    float lg2 = 0.0f;
+    if (ec < nlist) {
+      lst_c.ensure(ec, lane, load_lst);
+      jj = lst_c.at(ec);
+      lg2 = lst_c.gat(ec);
+    }
+    const bool diag = ec == nlist;
+    if (++gc == G) { gc = 0; ++ec; }
+    fetch(qn, on);
+    // S^T = K Q^T and dP^T = V dO^T for this wave's 32 keys x 32 query rows
+    int rx = rx0, tx = tx0;
+    asm volatile("" : "+v"(rx), "+v"(tx));   // keeps per-(buffer, read) addresses unhoisted
+    bf16x8 qr[D / 16], orw[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qr[ks] = as_bf16x8(ld16(&qc[rx ^ (ks << 4)]));
+      orw[ks] = as_bf16x8(ld16(&oc[rx ^ (ks << 4)]));
+    }
+    // keep the reads together ahead of the products (the scheduler would otherwise pair each
+    // read with its product and expose the LDS latency every time)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mfma32(qr[ks], kf[ks], s);
+      dp = mfma32(orw[ks], vf[ks], dp);
+    }
+    // transposed operands of dV and dK, read while the softmax runs
+    bf16x8 da[D / 32][2], qa[D / 32][2];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = 32 * qh + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
-        const bf16x8 da = join_tr16(lds_tr16(&sm.dob[buf][Tile<D>::off(r0, d0)]),
-                                    lds_tr16(&sm.dob[buf][Tile<D>::off(r0 + 8, d0)]));
-        const bf16x8 qa = join_tr16(lds_tr16(&sm.q[buf][Tile<D>::off(r0, d0)]),
-                                    lds_tr16(&sm.q[buf][Tile<D>::off(r0 + 8, d0)]));
-        dv[dt] = mfma32(da, pb[hh], dv[dt]);
-        dk[dt] = mfma32(qa, sb[hh], dk[dt]);
+        const int r0 = 32 * qh + 16 * hh;
+        const int o0 = r0 * D + (tx ^ ((4 * dt) << 3)), o1 = (r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3));
+        da[dt][hh] = join_tr16(lds_tr16(&oc[o0]), lds_tr16(&oc[o1]));
+        qa[dt][hh] = join_tr16(lds_tr16(&qc[o0]), lds_tr16(&qc[o1]));
       }
-    if (it + 1 < nitems) wait_vm();
-    __syncthreads();
+    finish(diag, lg2, qc, oc, s, dp, da, qa);
+  };
+
+  // Whole rounds of NBUF steps run without conditions inside (so the compiler's wait
+  // tracking is exact at every read); the remaining steps follow the loop.
+  const int nfull = nitems - nitems % NBUF;
+  if (NBUF == 2) {
+    fetch(sq0, so0);
+    for (int it = 0; it < nfull; it += 2) {
+      step(sq0, so0, sq1, so1);
+      step(sq1, so1, sq0, so0);
+    }
+    if (nfull < nitems) step(sq0, so0, sq1, so1);
+  } else {
+    fetch(sq0, so0);
+    fetch(sq1, so1);
+    for (int it = 0; it < nfull; it += 3) {
+      step(sq0, so0, sq2, so2);
+      step(sq1, so1, sq0, so0);
+      step(sq2, so2, sq1, so1);
+    }
+    if (nfull < nitems) step(sq0, so0, sq2, so2);
+    if (nfull + 1 < nitems) step(sq1, so1, sq0, so0);
   }
 
-  // Sum the two query halves: waves with qh = 1 hand their partials over through LDS.
-  float* red = reinterpret_cast<float*>(&sm.q[0][0]);   // 2 key halves x 2 x (D/32 x 16 x 64) floats
-  constexpr int PER = (D / 32) * 16 * 64;
+  // Sum the two query halves: waves with qh = 1 hand their partials over through LDS (the
+  // Q and dO buffers are free by now; key half 0 uses sq0 / sq1, key half 1 so0 / so1).
+  constexpr int PERW = (D / 32) * 16 * 64;
+  static_assert(PERW * sizeof(float) <= sizeof(so0), "reduction buffer");
   __syncthreads();
+  float* rk = reinterpret_cast<float*>(kh == 0 ? sq0 : so0);
+  float* rv = reinterpret_cast<float*>(kh == 0 ? sq1 : so1);
   if (qh == 1) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        red[(kh * 2 + 0) * PER + (dt * 16 + i) * 64 + lane] = dk[dt][i];
-        red[(kh * 2 + 1) * PER + (dt * 16 + i) * 64 + lane] = dv[dt][i];
+        rk[(dt * 16 + i) * 64 + lane] = dk[dt][i];
+        rv[(dt * 16 + i) * 64 + lane] = dv[dt][i];
       }
   }
   __syncthreads();
@@ -465,8 +577,8 @@ void dkv_kernel(const AttnArgs a) {
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i = 4 * g4 + x;
-          kv[x] = (dk[dt][i] + red[(kh * 2 + 0) * PER + (dt * 16 + i) * 64 + lane]) * a.scale;
-          vv[x] = dv[dt][i] + red[(kh * 2 + 1) * PER + (dt * 16 + i) * 64 + lane];
+          kv[x] = (dk[dt][i] + rk[(dt * 16 + i) * 64 + lane]) * a.scale;
+          vv[x] = dv[dt][i] + rv[(dt * 16 + i) * 64 + lane];
         }
         *reinterpret_cast<f32x4*>(dKp + d0) = kv;
         *reinterpret_cast<f32x4*>(dVp + d0) = vv;
@@ -477,6 +589,8 @@ void dkv_kernel(const AttnArgs a) {
 // ---------------------------------------------------------------- host side
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+
 
 static int dq_splits(int G) { return (G + 1) / 2; }
 
@@ -510,7 +624,7 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(dg_reduce_kernel, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)),
                        dim3(256), 0, st, (const float*)a.dg_part, a.dg, n, nsplit);
   }
-  hipLaunchKernelGGL(dkv_kernel<D>, dim3((unsigned)nrows), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((dkv_kernel<D, SAS_DKV_NBUF, SAS_DKV_WPE>), dim3((unsigned)nrows), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -26,12 +26,6 @@
 
 namespace sas {
 
-template <int D>
-struct FwdSmem {
-  uint16_t k[2][Tile<D>::ELEMS];   // K blocks, swizzled tiles (double buffer)
-  uint16_t v[2][Tile<D>::ELEMS];   // V blocks
-};
-
 constexpr float kRescaleThreshold = 8.0f;   // log2 of the largest unnormalised exponential
 
 // 32 rows per wave (NTILE 1) is sized to leave room for two waves per SIMD.
@@ -40,7 +34,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NTILE =
 void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   constexpr int NT = 64 * NW;              // threads
   constexpr int WPH = 2 / NTILE;           // waves per query head (64 rows / (32 * NTILE))
-  __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+  // Two K/V buffers as distinct LDS objects, always selected at compile time: the compiler
+  // can then prove that the asynchronous copy into one buffer does not alias reads of the
+  // other and does not wait for the copy before computing.
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[Tile<D>::ELEMS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
   const int hl = lane >> 5, ql = lane & 31;
@@ -78,13 +78,20 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
     for (int ks = 0; ks < D / 16; ++ks)
       qf[nt][ks] = active ? as_bf16x8(ld16(a.Q + q_off + (32 * nt + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
 
-  // block t of the visit order -> (block index, base-2 log-gate)
+  // block t of the visit order -> (block index, base-2 log-gate); the selection row is held
+  // one entry per lane
+  LaneList sel;
+  auto load_sel = [&](int i, int& v, float& g) {
+    v = i < cnt_j ? idx_row[i] : 0;
+    g = (i < cnt_j && lg_row != nullptr) ? lg_row[i] * kLog2e : 0.0f;
+  };
   auto block_of = [&](int t, int& m, float& lg2) {
     m = j;
     lg2 = 0.0f;
     if (t > 0) {
-      m = __builtin_amdgcn_readfirstlane(idx_row[t - 1]);
-      lg2 = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
+      sel.ensure(t - 1, lane, load_sel);
+      m = sel.at(t - 1);
+      lg2 = sel.gat(t - 1);
       if (m < 0 || m >= j) {  // ignored entry: stage block 0 with weight 0
         m = 0;
         lg2 = -INFINITY;
@@ -92,9 +99,9 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
     }
   };
   const TileLoader<D, NW> loader(wave, lane);
-  auto fetch = [&](int m, int buf) {
-    loader.load(sm.k[buf], Kh + (size_t)m * kBlock * D);
-    loader.load(sm.v[buf], Vh + (size_t)m * kBlock * D);
+  auto fetch = [&](int m, uint16_t* kb, uint16_t* vb) {
+    loader.load(kb, Kh + (size_t)m * kBlock * D);
+    loader.load(vb, Vh + (size_t)m * kBlock * D);
   };
 
   f32x16 oacc[D / 32][NTILE];
@@ -117,17 +124,17 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   int m0;
   float lg_next;
   block_of(0, m0, lg_next);
-  fetch(m0, 0);
+  fetch(m0, sk0, sv0);
   wait_vm();
   __syncthreads();
 
-  for (int t = 0; t <= cnt_j; ++t) {
-    const int buf = t & 1;
+  // one block: prefetch block t+1 into (kn, vn), compute block t from (kc, vc)
+  auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     const float lg2 = lg_next;
     if (t < cnt_j) {
       int mn;
       block_of(t + 1, mn, lg_next);
-      fetch(mn, buf ^ 1);
+      fetch(mn, kn, vn);
     }
     if (active) {
       f32x16 st[2][NTILE];
@@ -141,7 +148,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
       for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 ka = as_bf16x8(ld16(&sm.k[buf][Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl)]));
+          const bf16x8 ka = as_bf16x8(ld16(&kc[Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl)]));
 #pragma unroll
           for (int nt = 0; nt < NTILE; ++nt) st[mt][nt] = mfma32(ka, qf[nt][ks], st[mt][nt]);
         }
@@ -214,8 +221,8 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int r0 = 32 * mt + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
-            const bf16x8 va = join_tr16(lds_tr16(&sm.v[buf][Tile<D>::off(r0, d0)]),
-                                        lds_tr16(&sm.v[buf][Tile<D>::off(r0 + 8, d0)]));
+            const bf16x8 va = join_tr16(lds_tr16(&vc[Tile<D>::off(r0, d0)]),
+                                        lds_tr16(&vc[Tile<D>::off(r0 + 8, d0)]));
 #pragma unroll
             for (int nt = 0; nt < NTILE; ++nt) oacc[dt][nt] = mfma32(va, pf[mt][nt][hh], oacc[dt][nt]);
           }
@@ -224,6 +231,10 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
       wait_vm();
       __syncthreads();
     }
+  };
+  for (int t = 0; t <= cnt_j; t += 2) {
+    step(t, sk0, sv0, sk1, sv1);
+    if (t + 1 <= cnt_j) step(t + 1, sk1, sv1, sk0, sv0);
   }
   if (!active) return;
 

@@ -161,6 +161,9 @@ sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void*
   REQUIRE(O && dO && lse_rows, SAS_ERR_INVALID_ARG, "O, dO and lse_rows must be non-NULL");
   REQUIRE(dQ && dK && dV, SAS_ERR_INVALID_ARG, "dQ, dK and dV must be non-NULL");
   REQUIRE(kcap == 0 || dg != nullptr, SAS_ERR_INVALID_ARG, "dg is NULL");
+  // the key-major pass addresses the rows of one KV group with 31-bit buffer offsets
+  REQUIRE((long long)(Hq / Hkv) * n * d * 2 < (1ll << 31), SAS_ERR_UNSUPPORTED,
+          "(Hq/Hkv) * n * d * 2 bytes must be < 2^31 for the backward pass");
   REQUIRE(aligned16(O) && aligned16(dO) && aligned16(dQ) && aligned16(dK) && aligned16(dV),
           SAS_ERR_INVALID_ARG, "O, dO, dQ, dK, dV must be 16-byte aligned");
   const size_t need = sas::bwd_workspace_bytes(B, Hq, Hkv, n, d, kcap);

@@ -15,6 +15,9 @@ typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 64;                 // tokens per block (the pages' b)
+// word 3 of a raw buffer resource on gfx9 (32-bit data format, no swizzle); out-of-range
+// offsets read zero
+constexpr int kBufferFlags = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -122,7 +125,65 @@ struct TileLoader {
                                        16, 0, 0);
   }
 };
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Buffer loads straight into LDS: lane i of the wave copies 16 (or 4) bytes from
+// base + voffset_i + soffset (soffset wave-uniform) to lds + 16 i (4 i). The buffer
+// resource covers [base, base + bytes); reads beyond it return zero.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, int bytes, void* lds, uint32_t voffset,
+                                                  uint32_t soffset) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ void buffer_load_lds4(const void* base, int bytes, void* lds, uint32_t voffset,
+                                                 uint32_t soffset) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voffset, soffset, 0, 0);
+}
+
+// Wait until at most N vector-memory instructions of this wave are outstanding. Issued as
+// the s_waitcnt intrinsic (not inline asm) so that the compiler's own wait insertion knows
+// which copies have landed: otherwise it cannot tell that an LDS buffer filled by an
+// earlier asynchronous copy is complete and waits for every copy in flight before reading it.
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_vm() { wait_vm_n<0>(); }
+// Workgroup barrier without the memory fence of __syncthreads(): that fence makes the
+// compiler wait for every outstanding vector-memory instruction, including asynchronous
+// tile copies meant to stay in flight across the barrier. Callers wait explicitly for the
+// copies the next phase reads (wait_vm / wait_vm_n); LDS writes are drained here.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A wave-held window of a per-workgroup index list: lane i holds entry base + i, so entry
+// t is read with a scalar readlane instead of a dependent memory load per step. Loaded 64
+// entries at a time.
+struct LaneList {
+  int v = 0;
+  float g = 0.0f;
+  int base = -1;
+  template <class F>
+  __device__ __forceinline__ void ensure(int t, int lane, F&& load) {
+    const int nb = t & ~63;
+    if (nb != base) {
+      base = nb;
+      load(nb + lane, v, g);
+      // vmcnt(0) as the intrinsic the compiler tracks: the refilled registers are ready on
+      // this (rare) path, so no wait is needed where the paths merge (which would stall on
+      // every tile copy in flight)
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+  }
+  __device__ __forceinline__ int at(int t) const { return __builtin_amdgcn_readlane(v, t & 63); }
+  __device__ __forceinline__ float gat(int t) const {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(g), t & 63));
+  }
+};
 
 // 2^x with the hardware v_exp_f32 (no denormal range reduction: results below 2^-126
 // flush to zero, which is harmless for softmax weights relative to a maximum >= 1/256).

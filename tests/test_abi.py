@@ -109,6 +109,9 @@ def test_bwd_workspace_and_rejects():
     args[-3] = FAKE
     args[4] = NULL                          # dO
     assert L.sas_attn_bwd(*args) == sas.SAS_ERR_INVALID_ARG
+    # one KV group's query rows must stay below 2^31 bytes: 8 heads x 2^20 rows x 128 x 2
+    big = [FAKE] * 9 + [1, 8, 1, 1 << 20, 128, 64, 4, 0.125] + [FAKE] * 4 + [FAKE, 1 << 62, NULL]
+    assert L.sas_attn_bwd(*big) == sas.SAS_ERR_UNSUPPORTED
 
 
 def test_decode_rejects():
