@@ -117,12 +117,17 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, in
 
 // ---------------------------------------------------------------- query-major: dQ, dg
 
-// 4 waves: 2 query heads x 2 halves of the 64 query rows (32 rows per wave).
+// 4 waves: 2 query heads x 2 halves of the 64 query rows (32 rows per wave). When G is
+// odd the last split has one head; the waves of the missing head take part in the copies
+// and barriers only.
+// The K/V blocks stream through two LDS buffer sets (distinct objects selected at compile
+// time); block t+1 is copied in (buffer loads into LDS with a scalar per-block offset)
+// while block t is computed. The copy is issued on every step, past the end of the list it
+// repeats the last block, so the compiler's wait tracking stays exact.
 template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SAS_DQ_WPE, SAS_DQ_WPE)))
 void dq_kernel(const AttnArgs a, int nsplit) {
   constexpr int NW = 4;
-  // K/V double buffers as distinct LDS objects selected at compile time (see fwd_kernel)
   __shared__ __attribute__((aligned(16))) uint16_t sk0[Tile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t sk1[Tile<D>::ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t sv0[Tile<D>::ELEMS];
@@ -159,42 +164,50 @@ void dq_kernel(const AttnArgs a, int nsplit) {
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const size_t o = q_off + ql * D + 16 * ks + 8 * hl;
-    if (active) {
-      qf[ks] = as_bf16x8(ld16(a.Q + o));
-      dof[ks] = as_bf16x8(ld16(a.dO + o));
-      const u16x8 ov = ld16(a.O + o);
+    qf[ks] = as_bf16x8(ld16(a.Q + o));
+    dof[ks] = as_bf16x8(ld16(a.dO + o));
+    const u16x8 ov = ld16(a.O + o);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dlt += bf2f(ov[e]) * (float)dof[ks][e];
-    } else {
-      qf[ks] = bf16x8{};
-      dof[ks] = bf16x8{};
-    }
+    for (int e = 0; e < 8; ++e) dlt += bf2f(ov[e]) * (float)dof[ks][e];
   }
   dlt += __shfl_xor(dlt, 32, 64);
-  float lse2 = 0.0f;
-  if (active) {
-    if (hl == 0) a.delta[row_off + ql] = dlt;
-    lse2 = a.lse_rows[row_off + ql] * kLog2e;
-  }
+  if (active && hl == 0) a.delta[row_off + ql] = dlt;
+  const float lse2 = a.lse_rows[row_off + ql] * kLog2e;
 
-  const TileLoader<D, NW> loader(wave, lane);
-  LaneList sel;   // the selection row, one entry per lane
+  // per-lane byte offsets of this wave's 16-byte slots within a 64-row tile
+  constexpr int NWIN = Tile<D>::CPR / NW;
+  uint32_t voff[NWIN];
+#pragma unroll
+  for (int i = 0; i < NWIN; ++i) {
+    const int sidx = 64 * (wave + NW * i) + lane;
+    const int rr = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
+    voff[i] = (uint32_t)(rr * D + ((c ^ Tile<D>::swz(rr)) << 3)) * 2u;
+  }
+  const uint16_t* kbase = a.K + kv_off;
+  const uint16_t* vbase = a.V + kv_off;
+  const int kvbytes = a.n * D * 2;
+
+  // Block t of the list: t = 0 is block j itself, t >= 1 the selected block idx[t - 1].
+  // (tc: block being computed; tf: next block to copy, which stays at cnt_j once reached.)
   auto load_sel = [&](int i, int& v, float& g) {
     v = i < cnt_j ? idx_row[i] : 0;
     g = (i < cnt_j && lg_row != nullptr) ? lg_row[i] * kLog2e : 0.0f;
   };
-  auto block_of = [&](int t, int& m, float& lg2, bool& ok) {
-    m = j; lg2 = 0.0f; ok = true;
-    if (t > 0) {
-      sel.ensure(t - 1, lane, load_sel);
-      m = sel.at(t - 1);
-      lg2 = sel.gat(t - 1);
-      if (m < 0 || m >= j) { m = 0; lg2 = -INFINITY; ok = false; }
+  LaneList sel_c, sel_f;
+  int tc = 0, tf = 0;
+  auto fetch = [&](uint16_t* kb, uint16_t* vb) {
+    int mb = j;
+    if (tf > 0) {
+      sel_f.ensure(tf - 1, lane, load_sel);
+      mb = sel_f.at(tf - 1);
+      if (mb < 0 || mb >= j) mb = 0;
     }
-  };
-  auto fetch = [&](int m, uint16_t* kb, uint16_t* vb) {
-    loader.load(kb, a.K + kv_off + (size_t)m * kBlock * D);
-    loader.load(vb, a.V + kv_off + (size_t)m * kBlock * D);
+    const uint32_t so = (uint32_t)mb * (uint32_t)(kBlock * D * 2);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(kbase, kvbytes, kb + 512 * (wave + NW * i), voff[i], so);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(vbase, kvbytes, vb + 512 * (wave + NW * i), voff[i], so);
+    if (tf < cnt_j) ++tf;
   };
 
   f32x16 dq[D / 32];
@@ -205,83 +218,106 @@ void dq_kernel(const AttnArgs a, int nsplit) {
   const float c2 = a.scale * kLog2e;
   const int g16 = lane >> 4, lp = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
+  // Lane base offsets (elements) in the Tile layout: row read ks of key row 32 mt + ql at
+  // d = 16 ks + 8 hl sits at 32 mt D + (rx ^ (ks << 4)); the transposing read of rows
+  // r0 + tr_row (r0 = 32 mt + 16 hh + 8 half) at d = 32 dt + tr_d at
+  // r0 D + (tx ^ ((4 dt ^ 2 half) << 3)).
+  const int rx0 = ql * D + ((hl ^ Tile<D>::swz(ql)) << 3);
+  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
 
-  int m_cur;
-  float lg_next;
-  bool ok_next;
-  block_of(0, m_cur, lg_next, ok_next);
-  fetch(m_cur, sk0, sv0);
-  wait_vm();
-  __syncthreads();
-
-  // one block: prefetch block t+1 into (kn, vn), compute block t from (kc, vc)
-  auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
-    const float lg2 = lg_next;
-    const bool ok = ok_next;
-    if (t < cnt_j) {
-      int mn;
-      block_of(t + 1, mn, lg_next, ok_next);
-      fetch(mn, kn, vn);
+  // one block: copy the next block into (kn, vn), compute block tc from (kc, vc)
+  auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+    wait_vm();
+    barrier_lds();
+    const int t = tc;
+    float lg2 = 0.0f;
+    bool ok = true;
+    if (t > 0) {
+      sel_c.ensure(t - 1, lane, load_sel);
+      const int mb = sel_c.at(t - 1);
+      lg2 = sel_c.gat(t - 1);
+      if (mb < 0 || mb >= j) { lg2 = -INFINITY; ok = false; }
     }
+    ++tc;
+    fetch(kn, vn);
     // dg of the previous block: sum of the four waves' partials
     if (t >= 2 && tid == 0) {
       const float* pp = dgp[(t - 1) & 1];
       dg_out[t - 2] = (pp[0] + pp[1]) + (pp[2] + pp[3]);
     }
+    if (!active) {   // a missing head's waves only take part in the copies
+      if (lane == 0) dgp[t & 1][wave] = 0.0f;
+      return;
+    }
     float dgacc = 0.0f;
-    if (active) {
-      const float g = fast_exp2(lg2);
-      // The two 32-key halves of the block one after the other; the scheduling barrier keeps
-      // the second half from being hoisted into the first (which would overflow 256 VGPRs).
+    const float g = fast_exp2(lg2);
+    int rx = rx0, tx = tx0;
+    asm volatile("" : "+v"(rx), "+v"(tx));   // keeps per-(buffer, read) addresses unhoisted
+    // The two 32-key halves of the block one after the other; the scheduling barriers bound
+    // how many operand reads are in flight (registers are tight at 2 waves per SIMD).
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        if (mt == 1) __builtin_amdgcn_sched_barrier(0);
-        f32x16 st = {}, dpt = {};
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 st = {}, dpt = {};
 #pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const int o = Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl);
-          st = mfma32(as_bf16x8(ld16(&kc[o])), qf[ks], st);
-          dpt = mfma32(as_bf16x8(ld16(&vc[o])), dof[ks], dpt);
+      for (int k0 = 0; k0 < D / 16; k0 += 4) {
+        bf16x8 kr[4], vr[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int o = 32 * mt * D + (rx ^ ((k0 + u) << 4));
+          kr[u] = as_bf16x8(ld16(&kc[o]));
+          vr[u] = as_bf16x8(ld16(&vc[o]));
         }
-        bf16x8 dsf[2];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          st = mfma32(kr[u], qf[k0 + u], st);
+          dpt = mfma32(vr[u], dof[k0 + u], dpt);
+        }
+      }
+      // K^T operands of dQ^T += K^T dS^T over these 32 keys, read while the softmax runs
+      bf16x8 ka[D / 32][2];
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          float ds[8];
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            const int i = 8 * hh + x;
-            float u = fast_exp2(st[i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
-            if (t == 0) {
-              const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-              if (key > wrow0 + ql) u = 0.0f;
-            }
-            const float w = u * (dpt[i] - dlt);
-            dgacc += w;
-            ds[x] = w * g;
-          }
-          dsf[hh] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
+          const int r0 = 32 * mt + 16 * hh;
+          ka[dt][hh] = join_tr16(lds_tr16(&kc[r0 * D + (tx ^ ((4 * dt) << 3))]),
+                                 lds_tr16(&kc[(r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3))]));
         }
-        // dQ^T += K^T dS^T over these 32 keys (K^T read transposed from the natural K tile)
+      bf16x8 dsf[2];
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+      for (int hh = 0; hh < 2; ++hh) {
+        float ds[8];
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r0 = 32 * mt + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
-            const bf16x8 ka = join_tr16(lds_tr16(&kc[Tile<D>::off(r0, d0)]),
-                                        lds_tr16(&kc[Tile<D>::off(r0 + 8, d0)]));
-            dq[dt] = mfma32(ka, dsf[hh], dq[dt]);
-          }
+        for (int x = 0; x < 8; ++x) {
+          const int i = 8 * hh + x;
+          float u = fast_exp2(st[i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
+          const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (t == 0 && key > wrow0 + ql) u = 0.0f;   // causal mask of block j itself
+          const float w = u * (dpt[i] - dlt);
+          dgacc += w;
+          ds[x] = w * g;
+        }
+        dsf[hh] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       }
-      dgacc = ok ? wave_sum(dgacc) : 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) dq[dt] = mfma32(ka[dt][hh], dsf[hh], dq[dt]);
     }
-    if (lane == 0) dgp[t & 1][wave] = (t > 0 && active) ? dgacc : 0.0f;
-    if (t < cnt_j) wait_vm();
-    __syncthreads();
+    dgacc = wave_sum(dgacc);
+    if (lane == 0) dgp[t & 1][wave] = (t > 0 && ok) ? dgacc : 0.0f;
   };
-  for (int t = 0; t <= cnt_j; t += 2) {
-    step(t, sk0, sv0, sk1, sv1);
-    if (t + 1 <= cnt_j) step(t + 1, sk1, sv1, sk0, sv0);
+  const int nsteps = cnt_j + 1;
+  const int nfull = nsteps & ~1;
+  fetch(sk0, sv0);
+  for (int it = 0; it < nfull; it += 2) {
+    step(sk0, sv0, sk1, sv1);
+    step(sk1, sv1, sk0, sv0);
   }
+  if (nfull < nsteps) step(sk0, sv0, sk1, sv1);
+  wait_vm();
+  __syncthreads();
   if (tid == 0) {
     if (cnt_j >= 1) {
       const float* pp = dgp[cnt_j & 1];

@@ -16,8 +16,12 @@
 // read with the transposing ds_read_b64_tr_b16, in the key order the accumulator uses.
 //
 // Pipeline: the next block's K/V tiles are copied from global memory straight into the
-// other LDS buffer (global_load_lds, swizzled tiles) while the current block is computed;
-// one barrier per block. Blocks are visited current block first, so every row's reference maximum is
+// other LDS buffer (buffer loads into LDS with a scalar per-block offset, swizzled tiles)
+// while the current block is computed; one barrier per block. The copy is issued on every
+// step (past the end of the list it repeats the last block) and the steps run in whole
+// rounds of two, so the compiler's tracking of the copies in flight stays exact and it
+// never waits for the copy of the next block before reading the current one. Waves of a
+// missing head (odd G in the last split) take part in the copies and barriers only. Blocks are visited current block first, so every row's reference maximum is
 // finite from the start (each query sees itself). The reference maximum is only moved when
 // a row's maximum grows by more than 2^8 (exponentials stay <= 256), which skips nearly
 // all rescales of the output accumulator.
@@ -25,6 +29,13 @@
 #include "sas_kernels.h"
 
 namespace sas {
+
+#ifndef SAS_FWD_KBATCH
+#define SAS_FWD_KBATCH 0   // K operand reads in batches ahead of their products
+#endif
+#ifndef SAS_FWD_VBATCH
+#define SAS_FWD_VBATCH 1   // V^T operand reads issued before the softmax
+#endif
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 of the largest unnormalised exponential
 
@@ -76,32 +87,40 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qf[nt][ks] = active ? as_bf16x8(ld16(a.Q + q_off + (32 * nt + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
+      qf[nt][ks] = as_bf16x8(ld16(a.Q + q_off + (32 * nt + ql) * D + 16 * ks + 8 * hl));
 
-  // block t of the visit order -> (block index, base-2 log-gate); the selection row is held
-  // one entry per lane
-  LaneList sel;
+  // Block t of the visit order: t = 0 is block j itself, t >= 1 the selected block
+  // idx[t - 1] (an ignored entry stages block 0 with weight 0). The selection row is held
+  // one entry per lane. tc: block being computed; tf: next block to copy (stays at cnt_j).
   auto load_sel = [&](int i, int& v, float& g) {
     v = i < cnt_j ? idx_row[i] : 0;
     g = (i < cnt_j && lg_row != nullptr) ? lg_row[i] * kLog2e : 0.0f;
   };
-  auto block_of = [&](int t, int& m, float& lg2) {
-    m = j;
-    lg2 = 0.0f;
-    if (t > 0) {
-      sel.ensure(t - 1, lane, load_sel);
-      m = sel.at(t - 1);
-      lg2 = sel.gat(t - 1);
-      if (m < 0 || m >= j) {  // ignored entry: stage block 0 with weight 0
-        m = 0;
-        lg2 = -INFINITY;
-      }
+  LaneList sel_c, sel_f;
+  int tc = 0, tf = 0;
+  constexpr int NWIN = Tile<D>::CPR / NW;
+  static_assert(Tile<D>::CPR % NW == 0, "tile windows must split evenly over the waves");
+  uint32_t voff[NWIN];
+#pragma unroll
+  for (int i = 0; i < NWIN; ++i) {
+    const int sidx = 64 * (wave + NW * i) + lane;
+    const int rr = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
+    voff[i] = (uint32_t)(rr * D + ((c ^ Tile<D>::swz(rr)) << 3)) * 2u;
+  }
+  const int kvbytes = a.n * D * 2;
+  auto fetch = [&](uint16_t* kb, uint16_t* vb) {
+    int mb = j;
+    if (tf > 0) {
+      sel_f.ensure(tf - 1, lane, load_sel);
+      mb = sel_f.at(tf - 1);
+      if (mb < 0 || mb >= j) mb = 0;
     }
-  };
-  const TileLoader<D, NW> loader(wave, lane);
-  auto fetch = [&](int m, uint16_t* kb, uint16_t* vb) {
-    loader.load(kb, Kh + (size_t)m * kBlock * D);
-    loader.load(vb, Vh + (size_t)m * kBlock * D);
+    const uint32_t so = (uint32_t)mb * (uint32_t)(kBlock * D * 2);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, kvbytes, kb + 512 * (wave + NW * i), voff[i], so);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, kvbytes, vb + 512 * (wave + NW * i), voff[i], so);
+    if (tf < cnt_j) ++tf;
   };
 
   f32x16 oacc[D / 32][NTILE];
@@ -121,121 +140,152 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   const int g16 = lane >> 4, lp = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
 
-  int m0;
-  float lg_next;
-  block_of(0, m0, lg_next);
-  fetch(m0, sk0, sv0);
-  wait_vm();
-  __syncthreads();
+  // Lane base offsets (elements) in the Tile layout: row read ks of key row 32 mt + ql at
+  // d = 16 ks + 8 hl sits at 32 mt D + (rx ^ (ks << 4)); the transposing read of rows
+  // r0 + tr_row (r0 = 32 mt + 16 hh + 8 half) at d = 32 dt + tr_d at
+  // r0 D + (tx ^ ((4 dt ^ 2 half) << 3)).
+  const int rx0 = ql * D + ((hl ^ Tile<D>::swz(ql)) << 3);
+  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
 
-  // one block: prefetch block t+1 into (kn, vn), compute block t from (kc, vc)
-  auto step = [&](int t, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
-    const float lg2 = lg_next;
-    if (t < cnt_j) {
-      int mn;
-      block_of(t + 1, mn, lg_next);
-      fetch(mn, kn, vn);
+  // one block: copy the next block into (kn, vn), compute block tc from (kc, vc)
+  auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+    wait_vm();
+    barrier_lds();
+    const int t = tc;
+    float lg2 = 0.0f;
+    if (t > 0) {
+      sel_c.ensure(t - 1, lane, load_sel);
+      const int mb = sel_c.at(t - 1);
+      lg2 = sel_c.gat(t - 1);
+      if (mb < 0 || mb >= j) lg2 = -INFINITY;
     }
-    if (active) {
-      f32x16 st[2][NTILE];
+    ++tc;
+    fetch(kn, vn);
+    if (!active) return;   // a missing head's waves only take part in the copies
+    int rx = rx0, tx = tx0;
+    asm volatile("" : "+v"(rx), "+v"(tx));   // keeps per-(buffer, read) addresses unhoisted
+    f32x16 st[2][NTILE];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTILE; ++nt)
+      for (int nt = 0; nt < NTILE; ++nt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) st[mt][nt][i] = 0.0f;
+        for (int i = 0; i < 16; ++i) st[mt][nt][i] = 0.0f;
+    // S^T = K Q^T: the K operand reads go out in batches of 8 ahead of their products
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
+    for (int k0 = 0; k0 < D / 16; k0 += 4) {
+      bf16x8 kr[4][2];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const bf16x8 ka = as_bf16x8(ld16(&kc[Tile<D>::off(32 * mt + ql, 16 * ks + 8 * hl)]));
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int nt = 0; nt < NTILE; ++nt) st[mt][nt] = mfma32(ka, qf[nt][ks], st[mt][nt]);
-        }
-      if (t == 0) {  // causal mask on the current block (key > query)
+        for (int mt = 0; mt < 2; ++mt) kr[u][mt] = as_bf16x8(ld16(&kc[32 * mt * D + (rx ^ ((k0 + u) << 4))]));
+#if SAS_FWD_KBATCH
+      __builtin_amdgcn_sched_barrier(0);
+#endif
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < NTILE; ++nt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-              if (key > wrow0 + 32 * nt + ql) st[mt][nt][i] = -INFINITY;
-            }
-      }
-      // block maxima of the raw scores (scale > 0, so the max commutes with the affine map)
-      float bmax[NTILE];
-      bool grow = false;
-#pragma unroll
-      for (int nt = 0; nt < NTILE; ++nt) {
-        float mx = -INFINITY;
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mt][nt][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        bmax[nt] = mx * c2 + lg2;
-        grow |= bmax[nt] > mref[nt] + kRescaleThreshold;
-      }
-      if (__any(grow)) {
-#pragma unroll
-        for (int nt = 0; nt < NTILE; ++nt) {
-          const float mnew = fmaxf(mref[nt], bmax[nt]);
-          const float alpha = fast_exp2(mref[nt] - mnew);
-          mref[nt] = mnew;
-          lrow[nt] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][nt][i] *= alpha;
-        }
-      }
-      bf16x8 pf[2][NTILE][2];  // [mt][nt][half]
-#pragma unroll
-      for (int nt = 0; nt < NTILE; ++nt) {
-        const float off = lg2 - mref[nt];
-        float ls = 0.0f;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(st[mt][nt][i] * c2 + off);
-            st[mt][nt][i] = p;
-            ls += p;
-          }
-        lrow[nt] += ls;
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int o = 8 * hh;
-            pf[mt][nt][hh] = pack8(st[mt][nt][o], st[mt][nt][o + 1], st[mt][nt][o + 2], st[mt][nt][o + 3],
-                                   st[mt][nt][o + 4], st[mt][nt][o + 5], st[mt][nt][o + 6], st[mt][nt][o + 7]);
-          }
-      }
-      // O^T += V^T P^T; the V^T operand for keys 32mt + 16hh + ... comes from two transposing reads
+          for (int nt = 0; nt < NTILE; ++nt) st[mt][nt] = mfma32(kr[u][mt], qf[nt][k0 + u], st[mt][nt]);
+    }
+    // V^T operands of O^T += V^T P^T; with one row tile per wave they are read while the
+    // softmax runs (two row tiles leave no registers for that)
+    auto read_va = [&](int dt, int mt, int hh) {
+      const int r0 = 32 * mt + 16 * hh;
+      return join_tr16(lds_tr16(&vc[r0 * D + (tx ^ ((4 * dt) << 3))]),
+                       lds_tr16(&vc[(r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3))]));
+    };
+    bf16x8 va[D / 32][2][2];   // [dt][mt][hh]
+    if constexpr (NTILE == 1 && SAS_FWD_VBATCH) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r0 = 32 * mt + 16 * hh + tr_row, d0 = 32 * dt + tr_d;
-            const bf16x8 va = join_tr16(lds_tr16(&vc[Tile<D>::off(r0, d0)]),
-                                        lds_tr16(&vc[Tile<D>::off(r0 + 8, d0)]));
+          for (int hh = 0; hh < 2; ++hh) va[dt][mt][hh] = read_va(dt, mt, hh);
+    }
+    if (t == 0) {  // causal mask on the current block (key > query)
 #pragma unroll
-            for (int nt = 0; nt < NTILE; ++nt) oacc[dt][nt] = mfma32(va, pf[mt][nt][hh], oacc[dt][nt]);
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NTILE; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (key > wrow0 + 32 * nt + ql) st[mt][nt][i] = -INFINITY;
           }
     }
-    if (t < cnt_j) {
-      wait_vm();
-      __syncthreads();
+    // block maxima of the raw scores (scale > 0, so the max commutes with the affine map)
+    float bmax[NTILE];
+    bool grow = false;
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mt][nt][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      bmax[nt] = mx * c2 + lg2;
+      grow |= bmax[nt] > mref[nt] + kRescaleThreshold;
     }
+    if (__any(grow)) {
+#pragma unroll
+      for (int nt = 0; nt < NTILE; ++nt) {
+        const float mnew = fmaxf(mref[nt], bmax[nt]);
+        const float alpha = fast_exp2(mref[nt] - mnew);
+        mref[nt] = mnew;
+        lrow[nt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][nt][i] *= alpha;
+      }
+    }
+    bf16x8 pf[2][NTILE][2];  // [mt][nt][half]
+#pragma unroll
+    for (int nt = 0; nt < NTILE; ++nt) {
+      const float off = lg2 - mref[nt];
+      float ls = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(st[mt][nt][i] * c2 + off);
+          st[mt][nt][i] = p;
+          ls += p;
+        }
+      lrow[nt] += ls;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int o = 8 * hh;
+          pf[mt][nt][hh] = pack8(st[mt][nt][o], st[mt][nt][o + 1], st[mt][nt][o + 2], st[mt][nt][o + 3],
+                                 st[mt][nt][o + 4], st[mt][nt][o + 5], st[mt][nt][o + 6], st[mt][nt][o + 7]);
+        }
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const bf16x8 v = (NTILE == 1 && SAS_FWD_VBATCH) ? va[dt][mt][hh] : read_va(dt, mt, hh);
+#pragma unroll
+          for (int nt = 0; nt < NTILE; ++nt) oacc[dt][nt] = mfma32(v, pf[mt][nt][hh], oacc[dt][nt]);
+        }
   };
-  for (int t = 0; t <= cnt_j; t += 2) {
-    step(t, sk0, sv0, sk1, sv1);
-    if (t + 1 <= cnt_j) step(t + 1, sk1, sv1, sk0, sv0);
+  const int nsteps = cnt_j + 1;
+  const int nfull = nsteps & ~1;
+  fetch(sk0, sv0);
+  for (int it = 0; it < nfull; it += 2) {
+    step(sk0, sv0, sk1, sv1);
+    step(sk1, sv1, sk0, sv0);
   }
+  if (nfull < nsteps) step(sk0, sv0, sk1, sv1);
+  wait_vm();   // the last (repeated) copy lands before the workgroup's LDS is released
   if (!active) return;
 
   const size_t lse_off = (size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock + wrow0;
