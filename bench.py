@@ -37,6 +37,16 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def calibration_copy(torch, nbytes=256 << 20):
+    """A plain copy of a known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    y.copy_(x)
+    torch.cuda.synchronize()
+    log(f"[bench] calibration copy: {nbytes} bytes read, {nbytes} bytes written")
+
+
 def pair_count(cnt: np.ndarray, G: int, block: int = 64) -> int:
     """Attended (query row, key) pairs: causal current block plus cnt_j full history
     blocks for every query block, times the G query heads of each KV head."""
@@ -61,7 +71,7 @@ def train_inputs(w, torch):
     return host, dev
 
 
-def run_train(w, steps, warmup, torch):
+def run_train(w, steps, warmup, torch, kernel_timing=True):
     from learned_context_ranking_amd import sas
     log(f"[bench] generating {w.name} inputs")
     host, t = train_inputs(w, torch)
@@ -111,15 +121,20 @@ def run_train(w, steps, warmup, torch):
     flop_bwd = 8.0 * w.d * pairs
     log(f"[bench] timing {steps} steps")
     torch.cuda.synchronize()
+    sas.profile_collect()            # drop anything recorded before the timed region
+    sas.profile_enable(kernel_timing)   # per-kernel HIP events on the launch stream
     t0 = time.perf_counter()
     for _ in range(steps):
         step(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    sas.profile_enable(False)
+    prof = sas.profile_collect()
     ms_step = (t1 - t0) * 1e3 / steps
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
-    return dict(ms_step=ms_step, ms=ms, pairs=pairs, flop_fwd=flop_fwd, flop_bwd=flop_bwd,
-                host=host, cnt=cnt_h)
+    kern_ms = {k: tot / n for k, (n, tot) in prof.items()}
+    return dict(ms_step=ms_step, ms=ms, kern_ms=kern_ms, pairs=pairs, flop_fwd=flop_fwd,
+                flop_bwd=flop_bwd, host=host, cnt=cnt_h)
 
 
 def run_decode(steps, torch):
@@ -141,7 +156,10 @@ def run_decode(steps, torch):
     idx, cnt, _, _ = sas.sas_topk_select(s, K, mode="decode", row_valid=row_valid, kcap=K)
     ws = sas.decode_workspace(B, Hq, Hkv, d, K, dev)
     o = torch.empty_like(q)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)   # > L2 + Infinity Cache
+    # Evict the caches before each timed step by READING 1 GiB (> L2 + Infinity Cache).
+    # A write flush (zero_) would leave ~256 MB of dirty lines whose write-back then
+    # competes with the timed kernel's reads and halves its measured bandwidth.
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     scale = 1.0 / math.sqrt(d)
     for _ in range(3):
@@ -149,7 +167,7 @@ def run_decode(steps, torch):
     torch.cuda.synchronize()
     times, sel_times = [], []
     for _ in range(steps):
-        flush.zero_()
+        flush.sum()
         a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a.record(stream)
         sas.sas_topk_select(s, K, mode="decode", row_valid=row_valid, kcap=K)
@@ -211,6 +229,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--no-kernel-timing", action="store_true",
+                    help="time the step without the per-kernel events (no roofline figures)")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a 256 MiB copy (calibrates the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -220,24 +242,34 @@ def main():
 
     import torch
     from learned_context_ranking_amd import sas, synth
+    from learned_context_ranking_amd.profile_counters import profiled_traffic
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     sas.lib()
+    if args.calib_copy:
+        calibration_copy(torch)
     w = synth.WORKLOADS["qwen3_4b_train"]
-    tr = run_train(w, args.steps, args.warmup, torch)
+    tr = run_train(w, args.steps, args.warmup, torch, kernel_timing=not args.no_kernel_timing)
     flop_step = tr["flop_fwd"] + tr["flop_bwd"]
     value = flop_step / (tr["ms_step"] * 1e-3) / 1e12
     ms = tr["ms"]
-    kern = {
-        "select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"],
-    }
-    # dominant launch of the step
+    kern = {"select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"]}
+    kern.update({"kernel:" + k: v for k, v in tr["kern_ms"].items()})
     fwd_tf = tr["flop_fwd"] / (ms["fwd"] * 1e-3) / 1e12
     bwd_tf = tr["flop_bwd"] / (ms["bwd"] * 1e-3) / 1e12
-    roof = {"kernel": "sas_attn_bwd" if ms["bwd"] >= ms["fwd"] else "sas_attn_fwd",
-            "bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS, "traffic": None}
-    roof["achieved"] = bwd_tf if ms["bwd"] >= ms["fwd"] else fwd_tf
-    roof["frac"] = roof["achieved"] / PEAK_BF16_TFLOPS
+    # Roofline of the dominant kernel (longest average launch), from the library's event
+    # timing over the timed region. Algorithmic FLOPs per launch per kernel (pairs = attended
+    # (query, key) pairs): fwd 4d (q.k, p.v); dq 4d (dO.v, dS.k); dkv 4d (p^T dO, dS^T q).
+    kms = tr["kern_ms"] or {"sas_attn_bwd": ms["bwd"]}
+    dom = max(kms, key=kms.get)
+    flop_of = {"fwd": 4.0, "dq": 4.0, "dkv": 4.0}
+    roof = {"kernel": dom, "bound": "mfma", "unit": "TFLOP/s", "peak": PEAK_BF16_TFLOPS}
+    if dom in flop_of:
+        fl = flop_of[dom] * w.d * tr["pairs"]
+        roof["flop_per_launch"] = fl
+        roof["achieved"] = fl / (kms[dom] * 1e-3) / 1e12
+        roof["frac"] = roof["achieved"] / PEAK_BF16_TFLOPS
+    roof["traffic"] = profiled_traffic(dom)
     out = {
         "metric": "gated block-sparse attn TFLOP/s fwd+bwd @n=32K,K=32; decode KV GB/s",
         "value": round(value, 3),
@@ -267,9 +299,10 @@ def main():
         out["decode"] = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms": round(dec["ms"], 5),
                          "select_ms": round(dec["ms_select"], 5), "bytes": dec["bytes"],
                          "workload": dec["workload"],
-                         "roofline": {"bound": "hbm", "achieved": round(dec["gbs"], 1), "peak": PEAK_HBM_GBS,
-                                      "unit": "GB/s", "frac": round(dec["gbs"] / PEAK_HBM_GBS, 4),
-                                      "traffic": None}}
+                         "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(dec["gbs"], 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(dec["gbs"] / PEAK_HBM_GBS, 4),
+                                      "traffic": profiled_traffic("decode")}}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, tr["host"], tr["cnt"], args.cpu_seconds)

@@ -183,11 +183,31 @@ size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap);
  *            training forward).
  *   o        bf16 [B][Hq][d], out.
  *   ws       workspace of sas_decode_workspace_size() bytes, 16-byte aligned.
+ * Returns SAS_ERR_UNSUPPORTED when Hq / Hkv > 32 or Lmax * d * 2 >= 2^31.
  */
 sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
                       int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
                       int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Kernel timing, for measurement (not part of the pages' method; off by default).
+ *
+ * sas_profile_enable(on): while on, every kernel the library launches is bracketed by two
+ * HIP events recorded on the stream it is launched on (the library creates and keeps the
+ * events; enabling itself makes no HIP call). Returns SAS_OK.
+ *
+ * sas_profile_collect: waits for the events recorded since the last collect, sums the
+ * elapsed time per kernel and writes up to `max` entries in first-launch order:
+ *   names     max * name_len chars, out (NUL-terminated names; may be NULL),
+ *   launches  int[max], out (may be NULL): launches of each kernel,
+ *   total_ms  double[max], out (may be NULL): summed event time of each kernel.
+ * Returns the number of entries written, or -1 if an event query failed. The record is
+ * cleared either way. Kernel names: select, fwd, inv_count, inv_scan, inv_fill, dq,
+ * dg_reduce, dkv, decode, decode_merge.
+ */
+sas_status sas_profile_enable(int on);
+int sas_profile_collect(int max, char* names, int name_len, int* launches, double* total_ms);
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,9 @@
 #ifndef SAS_DKV_NBUF
 #define SAS_DKV_NBUF 3   // ring depth of the key-major pass
 #endif
+#ifndef SAS_DKV_ORDER
+#define SAS_DKV_ORDER 2  // (batch, KV head) pairs per launch phase; 0: all pairs interleaved
+#endif
 #ifndef SAS_DKV_WPE
 #define SAS_DKV_WPE 1    // waves per SIMD the key-major pass is built for
 #endif
@@ -386,12 +389,18 @@ void dkv_kernel(const AttnArgs a) {
   const int hl = lane >> 5, ql = lane & 31;
   const int kh = wave & 1, qh = wave >> 1;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
-  // Early key blocks are selected most often: launch them first; consecutive workgroups
-  // differ in (batch, KV head), so each KV head stays on one XCD (one L2) when B * Hkv is a
-  // multiple of 8.
-  const int per_m = a.B * a.Hkv;
-  const int m = (int)(blockIdx.x / per_m);
-  const int rr = blockIdx.x % per_m;
+  // Launch order: the (batch, KV head) pairs in phases of SAS_DKV_ORDER pairs (0: one phase
+  // with all pairs); within a phase key-block-major with the phase's pairs interleaved, so
+  // early key blocks (selected most often, the longest lists) start first and consecutive
+  // workgroups alternate between the phase's pairs, which keeps each pair on a fixed subset
+  // of XCDs (L2s). Fewer pairs per phase keep the working set of query rows smaller.
+  const int BHp = a.B * a.Hkv;
+  const int P = SAS_DKV_ORDER > 0 ? min(SAS_DKV_ORDER, BHp) : BHp;
+  const int phase = (int)(blockIdx.x / ((unsigned)P * NB));
+  const int np = min(P, BHp - phase * P);   // pairs in this phase (the last may have fewer)
+  const int rem = (int)(blockIdx.x - (unsigned)phase * P * NB);
+  const int m = rem / np;
+  const int rr = phase * P + rem % np;
   const int h = rr % a.Hkv, b = rr / a.Hkv;
   const long long bh = (long long)b * a.Hkv + h;
 
@@ -647,20 +656,36 @@ template <int D>
 static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   const int NB = a.n / kBlock;
   const long long nrows = (long long)a.B * a.Hkv * NB;
-  hipLaunchKernelGGL(inv_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, a.idx, a.cnt,
-                     NB, a.kcap, nrows, a.inv_cnt, (const int32_t*)nullptr, (int32_t*)nullptr);
-  hipLaunchKernelGGL(inv_scan_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, st, a.inv_cnt, NB,
-                     a.inv_off);
-  hipLaunchKernelGGL(inv_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, a.idx, a.cnt,
-                     NB, a.kcap, nrows, a.inv_cnt, (const int32_t*)a.inv_off, a.inv_list);
+  {
+    ProfScope prof("inv_count", st);
+    hipLaunchKernelGGL(inv_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, a.idx, a.cnt,
+                       NB, a.kcap, nrows, a.inv_cnt, (const int32_t*)nullptr, (int32_t*)nullptr);
+  }
+  {
+    ProfScope prof("inv_scan", st);
+    hipLaunchKernelGGL(inv_scan_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, st, a.inv_cnt, NB,
+                       a.inv_off);
+  }
+  {
+    ProfScope prof("inv_fill", st);
+    hipLaunchKernelGGL(inv_kernel, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st, a.idx, a.cnt,
+                       NB, a.kcap, nrows, a.inv_cnt, (const int32_t*)a.inv_off, a.inv_list);
+  }
   const int nsplit = dq_splits(a.Hq / a.Hkv);
-  hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+  {
+    ProfScope prof("dq", st);
+    hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+  }
   if (nsplit > 1 && a.kcap > 0) {
+    ProfScope prof("dg_reduce", st);
     const long long n = nrows * a.kcap;
     hipLaunchKernelGGL(dg_reduce_kernel, dim3((unsigned)std::min<long long>((n + 255) / 256, 4096)),
                        dim3(256), 0, st, (const float*)a.dg_part, a.dg, n, nsplit);
   }
-  hipLaunchKernelGGL((dkv_kernel<D, SAS_DKV_NBUF, SAS_DKV_WPE>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+  {
+    ProfScope prof("dkv", st);
+    hipLaunchKernelGGL((dkv_kernel<D, SAS_DKV_NBUF, SAS_DKV_WPE>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -314,6 +314,7 @@ template <int D, int NTILE, int NW>
 static hipError_t launch_fwd_t(const AttnArgs& a, int nsplit, int hpw, hipStream_t st) {
   const int NB = a.n / kBlock;
   const unsigned grid = (unsigned)(NB * a.B * a.Hkv * nsplit);
+  ProfScope prof("fwd", st);
   hipLaunchKernelGGL((fwd_kernel<D, NTILE, NW>), dim3(grid), dim3(64 * NW), 0, st, a, nsplit, hpw);
   return hipGetLastError();
 }

@@ -3,151 +3,225 @@
 // Top-K history blocks picked from s. Per (sequence, KV head) the G query heads share the
 // selected K/V blocks, so each block is read from HBM once for all G heads.
 //
-// The work is HBM-bound. The block list of each (sequence, KV head) is split into chunks
-// of `bpc` blocks so the launch has enough workgroups to fill 256 CUs; each workgroup
-// writes a partial (running max, running sum, unnormalised output) per query head and a
-// second kernel merges the partials with the usual log-sum-exp rescaling.
-//
-// Inside a workgroup (4 waves) wave w owns keys 16w..16w+15 of every block. A lane reads
-// 16 contiguous bytes of one key row (coalesced rows), forms bf16 dot products with the G
-// query heads held in registers, and reduces them across the lanes of its row.
+// The work is HBM-bound: the kernel's job is to keep enough bytes in flight. The block list
+// of each (sequence, KV head) is split into chunks so the launch fills the chip; each chunk
+// is one single-wave workgroup that streams its K/V blocks, in 32-key halves, through a
+// ring of LDS buffer sets (buffer loads into LDS, swizzled tiles; rows past the cache end
+// read as zero) and computes, like the prefill forward, S^T = K Q^T and O^T += V^T P^T with
+// 32x32x16 bf16 MFMAs, the G query heads forming the query columns (columns G..31 are
+// zero). The chunk's block list is held one entry per lane, so no step waits on an index
+// load. A wave needs no barrier: it waits only for its own copies. With one chunk per
+// (sequence, KV head) the output is written directly; otherwise each chunk writes a
+// partial (running max, running sum, unnormalised output) per query head and a second
+// kernel merges the partials with log-sum-exp rescaling.
 #include "sas_common.h"
 #include "sas_kernels.h"
 
 namespace sas {
 
-template <int D, int G>
-__global__ __launch_bounds__(256) void decode_split_kernel(const DecodeArgs a) {
-  constexpr int CPR = D / 8;      // lanes per key row (16 B each)
-  constexpr int RPI = 64 / CPR;   // key rows per wave instruction
-  constexpr int NI = 16 / RPI;    // instructions per wave per block
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c8 = lane % CPR, rsub = lane / CPR;
+constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalised exponential
+
+// 32-key half blocks through a ring of 4 LDS buffer sets: half block u+3 is copied in
+// while u is computed, so about three half blocks (48 KB) are in flight per wave.
+template <int D>
+__global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
+  constexpr int HE = 32 * D;   // elements of a 32-row half tile
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sk2[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sk3[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv0[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv1[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv2[HE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv3[HE];
+  const int lane = threadIdx.x;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int G = a.Hq / a.Hkv;
   const int chunk = blockIdx.x % a.nchunk;
   const long long bh = blockIdx.x / a.nchunk;
   const int h = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
   const int L = min(max(a.kv_len[b], 1), (int)a.Lmax);
   const int cur = (L - 1) / kBlock;
   const int cnt = min(max(a.cnt[bh], 0), min(a.kcap, cur));
-  const int t0 = chunk * a.bpc, t1 = min(t0 + a.bpc, cnt + 1);
+  // list position t: 0 is the current block, t >= 1 the selected block idx[t - 1]
+  // (a chunk past the end of a short list is empty: t1 == t0)
+  const int t0 = chunk * a.bpc, t1 = max(t0, min(t0 + a.bpc, cnt + 1));
   const int32_t* idx_row = a.idx + bh * a.kcap;
   const float* lg_row = a.logg != nullptr ? a.logg + bh * a.kcap : nullptr;
-  const size_t kv_base = (size_t)bh * a.Lmax * D;
+  const uint16_t* Kh = a.Kc + (size_t)bh * a.Lmax * D;
+  const uint16_t* Vh = a.Vc + (size_t)bh * a.Lmax * D;
+  const int cbytes = (int)(a.Lmax * D * 2);   // checked on the host to fit 31 bits
 
-  float qv[G][8];
+  // the G query heads as the B operand of S^T = K Q^T: lane holds query column ql,
+  // d = 16 ks + 8 hl + e; columns ql >= G are zero
+  bf16x8 qf[D / 16];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const u16x8 v = ld16(a.q + ((size_t)b * a.Hq + h * G + g) * D + c8 * 8);
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = ql < G ? as_bf16x8(ld16(a.q + ((size_t)b * a.Hq + h * G + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
+
+  constexpr int NWIN = Tile<D>::CPR / 2;   // 1 KB windows per half tile (one wave copies all)
+  uint32_t voff[NWIN];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qv[g][e] = bf2f(v[e]);
+  for (int i = 0; i < NWIN; ++i) {
+    const int sidx = 64 * i + lane;
+    const int rr = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
+    voff[i] = (uint32_t)(rr * D + ((c ^ Tile<D>::swz(rr)) << 3)) * 2u;
   }
-  float mrun[G], lrun[G], acc[G][8];
+  // The chunk's list positions, one per lane (lane i: position t0 + i): block and base-2
+  // log-gate; an ignored entry reads block 0 with weight 0.
+  LaneList lst;
+  auto load_lst = [&](int i, int& v, float& g) {
+    const int t = t0 + i;
+    v = cur;
+    g = 0.0f;
+    if (t > 0 && t < t1) {
+      v = idx_row[t - 1];
+      g = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
+      if (v < 0 || v >= cur) { v = 0; g = -INFINITY; }
+    }
+  };
+  LaneList lstf;   // the same list for the copies, which run ahead
+  const int nhalf = 2 * (t1 - t0);
+  int uf = 0;   // next half block to copy (stays at nhalf - 1 once reached)
+  auto fetch = [&](uint16_t* kb, uint16_t* vb) {
+    const int uu = max(min(uf, nhalf - 1), 0);
+    lstf.ensure(uu >> 1, lane, load_lst);
+    const int m = lstf.at(uu >> 1);
+    const uint32_t so = ((uint32_t)m * kBlock + 32u * (uu & 1)) * (uint32_t)(D * 2);
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    mrun[g] = -INFINITY;
-    lrun[g] = 0.0f;
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, cbytes, kb + 512 * i, voff[i], so);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
-  }
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, cbytes, vb + 512 * i, voff[i], so);
+    ++uf;
+  };
+  constexpr int PER = 2 * NWIN;   // copies per half block
+  static_assert(2 * PER < 64, "copies in flight exceed the vmcnt range");
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.0f;
+  float mref = -INFINITY, lrow = 0.0f;
   const float c2 = a.scale * kLog2e;
+  const int g16 = lane >> 4, lp = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
+  const int rx0 = ql * D + ((hl ^ Tile<D>::swz(ql)) << 3);
+  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
 
-  for (int t = t0; t < t1; ++t) {
-    int m = cur;
-    float lg2 = 0.0f;
-    if (t > 0) {
-      m = idx_row[t - 1];
-      lg2 = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
-      if (m < 0 || m >= cur) { m = 0; lg2 = -INFINITY; }
-    }
-    u16x8 kr[NI], vr[NI];
-    int tok[NI];
+  int uc = 0;   // half block being computed
+  auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+    wait_vm_n<2 * PER>();   // this half block has landed; the next two may still be in flight
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the buffer about to be refilled are done
+    const int u = uc++;
+    lst.ensure(u >> 1, lane, load_lst);
+    const int m = lst.at(u >> 1);
+    const float lg2 = lst.gat(u >> 1);
+    fetch(kn, vn);
+    int rx = rx0, tx = tx0;
+    asm volatile("" : "+v"(rx), "+v"(tx));
+    f32x16 st = {};
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      tok[i] = m * kBlock + 16 * wave + RPI * i + rsub;
-      const int tl = min(tok[i], (int)a.Lmax - 1);  // rows past the cache end are masked
-      kr[i] = ld16(a.Kc + kv_base + (size_t)tl * D + c8 * 8);
-      vr[i] = ld16(a.Vc + kv_base + (size_t)tl * D + c8 * 8);
-    }
-    float z[NI][G];
+    for (int ks = 0; ks < D / 16; ++ks) st = mfma32(as_bf16x8(ld16(&kc[rx ^ (ks << 4)])), qf[ks], st);
+    bf16x8 va[D / 32][2];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      float kf[8];
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kf[e] = bf2f(kr[i][e]);
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float s = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += qv[g][e] * kf[e];
-#pragma unroll
-        for (int off = CPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-        float zz = s * c2 + lg2;
-        if (tok[i] >= L) zz = -INFINITY;
-        z[i][g] = zz;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r0 = 16 * hh;
+        va[dt][hh] = join_tr16(lds_tr16(&vc[r0 * D + (tx ^ ((4 * dt) << 3))]),
+                               lds_tr16(&vc[(r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3))]));
       }
+    // keys past the end of the cache (only in the current block) do not count
+    const int key0 = m * kBlock + 32 * (u & 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = 8 * (i >> 2) + 4 * hl + (i & 3);
+      if (key0 + key >= L) st[i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float bmax = mx * c2 + lg2;
+    if (__any(bmax > mref + kDecRescaleThreshold)) {
+      const float mnew = fmaxf(mref, bmax);
+      const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(mref - mnew);
+      mref = mnew;
+      lrow *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    // a column whose reference is still -inf has seen only masked keys: weight 0
+    const float off = mref == -INFINITY ? -INFINITY : lg2 - mref;
+    float ls = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(st[i] * c2 + off);
+      st[i] = p;
+      ls += p;
+    }
+    lrow += ls;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int o = 8 * hh;
+      pf[hh] = pack8(st[o], st[o + 1], st[o + 2], st[o + 3], st[o + 4], st[o + 5], st[o + 6], st[o + 7]);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = -INFINITY;
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) mx = fmaxf(mx, z[i][g]);
-      mx = wave_max(mx);
-      const float mnew = fmaxf(mrun[g], mx);
-      if (mnew == -INFINITY) continue;  // nothing attendable yet
-      const float alpha = exp2f(mrun[g] - mnew);
-      mrun[g] = mnew;
-      float ls = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const float p = exp2f(z[i][g] - mnew);
-        ls += p;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] += p * bf2f(vr[i][e]);
-      }
-      lrun[g] = lrun[g] * alpha + ls;
-    }
+      for (int hh = 0; hh < 2; ++hh) oacc[dt] = mfma32(va[dt][hh], pf[hh], oacc[dt]);
+  };
+  // whole rounds of 4 half blocks without conditions inside, then the remainder
+  fetch(sk0, sv0);
+  fetch(sk1, sv1);
+  fetch(sk2, sv2);
+  const int nfull = nhalf & ~3;
+  for (int it = 0; it < nfull; it += 4) {
+    step(sk0, sv0, sk3, sv3);
+    step(sk1, sv1, sk0, sv0);
+    step(sk2, sv2, sk1, sv1);
+    step(sk3, sv3, sk2, sv2);
   }
+  if (nfull < nhalf) step(sk0, sv0, sk3, sv3);
+  if (nfull + 1 < nhalf) step(sk1, sv1, sk0, sv0);
+  if (nfull + 2 < nhalf) step(sk2, sv2, sk1, sv1);
+  wait_vm();
 
-  // Sum over the key rows of the wave (lanes with the same c8), then merge the 4 waves.
+  const float l = lrow + __shfl_xor(lrow, 32, 64);
+  if (a.nchunk == 1) {
+    // the whole list in one chunk: write the normalised output directly
+    if (ql < G) {
+      const float inv = 1.0f / l;
+      uint16_t* o = a.o + ((size_t)b * a.Hq + h * G + ql) * D;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-    for (int off = CPR; off < 64; off <<= 1) {
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+          bf16x4 v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] += __shfl_xor(acc[g][e], off, 64);
-      lrun[g] += __shfl_xor(lrun[g], off, 64);
+          for (int x = 0; x < 4; ++x) v[x] = (__bf16)(oacc[dt][4 * g4 + x] * inv);
+          *reinterpret_cast<bf16x4*>(o + d0) = v;
+        }
     }
+    return;
   }
-  __shared__ float sm_m[4][G], sm_l[4][G];
-  __shared__ float sm_acc[4][G][D];
-  if (lane < CPR) {
+  // partial of this chunk for query head ql < G: (m, l, unnormalised o)
+  if (ql < G) {
+    float* out = a.part + (((size_t)bh * a.nchunk + chunk) * G + ql) * (D + 2);
+    if (hl == 0) { out[0] = mref; out[1] = l; }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_acc[wave][g][c8 * 8 + e] = acc[g][e];
-      if (lane == 0) { sm_m[wave][g] = mrun[g]; sm_l[wave][g] = lrun[g]; }
-    }
-  }
-  __syncthreads();
-  float* out = a.part + ((size_t)bh * a.nchunk + chunk) * G * (D + 2);
-  for (int x = tid; x < G * D; x += 256) {
-    const int g = x / D, dd = x % D;
-    float M = -INFINITY;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][g]);
-    float o = 0.0f, l = 0.0f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float sc = exp2f(sm_m[w][g] - M);
-        o += sc * sm_acc[w][g][dd];
-        l += sc * sm_l[w][g];
+        for (int x = 0; x < 4; ++x) out[2 + d0 + x] = oacc[dt][4 * g4 + x];
       }
-    }
-    out[g * (D + 2) + 2 + dd] = o;
-    if (dd == 0) { out[g * (D + 2)] = M; out[g * (D + 2) + 1] = l; }
   }
 }
 
@@ -179,39 +253,33 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap) {
   return (size_t)B * Hkv * (size_t)(kcap + 1) * G * (d + 2) * sizeof(float);
 }
 
-template <int D, int G>
-static void launch_split(const DecodeArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)((long long)a.B * a.Hkv * a.nchunk);
-  hipLaunchKernelGGL((decode_split_kernel<D, G>), dim3(grid), dim3(256), 0, st, a);
-}
-
-template <int D>
-static bool launch_split_g(const DecodeArgs& a, int G, hipStream_t st) {
-  switch (G) {
-    case 1: launch_split<D, 1>(a, st); return true;
-    case 2: launch_split<D, 2>(a, st); return true;
-    case 4: launch_split<D, 4>(a, st); return true;
-    case 5: launch_split<D, 5>(a, st); return true;
-    case 8: launch_split<D, 8>(a, st); return true;
-    default: return false;
-  }
-}
+#ifndef SAS_DEC_TARGET_WG
+#define SAS_DEC_TARGET_WG 512    // aim for about this many single-wave workgroups
+#endif
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
-  const int G = a.Hq / a.Hkv;
   const long long pairs = (long long)a.B * a.Hkv;
   const int nblk = a.kcap + 1;
-  // Aim for >= 2048 workgroups (8 per CU) without chunks of fewer than 2 blocks.
-  int chunks = (int)((2048 + pairs - 1) / pairs);
+  // Enough chunks for about SAS_DEC_TARGET_WG workgroups, at least 2 blocks per chunk.
+  int chunks = (int)((SAS_DEC_TARGET_WG + pairs - 1) / pairs);
   chunks = max(1, min(chunks, (nblk + 1) / 2));
   a.bpc = (nblk + chunks - 1) / chunks;
   a.nchunk = (nblk + a.bpc - 1) / a.bpc;
-  const bool ok = a.d == 128 ? launch_split_g<128>(a, G, st) : launch_split_g<64>(a, G, st);
-  if (!ok) return hipErrorInvalidValue;
-  if (a.d == 128)
-    hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)(a.B * a.Hq)), dim3(128), 0, st, a);
-  else
-    hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, st, a);
+  const unsigned grid = (unsigned)(pairs * a.nchunk);
+  {
+    ProfScope prof("decode", st);
+    if (a.d == 128)
+      hipLaunchKernelGGL(decode_split_kernel<128>, dim3(grid), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL(decode_split_kernel<64>, dim3(grid), dim3(64), 0, st, a);
+  }
+  if (a.nchunk > 1) {
+    ProfScope prof("decode_merge", st);
+    if (a.d == 128)
+      hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)(a.B * a.Hq)), dim3(128), 0, st, a);
+    else
+      hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)(a.B * a.Hq)), dim3(64), 0, st, a);
+  }
   return hipGetLastError();
 }
 

@@ -192,7 +192,9 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
   REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && Lmax > 0, SAS_ERR_INVALID_ARG, "B, Hq, Hkv, Lmax must be > 0");
   REQUIRE(Hq % Hkv == 0, SAS_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
   const int G = Hq / Hkv;
-  REQUIRE(G == 1 || G == 2 || G == 4 || G == 5 || G == 8, SAS_ERR_UNSUPPORTED, "decode supports Hq/Hkv in {1,2,4,5,8} (got %d)", G);
+  REQUIRE(G <= 32, SAS_ERR_UNSUPPORTED, "decode supports Hq/Hkv <= 32 (got %d)", G);
+  REQUIRE((long long)Lmax * d * 2 < (1ll << 31), SAS_ERR_UNSUPPORTED,
+          "Lmax * d * 2 bytes must be < 2^31 (one cache row range per buffer resource)");
   REQUIRE(block == 64, SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
   REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
   REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);

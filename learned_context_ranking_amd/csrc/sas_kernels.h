@@ -7,6 +7,21 @@
 
 namespace sas {
 
+// Brackets one kernel launch with HIP events on its stream while timing is enabled
+// (sas_profile_enable); does nothing otherwise.
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t st);
+  ~ProfScope();
+  ProfScope(const ProfScope&) = delete;
+  ProfScope& operator=(const ProfScope&) = delete;
+
+ private:
+  const char* name_;
+  hipStream_t st_;
+  void* a_;
+};
+
 struct SelectArgs {
   const float* s;
   long long R;          // rows in total = B * H * rows

@@ -122,6 +122,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.R + 3) / 4)), block(256);
   const int c = a.cols;
+  ProfScope prof("select", st);
   if (c <= 64) hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, st, a);
   else if (c <= 128) hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, st, a);
   else if (c <= 256) hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, st, a);

@@ -39,6 +39,8 @@ SIGNATURES = {
                       _P, _P, _P, _P, _P, _SZ, _P], _I),
     "sas_decode_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "sas_decode": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
+    "sas_profile_enable": ([_I], _I),
+    "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
 }
 
 
@@ -204,3 +206,25 @@ def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None)
                             B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
                             _stream(q.device)))
     return o
+
+
+def profile_enable(on: bool = True):
+    """Turn the library's per-kernel event timing on or off (measurement only)."""
+    _check(lib().sas_profile_enable(1 if on else 0))
+
+
+def profile_collect(max_kernels: int = 32, name_len: int = 32):
+    """Per-kernel totals since the last collect: {name: (launches, total_ms)}, in first
+    launch order. Waits for the recorded events."""
+    names = ctypes.create_string_buffer(max_kernels * name_len)
+    launches = (ctypes.c_int * max_kernels)()
+    total = (ctypes.c_double * max_kernels)()
+    n = lib().sas_profile_collect(max_kernels, names, name_len, ctypes.cast(launches, ctypes.c_void_p),
+                                  ctypes.cast(total, ctypes.c_void_p))
+    if n < 0:
+        raise RuntimeError("sas_profile_collect: an event query failed")
+    out = {}
+    for i in range(n):
+        nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
+        out[nm] = (int(launches[i]), float(total[i]))
+    return out

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -121,9 +121,19 @@ def test_decode_rejects():
     args = [FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, NULL, 2, 8, 2, 128, 64, 4, 0.1, FAKE, FAKE, need, NULL]
     bad = list(args); bad[-2] = need - 1
     assert L.sas_decode(*bad) == sas.SAS_ERR_WORKSPACE
-    bad = list(args); bad[9] = 6; bad[10] = 2     # G = 3 not instantiated
+    bad = list(args); bad[9] = 66; bad[10] = 2    # G = 33 > 32 query columns
+    assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED
+    bad = list(args); bad[4] = 1 << 23            # Lmax * d * 2 = 2^31
     assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED
     bad = list(args); bad[3] = NULL               # kv_len
     assert L.sas_decode(*bad) == sas.SAS_ERR_INVALID_ARG
     bad = list(args); bad[12] = 128               # block
     assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED
+
+
+def test_profile_toggle_without_gpu():
+    """Enabling and collecting the kernel timing makes no HIP call while nothing ran."""
+    L = sas.lib()
+    assert L.sas_profile_enable(1) == sas.SAS_OK
+    assert sas.profile_collect() == {}
+    assert L.sas_profile_enable(0) == sas.SAS_OK
