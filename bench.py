@@ -8,9 +8,13 @@ backward with dQ, dK, dV and dg. Inputs are resident in HBM before timing starts
 
 value = algorithmic FLOPs / step time, counting only attended (query, key) pairs:
 4*d per pair forward (q.k, p.v) and 8*d backward (dO.v, p^T dO, dS k, dS^T q); the
-backward's recomputation of q.k is not counted. The decode workload (64 sequences,
-32,768 cached tokens, 16 blocks + the current block per KV head) is reported alongside
-as HBM GB/s of the decode kernel with the caches flushed from L2 / Infinity Cache.
+backward's recomputation of q.k is not counted. The roofline object covers the kernel
+with the longest launch (the key-major dK/dV pass), timed with the library's per-kernel
+HIP events over the timed region; its traffic comes from profiles/traffic_<kernel>.txt
+while the kernel's sources match the digest taken with the counters. The decode workload
+(64 sequences, 32,768 cached tokens, 16 blocks + the current block per KV head) is
+reported alongside as HBM GB/s of the decode kernel, with L2 / Infinity Cache evicted by
+a 1 GiB read before each launch.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
