@@ -34,6 +34,9 @@
 #ifndef SAS_DKV_NBUF
 #define SAS_DKV_NBUF 3   // ring depth of the key-major pass
 #endif
+#ifndef SAS_DKV_PIPE
+#define SAS_DKV_PIPE 1   // software-pipelined key-major pass
+#endif
 #ifndef SAS_DKV_ORDER
 #define SAS_DKV_ORDER 2  // (batch, KV head) pairs per launch phase; 0: all pairs interleaved
 #endif
@@ -369,7 +372,7 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 template <int D, int NBUF, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void dkv_kernel(const AttnArgs a) {
-  static_assert(NBUF == 2 || NBUF == 3, "ring depth");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
   constexpr int NW = 4;
   constexpr int TE = Tile<D>::ELEMS;
   // Each Q buffer carries the item's lse and delta rows behind the tile: every wave copies
@@ -378,12 +381,15 @@ void dkv_kernel(const AttnArgs a) {
   // which the compiler tracks apart and waits for one at a time.
   constexpr int TQ = TE + 4 * 128;
   constexpr int E2 = NBUF >= 3 ? TQ : 8, F2 = NBUF >= 3 ? TE : 8;
+  constexpr int E3 = NBUF >= 4 ? TQ : 8, F3 = NBUF >= 4 ? TE : 8;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sq2[E2];
+  __shared__ __attribute__((aligned(16))) uint16_t sq3[E3];
   __shared__ __attribute__((aligned(16))) uint16_t so0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t so1[TE];
   __shared__ __attribute__((aligned(16))) uint16_t so2[F2];
+  __shared__ __attribute__((aligned(16))) uint16_t so3[F3];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
@@ -527,7 +533,7 @@ void dkv_kernel(const AttnArgs a) {
   // buffer that is not read again), so every step has the same number of copies in flight
   // and the compiler's wait tracking stays exact across iterations.
   auto step = [&](const uint16_t* qc, const uint16_t* oc, uint16_t* qn, uint16_t* on) {
-    if (NBUF == 3) wait_vm_n<PER>(); else wait_vm();
+    if (NBUF == 4) wait_vm_n<2 * PER>(); else if (NBUF == 3) wait_vm_n<PER>(); else wait_vm();
     barrier_lds();
     int jj = m;
     float lg2 = 0.0f;
@@ -581,7 +587,7 @@ void dkv_kernel(const AttnArgs a) {
       step(sq1, so1, sq0, so0);
     }
     if (nfull < nitems) step(sq0, so0, sq1, so1);
-  } else {
+  } else if (NBUF == 3) {
     fetch(sq0, so0);
     fetch(sq1, so1);
     for (int it = 0; it < nfull; it += 3) {
@@ -591,12 +597,283 @@ void dkv_kernel(const AttnArgs a) {
     }
     if (nfull < nitems) step(sq0, so0, sq2, so2);
     if (nfull + 1 < nitems) step(sq1, so1, sq0, so0);
+  } else {
+    fetch(sq0, so0);
+    fetch(sq1, so1);
+    fetch(sq2, so2);
+    for (int it = 0; it < nfull; it += 4) {
+      step(sq0, so0, sq3, so3);
+      step(sq1, so1, sq0, so0);
+      step(sq2, so2, sq1, so1);
+      step(sq3, so3, sq2, so2);
+    }
+    if (nfull < nitems) step(sq0, so0, sq3, so3);
+    if (nfull + 1 < nitems) step(sq1, so1, sq0, so0);
+    if (nfull + 2 < nitems) step(sq2, so2, sq1, so1);
   }
 
   // Sum the two query halves: waves with qh = 1 hand their partials over through LDS (the
   // Q and dO buffers are free by now; key half 0 uses sq0 / sq1, key half 1 so0 / so1).
   constexpr int PERW = (D / 32) * 16 * 64;
   static_assert(PERW * sizeof(float) <= sizeof(so0), "reduction buffer");
+  __syncthreads();
+  float* rk = reinterpret_cast<float*>(kh == 0 ? sq0 : so0);
+  float* rv = reinterpret_cast<float*>(kh == 0 ? sq1 : so1);
+  if (qh == 1) {
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        rk[(dt * 16 + i) * 64 + lane] = dk[dt][i];
+        rv[(dt * 16 + i) * 64 + lane] = dv[dt][i];
+      }
+  }
+  __syncthreads();
+  if (qh == 0) {
+    float* dKp = a.dK + kv_off + key * D;
+    float* dVp = a.dV + kv_off + key * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+        f32x4 kv, vv;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int i = 4 * g4 + x;
+          kv[x] = (dk[dt][i] + rk[(dt * 16 + i) * 64 + lane]) * a.scale;
+          vv[x] = dv[dt][i] + rv[(dt * 16 + i) * 64 + lane];
+        }
+        *reinterpret_cast<f32x4*>(dKp + d0) = kv;
+        *reinterpret_cast<f32x4*>(dVp + d0) = vv;
+      }
+  }
+}
+
+// The key-major pass software-pipelined across items (same work split and results as
+// dkv_kernel). With one wave per SIMD the matrix and vector pipes only overlap when the
+// instruction stream interleaves them, so step it issues each S / dP product of item it+1
+// followed by one element of item it's softmax (scheduling barriers keep that order), then
+// item it's dV / dK products. A ring of 4 buffer sets holds item it (transposed reads),
+// item it+1 (row reads), item it+2 (copy in flight) and receives item it+3.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dkv_pipe_kernel(const AttnArgs a) {
+  constexpr int NW = 4;
+  constexpr int TE = Tile<D>::ELEMS;
+  constexpr int TQ = TE + 4 * 128;   // Q tile + lse / delta rows (see dkv_kernel)
+  __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sq2[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sq3[TQ];
+  __shared__ __attribute__((aligned(16))) uint16_t so0[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t so1[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t so2[TE];
+  __shared__ __attribute__((aligned(16))) uint16_t so3[TE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
+  // launch order as in dkv_kernel
+  const int BHp = a.B * a.Hkv;
+  const int P = SAS_DKV_ORDER > 0 ? min(SAS_DKV_ORDER, BHp) : BHp;
+  const int phase = (int)(blockIdx.x / ((unsigned)P * NB));
+  const int np = min(P, BHp - phase * P);
+  const int rem = (int)(blockIdx.x - (unsigned)phase * P * NB);
+  const int m = rem / np;
+  const int rr = phase * P + rem % np;
+  const int h = rr % a.Hkv, b = rr / a.Hkv;
+  const long long bh = (long long)b * a.Hkv + h;
+
+  const size_t kv_off = ((size_t)bh * a.n + (size_t)m * kBlock) * D;
+  const int key = 32 * kh + ql;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 16 * ks + 8 * hl));
+    vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 16 * ks + 8 * hl));
+  }
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+  const float c2 = a.scale * kLog2e;
+  const int g16 = lane >> 4, lp = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
+  const int rrow = 32 * qh + ql;
+  const int rx0 = rrow * D + ((hl ^ Tile<D>::swz(rrow)) << 3);
+  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
+  const int off0 = a.inv_off[bh * (NB + 1) + m];
+  const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
+  const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
+  const int nitems = (nlist + 1) * G;
+
+  const size_t head0 = (size_t)(b * a.Hq + h * G) * a.n;
+  const int qbytes = G * a.n * D * 2, rbytes = G * a.n * 4;
+  const uint16_t* qbase = a.Q + head0 * D;
+  const uint16_t* obase = a.dO + head0 * D;
+  const float* rbase = (wave == 1 ? a.delta : a.lse_rows) + head0;
+  constexpr int NWIN = Tile<D>::CPR / NW;
+  uint32_t voff[NWIN];
+#pragma unroll
+  for (int i = 0; i < NWIN; ++i) {
+    const int sidx = 64 * (wave + NW * i) + lane;
+    const int r = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
+    voff[i] = (uint32_t)(r * D + ((c ^ Tile<D>::swz(r)) << 3)) * 2u;
+  }
+  auto load_lst = [&](int e, int& v, float& g) {
+    v = m;
+    g = 0.0f;
+    if (e < nlist) {
+      const int p = list[nlist - 1 - e];
+      v = p / a.kcap;
+      const int slot = p - v * a.kcap;
+      g = a.logg != nullptr ? a.logg[((size_t)bh * NB + v) * a.kcap + slot] * kLog2e : 0.0f;
+    }
+  };
+  LaneList lst_c, lst_f;
+  int ec = 0, gc = 0, ef = 0, gf = 0;   // item being finished; next item to copy
+  auto fetch = [&](uint16_t* qb, uint16_t* ob) {
+    int jj = m;
+    if (ef < nlist) {
+      lst_f.ensure(ef, lane, load_lst);
+      jj = lst_f.at(ef);
+    }
+    const uint32_t row = (uint32_t)(gf * a.n + jj * kBlock);
+    const uint32_t so = row * (uint32_t)(D * 2);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(qbase, qbytes, qb + 512 * (wave + NW * i), voff[i], so);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(obase, qbytes, ob + 512 * (wave + NW * i), voff[i], so);
+    buffer_load_lds4(rbase, rbytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
+    if (!(ef == nlist && gf == G - 1)) {
+      if (++gf == G) { gf = 0; ++ef; }
+    }
+  };
+  constexpr int PER = 2 * NWIN + 1;
+  static_assert(2 * PER < 64, "copies in flight exceed the vmcnt range");
+
+  // row reads of the item in (qn, on) for its S^T and dP^T products
+  auto row_reads = [&](const uint16_t* qn, const uint16_t* on, bf16x8 (&qr)[D / 16], bf16x8 (&orw)[D / 16]) {
+    int rx = rx0;
+    asm volatile("" : "+v"(rx));
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qr[ks] = as_bf16x8(ld16(&qn[rx ^ (ks << 4)]));
+      orw[ks] = as_bf16x8(ld16(&on[rx ^ (ks << 4)]));
+    }
+  };
+  // step: item it in (qc, oc) with S^T / dP^T in (sc, dpc); item it+1 in (qn, on), whose
+  // products go to (sn, dpn); the next copy goes to (qf, of)
+  auto step = [&](const uint16_t* qc, const uint16_t* oc, const uint16_t* qn, const uint16_t* on,
+                  uint16_t* qf, uint16_t* of, const f32x16& sc, const f32x16& dpc, f32x16& sn,
+                  f32x16& dpn) {
+    wait_vm_n<PER>();   // item it+1 has landed; item it+2 may be in flight
+    barrier_lds();
+    int jj = m;
+    float lg2 = 0.0f;
+    if (ec < nlist) {
+      lst_c.ensure(ec, lane, load_lst);
+      jj = lst_c.at(ec);
+      lg2 = lst_c.gat(ec);
+    }
+    const bool diag = ec == nlist;
+    if (++gc == G) { gc = 0; ++ec; }
+    fetch(qf, of);
+    bf16x8 qr[D / 16], orw[D / 16];
+    row_reads(qn, on, qr, orw);
+    // transposed operands of item it, and its lse / delta rows
+    int tx = tx0;
+    asm volatile("" : "+v"(tx));
+    bf16x8 da[D / 32][2], qa[D / 32][2];
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int r0 = 32 * qh + 16 * hh;
+        const int o0 = r0 * D + (tx ^ ((4 * dt) << 3)), o1 = (r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3));
+        da[dt][hh] = join_tr16(lds_tr16(&oc[o0]), lds_tr16(&oc[o1]));
+        qa[dt][hh] = join_tr16(lds_tr16(&qc[o0]), lds_tr16(&qc[o1]));
+      }
+    const float* lc = reinterpret_cast<const float*>(qc + TE);
+    const float* dc = reinterpret_cast<const float*>(qc + TE + 128);
+    f32x4 l4[4], d4[4];
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {   // rows 32 qh + 8 grp + 4 hl + x
+      l4[grp] = *reinterpret_cast<const f32x4*>(&lc[32 * qh + 8 * grp + 4 * hl]);
+      d4[grp] = *reinterpret_cast<const f32x4*>(&dc[32 * qh + 8 * grp + 4 * hl]);
+    }
+    // S / dP products of item it+1 interleaved with item it's softmax, one element each
+    sn = f32x16{};
+    dpn = f32x16{};
+    float pv[16], dsv[16];
+    constexpr int NM = 2 * (D / 16);   // S and dP products, spread evenly over the 16 elements
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if ((e * NM) % 16 == 0) {
+        const int j = e * NM / 16, ks = j >> 1;
+        if ((j & 1) == 0) sn = mfma32(qr[ks], kf[ks], sn);
+        else dpn = mfma32(orw[ks], vf[ks], dpn);
+      }
+      const int grp = e >> 2, x = e & 3;
+      float p = fast_exp2(sc[e] * c2 + (lg2 - l4[grp][x] * kLog2e));
+      if (diag && key > 32 * qh + 8 * grp + 4 * hl + x) p = 0.0f;   // causal mask of block m
+      pv[e] = p;
+      dsv[e] = p * (dpc[e] - d4[grp][x]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int o = 8 * hh;
+      pb[hh] = pack8(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5], pv[o + 6], pv[o + 7]);
+      sb[hh] = pack8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS for item it
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        dv[dt] = mfma32(da[dt][hh], pb[hh], dv[dt]);
+        dk[dt] = mfma32(qa[dt][hh], sb[hh], dk[dt]);
+      }
+  };
+
+  // prologue: items 0, 1, 2 in flight; S / dP of item 0
+  fetch(sq0, so0);
+  fetch(sq1, so1);
+  fetch(sq2, so2);
+  wait_vm_n<2 * PER>();
+  barrier_lds();
+  f32x16 sA, dpA, sB, dpB;
+  {
+    bf16x8 qr[D / 16], orw[D / 16];
+    row_reads(sq0, so0, qr, orw);
+    sA = f32x16{};
+    dpA = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      sA = mfma32(qr[ks], kf[ks], sA);
+      dpA = mfma32(orw[ks], vf[ks], dpA);
+    }
+  }
+  const int nfull = nitems & ~3;
+  for (int it = 0; it < nfull; it += 4) {
+    step(sq0, so0, sq1, so1, sq3, so3, sA, dpA, sB, dpB);
+    step(sq1, so1, sq2, so2, sq0, so0, sB, dpB, sA, dpA);
+    step(sq2, so2, sq3, so3, sq1, so1, sA, dpA, sB, dpB);
+    step(sq3, so3, sq0, so0, sq2, so2, sB, dpB, sA, dpA);
+  }
+  if (nfull < nitems) step(sq0, so0, sq1, so1, sq3, so3, sA, dpA, sB, dpB);
+  if (nfull + 1 < nitems) step(sq1, so1, sq2, so2, sq0, so0, sB, dpB, sA, dpA);
+  if (nfull + 2 < nitems) step(sq2, so2, sq3, so3, sq1, so1, sA, dpA, sB, dpB);
+
+  // sum the two query halves through LDS (key half 0 uses sq0 / sq1, key half 1 so0 / so1)
+  constexpr int PERW = (D / 32) * 16 * 64;
+  static_assert(PERW * sizeof(float) <= sizeof(so0), "reduction buffer");
+  wait_vm();
   __syncthreads();
   float* rk = reinterpret_cast<float*>(kh == 0 ? sq0 : so0);
   float* rv = reinterpret_cast<float*>(kh == 0 ? sq1 : so1);
@@ -684,7 +961,10 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   }
   {
     ProfScope prof("dkv", st);
-    hipLaunchKernelGGL((dkv_kernel<D, SAS_DKV_NBUF, SAS_DKV_WPE>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+    if (SAS_DKV_PIPE)
+      hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)nrows), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((dkv_kernel<D, SAS_DKV_NBUF, SAS_DKV_WPE>), dim3((unsigned)nrows), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
