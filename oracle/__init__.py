@@ -1,5 +1,5 @@
 """CPU oracle for SAS log-gated block-sparse attention (test infrastructure only; see
 ``sas_oracle``)."""
 from .sas_oracle import (NEG_INF, attn_bwd, attn_fwd, bwd_query_block, decode,  # noqa: F401
-                         decode_rows_valid, fwd_query_block,
+                         decode_rows_valid, fwd_query_block, gates_bwd, gates_bwd_prefill,
                          dense_causal, row_log_gates, row_topk, select, select_prefill)

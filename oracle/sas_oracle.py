@@ -132,6 +132,43 @@ def select_prefill(s, topk, full_scope=False, kcap=None):
             logg.reshape(B, H, NB, kc))
 
 
+def gates_bwd(s, valid, idx, cnt, dg):
+    """Gradient with respect to the scores through the gate softmax.
+
+    [SAS-ko] "무엇과 다른가", choice 2: g = softmax(s) over the row's valid history blocks
+    (R2). dg holds dL/dg for the selected blocks, aligned with idx (R8); an unselected block
+    has no gradient of its own (choice 4, sparse scope), so its entry of dL/dg is 0. The
+    chain rule through the softmax, whose Jacobian is diag(g) - g g^T, gives
+    ds_m = g_m (dg_m - sum_m' g_m' dg_m') for every valid m. A NaN or -inf score has g = 0
+    (R5), hence ds = 0. Entries m >= valid are 0.
+    s: [R, ld]; valid [R]; idx, dg [R, kcap]; cnt [R]. Returns ds [R, ld] float64.
+    """
+    s = np.asarray(s)
+    R, ld = s.shape
+    valid = np.broadcast_to(np.asarray(valid, dtype=np.int64), (R,))
+    ds = np.zeros((R, ld), dtype=np.float64)
+    for r in range(R):
+        v = int(valid[r])
+        if v == 0:
+            continue
+        _, lg = row_log_gates(s[r, :v])
+        g = np.exp(lg)
+        dgf = np.zeros(v)
+        c = int(cnt[r])
+        dgf[np.asarray(idx[r, :c], dtype=np.int64)] = np.asarray(dg[r, :c], dtype=np.float64)
+        ds[r, :v] = g * dgf - g * np.dot(g, dgf)
+    return ds
+
+
+def gates_bwd_prefill(s, idx, cnt, dg):
+    """gates_bwd for prefill score tensors s [B, H, NB, NB] (row j has j valid blocks)."""
+    B, H, NB, ld = s.shape
+    valid = np.tile(np.arange(NB), B * H)
+    kc = idx.shape[-1]
+    ds = gates_bwd(s.reshape(-1, ld), valid, idx.reshape(-1, kc), cnt.reshape(-1), dg.reshape(-1, kc))
+    return ds.reshape(B, H, NB, ld)
+
+
 # ---------------------------------------------------------------- training forward/backward
 
 def _key_set(j, idx_row, cnt_j, logg_row, block):

@@ -197,6 +197,65 @@ def test_pd_finite_differences():
             assert abs(fd - dg[0, 0, j, t]) <= 1e-6 * max(1.0, abs(fd)), (j, t, fd, dg[0, 0, j, t])
 
 
+# ------------------------------------------------------------------ P-i: gate softmax backward
+
+@pytest.mark.parametrize("full", [False, True])
+def test_pi_score_gradient_through_the_whole_step(full):
+    """Central differences of L = sum(dO * O) with respect to the scores s, where the gates
+    come from s (g = softmax(s), SAS explainer (ko) section 무엇과 다른가, choice 2) and O
+    from the gated forward, against gates_bwd(dg of the oracle backward). In sparse scope
+    a small perturbation keeps the Top-K set, so unselected blocks receive only the
+    normalisation term; a dropped term, a wrong sign or a softmax over the wrong set fails."""
+    c = _rand_case(B=1, Hq=2, Hkv=1, n=64, d=8, block=8, topk=3, seed=21, full=full)
+    s64 = c["s"].astype(np.float64)
+
+    def loss(s):
+        idx, cnt, _, logg = oracle.select_prefill(s, 3, full_scope=full)
+        assert np.array_equal(idx, c["idx"])          # the selection did not move
+        O, _ = oracle.attn_fwd(c["Q"], c["K"], c["V"], idx, cnt, logg, c["scale"], c["block"])
+        return float(np.sum(c["dO"] * O))
+
+    _, _, _, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], c["logg"],
+                                  c["scale"], c["block"])
+    ds = oracle.gates_bwd_prefill(s64, c["idx"], c["cnt"], dg)
+    h = 1e-6
+    NB = s64.shape[2]
+    checked = 0
+    for j in range(2, NB):
+        for m in range(j):
+            sp = s64.copy(); sp[0, 0, j, m] += h
+            sm = s64.copy(); sm[0, 0, j, m] -= h
+            fd = (loss(sp) - loss(sm)) / (2 * h)
+            assert abs(fd - ds[0, 0, j, m]) <= 1e-6 * max(1.0, abs(fd)), (j, m, fd, ds[0, 0, j, m])
+            checked += 1
+    assert checked > 20
+    assert np.all(ds[0, 0][np.triu_indices(NB)] == 0.0)    # m >= j: no valid entry
+
+
+def test_pi_gates_bwd_invariants_and_special_cases():
+    """sum_m ds_m = 0 (a global shift of s leaves g unchanged, choice 2); a constant dL/dg
+    over every valid block gives ds = 0; one valid block gives ds = 0; a -inf or NaN score
+    (g = 0) gives ds = 0 there."""
+    g = np.random.default_rng(22)
+    R, ld = 6, 9
+    s = g.standard_normal((R, ld)).astype(np.float32)
+    s[4, 2] = -np.inf
+    s[5, 1] = np.nan
+    valid = np.array([9, 5, 1, 0, 7, 6])
+    idx, cnt, _, _ = oracle.select(s, valid, 3)
+    dg = g.standard_normal(idx.shape)
+    ds = oracle.gates_bwd(s, valid, idx, cnt, dg)
+    for r in range(R):
+        assert abs(ds[r].sum()) <= 1e-12 * max(1.0, np.abs(ds[r]).max())
+        assert np.all(ds[r, valid[r]:] == 0.0)
+    assert ds[2, 0] == 0.0 and np.all(ds[3] == 0.0)
+    assert ds[4, 2] == 0.0 and ds[5, 1] == 0.0
+    idx_f, cnt_f, _, _ = oracle.select(s, valid, 0, full_scope=True, kcap=ld)
+    dgc = np.where(idx_f >= 0, 0.75, 0.0)
+    ds_c = oracle.gates_bwd(s, valid, idx_f, cnt_f, dgc)
+    np.testing.assert_allclose(ds_c, 0.0, atol=1e-15)
+
+
 # ------------------------------------------------------------------ P-e: brute-force Top-K
 
 def _brute_topk(s, k):
