@@ -4,7 +4,8 @@
 A step is one pass of the training hot path over the Qwen3-4B-shaped single-layer
 workload (batch 1, 32 query / 8 KV heads, head_dim 128, n = 32,768, block 64, Top-K 32,
 bf16 Q/K/V/dO ~ N(0,1), fp32 scores ~ N(0,1)): gate + Top-K selection, gated forward,
-backward with dQ, dK, dV and dg. Inputs are resident in HBM before timing starts.
+backward with dQ, dK, dV and dg, and the score gradient ds through the gate softmax.
+Inputs are resident in HBM before timing starts.
 
 value = algorithmic FLOPs / step time, counting only attended (query, key) pairs:
 4*d per pair forward (q.k, p.v) and 8*d backward (dO.v, p^T dO, dS k, dS^T q); the
@@ -90,15 +91,16 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
     dK = torch.empty(t["K"].shape, dtype=torch.float32, device=dev)
     dV = torch.empty(t["V"].shape, dtype=torch.float32, device=dev)
     dg = torch.empty((w.B, w.Hkv, NB, w.topk), dtype=torch.float32, device=dev)
+    ds = torch.empty_like(t["s"])
     ws = sas.bwd_workspace(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dev)
     stream = torch.cuda.current_stream()
-    ev = {k: [] for k in ("sel", "fwd", "bwd")}
+    ev = {k: [] for k in ("sel", "fwd", "bwd", "gates_bwd")}
 
     def step(record):
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
             marks[0].record(stream)
-        idx_, cnt_, _, logg_ = sas.sas_topk_select(t["s"], w.topk, kcap=w.topk, cols=NB)
+        idx_, cnt_, lse_s, logg_ = sas.sas_topk_select(t["s"], w.topk, kcap=w.topk, cols=NB)
         if record:
             marks[1].record(stream)
         sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx_, cnt_, logg_, scale, out=O, lse_out=lse)
@@ -108,9 +110,14 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
                          outs=(dQ, dK, dV, dg))
         if record:
             marks[3].record(stream)
+        # gradient of the scores through the gate softmax
+        sas.sas_gates_bwd(t["s"], lse_s, idx_, cnt_, dg, cols=NB, out=ds)
+        if record:
+            marks[4].record(stream)
             ev["sel"].append((marks[0], marks[1]))
             ev["fwd"].append((marks[1], marks[2]))
             ev["bwd"].append((marks[2], marks[3]))
+            ev["gates_bwd"].append((marks[3], marks[4]))
         return cnt_
 
     log(f"[bench] warmup {warmup}")
@@ -257,7 +264,7 @@ def main():
     flop_step = tr["flop_fwd"] + tr["flop_bwd"]
     value = flop_step / (tr["ms_step"] * 1e-3) / 1e12
     ms = tr["ms"]
-    kern = {"select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"]}
+    kern = {"select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"], "gates_bwd": ms["gates_bwd"]}
     kern.update({"kernel:" + k: v for k, v in tr["kern_ms"].items()})
     fwd_tf = tr["flop_fwd"] / (ms["fwd"] * 1e-3) / 1e12
     bwd_tf = tr["flop_bwd"] / (ms["bwd"] * 1e-3) / 1e12
@@ -289,7 +296,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "qwen3_4b_train: B=1, Hq=32, Hkv=8, d=128, n=32768, block=64, Top-K=32, "
-                        "sparse scope, select+fwd+bwd with dg",
+                        "sparse scope, select+fwd+bwd with dg + score gradient through the gate softmax",
             "global_batch": w.B, "seq_len": w.n, "parallelism": "single GPU",
             "attended_pairs": tr["pairs"], "flop_per_step": flop_step,
         },

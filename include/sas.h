@@ -115,6 +115,34 @@ sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int
                            int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream);
 
 /*
+ * sas_gates_bwd - gradient with respect to the scores through the gate softmax.
+ * [SAS-ko] "무엇과 다른가", choice 2: g = softmax(s) over a row's valid history blocks; the
+ * chain rule through its Jacobian diag(g) - g g^T gives, for every valid block m,
+ *   ds_m = g_m (dg_m - c),   c = sum over the row's selected slots t of g_idx[t] dg[t],
+ * where dg_m is the gradient of block m's gate: dg[t] for the selected block idx[t] and 0
+ * for an unselected one (choice 4, sparse scope: only selected blocks reach the attention).
+ *
+ * Same s/B/H/rows/cols/ld/mode/row_valid arguments as sas_gates, and:
+ *   lse    fp32 [B][H][rows], in: the LSE sas_gates / sas_topk_select wrote for s. g_m is
+ *          recomputed as exp(s_m - lse); a NaN or -inf score, or a row whose lse is -inf,
+ *          has g = 0 and therefore ds = 0.
+ *   idx    int32 [B][H][rows][kcap], in: the selected blocks; entries t < cnt that lie in
+ *          [0, valid) must be distinct within a row (sas_topk_select writes them so);
+ *          others are ignored.
+ *   cnt    int32 [B][H][rows], in: selected slots per row, clamped to [0, kcap].
+ *   dg     fp32 [B][H][rows][kcap], in: dL/dg aligned with idx (sas_attn_bwd's dg output,
+ *          reshaped; in PREFILL mode H is the KV-head count).
+ *   kcap   0..8192; idx and dg may be NULL when kcap = 0.
+ *   ds     fp32 [B][H][rows][ld], out: every entry is written (0 for m >= valid). Must
+ *          not alias s.
+ * Errors: as sas_gates, plus SAS_ERR_INVALID_ARG for a NULL lse/cnt/ds, kcap out of range,
+ * or ds == s. Deterministic (no atomics to global memory).
+ */
+sas_status sas_gates_bwd(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                         const int32_t* row_valid, const float* lse, const int32_t* idx,
+                         const int32_t* cnt, const float* dg, int kcap, float* ds, void* stream);
+
+/*
  * sas_attn_fwd - log-gated block-sparse attention forward.
  * [SAS-ja] "仕組み", eq. (9) / [SAS-ko] "어떻게 동작하나": o = softmax(scale q K_S^T + log g_S) V_S
  * with S = the current block (causal, gate 1) plus the blocks in idx, log g broadcast to

@@ -109,6 +109,23 @@ sas_status sas_gates(const float* s, int B, int H, int rows, int cols, int ld, i
   return hip_result(sas::launch_select(a, (hipStream_t)stream), "sas_gates launch");
 }
 
+sas_status sas_gates_bwd(const float* s, int B, int H, int rows, int cols, int ld, int mode,
+                         const int32_t* row_valid, const float* lse, const int32_t* idx,
+                         const int32_t* cnt, const float* dg, int kcap, float* ds, void* stream) {
+  sas_status st = check_rows(s, B, H, rows, cols, ld, mode, row_valid);
+  if (st != SAS_OK) return st;
+  REQUIRE(lse != nullptr && cnt != nullptr && ds != nullptr, SAS_ERR_INVALID_ARG,
+          "lse, cnt and ds must be non-NULL");
+  REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);
+  REQUIRE(kcap == 0 || (idx != nullptr && dg != nullptr), SAS_ERR_INVALID_ARG, "idx and dg must be non-NULL");
+  REQUIRE((const void*)ds != (const void*)s, SAS_ERR_INVALID_ARG, "ds must not alias s");
+  sas::GatesBwdArgs a{};
+  a.s = s; a.R = (long long)B * H * rows; a.H = H; a.rows = rows; a.cols = cols; a.ld = ld;
+  a.mode = mode; a.row_valid = row_valid; a.lse = lse; a.idx = idx; a.cnt = cnt; a.dg = dg;
+  a.kcap = kcap; a.ds = ds;
+  return hip_result(sas::launch_gates_bwd(a, (hipStream_t)stream), "sas_gates_bwd launch");
+}
+
 sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int ld, int mode,
                            const int32_t* row_valid, int topk, int scope, int kcap,
                            int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream) {

@@ -38,6 +38,24 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs& a, hipStream_t st);
 
+constexpr int kMaxCols = 8192;   // longest score row (history blocks) the selection handles
+
+struct GatesBwdArgs {
+  const float* s;
+  long long R;          // rows in total = B * H * rows
+  int H, rows, cols;
+  long long ld;
+  int mode;             // 0 prefill, 1 decode
+  const int32_t* row_valid;
+  const float* lse;
+  const int32_t* idx;
+  const int32_t* cnt;
+  const float* dg;
+  int kcap;
+  float* ds;
+};
+hipError_t launch_gates_bwd(const GatesBwdArgs& a, hipStream_t st);
+
 struct AttnArgs {
   const uint16_t* Q;
   const uint16_t* K;

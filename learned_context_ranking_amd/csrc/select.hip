@@ -134,4 +134,70 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- gate softmax backward
+
+// [SAS-ko] "무엇과 다른가", choice 2 (g = softmax(s) over the valid history) with choice 4
+// (sparse scope: only selected blocks have a gradient dL/dg of their own): the chain rule
+// through the softmax gives ds_m = g_m (dg_m - c), c = sum over the selected slots of
+// g dg, for every valid m (dg_m = 0 when m is not selected). One wavefront per score row;
+// the selected blocks are marked in an LDS bitmap so every ds entry is written once.
+__global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
+  __shared__ uint32_t sel_bits[4][kMaxCols / 32];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + w;
+  const bool live = row < a.R;
+  int valid = 0;
+  if (live) {
+    if (a.mode == 0) {
+      valid = (int)(row % a.rows);
+    } else {
+      const long long b = row / ((long long)a.H * a.rows);
+      valid = a.row_valid[b];
+    }
+    valid = min(max(valid, 0), a.cols);
+  }
+  const float* srow = a.s + row * a.ld;
+  float* drow = a.ds + row * a.ld;
+  const float lse = live ? a.lse[row] : -INFINITY;
+  const int cnt = live ? min(max(a.cnt[row], 0), a.kcap) : 0;
+  const int32_t* irow = a.idx + row * a.kcap;
+  const float* grow = a.dg + row * a.kcap;
+  // gate of block m (0 for a NaN or -inf score, or a row without finite LSE)
+  auto gate = [&](int m) {
+    const float v = srow[m];
+    if (!(v > -INFINITY) || !(lse > -INFINITY)) return 0.0f;
+    return expf(v - lse);
+  };
+  for (int i = lane; i < kMaxCols / 32; i += 64) sel_bits[w][i] = 0u;
+  __syncthreads();
+  float c = 0.0f;
+  for (int t = lane; t < cnt; t += 64) {
+    const int m = irow[t];
+    if (m >= 0 && m < valid) {
+      atomicOr(&sel_bits[w][m >> 5], 1u << (m & 31));
+      c += gate(m) * grow[t];
+    }
+  }
+  c = wave_sum(c);
+  __syncthreads();
+  if (!live) return;  // uniform per wave; no barrier follows
+  for (int m = lane; m < a.ld; m += 64) {
+    if (m >= valid) {
+      drow[m] = 0.0f;
+    } else if (!((sel_bits[w][m >> 5] >> (m & 31)) & 1u)) {
+      drow[m] = -gate(m) * c;
+    }
+  }
+  for (int t = lane; t < cnt; t += 64) {
+    const int m = irow[t];
+    if (m >= 0 && m < valid) drow[m] = gate(m) * (grow[t] - c);
+  }
+}
+
+hipError_t launch_gates_bwd(const GatesBwdArgs& a, hipStream_t st) {
+  ProfScope prof("gates_bwd", st);
+  hipLaunchKernelGGL(gates_bwd_kernel, dim3((unsigned)((a.R + 3) / 4)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace sas

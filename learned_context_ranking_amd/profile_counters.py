@@ -22,7 +22,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernel short name -> (substring of the device symbol, the sources its code comes from)
 KERNELS = {
-    "dkv": ("dkv_kernel", ["attn_bwd.hip", "sas_common.h"]),
+    "dkv": ("dkv_pipe_kernel", ["attn_bwd.hip", "sas_common.h"]),
     "dq": ("dq_kernel", ["attn_bwd.hip", "sas_common.h"]),
     "fwd": ("fwd_kernel", ["attn_fwd.hip", "sas_common.h"]),
     "decode": ("decode_split_kernel", ["decode.hip", "sas_common.h"]),

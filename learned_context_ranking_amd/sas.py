@@ -33,6 +33,7 @@ SIGNATURES = {
     "sas_last_error": ([], ctypes.c_char_p),
     "sas_gates": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
+    "sas_gates_bwd": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P], _I),
     "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "sas_attn_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
     "sas_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -131,6 +132,31 @@ def sas_topk_select(s, topk, scope="sparse", mode="prefill", row_valid=None, kca
                                  SCOPE[scope], kcap, _ptr(idx), _ptr(cnt), _ptr(lse), _ptr(logg),
                                  _stream(dev)))
     return idx, cnt, lse, logg
+
+
+def sas_gates_bwd(s, lse, idx, cnt, dg, mode="prefill", row_valid=None, cols=None, out=None):
+    """Gradient with respect to s through the gate softmax.
+    s fp32 [B, H, rows, ld]; lse [B, H, rows] from sas_gates / sas_topk_select; idx int32 and
+    dg fp32 [B, H, rows, kcap]; cnt int32 [B, H, rows]. Returns ds fp32 [B, H, rows, ld]."""
+    _need(s, torch.float32, "s")
+    _need(lse, torch.float32, "lse")
+    _need(idx, torch.int32, "idx")
+    _need(cnt, torch.int32, "cnt")
+    _need(dg, torch.float32, "dg")
+    B, H, rows, ld = s.shape
+    kcap = idx.shape[-1]
+    if tuple(idx.shape) != (B, H, rows, kcap) or tuple(dg.shape) != (B, H, rows, kcap):
+        raise ValueError(f"idx {tuple(idx.shape)} / dg {tuple(dg.shape)} do not match s {tuple(s.shape)}")
+    if tuple(lse.shape) != (B, H, rows) or tuple(cnt.shape) != (B, H, rows):
+        raise ValueError(f"lse {tuple(lse.shape)} / cnt {tuple(cnt.shape)} do not match s {tuple(s.shape)}")
+    cols = ld if cols is None else cols
+    if row_valid is not None:
+        _need(row_valid, torch.int32, "row_valid")
+    ds = torch.empty_like(s) if out is None else out
+    _need(ds, torch.float32, "out")
+    _check(lib().sas_gates_bwd(_ptr(s), B, H, rows, cols, ld, ROWS[mode], _ptr(row_valid), _ptr(lse),
+                               _ptr(idx), _ptr(cnt), _ptr(dg), kcap, _ptr(ds), _stream(s.device)))
+    return ds
 
 
 def sas_attn_fwd(Q, K, V, idx, cnt, logg, scale, out=None, lse_out=None):

@@ -23,7 +23,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_PLANT, TID_QDEC = 0, 1, 2, 3, 4, 5, 6
+TID_Q, TID_K, TID_V, TID_S, TID_DO, TID_PLANT, TID_QDEC, TID_DG = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def rng(seed: int, tensor_id: int, chunk: int = 0) -> np.random.Generator:
@@ -87,6 +87,12 @@ def scores_normal(shape, seed: int, mu: float = 0.0, sigma: float = 1.0) -> np.n
             g = rng(seed, TID_S, b * H + h)
             out[b, h] = (mu + sigma * g.standard_normal(shape[2:], dtype=np.float32)).astype(np.float32)
     return out
+
+
+def normal_f32(shape, seed: int, tensor_id: int, sigma: float = 1.0) -> np.ndarray:
+    """fp32 N(0, sigma^2) draws of any shape from one generator (e.g. an upstream gradient)."""
+    g = rng(seed, tensor_id)
+    return (sigma * g.standard_normal(shape, dtype=np.float32)).astype(np.float32)
 
 
 def scores_planted(B: int, H: int, NB: int, seed: int, nplant: int = 8,

@@ -165,7 +165,8 @@ def gates_bwd_prefill(s, idx, cnt, dg):
     B, H, NB, ld = s.shape
     valid = np.tile(np.arange(NB), B * H)
     kc = idx.shape[-1]
-    ds = gates_bwd(s.reshape(-1, ld), valid, idx.reshape(-1, kc), cnt.reshape(-1), dg.reshape(-1, kc))
+    R = B * H * NB
+    ds = gates_bwd(s.reshape(R, ld), valid, idx.reshape(R, kc), cnt.reshape(R), dg.reshape(R, kc))
     return ds.reshape(B, H, NB, ld)
 
 

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -93,6 +93,27 @@ def test_select_rejects():
     assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
     g = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, NULL, NULL, NULL]
     assert L.sas_gates(*g) == sas.SAS_ERR_INVALID_ARG   # lse NULL
+
+
+def test_gates_bwd_rejects():
+    L = sas.lib()
+    # s, B, H, rows, cols, ld, mode, row_valid, lse, idx, cnt, dg, kcap, ds, stream
+    args = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, FAKE, FAKE, FAKE, FAKE, 4, ctypes.c_void_p(0x20000), NULL]
+    for i, code in ((0, sas.SAS_ERR_INVALID_ARG), (8, sas.SAS_ERR_INVALID_ARG), (10, sas.SAS_ERR_INVALID_ARG),
+                    (13, sas.SAS_ERR_INVALID_ARG), (9, sas.SAS_ERR_INVALID_ARG), (11, sas.SAS_ERR_INVALID_ARG)):
+        bad = list(args); bad[i] = NULL
+        assert L.sas_gates_bwd(*bad) == code, i
+    bad = list(args); bad[13] = FAKE        # ds aliases s
+    assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[12] = 8193
+    assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[6] = sas.ROWS["decode"]   # decode needs row_valid
+    assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[4] = 9000; bad[5] = 9000
+    assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_UNSUPPORTED
+    bad = list(args); bad[12] = -1
+    assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
+    assert "kcap" in L.sas_last_error().decode()
 
 
 def test_bwd_workspace_and_rejects():
