@@ -782,12 +782,21 @@ void dkv_pipe_kernel(const AttnArgs a) {
     const bool diag = ec == nlist;
     if (++gc == G) { gc = 0; ++ec; }
     fetch(qf, of);
+    // lse / delta rows of item it first (the softmax waits on them), then the row reads
+    f32x4 l4[4], d4[4];
+    const float* lc = reinterpret_cast<const float*>(qc + TE);
+    const float* dc = reinterpret_cast<const float*>(qc + TE + 128);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {   // rows 32 qh + 8 grp + 4 hl + x
+      l4[grp] = *reinterpret_cast<const f32x4*>(&lc[32 * qh + 8 * grp + 4 * hl]);
+      d4[grp] = *reinterpret_cast<const f32x4*>(&dc[32 * qh + 8 * grp + 4 * hl]);
+    }
     bf16x8 qr[D / 16], orw[D / 16];
     row_reads(qn, on, qr, orw);
-    // transposed operands of item it, and its lse / delta rows
+    // transposed operands of item it
+    bf16x8 da[D / 32][2], qa[D / 32][2];
     int tx = tx0;
     asm volatile("" : "+v"(tx));
-    bf16x8 da[D / 32][2], qa[D / 32][2];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -797,14 +806,6 @@ void dkv_pipe_kernel(const AttnArgs a) {
         da[dt][hh] = join_tr16(lds_tr16(&oc[o0]), lds_tr16(&oc[o1]));
         qa[dt][hh] = join_tr16(lds_tr16(&qc[o0]), lds_tr16(&qc[o1]));
       }
-    const float* lc = reinterpret_cast<const float*>(qc + TE);
-    const float* dc = reinterpret_cast<const float*>(qc + TE + 128);
-    f32x4 l4[4], d4[4];
-#pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {   // rows 32 qh + 8 grp + 4 hl + x
-      l4[grp] = *reinterpret_cast<const f32x4*>(&lc[32 * qh + 8 * grp + 4 * hl]);
-      d4[grp] = *reinterpret_cast<const f32x4*>(&dc[32 * qh + 8 * grp + 4 * hl]);
-    }
     // S / dP products of item it+1 interleaved with item it's softmax, one element each
     sn = f32x16{};
     dpn = f32x16{};
