@@ -21,6 +21,10 @@ Sources, cited by page title and section:
   one gate per block broadcast to its tokens), section 4.3 eq. (9) (log g added to the
   logits inside the softmax; exp(z + log g) = g exp(z)) and Algorithm 2 / section 5.1
   (inference: Top-K on s, no gates, plain sparse attention).
+* [PBS-ja] "Sparser Block-Sparse Attention via Token Permutation" (gist.science/ja/paper/
+  2510.21270), prior art cited for one step only: sections "3." (proxy scoring) and
+  "4. 実装" (block selection) estimate a block's importance by mean pooling of attention
+  scores, which stands in for the undefined SAS selector in long-context decode selection.
 * [SAS-ko] "SAS는 언어모델 손실로 문맥 순위를 직접 학습하는 사후 어텐션 희소화다"
   (onedev.kr/papers/5). Section "어떻게 동작하나" gives o = softmax(q K_S^T + log g_S) V_S.
   Section "무엇과 다른가" gives the four design choices: (1) the gate inside the softmax and
@@ -366,3 +370,63 @@ def decode(q, Kc, Vc, kv_len, idx, cnt, scale, block=64, logg=None):
                 e = np.exp(z - z.max())
                 o[b, h * G + g] = (e / e.sum()) @ Vb
     return o
+
+
+# ---------------------------------------------------------------- long-context decode selection
+
+def pool_keys(Kc, kv_len, block=64):
+    """Block means of the key cache: kbar[b, h, m] = (1/b) sum_{i in B_m} k_i for every
+    complete block m ((m + 1) * b <= kv_len[b]); incomplete and absent blocks are 0.
+
+    A cache of these means turns the block score below into one dot product per block.
+    Kc [B, Hkv, Lmax, d]; returns [B, Hkv, Lmax // b, d] float64.
+    """
+    Kc = np.asarray(Kc, np.float64)
+    B, Hkv, Lmax, d = Kc.shape
+    C = Lmax // block
+    out = np.zeros((B, Hkv, C, d))
+    for b in range(B):
+        full = min(int(kv_len[b]) // block, C)
+        if full > 0:
+            out[b, :, :full] = Kc[b, :, :full * block].reshape(Hkv, full, block, d).mean(axis=2)
+    return out
+
+
+def decode_block_scores(q, Kc, kv_len, scale, block=64):
+    """Stand-in selector score of each history block for one decode step.
+
+    The pages do not define the selector network (AttnGate), so block importance is taken
+    as in [PBS-ja] "4. 実装" (block selection) and "3." (proxy scoring): the mean of the
+    attention scores over the block. Here the mean runs over the b keys of block m and the
+    G query heads of the KV group (one score row per (sequence, KV head), R3):
+    s[b, h, m] = mean_{g, i in B_m} scale * q_{hG+g} . k_i, for the history blocks
+    m < (kv_len - 1) // b (R7); later entries are -inf.
+    q [B, Hq, d]; Kc [B, Hkv, Lmax, d]; returns [B, Hkv, Lmax // b] float64.
+    """
+    q = np.asarray(q, np.float64)
+    Kc = np.asarray(Kc, np.float64)
+    B, Hq, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    G = Hq // Hkv
+    C = Lmax // block
+    s = np.full((B, Hkv, C), NEG_INF)
+    for b in range(B):
+        hist = int(decode_rows_valid(kv_len[b], block))
+        if hist <= 0:
+            continue
+        for h in range(Hkv):
+            logits = scale * (q[b, h * G:(h + 1) * G] @ Kc[b, h, :hist * block].T)   # [G, hist * b]
+            s[b, h, :hist] = logits.reshape(G, hist, block).mean(axis=(0, 2))
+    return s
+
+
+def decode_select(q, Kc, kv_len, scale, topk, kcap=None, block=64):
+    """Block scores plus Top-K for one decode step (Algorithm 2 of [SAS-ja] "仕組み":
+    the K best-scoring history blocks). Returns (s, idx [B, Hkv, kcap], cnt [B, Hkv],
+    lse [B, Hkv], logg [B, Hkv, kcap])."""
+    s = decode_block_scores(q, Kc, kv_len, scale, block)
+    B, Hkv, C = s.shape
+    valid = np.repeat(decode_rows_valid(kv_len, block), Hkv)
+    idx, cnt, lse, logg = select(s.reshape(B * Hkv, C), valid, topk, kcap=kcap)
+    kc = idx.shape[-1]
+    return s, idx.reshape(B, Hkv, kc), cnt.reshape(B, Hkv), lse.reshape(B, Hkv), logg.reshape(B, Hkv, kc)

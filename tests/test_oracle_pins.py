@@ -432,3 +432,97 @@ def test_synth_bf16_rounding_and_determinism():
     z = synth.scores_zipf(1, 2, 16, 0)
     p = synth.scores_planted(1, 2, 16, 0)
     assert z.shape == p.shape == (1, 2, 16, 16) and z.dtype == np.float32
+
+
+# ------------------------------------------------------------------ P-j: long-context decode selection
+
+def test_pj_pool_keys_closed_form():
+    """Keys equal to their token index (plus a per-head offset) pool to 64 m + 31.5 (+ the
+    offset) for every complete block; incomplete and absent blocks stay 0."""
+    B, Hkv, L, d = 2, 3, 64 * 5, 4
+    Kc = np.zeros((B, Hkv, L, d))
+    Kc += np.arange(L)[None, None, :, None]
+    Kc += 1000.0 * np.arange(Hkv)[None, :, None, None]
+    kv_len = np.array([64 * 3 + 10, 63])
+    kb = oracle.pool_keys(Kc, kv_len)
+    assert kb.shape == (B, Hkv, 5, d)
+    for h in range(Hkv):
+        for m in range(3):
+            assert np.all(kb[0, h, m] == 64 * m + 31.5 + 1000.0 * h)
+    assert np.all(kb[0, :, 3:] == 0.0) and np.all(kb[1] == 0.0)
+
+
+def test_pj_block_scores_brute_force_loops():
+    """Plain loops over query heads and key tokens (mean of scale q.k over the block and
+    the KV group) on a tiny case with two sequences of different lengths."""
+    g = np.random.default_rng(30)
+    B, Hq, Hkv, d, L, blk = 2, 4, 2, 3, 40, 8
+    q = g.standard_normal((B, Hq, d))
+    Kc = g.standard_normal((B, Hkv, L, d))
+    kv_len = np.array([37, 9])
+    scale = 0.7
+    s = oracle.decode_block_scores(q, Kc, kv_len, scale, block=blk)
+    G = Hq // Hkv
+    for b in range(B):
+        hist = (kv_len[b] - 1) // blk
+        for h in range(Hkv):
+            for m in range(L // blk):
+                if m >= hist:
+                    assert s[b, h, m] == -np.inf
+                    continue
+                tot = 0.0
+                for gg in range(G):
+                    for i in range(m * blk, (m + 1) * blk):
+                        tot += scale * sum(q[b, h * G + gg, t] * Kc[b, h, i, t] for t in range(d))
+                assert abs(s[b, h, m] - tot / (G * blk)) <= 1e-12 * max(1.0, abs(tot))
+    assert hist == 1     # the second sequence has exactly one history block
+
+
+def test_pj_block_scores_closed_form_and_pooled_dot():
+    """Constant keys v_m per block and identical group queries u give s_m = scale u.v_m;
+    for random inputs the score equals scale * mean(group queries) . pooled key (the two
+    routes through the oracle share no code)."""
+    B, Hq, Hkv, d, L = 1, 6, 2, 5, 64 * 6 + 3
+    g = np.random.default_rng(31)
+    v = g.standard_normal((Hkv, L // 64, d))
+    Kc = np.repeat(v, 64, axis=1)[None]
+    Kc = np.concatenate([Kc, g.standard_normal((1, Hkv, L - Kc.shape[2], d))], axis=2)
+    u = g.standard_normal((Hkv, d))
+    q = np.repeat(u, Hq // Hkv, axis=0)[None]
+    kv_len = np.array([L])
+    s = oracle.decode_block_scores(q, Kc, kv_len, 0.25)
+    hist = (L - 1) // 64
+    assert hist == 6
+    for h in range(Hkv):
+        np.testing.assert_allclose(s[0, h, :hist], 0.25 * v[h, :hist] @ u[h], rtol=1e-12, atol=1e-12)
+    # random inputs: pooled-key route
+    q = g.standard_normal((2, 8, 16))
+    Kc = g.standard_normal((2, 2, 64 * 9, 16))
+    kv_len = np.array([64 * 9, 64 * 4 + 1])
+    s = oracle.decode_block_scores(q, Kc, kv_len, 0.3)
+    kb = oracle.pool_keys(Kc, kv_len)
+    for b in range(2):
+        hist = (kv_len[b] - 1) // 64
+        for h in range(2):
+            qbar = q[b, 4 * h:4 * h + 4].mean(axis=0)
+            np.testing.assert_allclose(s[b, h, :hist], 0.3 * kb[b, h, :hist] @ qbar, rtol=1e-12, atol=1e-12)
+            assert np.all(np.isneginf(s[b, h, hist:]))
+
+
+def test_pj_decode_select_planted_and_ties():
+    """A block whose keys align with the query ranks first; with all-equal keys every
+    score ties and the lowest K history blocks are kept (R5), ascending (R6)."""
+    d, L = 8, 64 * 20 + 5
+    g = np.random.default_rng(32)
+    Kc = 0.01 * g.standard_normal((1, 1, L, d))
+    q = np.zeros((1, 2, d)); q[0, :, 0] = 1.0
+    Kc[0, 0, 64 * 7:64 * 8, 0] += 5.0
+    Kc[0, 0, 64 * 13:64 * 14, 0] += 4.0
+    s, idx, cnt, lse, logg = oracle.decode_select(q, Kc, np.array([L]), 1.0, topk=2)
+    assert list(idx[0, 0]) == [7, 13] and cnt[0, 0] == 2
+    Kc = np.ones((1, 1, L, d))
+    s, idx, cnt, _, _ = oracle.decode_select(q, Kc, np.array([L]), 1.0, topk=4, kcap=6)
+    assert list(idx[0, 0]) == [0, 1, 2, 3, -1, -1] and cnt[0, 0] == 4
+    # budget above the history keeps every history block
+    s, idx, cnt, _, _ = oracle.decode_select(q, Kc, np.array([64 * 3 + 1]), 1.0, topk=8, kcap=8)
+    assert cnt[0, 0] == 3 and list(idx[0, 0, :3]) == [0, 1, 2]
