@@ -15,7 +15,9 @@ HIP events over the timed region; its traffic comes from profiles/traffic_<kerne
 while the kernel's sources match the digest taken with the counters. The decode workload
 (64 sequences, 32,768 cached tokens, 16 blocks + the current block per KV head) is
 reported alongside as HBM GB/s of the decode kernel, with L2 / Infinity Cache evicted by
-a 1 GiB read before each launch.
+a 1 GiB read before each launch. The long-context decode object times one decode step's
+selection (block scores over the pooled-key cache + Top-K) against its sparse attention
+at 32K-512K cached tokens.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
@@ -199,6 +201,60 @@ def run_decode(steps, torch):
                          f"K={K} blocks + current block, ungated (Algorithm 2)")
 
 
+def run_long_decode(torch, reps=20):
+    """Long-context decode selection: one decode step's block scoring + Top-K
+    (sas_decode_select over the pooled-key cache) against its sparse attention
+    (sas_decode) at 32K, 128K and 512K cached tokens, batch 1 and 8, 32 query / 8 KV heads,
+    d = 128, K = 16. The caches are allocated once at 512K capacity; kv_len sets the
+    context. Pooling is not timed: each block is pooled once, when it completes."""
+    from learned_context_ranking_amd import sas
+    dev = torch.device("cuda", 0)
+    Bmax, Hq, Hkv, d, Lmax, K = 8, 32, 8, 128, 1 << 19, 16
+    g = torch.Generator(device=dev)
+    g.manual_seed(4321)
+    log("[bench] long-context decode: generating 512K-token caches for 8 sequences on device")
+    Kc = torch.randn((Bmax, Hkv, Lmax, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    Vc = torch.randn((Bmax, Hkv, Lmax, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    q = torch.randn((Bmax, Hq, d), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    full = torch.full((Bmax,), Lmax, dtype=torch.int32, device=dev)
+    kbar = sas.sas_pool_keys(Kc, full)
+    C = Lmax // 64
+    s = torch.empty((Bmax, Hkv, C), dtype=torch.float32, device=dev)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    scale = 1.0 / math.sqrt(d)
+    out = []
+    for B in (1, 8):
+        ws = sas.decode_workspace(B, Hq, Hkv, d, K, dev)
+        o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device=dev)
+        for L in (1 << 15, 1 << 17, 1 << 19):
+            kv_len = torch.full((B,), L, dtype=torch.int32, device=dev)
+            sel_t, att_t = [], []
+            for r in range(reps + 3):
+                flush.sum()
+                a, b_, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                a.record(stream)
+                _, idx, cnt, _, _ = sas.sas_decode_select(q[:B], kbar[:B], kv_len, scale, K, s_out=s[:B])
+                b_.record(stream)
+                sas.sas_decode(q[:B], Kc[:B], Vc[:B], kv_len, idx, cnt, scale, ws=ws, out=o)
+                c.record(stream)
+                if r >= 3:
+                    sel_t.append((a, b_))
+                    att_t.append((b_, c))
+            torch.cuda.synchronize()
+            ms_sel = float(np.median([x.elapsed_time(y) for x, y in sel_t]))
+            ms_att = float(np.median([x.elapsed_time(y) for x, y in att_t]))
+            hist = (L - 1) // 64
+            sel_bytes = B * Hkv * hist * (d * 2 + 4)
+            out.append({"context": L, "batch": B, "select_us": round(ms_sel * 1e3, 2),
+                        "attn_us": round(ms_att * 1e3, 2),
+                        "select_share": round(ms_sel / (ms_sel + ms_att), 3),
+                        "select_gbs": round(sel_bytes / ms_sel / 1e6, 1)})
+            log(f"[bench]   B={B} L={L}: select {ms_sel * 1e3:.1f} us, attention {ms_att * 1e3:.1f} us")
+    del Kc, Vc, kbar
+    return out
+
+
 def cpu_baseline(w, host, cnt, budget_s=20.0):
     """The oracle (NumPy, float64) on a sample of query blocks of the same workload; FLOPs
     of the sampled blocks over their wall time. Threads = the BLAS pool's size."""
@@ -239,6 +295,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the step without the per-kernel events (no roofline figures)")
@@ -314,6 +371,12 @@ def main():
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(dec["gbs"] / PEAK_HBM_GBS, 4),
                                       "traffic": profiled_traffic("decode")}}
+    if not args.no_long_decode:
+        out["long_decode"] = {
+            "workload": "one decode step: block scores over pooled keys + Top-K (sas_decode_select), then "
+                        "sparse attention (sas_decode); Hq=32, Hkv=8, d=128, K=16 blocks + current block; "
+                        "select GB/s counts pooled keys read and scores written",
+            "points": run_long_decode(torch)}
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, tr["host"], tr["cnt"], args.cpu_seconds)

@@ -219,6 +219,49 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sas_pool_keys - block means of a decode key cache, the input of sas_decode_select.
+ * kbar_m = (1/64) sum of the 64 keys of block m, summed in fp32 and rounded to bf16
+ * (nearest even). In serving, call it with first_block = the first block completed since
+ * the last call; a block is pooled once, when it is complete.
+ *
+ *   Kc          bf16 [B][Hkv][Lmax][d], device, 16-byte aligned.
+ *   Lmax        multiple of 64; C = Lmax / 64 blocks per (sequence, KV head).
+ *   d           64 or 128.
+ *   kv_len      int32 [B], device: tokens in each sequence's cache.
+ *   first_block blocks m in [first_block, C) with (m + 1) * 64 <= kv_len[b] are pooled.
+ *   kbar        bf16 [B][Hkv][C][d], device, 16-byte aligned, out; other blocks untouched.
+ */
+sas_status sas_pool_keys(const void* Kc, int B, int Hkv, int Lmax, int d, const int32_t* kv_len,
+                         int first_block, void* kbar, void* stream);
+
+/*
+ * sas_decode_select - block scores and Top-K blocks for one decode step (long contexts).
+ * The pages leave the selector network undefined; the block score stands in for it as the
+ * mean attention score over the block ([PBS-ja] "Sparser Block-Sparse Attention via Token
+ * Permutation", sections 3 and 4: block importance by mean pooling), averaged over the G
+ * query heads of the KV group:
+ *   s[b][h][m] = scale * qbar . kbar_m,  qbar = (1/G) sum_g q[b][hG+g],
+ * for the history blocks m < V_b = (kv_len[b] - 1) / 64 (clamped to [0, C]). Selection then
+ * follows [SAS-ja] "仕組み" Algorithm 2 exactly as sas_topk_select in DECODE / SPARSE mode:
+ * the k = min(topk, V_b) largest s (ties to the lower index, -0 equals +0, NaN as -inf),
+ * ascending, -1 pad; the comparison uses the fp32 scores written to s.
+ *
+ *   q       bf16 [B][Hq][d], device.   kbar  bf16 [B][Hkv][C][d] from sas_pool_keys.
+ *   C       blocks per row of kbar and s, 1..8192.   d  64 or 128.   Hq % Hkv == 0.
+ *   kv_len  int32 [B], device.   scale  finite, > 0 (1/sqrt(d) for the attention scale).
+ *   topk    >= 0.   kcap  row stride of idx / logg, in [min(topk, C), 8192].
+ *   s       fp32 [B][Hkv][C], device, out: entries m < V_b written, the rest untouched.
+ *   idx     int32 [B][Hkv][kcap], out.   cnt  int32 [B][Hkv], out: k.
+ *   lse     fp32 [B][Hkv], out, nullable: LSE of the row's V_b scores (-inf if none).
+ *   logg    fp32 [B][Hkv][kcap], out, nullable: s - LSE per kept block, 0 pad.
+ * Two kernels on the stream: block scores (rows x chunks of the pooled cache), then one
+ * workgroup per row for the Top-K. No workspace beyond s.
+ */
+sas_status sas_decode_select(const void* q, const void* kbar, int B, int Hq, int Hkv, int d, int C,
+                             const int32_t* kv_len, float scale, int topk, int kcap, float* s,
+                             int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream);
+
+/*
  * Kernel timing, for measurement (not part of the pages' method; off by default).
  *
  * sas_profile_enable(on): while on, every kernel the library launches is bracketed by two

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsas.so")
-SOURCES = ["sas_api.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "profile.hip"]
+SOURCES = ["sas_api.hip", "select.hip", "attn_fwd.hip", "attn_bwd.hip", "decode.hip", "decode_select.hip",
+           "profile.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops keeps the compiler from forming packed fp32 VALU instructions.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",

@@ -2,6 +2,7 @@
 // Every check runs before any HIP call, so a rejected call enqueues nothing and touches
 // no device state (the checks also run on machines without a GPU).
 #include <math.h>
+#include <algorithm>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -227,6 +228,44 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.kcap = kcap; a.scale = scale;
   a.o = (uint16_t*)o; a.part = (float*)ws;
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode launch");
+}
+
+sas_status sas_pool_keys(const void* Kc, int B, int Hkv, int Lmax, int d, const int32_t* kv_len,
+                         int first_block, void* kbar, void* stream) {
+  REQUIRE(Kc && kv_len && kbar, SAS_ERR_INVALID_ARG, "Kc, kv_len and kbar must be non-NULL");
+  REQUIRE(B > 0 && Hkv > 0 && Lmax > 0, SAS_ERR_INVALID_ARG, "B, Hkv, Lmax must be > 0");
+  REQUIRE(Lmax % 64 == 0, SAS_ERR_INVALID_ARG, "Lmax=%d is not a multiple of 64", Lmax);
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  const int C = Lmax / 64;
+  REQUIRE(first_block >= 0 && first_block <= C, SAS_ERR_INVALID_ARG, "first_block=%d out of [0, %d]", first_block, C);
+  REQUIRE((long long)B * Hkv * (C - first_block) < (1ll << 31), SAS_ERR_UNSUPPORTED, "too many blocks");
+  REQUIRE(aligned16(Kc) && aligned16(kbar), SAS_ERR_INVALID_ARG, "Kc and kbar must be 16-byte aligned");
+  sas::PoolArgs a{};
+  a.K = (const uint16_t*)Kc; a.B = B; a.Hkv = Hkv; a.Lmax = Lmax; a.C = C; a.d = d;
+  a.kv_len = kv_len; a.first_block = first_block; a.nblk = C - first_block; a.kbar = (uint16_t*)kbar;
+  return hip_result(sas::launch_pool(a, (hipStream_t)stream), "sas_pool_keys launch");
+}
+
+sas_status sas_decode_select(const void* q, const void* kbar, int B, int Hq, int Hkv, int d, int C,
+                             const int32_t* kv_len, float scale, int topk, int kcap, float* s,
+                             int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream) {
+  REQUIRE(q && kbar && kv_len && s && cnt, SAS_ERR_INVALID_ARG, "q, kbar, kv_len, s, cnt must be non-NULL");
+  REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
+  REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && C > 0, SAS_ERR_INVALID_ARG, "B, Hq, Hkv, C must be > 0");
+  REQUIRE(Hq % Hkv == 0, SAS_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  REQUIRE(C <= 8192, SAS_ERR_UNSUPPORTED, "C=%d exceeds 8192 blocks", C);
+  REQUIRE(topk >= 0, SAS_ERR_INVALID_ARG, "topk must be >= 0");
+  REQUIRE(kcap >= std::min(topk, C) && kcap <= 8192, SAS_ERR_INVALID_ARG,
+          "kcap=%d must be in [min(topk, C), 8192]", kcap);
+  REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  REQUIRE(aligned16(q) && aligned16(kbar), SAS_ERR_INVALID_ARG, "q and kbar must be 16-byte aligned");
+  REQUIRE((long long)B * Hkv * C * d * 2 < (1ll << 40), SAS_ERR_UNSUPPORTED, "pooled cache too large");
+  sas::DecSelArgs a{};
+  a.q = (const uint16_t*)q; a.kbar = (const uint16_t*)kbar; a.B = B; a.Hq = Hq; a.Hkv = Hkv;
+  a.G = Hq / Hkv; a.d = d; a.C = C; a.kv_len = kv_len; a.scale = scale; a.topk = topk; a.kcap = kcap;
+  a.s = s; a.idx = idx; a.cnt = cnt; a.lse = lse; a.logg = logg;
+  return hip_result(sas::launch_decode_select(a, (hipStream_t)stream), "sas_decode_select launch");
 }
 
 }  // extern "C"

@@ -56,6 +56,30 @@ struct GatesBwdArgs {
 };
 hipError_t launch_gates_bwd(const GatesBwdArgs& a, hipStream_t st);
 
+struct PoolArgs {
+  const uint16_t* K;    // [B][Hkv][Lmax][d] bf16
+  int B, Hkv, Lmax, C, d;
+  const int32_t* kv_len;
+  int first_block, nblk;   // blocks first_block .. first_block + nblk - 1
+  uint16_t* kbar;       // [B][Hkv][C][d] bf16
+};
+hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
+
+struct DecSelArgs {
+  const uint16_t* q;    // [B][Hq][d] bf16
+  const uint16_t* kbar; // [B][Hkv][C][d] bf16
+  int B, Hq, Hkv, G, d, C;
+  const int32_t* kv_len;
+  float scale;
+  int topk, kcap;
+  float* s;             // [B][Hkv][C]
+  int32_t* idx;         // [B][Hkv][kcap]
+  int32_t* cnt;         // [B][Hkv]
+  float* lse;           // [B][Hkv] or null
+  float* logg;          // [B][Hkv][kcap] or null
+};
+hipError_t launch_decode_select(const DecSelArgs& a, hipStream_t st);
+
 struct AttnArgs {
   const uint16_t* Q;
   const uint16_t* K;

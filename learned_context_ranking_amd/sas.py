@@ -34,6 +34,8 @@ SIGNATURES = {
     "sas_gates": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "sas_gates_bwd": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P], _I),
+    "sas_pool_keys": ([_P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "sas_decode_select": ([_P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P, _P, _P], _I),
     "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "sas_attn_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
     "sas_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -232,6 +234,44 @@ def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None)
                             B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
                             _stream(q.device)))
     return o
+
+
+def sas_pool_keys(Kc, kv_len, first_block=0, out=None):
+    """Kc bf16 [B, Hkv, Lmax, d]; kv_len int32 [B]. Returns kbar bf16 [B, Hkv, Lmax // 64, d]
+    (block means of the complete blocks >= first_block; other blocks of ``out`` untouched,
+    zero in a new tensor)."""
+    _need(Kc, torch.bfloat16, "Kc")
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hkv, Lmax, d = Kc.shape
+    if out is None:
+        out = torch.zeros((B, Hkv, Lmax // BLOCK, d), dtype=torch.bfloat16, device=Kc.device)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().sas_pool_keys(_ptr(Kc), B, Hkv, Lmax, d, _ptr(kv_len), int(first_block), _ptr(out),
+                               _stream(Kc.device)))
+    return out
+
+
+def sas_decode_select(q, kbar, kv_len, scale, topk, kcap=None, want_lse=False, want_logg=False, s_out=None):
+    """q bf16 [B, Hq, d]; kbar bf16 [B, Hkv, C, d] (sas_pool_keys); kv_len int32 [B].
+    Returns (s fp32 [B, Hkv, C], idx int32 [B, Hkv, kcap], cnt int32 [B, Hkv], lse or None,
+    logg or None). Entries of s past each row's history are left as they were (-inf in a
+    new tensor)."""
+    _need(q, torch.bfloat16, "q")
+    _need(kbar, torch.bfloat16, "kbar")
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hq, d = q.shape
+    Hkv, C = kbar.shape[1], kbar.shape[2]
+    kcap = min(int(topk), C) if kcap is None else int(kcap)
+    dev = q.device
+    s = torch.full((B, Hkv, C), float("-inf"), dtype=torch.float32, device=dev) if s_out is None else s_out
+    _need(s, torch.float32, "s_out")
+    idx = torch.empty((B, Hkv, kcap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    lse = torch.empty((B, Hkv), dtype=torch.float32, device=dev) if want_lse else None
+    logg = torch.empty((B, Hkv, kcap), dtype=torch.float32, device=dev) if want_logg else None
+    _check(lib().sas_decode_select(_ptr(q), _ptr(kbar), B, Hq, Hkv, d, C, _ptr(kv_len), float(scale), int(topk),
+                                   kcap, _ptr(s), _ptr(idx), _ptr(cnt), _ptr(lse), _ptr(logg), _stream(dev)))
+    return s, idx, cnt, lse, logg
 
 
 def profile_enable(on: bool = True):

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -114,6 +114,32 @@ def test_gates_bwd_rejects():
     bad = list(args); bad[12] = -1
     assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
     assert "kcap" in L.sas_last_error().decode()
+
+
+def test_pool_and_decode_select_reject():
+    L = sas.lib()
+    # Kc, B, Hkv, Lmax, d, kv_len, first_block, kbar, stream
+    pool = [FAKE, 1, 2, 640, 128, FAKE, 0, FAKE, NULL]
+    assert L.sas_pool_keys(*[NULL] + pool[1:]) == sas.SAS_ERR_INVALID_ARG
+    for i, v, code in ((3, 600, sas.SAS_ERR_INVALID_ARG), (4, 96, sas.SAS_ERR_UNSUPPORTED),
+                       (6, 11, sas.SAS_ERR_INVALID_ARG), (6, -1, sas.SAS_ERR_INVALID_ARG),
+                       (7, MIS, sas.SAS_ERR_INVALID_ARG), (1, 0, sas.SAS_ERR_INVALID_ARG)):
+        bad = list(pool); bad[i] = v
+        assert L.sas_pool_keys(*bad) == code, (i, v)
+    # q, kbar, B, Hq, Hkv, d, C, kv_len, scale, topk, kcap, s, idx, cnt, lse, logg, stream
+    sel = [FAKE, FAKE, 2, 8, 2, 128, 8192, FAKE, 0.088, 32, 32, FAKE, FAKE, FAKE, NULL, NULL, NULL]
+    for i, v, code in ((0, NULL, sas.SAS_ERR_INVALID_ARG), (11, NULL, sas.SAS_ERR_INVALID_ARG),
+                       (12, NULL, sas.SAS_ERR_INVALID_ARG), (13, NULL, sas.SAS_ERR_INVALID_ARG),
+                       (3, 7, sas.SAS_ERR_INVALID_ARG), (5, 80, sas.SAS_ERR_UNSUPPORTED),
+                       (6, 8193, sas.SAS_ERR_UNSUPPORTED), (6, 0, sas.SAS_ERR_INVALID_ARG),
+                       (9, -1, sas.SAS_ERR_INVALID_ARG), (10, 31, sas.SAS_ERR_INVALID_ARG),
+                       (8, 0.0, sas.SAS_ERR_INVALID_ARG), (8, float("inf"), sas.SAS_ERR_INVALID_ARG),
+                       (1, MIS, sas.SAS_ERR_INVALID_ARG)):
+        bad = list(sel); bad[i] = v
+        assert L.sas_decode_select(*bad) == code, (i, v)
+    bad = list(sel); bad[6] = 16; bad[10] = 16     # kcap >= min(topk, C) = 16 is enough
+    bad[12] = NULL
+    assert L.sas_decode_select(*bad) == sas.SAS_ERR_INVALID_ARG   # idx NULL with kcap > 0
 
 
 def test_bwd_workspace_and_rejects():
