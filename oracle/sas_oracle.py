@@ -82,6 +82,41 @@ def row_log_gates(s_row):
     return lse, s - lse
 
 
+GATES = ("softmax", "softmax_selected", "sigmoid", "exp")
+
+
+def row_log_gates_variant(s_row, sel, gate):
+    """Log-gates of the selected blocks ``sel`` of one row under a gate activation phi
+    ([SAS-ko] "무엇과 다른가", choices 2 and 3 and the alternatives they are compared with):
+
+    * "softmax": g = softmax(s) over every valid history block (choice 2; row_log_gates);
+    * "softmax_selected": g = softmax(s) over the selected set only, the normalisation a
+      binary Top-K mask trained with a straight-through estimator implies (choice 3);
+    * "sigmoid": g = sigmoid(s), log g = -log(1 + exp(-s));
+    * "exp": the raw score injected as the logit, log g = s (unnormalised).
+    Returns (normaliser, log g[sel]): LSE over the valid blocks, LSE over the selected
+    ones, or 0 for the unnormalised gates. NaN scores read as -inf (gate 0).
+    """
+    s = _rank_keys(s_row)
+    sel = np.asarray(sel, dtype=np.int64)
+    if gate == "softmax":
+        lse, lg = row_log_gates(s_row)
+        return lse, lg[sel]
+    x = s[sel]
+    if gate == "softmax_selected":
+        if x.size == 0 or x.max() == NEG_INF:
+            return NEG_INF, np.full_like(x, NEG_INF)
+        mx = x.max()
+        lse = mx + np.log(np.sum(np.exp(x - mx)))
+        return lse, x - lse
+    if gate == "sigmoid":
+        # log sigmoid(x) = -log(1 + e^-x), evaluated without overflow on either side
+        return 0.0, np.where(x >= 0, -np.log1p(np.exp(-np.abs(x))), x - np.log1p(np.exp(-np.abs(x))))
+    if gate == "exp":
+        return 0.0, x.copy()
+    raise ValueError(f"unknown gate {gate!r}")
+
+
 def row_topk(s_row, k):
     """The k highest-scoring history blocks of one row, ties to the lowest index (R5),
     reported in ascending block order (R6).
@@ -94,14 +129,14 @@ def row_topk(s_row, k):
     return np.sort(order[:k])
 
 
-def select(s, valid, topk, full_scope=False, kcap=None):
+def select(s, valid, topk, full_scope=False, kcap=None, gate="softmax"):
     """Gates plus Top-K selection for a stack of score rows.
 
     s: [R, ld] fp32 scores; row r has ``valid[r]`` history blocks (columns 0..valid-1).
     Sparse scope keeps min(topk, valid) blocks; full scope keeps all of them
-    ([SAS-ko] "무엇과 다른가", choice 4).
-    Returns idx [R, kcap] int32 (ascending, -1 pad), cnt [R] int32, lse [R] float64,
-    logg [R, kcap] float64 (log g of each selected block, 0 pad).
+    ([SAS-ko] "무엇과 다른가", choice 4). ``gate`` picks phi (row_log_gates_variant).
+    Returns idx [R, kcap] int32 (ascending, -1 pad), cnt [R] int32, lse [R] float64 (the
+    gate's normaliser), logg [R, kcap] float64 (log g of each selected block, 0 pad).
     """
     s = np.asarray(s)
     R = s.shape[0]
@@ -114,30 +149,29 @@ def select(s, valid, topk, full_scope=False, kcap=None):
     logg = np.zeros((R, kcap), dtype=np.float64)
     for r in range(R):
         row = s[r, : valid[r]]
-        lse[r], lg = row_log_gates(row)
         k = row.size if full_scope else min(int(topk), row.size)
         if k > kcap:
             raise ValueError("kcap smaller than the number of selected blocks")
         sel = row_topk(row, k)
         idx[r, :k] = sel
         cnt[r] = k
-        logg[r, :k] = lg[sel]
+        lse[r], logg[r, :k] = row_log_gates_variant(row, sel, gate)
     return idx, cnt, lse, logg
 
 
-def select_prefill(s, topk, full_scope=False, kcap=None):
+def select_prefill(s, topk, full_scope=False, kcap=None, gate="softmax"):
     """Selection for prefill/training score tensors s [B, H, NB, NB]: row j has j valid
     history blocks (R4). Returns tensors shaped [B, H, NB, kcap] / [B, H, NB]."""
     B, H, NB, ld = s.shape
     valid = np.tile(np.arange(NB), B * H)
-    idx, cnt, lse, logg = select(s.reshape(B * H * NB, ld), valid, topk, full_scope, kcap)
+    idx, cnt, lse, logg = select(s.reshape(B * H * NB, ld), valid, topk, full_scope, kcap, gate)
     kc = idx.shape[1]
     return (idx.reshape(B, H, NB, kc), cnt.reshape(B, H, NB), lse.reshape(B, H, NB),
             logg.reshape(B, H, NB, kc))
 
 
-def gates_bwd(s, valid, idx, cnt, dg):
-    """Gradient with respect to the scores through the gate softmax.
+def gates_bwd(s, valid, idx, cnt, dg, gate="softmax"):
+    """Gradient with respect to the scores through the gate activation.
 
     [SAS-ko] "무엇과 다른가", choice 2: g = softmax(s) over the row's valid history blocks
     (R2). dg holds dL/dg for the selected blocks, aligned with idx (R8); an unselected block
@@ -145,6 +179,9 @@ def gates_bwd(s, valid, idx, cnt, dg):
     chain rule through the softmax, whose Jacobian is diag(g) - g g^T, gives
     ds_m = g_m (dg_m - sum_m' g_m' dg_m') for every valid m. A NaN or -inf score has g = 0
     (R5), hence ds = 0. Entries m >= valid are 0.
+    The other activations of row_log_gates_variant: "softmax_selected" applies the same
+    Jacobian over the selected set only (ds = 0 elsewhere); "sigmoid" gives
+    ds_m = dg_m g_m (1 - g_m) and "exp" ds_m = dg_m g_m, on the selected blocks.
     s: [R, ld]; valid [R]; idx, dg [R, kcap]; cnt [R]. Returns ds [R, ld] float64.
     """
     s = np.asarray(s)
@@ -155,22 +192,36 @@ def gates_bwd(s, valid, idx, cnt, dg):
         v = int(valid[r])
         if v == 0:
             continue
-        _, lg = row_log_gates(s[r, :v])
-        g = np.exp(lg)
-        dgf = np.zeros(v)
         c = int(cnt[r])
-        dgf[np.asarray(idx[r, :c], dtype=np.int64)] = np.asarray(dg[r, :c], dtype=np.float64)
-        ds[r, :v] = g * dgf - g * np.dot(g, dgf)
+        sel = np.asarray(idx[r, :c], dtype=np.int64)
+        dgs = np.asarray(dg[r, :c], dtype=np.float64)
+        if gate == "softmax":
+            _, lg = row_log_gates(s[r, :v])
+            g = np.exp(lg)
+            dgf = np.zeros(v)
+            dgf[sel] = dgs
+            ds[r, :v] = g * dgf - g * np.dot(g, dgf)
+            continue
+        _, lg = row_log_gates_variant(s[r, :v], sel, gate)
+        g = np.exp(lg)
+        if gate == "softmax_selected":
+            ds[r, sel] = g * dgs - g * np.dot(g, dgs)
+        elif gate == "sigmoid":
+            ds[r, sel] = dgs * g * (1.0 - g)
+        elif gate == "exp":
+            ds[r, sel] = dgs * g
+        else:
+            raise ValueError(f"unknown gate {gate!r}")
     return ds
 
 
-def gates_bwd_prefill(s, idx, cnt, dg):
+def gates_bwd_prefill(s, idx, cnt, dg, gate="softmax"):
     """gates_bwd for prefill score tensors s [B, H, NB, NB] (row j has j valid blocks)."""
     B, H, NB, ld = s.shape
     valid = np.tile(np.arange(NB), B * H)
     kc = idx.shape[-1]
     R = B * H * NB
-    ds = gates_bwd(s.reshape(R, ld), valid, idx.reshape(R, kc), cnt.reshape(R), dg.reshape(R, kc))
+    ds = gates_bwd(s.reshape(R, ld), valid, idx.reshape(R, kc), cnt.reshape(R), dg.reshape(R, kc), gate)
     return ds.reshape(B, H, NB, ld)
 
 

@@ -199,25 +199,28 @@ def test_pd_finite_differences():
 
 # ------------------------------------------------------------------ P-i: gate softmax backward
 
-@pytest.mark.parametrize("full", [False, True])
-def test_pi_score_gradient_through_the_whole_step(full):
+@pytest.mark.parametrize("full,gate", [(False, "softmax"), (True, "softmax"), (False, "softmax_selected"),
+                                       (False, "sigmoid"), (False, "exp")])
+def test_pi_score_gradient_through_the_whole_step(full, gate):
     """Central differences of L = sum(dO * O) with respect to the scores s, where the gates
-    come from s (g = softmax(s), SAS explainer (ko) section 무엇과 다른가, choice 2) and O
-    from the gated forward, against gates_bwd(dg of the oracle backward). In sparse scope
-    a small perturbation keeps the Top-K set, so unselected blocks receive only the
-    normalisation term; a dropped term, a wrong sign or a softmax over the wrong set fails."""
+    come from s (g = softmax(s), SAS explainer (ko) section 무엇과 다른가, choice 2, and the
+    activations it is compared with) and O from the gated forward, against gates_bwd(dg of
+    the oracle backward). In sparse scope a small perturbation keeps the Top-K set, so
+    unselected blocks receive only the normalisation term (none for the gates that do not
+    normalise over the history); a dropped term, a wrong sign or a softmax over the wrong
+    set fails."""
     c = _rand_case(B=1, Hq=2, Hkv=1, n=64, d=8, block=8, topk=3, seed=21, full=full)
     s64 = c["s"].astype(np.float64)
+    idx0, cnt0, _, logg0 = oracle.select_prefill(s64, 3, full_scope=full, gate=gate)
 
     def loss(s):
-        idx, cnt, _, logg = oracle.select_prefill(s, 3, full_scope=full)
-        assert np.array_equal(idx, c["idx"])          # the selection did not move
+        idx, cnt, _, logg = oracle.select_prefill(s, 3, full_scope=full, gate=gate)
+        assert np.array_equal(idx, idx0)          # the selection did not move
         O, _ = oracle.attn_fwd(c["Q"], c["K"], c["V"], idx, cnt, logg, c["scale"], c["block"])
         return float(np.sum(c["dO"] * O))
 
-    _, _, _, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], c["logg"],
-                                  c["scale"], c["block"])
-    ds = oracle.gates_bwd_prefill(s64, c["idx"], c["cnt"], dg)
+    _, _, _, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], idx0, cnt0, logg0, c["scale"], c["block"])
+    ds = oracle.gates_bwd_prefill(s64, idx0, cnt0, dg, gate=gate)
     h = 1e-6
     NB = s64.shape[2]
     checked = 0
@@ -230,6 +233,11 @@ def test_pi_score_gradient_through_the_whole_step(full):
             checked += 1
     assert checked > 20
     assert np.all(ds[0, 0][np.triu_indices(NB)] == 0.0)    # m >= j: no valid entry
+    if gate != "softmax" and not full:
+        # only the selected blocks carry a gradient
+        for j in range(NB):
+            mask = np.ones(NB, bool); mask[idx0[0, 0, j, :cnt0[0, 0, j]]] = False
+            assert np.all(ds[0, 0, j, mask] == 0.0)
 
 
 def test_pi_gates_bwd_invariants_and_special_cases():
@@ -526,3 +534,55 @@ def test_pj_decode_select_planted_and_ties():
     # budget above the history keeps every history block
     s, idx, cnt, _, _ = oracle.decode_select(q, Kc, np.array([64 * 3 + 1]), 1.0, topk=8, kcap=8)
     assert cnt[0, 0] == 3 and list(idx[0, 0, :3]) == [0, 1, 2]
+
+
+# ------------------------------------------------------------------ P-k: gate activations
+
+def test_pk_gate_activation_closed_forms():
+    """sigmoid(0) = 1/2 and sigmoid saturates to 1 (log g -> 0) for large scores; the raw
+    logit gate is the score itself; the selected-set softmax sums to one over the kept
+    blocks and, like the history softmax, is invariant to a global shift of s, which the
+    unnormalised gates are not (SAS explainer (ko), 무엇과 다른가, choices 2 and 3)."""
+    s = np.array([0.0, 40.0, -3.0, 1.5, np.nan, -np.inf, 2.0])
+    sel = np.array([0, 1, 2, 3, 4, 5])
+    _, lg = oracle.row_log_gates_variant(s, sel, "sigmoid")
+    assert abs(lg[0] + math.log(2.0)) < 1e-15 and abs(lg[1]) < 1e-15
+    assert abs(lg[2] - math.log(1.0 / (1.0 + math.exp(3.0)))) < 1e-14
+    assert lg[4] == -np.inf and lg[5] == -np.inf
+    _, lg = oracle.row_log_gates_variant(s, sel, "exp")
+    assert np.array_equal(lg[:4], s[:4]) and lg[4] == -np.inf and lg[5] == -np.inf
+    sel = np.array([1, 3, 6])
+    lse, lg = oracle.row_log_gates_variant(s, sel, "softmax_selected")
+    assert abs(np.exp(lg).sum() - 1.0) < 1e-14
+    lse2, lg2 = oracle.row_log_gates_variant(s + 7.25, sel, "softmax_selected")
+    np.testing.assert_allclose(lg2, lg, rtol=0, atol=1e-12)
+    assert abs(lse2 - lse - 7.25) < 1e-12
+    _, a = oracle.row_log_gates_variant(s, sel, "sigmoid")
+    _, b = oracle.row_log_gates_variant(s + 1.0, sel, "sigmoid")
+    assert np.all(b > a)
+
+
+def test_pk_gates_bwd_variant_invariants():
+    """The selected-set softmax's ds sums to zero over the kept blocks; sigmoid's ds is
+    dg g (1 - g) and the raw gate's dg g on the kept blocks; every variant is zero off the
+    selection and past the history."""
+    g = np.random.default_rng(40)
+    R, ld = 5, 12
+    s = g.standard_normal((R, ld)).astype(np.float32)
+    valid = np.array([12, 7, 1, 0, 9])
+    for gate in ("softmax_selected", "sigmoid", "exp"):
+        idx, cnt, lse, logg = oracle.select(s, valid, 4, gate=gate)
+        dg = g.standard_normal(idx.shape)
+        ds = oracle.gates_bwd(s, valid, idx, cnt, dg, gate=gate)
+        for r in range(R):
+            sel = idx[r, :cnt[r]]
+            off = np.ones(ld, bool); off[sel] = False
+            assert np.all(ds[r, off] == 0.0)
+            gg = np.exp(logg[r, :cnt[r]])
+            if gate == "softmax_selected":
+                assert abs(ds[r, sel].sum()) <= 1e-12
+            elif gate == "sigmoid":
+                np.testing.assert_allclose(ds[r, sel], dg[r, :cnt[r]] * gg * (1 - gg), rtol=1e-12)
+            else:
+                np.testing.assert_allclose(ds[r, sel], dg[r, :cnt[r]] * np.exp(s[r, sel].astype(np.float64)),
+                                           rtol=1e-12)
