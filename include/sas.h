@@ -61,6 +61,16 @@ typedef enum {
                                   row_valid[b] valid history scores                       */
 } sas_rows;
 
+/* Gate activation phi, [SAS-ko] "무엇과 다른가": choice 2 (the method) and the alternatives
+ * the explainer compares it with. */
+typedef enum {
+  SAS_GATE_SOFTMAX = 0,           /* g = softmax(s) over the row's valid history (choice 2) */
+  SAS_GATE_SOFTMAX_SELECTED = 1,  /* softmax over the kept blocks only: the normalisation a
+                                     straight-through binary Top-K mask implies (choice 3) */
+  SAS_GATE_SIGMOID = 2,           /* g = sigmoid(s) */
+  SAS_GATE_EXP = 3                /* the raw score injected as the logit: log g = s */
+} sas_gate;
+
 /* Library version string, e.g. "sas-mi355x 0.1.0 gfx950". */
 const char* sas_version(void);
 
@@ -101,17 +111,23 @@ sas_status sas_gates(const float* s, int B, int H, int rows, int cols, int ld, i
  * Same s/B/H/rows/cols/ld/mode/row_valid arguments as sas_gates, and:
  *   topk   budget K >= 0 in blocks (ignored for SAS_SCOPE_FULL).
  *   scope  sas_scope. A row keeps k = min(topk, valid) blocks (SPARSE) or valid (FULL).
+ *   gate   sas_gate: the activation whose log g is written to logg (selection itself
+ *          always ranks the raw scores).
  *   kcap   row stride of idx/logg; must be >= min(topk, V) (SPARSE) or >= V (FULL), where
  *          V = min(cols, rows - 1) in PREFILL mode and V = cols in DECODE mode.
  *   idx    int32 [B][H][rows][kcap], out: the kept block indices in ascending order,
  *          padded with -1. Ties in s go to the lower block index; -0 equals +0; NaN ranks
  *          as -inf. The comparison uses the fp32 scores, so the result is exact.
  *   cnt    int32 [B][H][rows], out: k.
- *   lse    fp32 [B][H][rows], out, nullable: LSE of the row's valid scores.
- *   logg   fp32 [B][H][rows][kcap], out, nullable: s_m - LSE for each kept block, 0 pad.
+ *   lse    fp32 [B][H][rows], out, nullable: the gate's normaliser: LSE of the row's
+ *          valid scores (SOFTMAX), LSE of the kept scores (SOFTMAX_SELECTED; -inf if none),
+ *          0 (SIGMOID, EXP).
+ *   logg   fp32 [B][H][rows][kcap], out, nullable: log g for each kept block, 0 pad:
+ *          s_m - lse (both softmax gates), log sigmoid(s_m), or s_m (EXP); -inf for a NaN
+ *          or -inf score.
  */
 sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int ld, int mode,
-                           const int32_t* row_valid, int topk, int scope, int kcap,
+                           const int32_t* row_valid, int topk, int scope, int gate, int kcap,
                            int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream);
 
 /*
@@ -123,9 +139,13 @@ sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int
  * for an unselected one (choice 4, sparse scope: only selected blocks reach the attention).
  *
  * Same s/B/H/rows/cols/ld/mode/row_valid arguments as sas_gates, and:
- *   lse    fp32 [B][H][rows], in: the LSE sas_gates / sas_topk_select wrote for s. g_m is
- *          recomputed as exp(s_m - lse); a NaN or -inf score, or a row whose lse is -inf,
- *          has g = 0 and therefore ds = 0.
+ *   gate   sas_gate used for the forward. SOFTMAX: the formula above. SOFTMAX_SELECTED: the
+ *          same Jacobian over the kept blocks only (ds = 0 elsewhere). SIGMOID:
+ *          ds_m = dg_m g_m (1 - g_m); EXP: ds_m = dg_m g_m; on kept blocks, 0 elsewhere.
+ *   lse    fp32 [B][H][rows], in: the normaliser sas_topk_select wrote for s with the same
+ *          gate (NULL allowed for SIGMOID and EXP). For the softmax gates g_m is recomputed
+ *          as exp(s_m - lse); a NaN or -inf score, or a row whose lse is -inf, has g = 0
+ *          and therefore ds = 0.
  *   idx    int32 [B][H][rows][kcap], in: the selected blocks; entries t < cnt that lie in
  *          [0, valid) must be distinct within a row (sas_topk_select writes them so);
  *          others are ignored.
@@ -135,11 +155,11 @@ sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int
  *   kcap   0..8192; idx and dg may be NULL when kcap = 0.
  *   ds     fp32 [B][H][rows][ld], out: every entry is written (0 for m >= valid). Must
  *          not alias s.
- * Errors: as sas_gates, plus SAS_ERR_INVALID_ARG for a NULL lse/cnt/ds, kcap out of range,
- * or ds == s. Deterministic (no atomics to global memory).
+ * Errors: as sas_gates, plus SAS_ERR_INVALID_ARG for a bad gate, a NULL cnt/ds (or lse
+ * with a softmax gate), kcap out of range, or ds == s. Deterministic (no atomics to global memory).
  */
 sas_status sas_gates_bwd(const float* s, int B, int H, int rows, int cols, int ld, int mode,
-                         const int32_t* row_valid, const float* lse, const int32_t* idx,
+                         const int32_t* row_valid, int gate, const float* lse, const int32_t* idx,
                          const int32_t* cnt, const float* dg, int kcap, float* ds, void* stream);
 
 /*

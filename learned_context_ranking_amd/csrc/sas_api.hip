@@ -111,28 +111,31 @@ sas_status sas_gates(const float* s, int B, int H, int rows, int cols, int ld, i
 }
 
 sas_status sas_gates_bwd(const float* s, int B, int H, int rows, int cols, int ld, int mode,
-                         const int32_t* row_valid, const float* lse, const int32_t* idx,
+                         const int32_t* row_valid, int gate, const float* lse, const int32_t* idx,
                          const int32_t* cnt, const float* dg, int kcap, float* ds, void* stream) {
   sas_status st = check_rows(s, B, H, rows, cols, ld, mode, row_valid);
   if (st != SAS_OK) return st;
-  REQUIRE(lse != nullptr && cnt != nullptr && ds != nullptr, SAS_ERR_INVALID_ARG,
-          "lse, cnt and ds must be non-NULL");
+  REQUIRE(gate >= SAS_GATE_SOFTMAX && gate <= SAS_GATE_EXP, SAS_ERR_INVALID_ARG, "bad gate %d", gate);
+  REQUIRE(cnt != nullptr && ds != nullptr, SAS_ERR_INVALID_ARG, "cnt and ds must be non-NULL");
+  REQUIRE(lse != nullptr || gate == SAS_GATE_SIGMOID || gate == SAS_GATE_EXP, SAS_ERR_INVALID_ARG,
+          "lse must be non-NULL for the softmax gates");
   REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);
   REQUIRE(kcap == 0 || (idx != nullptr && dg != nullptr), SAS_ERR_INVALID_ARG, "idx and dg must be non-NULL");
   REQUIRE((const void*)ds != (const void*)s, SAS_ERR_INVALID_ARG, "ds must not alias s");
   sas::GatesBwdArgs a{};
   a.s = s; a.R = (long long)B * H * rows; a.H = H; a.rows = rows; a.cols = cols; a.ld = ld;
   a.mode = mode; a.row_valid = row_valid; a.lse = lse; a.idx = idx; a.cnt = cnt; a.dg = dg;
-  a.kcap = kcap; a.ds = ds;
+  a.kcap = kcap; a.gate = gate; a.ds = ds;
   return hip_result(sas::launch_gates_bwd(a, (hipStream_t)stream), "sas_gates_bwd launch");
 }
 
 sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int ld, int mode,
-                           const int32_t* row_valid, int topk, int scope, int kcap,
+                           const int32_t* row_valid, int topk, int scope, int gate, int kcap,
                            int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream) {
   sas_status st = check_rows(s, B, H, rows, cols, ld, mode, row_valid);
   if (st != SAS_OK) return st;
   REQUIRE(scope == SAS_SCOPE_SPARSE || scope == SAS_SCOPE_FULL, SAS_ERR_INVALID_ARG, "bad scope %d", scope);
+  REQUIRE(gate >= SAS_GATE_SOFTMAX && gate <= SAS_GATE_EXP, SAS_ERR_INVALID_ARG, "bad gate %d", gate);
   REQUIRE(topk >= 0, SAS_ERR_INVALID_ARG, "topk=%d < 0", topk);
   REQUIRE(cnt != nullptr, SAS_ERR_INVALID_ARG, "cnt is NULL");
   // most history blocks any row can have: rows - 1 in PREFILL (row j has j), cols in DECODE
@@ -143,7 +146,7 @@ sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int
   sas::SelectArgs a{};
   a.s = s; a.R = (long long)B * H * rows; a.H = H; a.rows = rows; a.cols = cols; a.ld = ld;
   a.mode = mode; a.row_valid = row_valid; a.topk = topk; a.full = scope == SAS_SCOPE_FULL;
-  a.kcap = kcap; a.do_select = 1; a.idx = idx; a.cnt = cnt; a.lse = lse; a.logg = logg;
+  a.kcap = kcap; a.do_select = 1; a.gate = gate; a.idx = idx; a.cnt = cnt; a.lse = lse; a.logg = logg;
   return hip_result(sas::launch_select(a, (hipStream_t)stream), "sas_topk_select launch");
 }
 

@@ -22,6 +22,9 @@ class ProfScope {
   void* a_;
 };
 
+// gate activations (sas_gate in include/sas.h)
+constexpr int kGateSoftmax = 0, kGateSoftmaxSelected = 1, kGateSigmoid = 2, kGateExp = 3;
+
 struct SelectArgs {
   const float* s;
   long long R;          // rows in total = B * H * rows
@@ -29,7 +32,7 @@ struct SelectArgs {
   long long ld;
   int mode;             // 0 prefill, 1 decode
   const int32_t* row_valid;
-  int topk, full, kcap, do_select;
+  int topk, full, kcap, do_select, gate;
   int32_t* idx;
   int32_t* cnt;
   float* lse;
@@ -52,6 +55,7 @@ struct GatesBwdArgs {
   const int32_t* cnt;
   const float* dg;
   int kcap;
+  int gate;
   float* ds;
 };
 hipError_t launch_gates_bwd(const GatesBwdArgs& a, hipStream_t st);

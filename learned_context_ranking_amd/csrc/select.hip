@@ -21,6 +21,17 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// log g of a kept block with score x (NaN already read as -inf) under each activation;
+// norm is the softmax normaliser (LSE over the history or over the kept set)
+__device__ __forceinline__ float log_gate(int gate, float x, float norm) {
+  if (gate == kGateSigmoid) {
+    // log sigmoid(x) = min(x, 0) - log(1 + e^-|x|)
+    return x == -INFINITY ? -INFINITY : fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
+  }
+  if (gate == kGateExp) return x;
+  return norm == -INFINITY ? -INFINITY : x - norm;
+}
+
 template <int PL>
 __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   const int lane = threadIdx.x & 63;
@@ -62,7 +73,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     sum = wave_sum(sum);
     lse = mx + logf(sum);
   }
-  if (a.lse != nullptr && lane == 0) a.lse[row] = lse;
+  if (a.lse != nullptr && lane == 0 && (!a.do_select || a.gate == kGateSoftmax)) a.lse[row] = lse;
   if (a.g != nullptr) {
     float* grow = a.g + row * a.ld;
 #pragma unroll
@@ -95,22 +106,41 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     for (int i = 0; i < PL; ++i) n_gt += __popcll(__ballot(key[i] > T));
     const int need_eq = k - n_gt;
     const unsigned long long lt = (1ull << lane) - 1ull;
-    int base = 0, eq_before = 0;
+    // calls f(i, pos) for every kept register i of this lane, pos = its output slot
+    auto walk = [&](auto&& f) {
+      int base = 0, eq_before = 0;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) {
-      const bool eq = key[i] == T;
-      const unsigned long long beq = __ballot(eq);
-      const int eq_rank = eq_before + __popcll(beq & lt);
-      const bool sel = key[i] > T || (eq && eq_rank < need_eq);
-      const unsigned long long bsel = __ballot(sel);
-      if (sel) {
-        const int pos = base + __popcll(bsel & lt);
-        idx_row[pos] = lane + 64 * i;
-        if (lg_row != nullptr) lg_row[pos] = (lse == -INFINITY) ? -INFINITY : x[i] - lse;
+      for (int i = 0; i < PL; ++i) {
+        const bool eq = key[i] == T;
+        const unsigned long long beq = __ballot(eq);
+        const int eq_rank = eq_before + __popcll(beq & lt);
+        const bool sel = key[i] > T || (eq && eq_rank < need_eq);
+        const unsigned long long bsel = __ballot(sel);
+        if (sel) f(i, base + __popcll(bsel & lt));
+        base += __popcll(bsel);
+        eq_before += __popcll(beq);
       }
-      base += __popcll(bsel);
-      eq_before += __popcll(beq);
+    };
+    float norm = lse;   // the gate's normaliser (reported as lse)
+    if (a.gate == kGateSoftmaxSelected) {
+      float m = -INFINITY, sum = 0.0f;   // online LSE over the kept scores
+      walk([&](int i, int) {
+        if (x[i] > m) { sum = sum * expf(m - x[i]) + 1.0f; m = x[i]; }
+        else if (x[i] != -INFINITY) sum += expf(x[i] - m);
+      });
+      const float wm = wave_max(m);
+      sum = wave_sum(m == -INFINITY ? 0.0f : sum * expf(m - wm));
+      norm = wm == -INFINITY ? -INFINITY : wm + logf(sum);
+    } else if (a.gate != kGateSoftmax) {
+      norm = 0.0f;
     }
+    if (a.lse != nullptr && lane == 0 && a.gate != kGateSoftmax) a.lse[row] = norm;
+    walk([&](int i, int pos) {
+      idx_row[pos] = lane + 64 * i;
+      if (lg_row != nullptr) lg_row[pos] = log_gate(a.gate, x[i], norm);
+    });
+  } else if (a.lse != nullptr && lane == 0 && a.gate != kGateSoftmax) {
+    a.lse[row] = a.gate == kGateSoftmaxSelected ? -INFINITY : 0.0f;
   }
   for (int p = k + lane; p < a.kcap; p += 64) {
     idx_row[p] = -1;
@@ -158,16 +188,20 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
   }
   const float* srow = a.s + row * a.ld;
   float* drow = a.ds + row * a.ld;
-  const float lse = live ? a.lse[row] : -INFINITY;
+  const float lse = (live && a.lse != nullptr) ? a.lse[row] : -INFINITY;
   const int cnt = live ? min(max(a.cnt[row], 0), a.kcap) : 0;
   const int32_t* irow = a.idx + row * a.kcap;
   const float* grow = a.dg + row * a.kcap;
   // gate of block m (0 for a NaN or -inf score, or a row without finite LSE)
   auto gate = [&](int m) {
     const float v = srow[m];
-    if (!(v > -INFINITY) || !(lse > -INFINITY)) return 0.0f;
+    if (!(v > -INFINITY)) return 0.0f;   // -inf or NaN score: gate 0
+    if (a.gate == kGateSigmoid) return 1.0f / (1.0f + expf(-v));
+    if (a.gate == kGateExp) return expf(v);
+    if (!(lse > -INFINITY)) return 0.0f;
     return expf(v - lse);
   };
+  const bool softmax_like = a.gate == kGateSoftmax || a.gate == kGateSoftmaxSelected;
   for (int i = lane; i < kMaxCols / 32; i += 64) sel_bits[w][i] = 0u;
   __syncthreads();
   float c = 0.0f;
@@ -175,7 +209,7 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
     const int m = irow[t];
     if (m >= 0 && m < valid) {
       atomicOr(&sel_bits[w][m >> 5], 1u << (m & 31));
-      c += gate(m) * grow[t];
+      if (softmax_like) c += gate(m) * grow[t];
     }
   }
   c = wave_sum(c);
@@ -185,12 +219,16 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
     if (m >= valid) {
       drow[m] = 0.0f;
     } else if (!((sel_bits[w][m >> 5] >> (m & 31)) & 1u)) {
-      drow[m] = -gate(m) * c;
+      // only the history softmax couples unselected blocks to the kept ones
+      drow[m] = a.gate == kGateSoftmax ? -gate(m) * c : 0.0f;
     }
   }
   for (int t = lane; t < cnt; t += 64) {
     const int m = irow[t];
-    if (m >= 0 && m < valid) drow[m] = gate(m) * (grow[t] - c);
+    if (m >= 0 && m < valid) {
+      const float g = gate(m);
+      drow[m] = softmax_like ? g * (grow[t] - c) : (a.gate == kGateSigmoid ? grow[t] * g * (1.0f - g) : grow[t] * g);
+    }
   }
 }
 

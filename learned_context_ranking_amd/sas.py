@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
 SCOPE = {"sparse": 0, "full": 1}
+GATE = {"softmax": 0, "softmax_selected": 1, "sigmoid": 2, "exp": 3}
 ROWS = {"prefill": 0, "decode": 1}
 BLOCK = 64
 
@@ -32,8 +33,8 @@ SIGNATURES = {
     "sas_status_string": ([_I], ctypes.c_char_p),
     "sas_last_error": ([], ctypes.c_char_p),
     "sas_gates": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
-    "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _P, _P, _P, _P, _P], _I),
-    "sas_gates_bwd": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P, _P], _I),
+    "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P], _I),
+    "sas_gates_bwd": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _P, _P], _I),
     "sas_pool_keys": ([_P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
     "sas_decode_select": ([_P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P, _P, _P], _I),
     "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
@@ -115,9 +116,10 @@ def sas_gates(s, mode="prefill", row_valid=None, cols=None, want_g=False):
     return lse, g
 
 
-def sas_topk_select(s, topk, scope="sparse", mode="prefill", row_valid=None, kcap=None, cols=None):
+def sas_topk_select(s, topk, scope="sparse", mode="prefill", row_valid=None, kcap=None, cols=None,
+                    gate="softmax"):
     """s: fp32 [B, H, rows, ld]. Returns idx int32 [B, H, rows, kcap], cnt int32 [B, H, rows],
-    lse fp32 [B, H, rows], logg fp32 [B, H, rows, kcap]."""
+    lse fp32 [B, H, rows] (the gate's normaliser), logg fp32 [B, H, rows, kcap]."""
     _need(s, torch.float32, "s")
     B, H, rows, ld = s.shape
     cols = ld if cols is None else cols
@@ -131,17 +133,19 @@ def sas_topk_select(s, topk, scope="sparse", mode="prefill", row_valid=None, kca
     if row_valid is not None:
         _need(row_valid, torch.int32, "row_valid")
     _check(lib().sas_topk_select(_ptr(s), B, H, rows, cols, ld, ROWS[mode], _ptr(row_valid), int(topk),
-                                 SCOPE[scope], kcap, _ptr(idx), _ptr(cnt), _ptr(lse), _ptr(logg),
+                                 SCOPE[scope], GATE[gate], kcap, _ptr(idx), _ptr(cnt), _ptr(lse), _ptr(logg),
                                  _stream(dev)))
     return idx, cnt, lse, logg
 
 
-def sas_gates_bwd(s, lse, idx, cnt, dg, mode="prefill", row_valid=None, cols=None, out=None):
-    """Gradient with respect to s through the gate softmax.
-    s fp32 [B, H, rows, ld]; lse [B, H, rows] from sas_gates / sas_topk_select; idx int32 and
-    dg fp32 [B, H, rows, kcap]; cnt int32 [B, H, rows]. Returns ds fp32 [B, H, rows, ld]."""
+def sas_gates_bwd(s, lse, idx, cnt, dg, mode="prefill", row_valid=None, cols=None, out=None, gate="softmax"):
+    """Gradient with respect to s through the gate activation.
+    s fp32 [B, H, rows, ld]; lse [B, H, rows] from sas_topk_select with the same gate (may
+    be None for sigmoid / exp); idx int32 and dg fp32 [B, H, rows, kcap]; cnt int32
+    [B, H, rows]. Returns ds fp32 [B, H, rows, ld]."""
     _need(s, torch.float32, "s")
-    _need(lse, torch.float32, "lse")
+    if lse is not None:
+        _need(lse, torch.float32, "lse")
     _need(idx, torch.int32, "idx")
     _need(cnt, torch.int32, "cnt")
     _need(dg, torch.float32, "dg")
@@ -149,14 +153,14 @@ def sas_gates_bwd(s, lse, idx, cnt, dg, mode="prefill", row_valid=None, cols=Non
     kcap = idx.shape[-1]
     if tuple(idx.shape) != (B, H, rows, kcap) or tuple(dg.shape) != (B, H, rows, kcap):
         raise ValueError(f"idx {tuple(idx.shape)} / dg {tuple(dg.shape)} do not match s {tuple(s.shape)}")
-    if tuple(lse.shape) != (B, H, rows) or tuple(cnt.shape) != (B, H, rows):
+    if (lse is not None and tuple(lse.shape) != (B, H, rows)) or tuple(cnt.shape) != (B, H, rows):
         raise ValueError(f"lse {tuple(lse.shape)} / cnt {tuple(cnt.shape)} do not match s {tuple(s.shape)}")
     cols = ld if cols is None else cols
     if row_valid is not None:
         _need(row_valid, torch.int32, "row_valid")
     ds = torch.empty_like(s) if out is None else out
     _need(ds, torch.float32, "out")
-    _check(lib().sas_gates_bwd(_ptr(s), B, H, rows, cols, ld, ROWS[mode], _ptr(row_valid), _ptr(lse),
+    _check(lib().sas_gates_bwd(_ptr(s), B, H, rows, cols, ld, ROWS[mode], _ptr(row_valid), GATE[gate], _ptr(lse),
                                _ptr(idx), _ptr(cnt), _ptr(dg), kcap, _ptr(ds), _stream(s.device)))
     return ds
 

@@ -74,10 +74,14 @@ def test_fwd_rejects(kw, code):
 
 def test_select_rejects():
     L = sas.lib()
-    args = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, 4, 0, 4, FAKE, FAKE, FAKE, FAKE, NULL]
+    # s, B, H, rows, cols, ld, mode, row_valid, topk, scope, gate, kcap, idx, cnt, lse, logg, stream
+    args = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, 4, 0, 0, 4, FAKE, FAKE, FAKE, FAKE, NULL]
     bad = list(args); bad[0] = NULL
     assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
-    bad = list(args); bad[10] = 3          # kcap < topk
+    for gate in (-1, 4):
+        bad = list(args); bad[10] = gate
+        assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[11] = 3          # kcap < topk
     assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
     bad = list(args); bad[9] = 1           # full scope needs kcap >= rows - 1 = 15
     assert L.sas_topk_select(*bad) == sas.SAS_ERR_INVALID_ARG
@@ -97,21 +101,25 @@ def test_select_rejects():
 
 def test_gates_bwd_rejects():
     L = sas.lib()
-    # s, B, H, rows, cols, ld, mode, row_valid, lse, idx, cnt, dg, kcap, ds, stream
-    args = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, FAKE, FAKE, FAKE, FAKE, 4, ctypes.c_void_p(0x20000), NULL]
-    for i, code in ((0, sas.SAS_ERR_INVALID_ARG), (8, sas.SAS_ERR_INVALID_ARG), (10, sas.SAS_ERR_INVALID_ARG),
-                    (13, sas.SAS_ERR_INVALID_ARG), (9, sas.SAS_ERR_INVALID_ARG), (11, sas.SAS_ERR_INVALID_ARG)):
+    # s, B, H, rows, cols, ld, mode, row_valid, gate, lse, idx, cnt, dg, kcap, ds, stream
+    args = [FAKE, 1, 2, 16, 16, 16, sas.ROWS["prefill"], NULL, 0, FAKE, FAKE, FAKE, FAKE, 4,
+            ctypes.c_void_p(0x20000), NULL]
+    for i, code in ((0, sas.SAS_ERR_INVALID_ARG), (9, sas.SAS_ERR_INVALID_ARG), (11, sas.SAS_ERR_INVALID_ARG),
+                    (14, sas.SAS_ERR_INVALID_ARG), (10, sas.SAS_ERR_INVALID_ARG), (12, sas.SAS_ERR_INVALID_ARG)):
         bad = list(args); bad[i] = NULL
         assert L.sas_gates_bwd(*bad) == code, i
-    bad = list(args); bad[13] = FAKE        # ds aliases s
+    for gate in (-1, 4):
+        bad = list(args); bad[8] = gate
+        assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
+    bad = list(args); bad[14] = FAKE        # ds aliases s
     assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
-    bad = list(args); bad[12] = 8193
+    bad = list(args); bad[13] = 8193
     assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
     bad = list(args); bad[6] = sas.ROWS["decode"]   # decode needs row_valid
     assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
     bad = list(args); bad[4] = 9000; bad[5] = 9000
     assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_UNSUPPORTED
-    bad = list(args); bad[12] = -1
+    bad = list(args); bad[13] = -1
     assert L.sas_gates_bwd(*bad) == sas.SAS_ERR_INVALID_ARG
     assert "kcap" in L.sas_last_error().decode()
 

@@ -136,3 +136,44 @@ def test_gates_bwd_full_size_train_scores():
     log("gates_bwd full size: 8 x 512 x 512, K=32")
     s = synth.scores_normal((1, 8, 512, 512), seed=0)
     _prefill_case(s, 32, seed=11)
+
+
+@pytest.mark.parametrize("gate", ["softmax_selected", "sigmoid", "exp"])
+def test_gates_bwd_gate_variants(gate):
+    """ds under each gate activation against the oracle (prefill rows with NaN-poisoned
+    invalid entries, -inf scores, a budget above the history)."""
+    log(f"gates_bwd gate={gate}")
+    NB = 200
+    s = synth.scores_normal((1, 3, NB, NB), seed=23)
+    s[0, 2, :, ::13] = -np.inf
+    for topk in (9, 250):
+        kcap = min(topk, NB)
+        sd = dev(_poison_prefill(s))
+        idx, cnt, lse, _ = sas.sas_topk_select(sd, topk, kcap=kcap, cols=NB, gate=gate)
+        dg = synth.normal_f32((1, 3, NB, kcap), topk, synth.TID_DG)
+        out = torch.full_like(sd, float("nan"))
+        ds = sas.sas_gates_bwd(sd, lse if gate == "softmax_selected" else None, idx, cnt, dev(dg), cols=NB, out=out,
+                               gate=gate)
+        torch.cuda.synchronize()
+        idx_r, cnt_r, _, _ = oracle.select_prefill(s, topk, kcap=kcap, gate=gate)
+        assert np.array_equal(host(idx), idx_r)
+        ds_r = oracle.gates_bwd_prefill(s, idx_r, cnt_r, dg, gate=gate)
+        _close(f"ds gate={gate} K={topk}", host(ds), ds_r)
+
+
+def test_gates_bwd_variant_score_gradient_chain():
+    """The sigmoid-gated step end to end on device: select -> fwd -> bwd -> gates_bwd."""
+    B, Hq, Hkv, n, d, topk = 1, 8, 2, 1024, 128, 8
+    P = Prefill(B, Hq, Hkv, n, d, seed=4, scores="normal")
+    t = P.device()
+    idx, cnt, _, logg = sas.sas_topk_select(t["s"], topk, cols=P.NB, gate="sigmoid")
+    O, lse = sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx, cnt, logg, P.scale)
+    _, _, _, dg = sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx, cnt, logg, P.scale)
+    ds = sas.sas_gates_bwd(t["s"], None, idx, cnt, dg.reshape(idx.shape), cols=P.NB, gate="sigmoid")
+    torch.cuda.synchronize()
+    idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk, gate="sigmoid")
+    assert np.array_equal(host(idx), idx_r)
+    Q, K, V, dO = P.f32("q"), P.f32("k"), P.f32("v"), P.f32("do")
+    _, _, _, dg_r = oracle.attn_bwd(Q, K, V, dO, idx_r, cnt_r, logg_r, P.scale)
+    ds_r = oracle.gates_bwd_prefill(P.s, idx_r, cnt_r, dg_r, gate="sigmoid")
+    assert_close("ds (sigmoid chain)", host(ds), ds_r)

@@ -127,3 +127,41 @@ def test_select_full_size_long_prefill():
     assert np.array_equal(host(idx), idx_r)
     assert np.array_equal(host(cnt), cnt_r)
     np.testing.assert_allclose(host(logg), logg_r, rtol=0, atol=3e-5)
+
+
+@pytest.mark.parametrize("gate", ["softmax_selected", "sigmoid", "exp"])
+def test_select_gate_variants(gate):
+    """Indices are independent of the gate; log g and the reported normaliser follow the
+    activation (the explainer's choice 2 alternatives and choice 3), including NaN / -inf
+    scores among the kept blocks and a row with no history; prefill and decode rows."""
+    log(f"select gate={gate}")
+    g = np.random.default_rng(17)
+    NB = 150
+    s = (2.0 * g.standard_normal((2, 2, NB, NB))).astype(np.float32)
+    s[0, 1, :, ::9] = -np.inf
+    s[1, 0, :, 3::10] = np.nan
+    for topk, full in ((12, False), (200, False), (0, True)):
+        scope = "full" if full else "sparse"
+        kcap = NB - 1 if full else min(topk, NB - 1)
+        idx_r, cnt_r, lse_r, logg_r = oracle.select_prefill(s, topk, full_scope=full, kcap=kcap, gate=gate)
+        idx, cnt, lse, logg = sas.sas_topk_select(dev(_poison_prefill(s)), topk, scope=scope, kcap=kcap, cols=NB,
+                                                  gate=gate)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx), idx_r) and np.array_equal(host(cnt), cnt_r)
+        lg = host(logg)
+        assert np.array_equal(np.isneginf(lg), np.isneginf(logg_r))
+        fin = np.isfinite(logg_r)
+        np.testing.assert_allclose(lg[fin], logg_r[fin], rtol=1e-6, atol=3e-5)
+        le = host(lse)
+        assert np.array_equal(np.isneginf(le), np.isneginf(lse_r))
+        fin = np.isfinite(lse_r)
+        np.testing.assert_allclose(le[fin], lse_r[fin], rtol=1e-6, atol=3e-5)
+    # decode rows
+    cols = 700
+    sd = g.standard_normal((3, 2, 1, cols)).astype(np.float32)
+    valid = np.array([cols, 0, 321], np.int32)
+    idx_r, cnt_r, lse_r, logg_r = oracle.select(sd.reshape(6, cols), np.repeat(valid, 2), 16, kcap=16, gate=gate)
+    idx, cnt, lse, logg = sas.sas_topk_select(dev(sd), 16, mode="decode", row_valid=dev(valid), kcap=16, gate=gate)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx).reshape(6, 16), idx_r)
+    np.testing.assert_allclose(host(logg).reshape(6, 16), logg_r, rtol=1e-6, atol=3e-5)
