@@ -481,3 +481,28 @@ def decode_select(q, Kc, kv_len, scale, topk, kcap=None, block=64):
     idx, cnt, lse, logg = select(s.reshape(B * Hkv, C), valid, topk, kcap=kcap)
     kc = idx.shape[-1]
     return s, idx.reshape(B, Hkv, kc), cnt.reshape(B, Hkv), lse.reshape(B, Hkv), logg.reshape(B, Hkv, kc)
+
+
+# ---------------------------------------------------------------- paged decode
+
+def gather_pages(pool, page_table, kv_len, block=64):
+    """The logical cache of each sequence from a paged pool: pool [P, Hkv, b, d] holds
+    one block of b tokens per page; page_table[b, m] is the page of logical block m.
+    Returns [B, Hkv, Lmax, d] with Lmax = page_table.shape[1] * b; blocks at or past
+    ceil(kv_len / b) are zero."""
+    pool = np.asarray(pool, np.float64)
+    B, maxp = page_table.shape
+    Hkv, d = pool.shape[1], pool.shape[3]
+    out = np.zeros((B, Hkv, maxp * block, d))
+    for b in range(B):
+        for m in range(-(-int(kv_len[b]) // block)):
+            out[b, :, m * block:(m + 1) * block] = pool[int(page_table[b, m])]
+    return out
+
+
+def decode_paged(q, Kpool, Vpool, page_table, kv_len, idx, cnt, scale, block=64, logg=None):
+    """Decode (Algorithm 2 of [SAS-ja] "仕組み") over a paged cache: the same attention as
+    ``decode`` on the logical cache the page table describes."""
+    Kc = gather_pages(Kpool, page_table, kv_len, block)
+    Vc = gather_pages(Vpool, page_table, kv_len, block)
+    return decode(q, Kc, Vc, kv_len, idx, cnt, scale, block, logg)

@@ -586,3 +586,41 @@ def test_pk_gates_bwd_variant_invariants():
             else:
                 np.testing.assert_allclose(ds[r, sel], dg[r, :cnt[r]] * np.exp(s[r, sel].astype(np.float64)),
                                            rtol=1e-12)
+
+
+# ------------------------------------------------------------------ P-l: paged decode
+
+def test_pl_paged_decode_equals_contiguous():
+    """Scattering each sequence's blocks to random pages of a pool and reading them back
+    through the page table gives the contiguous cache, so the paged decode equals the
+    contiguous one; pages of other sequences and unused pages do not leak in."""
+    g = np.random.default_rng(50)
+    B, Hq, Hkv, d, blk = 3, 4, 2, 8, 16
+    kv_len = np.array([16 * 5 + 3, 16 * 2, 1])
+    maxp = 6
+    Kc = g.standard_normal((B, Hkv, maxp * blk, d))
+    Vc = g.standard_normal((B, Hkv, maxp * blk, d))
+    npages = 30
+    perm = g.permutation(npages)
+    page_table = np.zeros((B, maxp), np.int32)
+    Kp = 100.0 * g.standard_normal((npages, Hkv, blk, d))   # unused pages hold junk
+    Vp = 100.0 * g.standard_normal((npages, Hkv, blk, d))
+    used = 0
+    for b in range(B):
+        for m in range(-(-kv_len[b] // blk)):
+            p = perm[used]; used += 1
+            page_table[b, m] = p
+            Kp[p] = Kc[b, :, m * blk:(m + 1) * blk]
+            Vp[p] = Vc[b, :, m * blk:(m + 1) * blk]
+    G = oracle.gather_pages(Kp, page_table, kv_len, blk)
+    for b in range(B):
+        n = -(-kv_len[b] // blk) * blk
+        assert np.array_equal(G[b, :, :n], Kc[b, :, :n]) and np.all(G[b, :, n:] == 0)
+    s = g.standard_normal((B * Hkv, maxp)).astype(np.float32)
+    valid = np.repeat((kv_len - 1) // blk, Hkv)
+    idx, cnt, _, _ = oracle.select(s, valid, 2, kcap=2)
+    idx = idx.reshape(B, Hkv, 2); cnt = cnt.reshape(B, Hkv)
+    q = g.standard_normal((B, Hq, d))
+    ref = oracle.decode(q, Kc, Vc, kv_len, idx, cnt, 0.3, block=blk)
+    got = oracle.decode_paged(q, Kp, Vp, page_table, kv_len, idx, cnt, 0.3, block=blk)
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
