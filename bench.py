@@ -192,11 +192,37 @@ def run_decode(steps, torch):
     torch.cuda.synchronize()
     ms = float(np.median([x.elapsed_time(y) for x, y in times]))
     ms_sel = float(np.median([x.elapsed_time(y) for x, y in sel_times]))
+    # the same step over a paged cache: the sequences' blocks scattered over a pool of
+    # 64-token pages in random order, read through a page table
+    C = L // 64
+    perm = torch.randperm(B * C, generator=torch.Generator().manual_seed(7))
+    Kp = Kc.reshape(B, Hkv, C, 64, d).permute(0, 2, 1, 3, 4).reshape(B * C, Hkv, 64, d)[perm.to(dev)].contiguous()
+    Vp = Vc.reshape(B, Hkv, C, 64, d).permute(0, 2, 1, 3, 4).reshape(B * C, Hkv, 64, d)[perm.to(dev)].contiguous()
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(B * C)
+    page_table = inv.reshape(B, C).to(torch.int32).to(dev)
+    op = torch.empty_like(q)
+    for _ in range(3):
+        sas.sas_decode_paged(q, Kp, Vp, page_table, kv_len, idx, cnt, scale, ws=ws, out=op)
+    torch.cuda.synchronize()
+    assert torch.equal(op, o), "paged decode differs from the contiguous decode"
+    ptimes = []
+    for _ in range(steps):
+        flush.sum()
+        a, c = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record(stream)
+        sas.sas_decode_paged(q, Kp, Vp, page_table, kv_len, idx, cnt, scale, ws=ws, out=op)
+        c.record(stream)
+        ptimes.append((a, c))
+    torch.cuda.synchronize()
+    ms_paged = float(np.median([x.elapsed_time(y) for x, y in ptimes]))
+    del Kp, Vp
     cnt_h = cnt.cpu().numpy()
     # algorithmic bytes: the selected K/V blocks plus the current block, q and o
     blocks = int(cnt_h.sum()) + B * Hkv
     nbytes = blocks * 64 * d * 2 * 2 + 2 * B * Hq * d * 2
-    return dict(ms=ms, ms_select=ms_sel, bytes=nbytes, gbs=nbytes / ms / 1e6,
+    return dict(ms=ms, ms_select=ms_sel, bytes=nbytes, gbs=nbytes / ms / 1e6, ms_paged=ms_paged,
+                gbs_paged=nbytes / ms_paged / 1e6,
                 workload=f"decode: B={B} sequences, Hq={Hq}, Hkv={Hkv}, d={d}, kv_len={L}, block=64, "
                          f"K={K} blocks + current block, ungated (Algorithm 2)")
 
@@ -366,6 +392,8 @@ def main():
         dec = run_decode(max(args.steps, 20), torch)
         out["decode"] = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms": round(dec["ms"], 5),
                          "select_ms": round(dec["ms_select"], 5), "bytes": dec["bytes"],
+                         "paged": {"ms": round(dec["ms_paged"], 5), "value": round(dec["gbs_paged"], 1),
+                                   "unit": "GB/s", "layout": "pool of 64-token pages in random order + page table"},
                          "workload": dec["workload"],
                          "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(dec["gbs"], 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",

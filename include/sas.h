@@ -239,6 +239,26 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sas_decode_paged - sas_decode over a paged KV cache (serving layout).
+ * Same computation as sas_decode ([SAS-ja] "仕組み", Algorithm 2); the cache is a pool of
+ * pages of 64 tokens (one SAS block each) and a page table per sequence:
+ *   Kpool, Vpool  bf16 [num_pages][Hkv][64][d], device, 16-byte aligned.
+ *   page_table    int32 [B][max_pages], device: page of logical block m of sequence b,
+ *                 read for m <= (kv_len[b] - 1) / 64 (the current block and every block
+ *                 idx may name). A page id outside [0, num_pages) makes that block read
+ *                 as empty (weight 0).
+ *   kv_len        int32 [B], device, clamped to [1, 64 * max_pages].
+ * Rows of the current page at or past kv_len are never read (they read as zero), so a
+ * page allocator may leave them unwritten. Other arguments and the workspace as
+ * sas_decode (kcap, idx, cnt, logg, scale, o, ws).
+ */
+sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                            const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                            const int32_t* idx, const int32_t* cnt, const float* logg, int B, int Hq,
+                            int Hkv, int d, int block, int kcap, float scale, void* o, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/*
  * sas_pool_keys - block means of a decode key cache, the input of sas_decode_select.
  * kbar_m = (1/64) sum of the 64 keys of block m, summed in fp32 and rounded to bf16
  * (nearest even). In serving, call it with first_block = the first block completed since

@@ -23,7 +23,12 @@ constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalis
 
 // 32-key half blocks through a ring of 4 LDS buffer sets: half block u+3 is copied in
 // while u is computed, so about three half blocks (48 KB) are in flight per wave.
-template <int D>
+//
+// PAGED: the cache is a pool of 64-token pages and a page table per sequence. The list
+// then holds page ids, and every half block is copied through a buffer resource that
+// starts at its page and covers only its valid rows, so rows past kv_len (which a page
+// allocator leaves unwritten) read as zero rather than whatever the page holds.
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   constexpr int HE = 32 * D;   // elements of a 32-row half tile
   __shared__ __attribute__((aligned(16))) uint16_t sk0[HE];
@@ -79,19 +84,37 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       g = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
       if (v < 0 || v >= cur) { v = 0; g = -INFINITY; }
     }
+    if (PAGED) {   // logical block -> page; a page id out of range reads nothing
+      const int pg = a.page_table[(size_t)b * a.max_pages + v];
+      v = pg;
+      if (pg < 0 || pg >= a.num_pages) { v = -1; g = -INFINITY; }
+    }
   };
   LaneList lstf;   // the same list for the copies, which run ahead
   const int nhalf = 2 * (t1 - t0);
   int uf = 0;   // next half block to copy (stays at nhalf - 1 once reached)
+  // valid keys of half block u of this chunk: all 32, except in the current block
+  auto half_keys = [&](int u) {
+    return t0 + (u >> 1) == 0 ? min(max(L - cur * kBlock - 32 * (u & 1), 0), 32) : 32;
+  };
   auto fetch = [&](uint16_t* kb, uint16_t* vb) {
     const int uu = max(min(uf, nhalf - 1), 0);
     lstf.ensure(uu >> 1, lane, load_lst);
     const int m = lstf.at(uu >> 1);
-    const uint32_t so = ((uint32_t)m * kBlock + 32u * (uu & 1)) * (uint32_t)(D * 2);
+    if (PAGED) {
+      const size_t off = ((size_t)max(m, 0) * a.Hkv + h) * (size_t)(kBlock * D) + (size_t)(32 * (uu & 1)) * D;
+      const int bytes = m < 0 ? 0 : half_keys(uu) * D * 2;
 #pragma unroll
-    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, cbytes, kb + 512 * i, voff[i], so);
+      for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Kc + off, bytes, kb + 512 * i, voff[i], 0u);
 #pragma unroll
-    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, cbytes, vb + 512 * i, voff[i], so);
+      for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Vc + off, bytes, vb + 512 * i, voff[i], 0u);
+    } else {
+      const uint32_t so = ((uint32_t)m * kBlock + 32u * (uu & 1)) * (uint32_t)(D * 2);
+#pragma unroll
+      for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, cbytes, kb + 512 * i, voff[i], so);
+#pragma unroll
+      for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, cbytes, vb + 512 * i, voff[i], so);
+    }
     ++uf;
   };
   constexpr int PER = 2 * NWIN;   // copies per half block
@@ -133,11 +156,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
                                lds_tr16(&vc[(r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3))]));
       }
     // keys past the end of the cache (only in the current block) do not count
-    const int key0 = m * kBlock + 32 * (u & 1);
+    if (PAGED) {
+      const int lim = half_keys(u);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * hl + (i & 3);
-      if (key0 + key >= L) st[i] = -INFINITY;
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (key >= lim) st[i] = -INFINITY;
+      }
+    } else {
+      const int key0 = m * kBlock + 32 * (u & 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + 4 * hl + (i & 3);
+        if (key0 + key >= L) st[i] = -INFINITY;
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -268,10 +300,14 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   const unsigned grid = (unsigned)(pairs * a.nchunk);
   {
     ProfScope prof("decode", st);
-    if (a.d == 128)
-      hipLaunchKernelGGL(decode_split_kernel<128>, dim3(grid), dim3(64), 0, st, a);
-    else
-      hipLaunchKernelGGL(decode_split_kernel<64>, dim3(grid), dim3(64), 0, st, a);
+    const bool paged = a.page_table != nullptr;
+    if (a.d == 128) {
+      if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<128, false>), dim3(grid), dim3(64), 0, st, a);
+    } else {
+      if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<64, false>), dim3(grid), dim3(64), 0, st, a);
+    }
   }
   if (a.nchunk > 1) {
     ProfScope prof("decode_merge", st);

@@ -233,6 +233,37 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode launch");
 }
 
+sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                            const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                            const int32_t* idx, const int32_t* cnt, const float* logg, int B, int Hq,
+                            int Hkv, int d, int block, int kcap, float scale, void* o, void* ws,
+                            size_t ws_bytes, void* stream) {
+  REQUIRE(q && Kpool && Vpool && page_table && kv_len && cnt && o, SAS_ERR_INVALID_ARG,
+          "q, Kpool, Vpool, page_table, kv_len, cnt, o must be non-NULL");
+  REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
+  REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && num_pages > 0 && max_pages > 0, SAS_ERR_INVALID_ARG,
+          "B, Hq, Hkv, num_pages, max_pages must be > 0");
+  REQUIRE(Hq % Hkv == 0, SAS_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  REQUIRE(Hq / Hkv <= 32, SAS_ERR_UNSUPPORTED, "decode supports Hq/Hkv <= 32 (got %d)", Hq / Hkv);
+  REQUIRE(block == 64, SAS_ERR_UNSUPPORTED, "block (page size) must be 64 (got %d)", block);
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  REQUIRE((long long)max_pages * 64 < (1ll << 31), SAS_ERR_UNSUPPORTED, "max_pages too large");
+  REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);
+  REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  REQUIRE(aligned16(q) && aligned16(Kpool) && aligned16(Vpool) && aligned16(o), SAS_ERR_INVALID_ARG,
+          "q, Kpool, Vpool, o must be 16-byte aligned");
+  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  sas::DecodeArgs a{};
+  a.q = (const uint16_t*)q; a.Kc = (const uint16_t*)Kpool; a.Vc = (const uint16_t*)Vpool;
+  a.kv_len = kv_len; a.Lmax = (long long)max_pages * 64; a.idx = idx; a.cnt = cnt; a.logg = logg;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.o = (uint16_t*)o; a.part = (float*)ws;
+  a.page_table = page_table; a.max_pages = max_pages; a.num_pages = num_pages;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_paged launch");
+}
+
 sas_status sas_pool_keys(const void* Kc, int B, int Hkv, int Lmax, int d, const int32_t* kv_len,
                          int first_block, void* kbar, void* stream) {
   REQUIRE(Kc && kv_len && kbar, SAS_ERR_INVALID_ARG, "Kc, kv_len and kbar must be non-NULL");

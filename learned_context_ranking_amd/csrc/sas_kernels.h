@@ -127,6 +127,10 @@ struct DecodeArgs {
   float* part;           // workspace: partial (m, l, acc) per chunk
   int bpc;               // blocks per chunk
   int nchunk;            // chunks per (b, h_kv) = ceil((kcap + 1) / bpc)
+  // paged cache (page_table != null): Kc / Vc are pools [num_pages][Hkv][64][d], logical
+  // block m of sequence b lives in page page_table[b * max_pages + m]; Lmax = 64 max_pages
+  const int32_t* page_table;
+  int max_pages, num_pages;
 };
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap);
 hipError_t launch_decode(DecodeArgs a, hipStream_t st);

@@ -36,6 +36,7 @@ SIGNATURES = {
     "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "sas_gates_bwd": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _P, _P], _I),
     "sas_pool_keys": ([_P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "sas_decode_paged": ([_P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
     "sas_decode_select": ([_P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P, _P, _P], _I),
     "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "sas_attn_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
@@ -237,6 +238,29 @@ def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None)
     _check(lib().sas_decode(_ptr(q), _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, _ptr(idx), _ptr(cnt), _ptr(logg),
                             B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
                             _stream(q.device)))
+    return o
+
+
+def sas_decode_paged(q, Kpool, Vpool, page_table, kv_len, idx, cnt, scale, logg=None, ws=None, out=None):
+    """q bf16 [B, Hq, d]; Kpool, Vpool bf16 [num_pages, Hkv, 64, d]; page_table int32
+    [B, max_pages]; kv_len int32 [B]; idx int32 [B, Hkv, kcap]; cnt int32 [B, Hkv].
+    Returns o bf16 [B, Hq, d]."""
+    for t, nm in ((q, "q"), (Kpool, "Kpool"), (Vpool, "Vpool")):
+        _need(t, torch.bfloat16, nm)
+    _need(page_table, torch.int32, "page_table")
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hq, d = q.shape
+    num_pages, Hkv = Kpool.shape[0], Kpool.shape[1]
+    if Kpool.shape[2] != BLOCK or tuple(Vpool.shape) != tuple(Kpool.shape):
+        raise ValueError(f"pools must be [num_pages, Hkv, {BLOCK}, d] (got {tuple(Kpool.shape)}, {tuple(Vpool.shape)})")
+    max_pages = page_table.shape[1]
+    kcap = idx.shape[-1]
+    if ws is None:
+        ws = decode_workspace(B, Hq, Hkv, d, kcap, q.device)
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().sas_decode_paged(_ptr(q), _ptr(Kpool), _ptr(Vpool), num_pages, _ptr(page_table), max_pages,
+                                  _ptr(kv_len), _ptr(idx), _ptr(cnt), _ptr(logg), B, Hq, Hkv, d, BLOCK, kcap,
+                                  float(scale), _ptr(o), _ptr(ws), ws.numel(), _stream(q.device)))
     return o
 
 

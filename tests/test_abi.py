@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -184,6 +184,22 @@ def test_decode_rejects():
     assert L.sas_decode(*bad) == sas.SAS_ERR_INVALID_ARG
     bad = list(args); bad[12] = 128               # block
     assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED
+
+
+def test_decode_paged_rejects():
+    L = sas.lib()
+    need = L.sas_decode_workspace_size(2, 8, 2, 128, 4)
+    # q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, idx, cnt, logg, B, Hq, Hkv, d, block,
+    # kcap, scale, o, ws, ws_bytes, stream
+    args = [FAKE, FAKE, FAKE, 100, FAKE, 16, FAKE, FAKE, FAKE, NULL, 2, 8, 2, 128, 64, 4, 0.1, FAKE, FAKE, need, NULL]
+    for i, v, code in ((4, NULL, sas.SAS_ERR_INVALID_ARG), (3, 0, sas.SAS_ERR_INVALID_ARG),
+                       (5, 0, sas.SAS_ERR_INVALID_ARG), (14, 32, sas.SAS_ERR_UNSUPPORTED),
+                       (13, 96, sas.SAS_ERR_UNSUPPORTED), (11, 9, sas.SAS_ERR_INVALID_ARG),
+                       (1, MIS, sas.SAS_ERR_INVALID_ARG), (19, need - 1, sas.SAS_ERR_WORKSPACE),
+                       (16, -1.0, sas.SAS_ERR_INVALID_ARG), (7, NULL, sas.SAS_ERR_INVALID_ARG),
+                       (11, 66, sas.SAS_ERR_UNSUPPORTED), (5, 1 << 25, sas.SAS_ERR_UNSUPPORTED)):
+        bad = list(args); bad[i] = v      # Hq = 66 over Hkv = 2 is a group of 33 > 32
+        assert L.sas_decode_paged(*bad) == code, (i, v)
 
 
 def test_profile_toggle_without_gpu():

@@ -61,3 +61,67 @@ def test_decode_full_size():
     """64 sequences, 32 query / 8 KV heads, 32,768 cached tokens, 16 blocks + the current
     one; the oracle checks 4 sampled sequences, the selection is checked on all."""
     _decode_case(64, 32, 8, 128, 32768, [32768] * 64, 16, check=[0, 17, 40, 63])
+
+
+def _paged_case(B, Hq, Hkv, d, kv_len, topk, seed, npages_extra=37, gated=False):
+    """Scatter seeded contiguous caches to random pages of a pool whose other pages (and
+    the unused rows of every partial page) hold NaN, then compare with the oracle's paged
+    decode and with sas_decode on the contiguous cache."""
+    kv_len = np.asarray(kv_len, np.int32)
+    maxp = int(-(-kv_len.max() // 64))
+    Lmax = maxp * 64
+    log(f"paged decode B={B} Hq={Hq} Hkv={Hkv} d={d} kv_len={list(kv_len)} K={topk}")
+    q_bits = synth.normal_bf16((B, Hq, 1, d), seed, synth.TID_QDEC)[:, :, 0]
+    k_bits = synth.normal_bf16((B, Hkv, Lmax, d), seed, synth.TID_K)
+    v_bits = synth.normal_bf16((B, Hkv, Lmax, d), seed, synth.TID_V)
+    g = np.random.default_rng(seed)
+    need = [int(-(-L // 64)) for L in kv_len]
+    npages = sum(need) + npages_extra
+    perm = g.permutation(npages)
+    nan = synth.f32_to_bf16_bits(np.array([np.nan], np.float32))[0]
+    Kp = np.full((npages, Hkv, 64, d), nan, np.uint16)
+    Vp = np.full((npages, Hkv, 64, d), nan, np.uint16)
+    pt = np.full((B, maxp), -7, np.int32)        # entries past a sequence's blocks are junk
+    used = 0
+    for b in range(B):
+        for m in range(need[b]):
+            p = perm[used]; used += 1
+            pt[b, m] = p
+            rows = min(64, int(kv_len[b]) - 64 * m)
+            Kp[p, :, :rows] = k_bits[b, :, 64 * m:64 * m + rows]
+            Vp[p, :, :rows] = v_bits[b, :, 64 * m:64 * m + rows]
+    C = maxp
+    s = synth.scores_normal((B, Hkv, 1, C), seed)
+    row_valid = ((kv_len - 1) // 64).astype(np.int32)
+    kcap = min(topk, C)
+    idx, cnt, _, logg = sas.sas_topk_select(dev(s), topk, mode="decode", row_valid=dev(row_valid), kcap=kcap)
+    scale = 1.0 / math.sqrt(d)
+    o = sas.sas_decode_paged(dev_bf16(q_bits), dev_bf16(Kp), dev_bf16(Vp), dev(pt), dev(kv_len), idx, cnt, scale,
+                             logg=logg if gated else None)
+    o_c = sas.sas_decode(dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits), dev(kv_len), idx, cnt, scale,
+                         logg=logg if gated else None)
+    torch.cuda.synchronize()
+    idx_r, cnt_r, _, logg_r = oracle.select(s.reshape(B * Hkv, C), np.repeat(row_valid, Hkv), topk, kcap=kcap)
+    idx_r = idx_r.reshape(B, Hkv, kcap); cnt_r = cnt_r.reshape(B, Hkv); logg_r = logg_r.reshape(B, Hkv, kcap)
+    assert np.array_equal(host(idx)[:, :, 0], idx_r)
+    Kf = synth.bf16_bits_to_f32(Kp); Vf = synth.bf16_bits_to_f32(Vp)
+    Kf[np.isnan(Kf)] = 0.0; Vf[np.isnan(Vf)] = 0.0      # never read by a correct kernel
+    ref = oracle.decode_paged(synth.bf16_bits_to_f32(q_bits), Kf, Vf, pt, kv_len, idx_r, cnt_r, scale,
+                              logg=logg_r if gated else None)
+    assert_close("o paged", host(o), ref)
+    # same arithmetic as the contiguous kernel, block for block
+    assert torch.equal(o, o_c)
+
+
+def test_decode_paged_mixed_lengths():
+    _paged_case(5, 8, 2, 128, [4096, 1000, 65, 1, 64 * 20], 8, seed=1)
+
+
+def test_decode_paged_groups_and_gated():
+    _paged_case(3, 10, 2, 128, [1536, 900, 64], 5, seed=2, gated=True)
+    _paged_case(2, 5, 1, 64, [777, 130], 4, seed=3)
+
+
+def test_decode_paged_large_batch():
+    """64 sequences (one chunk per (sequence, KV head), the direct-output path)."""
+    _paged_case(64, 32, 8, 128, [4096 - 13 * b for b in range(64)], 16, seed=4, npages_extra=5)
