@@ -250,9 +250,14 @@ def _block_logits(q, Kb, keys, ell, j, block, scale):
     return zu + ell[None, :], zu
 
 
-def fwd_query_block(Q, K, V, b, h, j, idx_row, cnt_j, logg_row, scale, block=64):
+def fwd_query_block(Q, K, V, b, h, j, idx_row, cnt_j, logg_row, scale, block=64, placement="inside"):
     """One query block of the forward for every query head of KV head h: returns
-    O [G, block, d] and LSE [G, block] (eq. (9) of [SAS-ja] "仕組み")."""
+    O [G, block, d] and LSE [G, block] (eq. (9) of [SAS-ja] "仕組み").
+
+    placement "outside" is the alternative of [SAS-ko] "무엇과 다른가", choice 1: the gate
+    multiplies the attention probabilities after the softmax, o = sum_i p_i g_m(i) v_i with
+    p = softmax(scale q K_S^T) (no gate in the logits); LSE is then that of the ungated
+    logits."""
     Hq, Hkv = Q.shape[1], K.shape[1]
     G = Hq // Hkv
     keys, ell = _key_set(j, idx_row, cnt_j, logg_row, block)
@@ -263,16 +268,22 @@ def fwd_query_block(Q, K, V, b, h, j, idx_row, cnt_j, logg_row, scale, block=64)
     LSE = np.zeros((G, block))
     for g in range(G):
         q = np.asarray(Q[b, h * G + g, rows], np.float64)
-        z, _ = _block_logits(q, Kb, keys, ell, j, block, scale)
-        mx = z.max(axis=1, keepdims=True)
-        e = np.exp(z - mx)
-        Z = e.sum(axis=1, keepdims=True)
-        O[g] = (e / Z) @ Vb
+        z, zu = _block_logits(q, Kb, keys, ell, j, block, scale)
+        if placement == "outside":
+            mx = zu.max(axis=1, keepdims=True)
+            e = np.exp(zu - mx)
+            Z = e.sum(axis=1, keepdims=True)
+            O[g] = ((e / Z) * np.exp(ell)[None, :]) @ Vb
+        else:
+            mx = z.max(axis=1, keepdims=True)
+            e = np.exp(z - mx)
+            Z = e.sum(axis=1, keepdims=True)
+            O[g] = (e / Z) @ Vb
         LSE[g] = (mx + np.log(Z))[:, 0]
     return O, LSE
 
 
-def attn_fwd(Q, K, V, idx, cnt, logg, scale, block=64):
+def attn_fwd(Q, K, V, idx, cnt, logg, scale, block=64, placement="inside"):
     """Gated block-sparse attention forward, eq. (9) of [SAS-ja] "仕組み".
 
     Q [B, Hq, n, d]; K, V [B, Hkv, n, d]; idx/logg [B, Hkv, NB, kcap]; cnt [B, Hkv, NB].
@@ -288,14 +299,14 @@ def attn_fwd(Q, K, V, idx, cnt, logg, scale, block=64):
         for h in range(Hkv):
             for j in range(NB):
                 o, l = fwd_query_block(Q, K, V, b, h, j, idx[b, h, j], cnt[b, h, j], logg[b, h, j],
-                                       scale, block)
+                                       scale, block, placement)
                 rows = slice(j * block, (j + 1) * block)
                 O[b, h * G:(h + 1) * G, rows] = o
                 LSE[b, h * G:(h + 1) * G, rows] = l
     return O, LSE
 
 
-def bwd_query_block(Q, K, V, dO, b, h, j, idx_row, cnt_j, logg_row, scale, block=64):
+def bwd_query_block(Q, K, V, dO, b, h, j, idx_row, cnt_j, logg_row, scale, block=64, placement="inside"):
     """Backward contributions of one query block (all G query heads of KV head h).
 
     Content gradients are those of softmax attention over S_j; gradients reach only the
@@ -305,6 +316,10 @@ def bwd_query_block(Q, K, V, dO, b, h, j, idx_row, cnt_j, logg_row, scale, block
     (p~_ti / g_jm) * dO_t^T (v_i - o_t). By eq. (9) p~_ti / g_jm = exp(z_ti - LSE_t) with
     z_ti the logit before the gate is added, which is what is evaluated (it stays
     defined when g_jm = 0).
+    With placement "outside" (choice 1's alternative, see fwd_query_block) the weights are
+    w_ti = p_ti g_m(i): dV = w^T dO, the probabilities' gradient is g_m(i) dO_t^T v_i,
+    dS = p (g dP - delta) with the same delta = dO_t^T o_t, and the gate gradient is the
+    one the explainer gives for that placement, dg_jm = sum_{t, i in B_m} p_ti dO_t^T v_i.
     Returns dQ [G, block, d], the key token indices of S_j, dK and dV over those keys
     ([len(keys), d], summed over the G heads) and dg [cnt_j].
     """
@@ -322,6 +337,24 @@ def bwd_query_block(Q, K, V, dO, b, h, j, idx_row, cnt_j, logg_row, scale, block
     for g in range(G):
         q = np.asarray(Q[b, h * G + g, rows], np.float64)
         z, zu = _block_logits(q, Kb, keys, ell, j, block, scale)
+        if placement == "outside":
+            mx = zu.max(axis=1, keepdims=True)
+            e = np.exp(zu - mx)
+            P = e / e.sum(axis=1, keepdims=True)
+            gk = np.exp(ell)[None, :]                    # gate of each key's block
+            W = P * gk
+            o = W @ Vb
+            do = np.asarray(dO[b, h * G + g, rows], np.float64)
+            dP = do @ Vb.T
+            delta = np.sum(do * o, axis=1, keepdims=True)
+            dS = P * (gk * dP - delta)
+            dQ[g] = scale * (dS @ Kb)
+            dKs += scale * (dS.T @ q)
+            dVs += W.T @ do
+            for t in range(int(cnt_j)):
+                cols = slice(block * (t + 1), block * (t + 2))
+                dg[t] += np.sum(P[:, cols] * dP[:, cols])
+            continue
         mx = z.max(axis=1, keepdims=True)
         e = np.exp(z - mx)
         Z = e.sum(axis=1, keepdims=True)
@@ -342,7 +375,7 @@ def bwd_query_block(Q, K, V, dO, b, h, j, idx_row, cnt_j, logg_row, scale, block
     return dQ, keys, dKs, dVs, dg
 
 
-def attn_bwd(Q, K, V, dO, idx, cnt, logg, scale, block=64):
+def attn_bwd(Q, K, V, dO, idx, cnt, logg, scale, block=64, placement="inside"):
     """Backward of :func:`attn_fwd` with the gate gradient (see :func:`bwd_query_block`).
     Returns dQ, dK, dV (float64, shapes of Q, K, V) and dg [B, Hkv, NB, kcap] (0 pad)."""
     B, Hq, n, d = Q.shape
@@ -357,7 +390,7 @@ def attn_bwd(Q, K, V, dO, idx, cnt, logg, scale, block=64):
             for j in range(NB):
                 c = int(cnt[b, h, j])
                 dq, keys, dks, dvs, dgj = bwd_query_block(Q, K, V, dO, b, h, j, idx[b, h, j], c,
-                                                          logg[b, h, j], scale, block)
+                                                          logg[b, h, j], scale, block, placement)
                 dQ[b, h * G:(h + 1) * G, j * block:(j + 1) * block] = dq
                 np.add.at(dK[b, h], keys, dks)
                 np.add.at(dV[b, h], keys, dvs)

@@ -624,3 +624,84 @@ def test_pl_paged_decode_equals_contiguous():
     ref = oracle.decode(q, Kc, Vc, kv_len, idx, cnt, 0.3, block=blk)
     got = oracle.decode_paged(q, Kp, Vp, page_table, kv_len, idx, cnt, 0.3, block=blk)
     np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------------ P-m: gate outside the softmax
+
+def _autograd_gate_outside(c):
+    """The outside placement written as dense attention: an additive mask keeps S_j,
+    softmax over the ungated logits, then each probability is multiplied by the gate of
+    its key's block (built from leaf log-gates); torch autograd returns every gradient."""
+    B, Hq, n, d = c["Q"].shape
+    Hkv = c["K"].shape[1]
+    G = Hq // Hkv
+    blk = c["block"]
+    NB = n // blk
+    Qt = torch.tensor(c["Q"], requires_grad=True)
+    Kt = torch.tensor(c["K"], requires_grad=True)
+    Vt = torch.tensor(c["V"], requires_grad=True)
+    lg = torch.tensor(c["logg"], requires_grad=True)
+    masks, gates = [], []
+    for b in range(B):
+        mh, gh = [], []
+        for h in range(Hkv):
+            mrows, grows = [], []
+            for j in range(NB):
+                mcols = [torch.full((blk,), float("-inf"), dtype=torch.float64) for _ in range(NB)]
+                gcols = [torch.zeros(blk, dtype=torch.float64) for _ in range(NB)]
+                for t in range(int(c["cnt"][b, h, j])):
+                    m = int(c["idx"][b, h, j, t])
+                    mcols[m] = torch.zeros(blk, dtype=torch.float64)
+                    gcols[m] = torch.exp(lg[b, h, j, t]).expand(blk)
+                mcols[j] = torch.zeros(blk, dtype=torch.float64)
+                gcols[j] = torch.ones(blk, dtype=torch.float64)
+                mrows.append(torch.cat(mcols).unsqueeze(0).expand(blk, n))
+                grows.append(torch.cat(gcols).unsqueeze(0).expand(blk, n))
+            M = torch.cat(mrows, 0).masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+            mh.append(M)
+            gh.append(torch.cat(grows, 0))
+        masks.append(torch.stack(mh))
+        gates.append(torch.stack(gh))
+    M = torch.stack(masks).repeat_interleave(G, 1)
+    Gm = torch.stack(gates).repeat_interleave(G, 1)
+    z = c["scale"] * Qt @ Kt.repeat_interleave(G, 1).transpose(-1, -2) + M
+    Ot = (torch.softmax(z, -1) * Gm) @ Vt.repeat_interleave(G, 1)
+    (Ot * torch.tensor(c["dO"])).sum().backward()
+    return Ot.detach().numpy(), Qt.grad.numpy(), Kt.grad.numpy(), Vt.grad.numpy(), lg.grad.numpy()
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_pm_gate_outside_matches_autograd(full):
+    """Gate after the softmax (the alternative of the explainer's choice 1): the oracle's
+    forward, LSE of the ungated logits and hand-written backward agree with torch autograd
+    of the dense formulation; its dg is the explainer's sum_i p_i dO^T v_i."""
+    c = _rand_case(B=1, Hq=4, Hkv=2, n=128, d=16, block=16, topk=3, full=full, seed=7)
+    O, LSE = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], c["logg"], c["scale"], c["block"],
+                             placement="outside")
+    dQ, dK, dV, dg = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], c["logg"],
+                                     c["scale"], c["block"], placement="outside")
+    Oa, dQa, dKa, dVa, dlg = _autograd_gate_outside(c)
+    np.testing.assert_allclose(O, Oa, rtol=RTOL, atol=1e-12)
+    np.testing.assert_allclose(dQ, dQa, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dK, dKa, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(dV, dVa, rtol=1e-9, atol=1e-11)
+    valid = np.arange(c["idx"].shape[-1])[None, None, None, :] < c["cnt"][..., None]
+    np.testing.assert_allclose(dg, np.where(valid, dlg / np.exp(c["logg"]), 0.0), rtol=1e-9, atol=1e-11)
+    # LSE is that of the ungated logits: with every gate 1 both placements coincide
+    _, LSE_in = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], np.zeros_like(c["logg"]),
+                                c["scale"], c["block"])
+    np.testing.assert_allclose(LSE, LSE_in, rtol=1e-12, atol=1e-12)
+
+
+def test_pm_unit_gates_make_the_placements_equal():
+    """With g = 1 for every block both placements are plain sparse attention."""
+    c = _rand_case(B=1, Hq=2, Hkv=1, n=96, d=8, block=16, topk=2, seed=8)
+    z = np.zeros_like(c["logg"])
+    a = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], z, c["scale"], c["block"])
+    b = oracle.attn_fwd(c["Q"], c["K"], c["V"], c["idx"], c["cnt"], z, c["scale"], c["block"], placement="outside")
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-13, atol=1e-13)
+    ga = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], z, c["scale"], c["block"])
+    gb = oracle.attn_bwd(c["Q"], c["K"], c["V"], c["dO"], c["idx"], c["cnt"], z, c["scale"], c["block"],
+                         placement="outside")
+    for x, y in zip(ga[:3], gb[:3]):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-12)
