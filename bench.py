@@ -146,6 +146,21 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
     ms_step = (t1 - t0) * 1e3 / steps
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
     kern_ms = {k: tot / n for k, (n, tot) in prof.items()}
+    # the same forward + backward with the gate placed after the softmax (the design
+    # alternative the method is compared with), on the same selection
+    idx_, cnt_, _, logg_ = sas.sas_topk_select(t["s"], w.topk, kcap=w.topk, cols=NB)
+    outside = []
+    for r in range(steps + 2):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx_, cnt_, logg_, scale, out=O, lse_out=lse, placement="outside")
+        sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx_, cnt_, logg_, scale, ws=ws,
+                         outs=(dQ, dK, dV, dg), placement="outside")
+        b_.record(stream)
+        if r >= 2:
+            outside.append((a_, b_))
+    torch.cuda.synchronize()
+    ms["fwd_bwd_gate_outside"] = float(np.mean([a_.elapsed_time(b_) for a_, b_ in outside]))
     return dict(ms_step=ms_step, ms=ms, kern_ms=kern_ms, pairs=pairs, flop_fwd=flop_fwd,
                 flop_bwd=flop_bwd, host=host, cnt=cnt_h)
 
@@ -347,7 +362,8 @@ def main():
     flop_step = tr["flop_fwd"] + tr["flop_bwd"]
     value = flop_step / (tr["ms_step"] * 1e-3) / 1e12
     ms = tr["ms"]
-    kern = {"select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"], "gates_bwd": ms["gates_bwd"]}
+    kern = {"select": ms["sel"], "fwd": ms["fwd"], "bwd": ms["bwd"], "gates_bwd": ms["gates_bwd"],
+            "fwd_bwd_gate_outside": ms["fwd_bwd_gate_outside"]}
     kern.update({"kernel:" + k: v for k, v in tr["kern_ms"].items()})
     fwd_tf = tr["flop_fwd"] / (ms["fwd"] * 1e-3) / 1e12
     bwd_tf = tr["flop_bwd"] / (ms["bwd"] * 1e-3) / 1e12

@@ -61,6 +61,13 @@ typedef enum {
                                   row_valid[b] valid history scores                       */
 } sas_rows;
 
+/* Where the gate enters the attention, [SAS-ko] "무엇과 다른가", choice 1. */
+typedef enum {
+  SAS_GATE_INSIDE = 0,   /* the method: log g added to the logits inside the softmax */
+  SAS_GATE_OUTSIDE = 1   /* the alternative: o = sum_i p_i g_m(i) v_i with p the softmax of
+                            the ungated logits (the gate only rescales V) */
+} sas_gate_placement;
+
 /* Gate activation phi, [SAS-ko] "무엇과 다른가": choice 2 (the method) and the alternatives
  * the explainer compares it with. */
 typedef enum {
@@ -175,14 +182,17 @@ sas_status sas_gates_bwd(const float* s, int B, int H, int rows, int cols, int l
  *            logg may be NULL: every kept block then has gate 1 (ungated sparse attention).
  *   n        multiple of 64.  d in {64, 128}.  block must be 64.  kcap >= 0.
  *   scale    finite, > 0 (typically 1/sqrt(d)).
+ *   placement sas_gate_placement. OUTSIDE: the softmax runs over the ungated logits of S
+ *            (a block whose gate is 0 still counts in the normaliser) and each probability
+ *            is multiplied by its block's gate before the V product.
  *   O        bf16 [B][Hq][n][d], out.
- *   lse_rows fp32 [B][Hq][n], out: natural-log softmax normaliser of each query row (the
- *            backward needs it).
+ *   lse_rows fp32 [B][Hq][n], out: natural-log softmax normaliser of each query row (of the
+ *            ungated logits for OUTSIDE; the backward needs it).
  */
 sas_status sas_attn_fwd(const void* Q, const void* K, const void* V, const int32_t* idx,
                         const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
-                        int d, int block, int kcap, float scale, void* O, float* lse_rows,
-                        void* stream);
+                        int d, int block, int kcap, float scale, int placement, void* O,
+                        float* lse_rows, void* stream);
 
 /* Bytes of device workspace sas_attn_bwd needs for these sizes (0 on invalid sizes). */
 size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int block, int kcap);
@@ -193,8 +203,11 @@ size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int blo
  * gradient: [SAS-ko] choice 4, sparse scope). The gate gradient follows [SAS-ko] choice 1:
  * dg_jm = sum over the G*64 query rows t of KV head h's group in block j and keys i of
  * block m of (p~_ti / g_jm) dO_t.(v_i - o_t), i.e. the derivative with respect to g_jm.
+ * With placement OUTSIDE the gradients are those of o = sum_i p_i g_m(i) v_i: dV uses the
+ * weights p g, dS = p (g dP - delta), and dg_jm = sum_{t, i in B_m} p_ti dO_t.v_i (the
+ * gradient the explainer gives for that placement).
  *
- *   Q, K, V, idx, cnt, logg, sizes, scale: exactly as passed to sas_attn_fwd.
+ *   Q, K, V, idx, cnt, logg, sizes, scale, placement: exactly as passed to sas_attn_fwd.
  *   O, lse_rows  the forward's outputs. dO bf16 [B][Hq][n][d].
  *   idx rows must be ascending (as sas_topk_select writes them).
  *   dQ fp32 [B][Hq][n][d], dK, dV fp32 [B][Hkv][n][d], out (overwritten, not accumulated).
@@ -207,8 +220,8 @@ size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int blo
 sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                         const void* dO, const float* lse_rows, const int32_t* idx,
                         const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
-                        int d, int block, int kcap, float scale, float* dQ, float* dK,
-                        float* dV, float* dg, void* ws, size_t ws_bytes, void* stream);
+                        int d, int block, int kcap, float scale, int placement, float* dQ,
+                        float* dK, float* dV, float* dg, void* ws, size_t ws_bytes, void* stream);
 
 /* Bytes of device workspace sas_decode needs for these sizes (0 on invalid sizes). */
 size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap);

@@ -31,17 +31,8 @@
 #ifndef SAS_DQ_WPE
 #define SAS_DQ_WPE 2
 #endif
-#ifndef SAS_DKV_NBUF
-#define SAS_DKV_NBUF 3   // ring depth of the key-major pass
-#endif
-#ifndef SAS_DKV_PIPE
-#define SAS_DKV_PIPE 1   // software-pipelined key-major pass
-#endif
 #ifndef SAS_DKV_ORDER
 #define SAS_DKV_ORDER 2  // (batch, KV head) pairs per launch phase; 0: all pairs interleaved
-#endif
-#ifndef SAS_DKV_WPE
-#define SAS_DKV_WPE 1    // waves per SIMD the key-major pass is built for
 #endif
 
 namespace sas {
@@ -130,7 +121,7 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, in
 // time); block t+1 is copied in (buffer loads into LDS with a scalar per-block offset)
 // while block t is computed. The copy is issued on every step, past the end of the list it
 // repeats the last block, so the compiler's wait tracking stays exact.
-template <int D>
+template <int D, bool OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SAS_DQ_WPE, SAS_DQ_WPE)))
 void dq_kernel(const AttnArgs a, int nsplit) {
   constexpr int NW = 4;
@@ -300,9 +291,17 @@ void dq_kernel(const AttnArgs a, int nsplit) {
           float u = fast_exp2(st[i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
           const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
           if (t == 0 && key > wrow0 + ql) u = 0.0f;   // causal mask of block j itself
-          const float w = u * (dpt[i] - dlt);
-          dgacc += w;
-          ds[x] = w * g;
+          if (OUT) {
+            // gate after the softmax: u is the probability itself (LSE of the ungated
+            // logits); dS = u (g dP - delta), dg = sum u dP; a block outside S has u = 0
+            if (!ok) u = 0.0f;
+            dgacc += u * dpt[i];
+            ds[x] = u * (g * dpt[i] - dlt);
+          } else {
+            const float w = u * (dpt[i] - dlt);
+            dgacc += w;
+            ds[x] = w * g;
+          }
         }
         dsf[hh] = pack8(ds[0], ds[1], ds[2], ds[3], ds[4], ds[5], ds[6], ds[7]);
       }
@@ -361,307 +360,25 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 // 4 waves per (b, KV head, key block m): wave w owns keys 32 (w & 1) .. + 31 and query rows
 // 32 (w >> 1) .. + 31 of every (query block, head) item; K and V of its keys stay in
 // registers for the whole list. The two query halves are summed through LDS at the end.
-// Items stream through a ring of NBUF buffer sets (distinct LDS objects, selected at compile
-// time, so the compiler never waits for a copy in flight before computing): item it+NBUF-1
-// is copied in while item it is computed. The copies are buffer loads into LDS addressed
-// by a per-lane constant offset plus a scalar per-item offset, so they cost no vector
-// instructions. Operand reads are issued in two batches (row reads before S and dP, the
-// transposed reads before the softmax); in the swizzled Tile layout each read address is
-// one of two lane base offsets XORed with a constant plus an immediate. WPE is the number
-// of waves per SIMD the kernel is built for (1: 512 registers, 2: 256).
-template <int D, int NBUF, int WPE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void dkv_kernel(const AttnArgs a) {
-  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
-  constexpr int NW = 4;
-  constexpr int TE = Tile<D>::ELEMS;
-  // Each Q buffer carries the item's lse and delta rows behind the tile: every wave copies
-  // one 64-float row (waves 0 / 1: lse / delta, waves 2 / 3 a spare copy of lse) into its
-  // own slot, without a branch, so the copies target only 2 * NBUF distinct LDS objects,
-  // which the compiler tracks apart and waits for one at a time.
-  constexpr int TQ = TE + 4 * 128;
-  constexpr int E2 = NBUF >= 3 ? TQ : 8, F2 = NBUF >= 3 ? TE : 8;
-  constexpr int E3 = NBUF >= 4 ? TQ : 8, F3 = NBUF >= 4 ? TE : 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sq2[E2];
-  __shared__ __attribute__((aligned(16))) uint16_t sq3[E3];
-  __shared__ __attribute__((aligned(16))) uint16_t so0[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t so1[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t so2[F2];
-  __shared__ __attribute__((aligned(16))) uint16_t so3[F3];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5, ql = lane & 31;
-  const int kh = wave & 1, qh = wave >> 1;
-  const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
-  // Launch order: the (batch, KV head) pairs in phases of SAS_DKV_ORDER pairs (0: one phase
-  // with all pairs); within a phase key-block-major with the phase's pairs interleaved, so
-  // early key blocks (selected most often, the longest lists) start first and consecutive
-  // workgroups alternate between the phase's pairs, which keeps each pair on a fixed subset
-  // of XCDs (L2s). Fewer pairs per phase keep the working set of query rows smaller.
-  const int BHp = a.B * a.Hkv;
-  const int P = SAS_DKV_ORDER > 0 ? min(SAS_DKV_ORDER, BHp) : BHp;
-  const int phase = (int)(blockIdx.x / ((unsigned)P * NB));
-  const int np = min(P, BHp - phase * P);   // pairs in this phase (the last may have fewer)
-  const int rem = (int)(blockIdx.x - (unsigned)phase * P * NB);
-  const int m = rem / np;
-  const int rr = phase * P + rem % np;
-  const int h = rr % a.Hkv, b = rr / a.Hkv;
-  const long long bh = (long long)b * a.Hkv + h;
-
-  const size_t kv_off = ((size_t)bh * a.n + (size_t)m * kBlock) * D;
-  const int key = 32 * kh + ql;  // this lane's key column within block m
-  // K and V as B operands of S = Q K^T and dP = dO V^T: key column, d = 16 ks + 8 hl + e
-  bf16x8 kf[D / 16], vf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 16 * ks + 8 * hl));
-    vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 16 * ks + 8 * hl));
-  }
-  f32x16 dk[D / 32], dv[D / 32];
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
-  const float c2 = a.scale * kLog2e;
-  const int g16 = lane >> 4, lp = lane & 15;
-  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
-  // Lane base offsets (elements) in the Tile layout. Row read ks of row r = 32 qh + ql at
-  // d = 16 ks + 8 hl sits at rx ^ (ks << 4); the transposing read of rows r0 + tr_row
-  // (r0 = 32 qh + 16 hh + 8 half) at d = 32 dt + tr_d sits at r0 D + (tx ^ ((4 dt ^ 2 half) << 3)):
-  // the swizzle of row r0 + tr_row is swz(tr_row) ^ 2 half because r0 is a multiple of 8.
-  const int rrow = 32 * qh + ql;
-  const int rx0 = rrow * D + ((hl ^ Tile<D>::swz(rrow)) << 3);
-  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
-  const int off0 = a.inv_off[bh * (NB + 1) + m];
-  const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
-  const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
-  const int nitems = (nlist + 1) * G;
-
-  // Buffer resources over the G query heads of this (b, KV head): Q and dO rows, lse and
-  // delta rows. Sizes were checked on the host to fit 31 bits.
-  const size_t head0 = (size_t)(b * a.Hq + h * G) * a.n;
-  const int qbytes = G * a.n * D * 2, rbytes = G * a.n * 4;
-  const uint16_t* qbase = a.Q + head0 * D;
-  const uint16_t* obase = a.dO + head0 * D;
-  const float* rbase = (wave == 1 ? a.delta : a.lse_rows) + head0;
-  // per-lane byte offsets of this wave's 16-byte slots within a 64-row tile
-  constexpr int NWIN = Tile<D>::CPR / NW;
-  uint32_t voff[NWIN];
-#pragma unroll
-  for (int i = 0; i < NWIN; ++i) {
-    const int sidx = 64 * (wave + NW * i) + lane;
-    const int r = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
-    voff[i] = (uint32_t)(r * D + ((c ^ Tile<D>::swz(r)) << 3)) * 2u;
-  }
-
-  // Entries are visited in descending j with the diagonal block j = m last; each list is
-  // held one entry per lane (one window for the item being computed, one for the copies).
-  auto load_lst = [&](int e, int& v, float& g) {
-    v = m;
-    g = 0.0f;
-    if (e < nlist) {
-      const int p = list[nlist - 1 - e];
-      v = p / a.kcap;
-      const int slot = p - v * a.kcap;
-      g = a.logg != nullptr ? a.logg[((size_t)bh * NB + v) * a.kcap + slot] * kLog2e : 0.0f;
-    }
-  };
-  LaneList lst_c, lst_f;
-  // (ec, gc): entry and head of the item being computed; (ef, gf): the next item to copy,
-  // which stays at the last item once reached (copies past the end repeat it)
-  int ec = 0, gc = 0, ef = 0, gf = 0;
-  auto fetch = [&](uint16_t* qb, uint16_t* ob) {
-    int jj = m;
-    if (ef < nlist) {
-      lst_f.ensure(ef, lane, load_lst);
-      jj = lst_f.at(ef);
-    }
-    const uint32_t row = (uint32_t)(gf * a.n + jj * kBlock);
-    const uint32_t so = row * (uint32_t)(D * 2);
-#pragma unroll
-    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(qbase, qbytes, qb + 512 * (wave + NW * i), voff[i], so);
-#pragma unroll
-    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(obase, qbytes, ob + 512 * (wave + NW * i), voff[i], so);
-    buffer_load_lds4(rbase, rbytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
-    if (!(ef == nlist && gf == G - 1)) {
-      if (++gf == G) { gf = 0; ++ef; }
-    }
-  };
-  // per item each wave issues 2 * NWIN tile copies and one row copy
-  constexpr int PER = 2 * NWIN + 1;
-  static_assert(PER < 64, "copies in flight exceed the vmcnt range");
-
-  // softmax of the item in (qc, oc) from its S^T and dP^T, then dV^T += dO^T P, dK^T += Q^T dS
-  // (one code path for both cases: a branch here would make the compiler copy the
-  // accumulators at the merge)
-  auto finish = [&](bool diag, float lg2, const uint16_t* qc, const uint16_t* oc,
-                    const f32x16& s, const f32x16& dp, const bf16x8 (&da)[D / 32][2],
-                    const bf16x8 (&qa)[D / 32][2]) {
-    const float* lc = reinterpret_cast<const float*>(qc + TE);
-    const float* dc = reinterpret_cast<const float*>(qc + TE + 128);
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int q4 = 0; q4 < 2; ++q4) {
-        const int qb = 32 * qh + 16 * hh + 8 * q4 + 4 * hl;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lc[qb]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dc[qb]);
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i = 8 * hh + 4 * q4 + x;
-          float p = fast_exp2(s[i] * c2 + (lg2 - l4[x] * kLog2e));
-          if (diag && key > qb + x) p = 0.0f;   // causal mask of the diagonal block
-          pv[4 * q4 + x] = p;
-          dsv[4 * q4 + x] = p * (dp[i] - d4[x]);
-        }
-      }
-      const bf16x8 pb = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
-      const bf16x8 sb = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = mfma32(da[dt][hh], pb, dv[dt]);
-        dk[dt] = mfma32(qa[dt][hh], sb, dk[dt]);
-      }
-    }
-  };
-
-  // one item: copy the next item into (qn, on), compute the current one from (qc, oc). A
-  // copy is issued on every step (past the end of the list it repeats the last item into a
-  // buffer that is not read again), so every step has the same number of copies in flight
-  // and the compiler's wait tracking stays exact across iterations.
-  auto step = [&](const uint16_t* qc, const uint16_t* oc, uint16_t* qn, uint16_t* on) {
-    if (NBUF == 4) wait_vm_n<2 * PER>(); else if (NBUF == 3) wait_vm_n<PER>(); else wait_vm();
-    barrier_lds();
-    int jj = m;
-    float lg2 = 0.0f;
-    if (ec < nlist) {
-      lst_c.ensure(ec, lane, load_lst);
-      jj = lst_c.at(ec);
-      lg2 = lst_c.gat(ec);
-    }
-    const bool diag = ec == nlist;
-    if (++gc == G) { gc = 0; ++ec; }
-    fetch(qn, on);
-    // S^T = K Q^T and dP^T = V dO^T for this wave's 32 keys x 32 query rows
-    int rx = rx0, tx = tx0;
-    asm volatile("" : "+v"(rx), "+v"(tx));   // keeps per-(buffer, read) addresses unhoisted
-    bf16x8 qr[D / 16], orw[D / 16];
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qr[ks] = as_bf16x8(ld16(&qc[rx ^ (ks << 4)]));
-      orw[ks] = as_bf16x8(ld16(&oc[rx ^ (ks << 4)]));
-    }
-    // keep the reads together ahead of the products (the scheduler would otherwise pair each
-    // read with its product and expose the LDS latency every time)
-    __builtin_amdgcn_sched_barrier(0);
-    f32x16 s = {}, dp = {};
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      s = mfma32(qr[ks], kf[ks], s);
-      dp = mfma32(orw[ks], vf[ks], dp);
-    }
-    // transposed operands of dV and dK, read while the softmax runs
-    bf16x8 da[D / 32][2], qa[D / 32][2];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = 32 * qh + 16 * hh;
-        const int o0 = r0 * D + (tx ^ ((4 * dt) << 3)), o1 = (r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3));
-        da[dt][hh] = join_tr16(lds_tr16(&oc[o0]), lds_tr16(&oc[o1]));
-        qa[dt][hh] = join_tr16(lds_tr16(&qc[o0]), lds_tr16(&qc[o1]));
-      }
-    finish(diag, lg2, qc, oc, s, dp, da, qa);
-  };
-
-  // Whole rounds of NBUF steps run without conditions inside (so the compiler's wait
-  // tracking is exact at every read); the remaining steps follow the loop.
-  const int nfull = nitems - nitems % NBUF;
-  if (NBUF == 2) {
-    fetch(sq0, so0);
-    for (int it = 0; it < nfull; it += 2) {
-      step(sq0, so0, sq1, so1);
-      step(sq1, so1, sq0, so0);
-    }
-    if (nfull < nitems) step(sq0, so0, sq1, so1);
-  } else if (NBUF == 3) {
-    fetch(sq0, so0);
-    fetch(sq1, so1);
-    for (int it = 0; it < nfull; it += 3) {
-      step(sq0, so0, sq2, so2);
-      step(sq1, so1, sq0, so0);
-      step(sq2, so2, sq1, so1);
-    }
-    if (nfull < nitems) step(sq0, so0, sq2, so2);
-    if (nfull + 1 < nitems) step(sq1, so1, sq0, so0);
-  } else {
-    fetch(sq0, so0);
-    fetch(sq1, so1);
-    fetch(sq2, so2);
-    for (int it = 0; it < nfull; it += 4) {
-      step(sq0, so0, sq3, so3);
-      step(sq1, so1, sq0, so0);
-      step(sq2, so2, sq1, so1);
-      step(sq3, so3, sq2, so2);
-    }
-    if (nfull < nitems) step(sq0, so0, sq3, so3);
-    if (nfull + 1 < nitems) step(sq1, so1, sq0, so0);
-    if (nfull + 2 < nitems) step(sq2, so2, sq1, so1);
-  }
-
-  // Sum the two query halves: waves with qh = 1 hand their partials over through LDS (the
-  // Q and dO buffers are free by now; key half 0 uses sq0 / sq1, key half 1 so0 / so1).
-  constexpr int PERW = (D / 32) * 16 * 64;
-  static_assert(PERW * sizeof(float) <= sizeof(so0), "reduction buffer");
-  __syncthreads();
-  float* rk = reinterpret_cast<float*>(kh == 0 ? sq0 : so0);
-  float* rv = reinterpret_cast<float*>(kh == 0 ? sq1 : so1);
-  if (qh == 1) {
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        rk[(dt * 16 + i) * 64 + lane] = dk[dt][i];
-        rv[(dt * 16 + i) * 64 + lane] = dv[dt][i];
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
-    float* dKp = a.dK + kv_off + key * D;
-    float* dVp = a.dV + kv_off + key * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-        f32x4 kv, vv;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i = 4 * g4 + x;
-          kv[x] = (dk[dt][i] + rk[(dt * 16 + i) * 64 + lane]) * a.scale;
-          vv[x] = dv[dt][i] + rv[(dt * 16 + i) * 64 + lane];
-        }
-        *reinterpret_cast<f32x4*>(dKp + d0) = kv;
-        *reinterpret_cast<f32x4*>(dVp + d0) = vv;
-      }
-  }
-}
-
-// The key-major pass software-pipelined across items (same work split and results as
-// dkv_kernel). With one wave per SIMD the matrix and vector pipes only overlap when the
-// instruction stream interleaves them, so step it issues each S / dP product of item it+1
-// followed by one element of item it's softmax (scheduling barriers keep that order), then
-// item it's dV / dK products. A ring of 4 buffer sets holds item it (transposed reads),
-// item it+1 (row reads), item it+2 (copy in flight) and receives item it+3.
-template <int D>
+// The items (the query blocks that selected m, then m itself, for each of the G heads)
+// stream through a ring of 4 LDS buffer sets (distinct LDS objects selected at compile
+// time, so the compiler never waits for a copy in flight before computing): item it
+// (transposed reads), item it+1 (row reads), item it+2 (copy in flight), and the ring
+// receives item it+3. The copies are buffer loads into LDS addressed by a per-lane
+// constant offset plus a scalar per-item offset; in the swizzled Tile layout each operand
+// read is a laundered lane base XORed with a constant plus an immediate.
+// The pass is software-pipelined across items: with one wave per SIMD the matrix and
+// vector pipes only overlap when the instruction stream interleaves them, so step it
+// issues each S / dP product of item it+1 followed by one element of item it's softmax
+// (scheduling barriers keep that order), then item it's dV / dK products.
+template <int D, bool OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dkv_pipe_kernel(const AttnArgs a) {
   constexpr int NW = 4;
   constexpr int TE = Tile<D>::ELEMS;
-  constexpr int TQ = TE + 4 * 128;   // Q tile + lse / delta rows (see dkv_kernel)
+  // Q tile + lse / delta rows: every wave copies one 64-float row behind the tile
+  // (wave 1 delta, the others lse; rows 2 and 3 are spare copies)
+  constexpr int TQ = TE + 4 * 128;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sq2[TQ];
@@ -675,7 +392,9 @@ void dkv_pipe_kernel(const AttnArgs a) {
   const int hl = lane >> 5, ql = lane & 31;
   const int kh = wave & 1, qh = wave >> 1;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
-  // launch order as in dkv_kernel
+  // Launch order: the (batch, KV head) pairs in phases of SAS_DKV_ORDER pairs (0: one
+  // phase), key blocks ascending within a phase (the earliest blocks have the longest
+  // lists), the pairs of a phase interleaved so each pair's workgroups spread over the XCDs.
   const int BHp = a.B * a.Hkv;
   const int P = SAS_DKV_ORDER > 0 ? min(SAS_DKV_ORDER, BHp) : BHp;
   const int phase = (int)(blockIdx.x / ((unsigned)P * NB));
@@ -780,6 +499,7 @@ void dkv_pipe_kernel(const AttnArgs a) {
       lg2 = lst_c.gat(ec);
     }
     const bool diag = ec == nlist;
+    const float gmul = OUT ? fast_exp2(lg2) : 1.0f;   // the item's gate (1 on the diagonal)
     if (++gc == G) { gc = 0; ++ec; }
     fetch(qf, of);
     // lse / delta rows of item it first (the softmax waits on them), then the row reads
@@ -819,10 +539,19 @@ void dkv_pipe_kernel(const AttnArgs a) {
         else dpn = mfma32(orw[ks], vf[ks], dpn);
       }
       const int grp = e >> 2, x = e & 3;
-      float p = fast_exp2(sc[e] * c2 + (lg2 - l4[grp][x] * kLog2e));
-      if (diag && key > 32 * qh + 8 * grp + 4 * hl + x) p = 0.0f;   // causal mask of block m
-      pv[e] = p;
-      dsv[e] = p * (dpc[e] - d4[grp][x]);
+      if (OUT) {
+        // gate after the softmax: p~ from the ungated LSE, weights p~ g for dV,
+        // dS = p~ (g dP - delta)
+        float p = fast_exp2(sc[e] * c2 - l4[grp][x] * kLog2e);
+        if (diag && key > 32 * qh + 8 * grp + 4 * hl + x) p = 0.0f;   // causal mask of block m
+        pv[e] = p * gmul;
+        dsv[e] = p * (gmul * dpc[e] - d4[grp][x]);
+      } else {
+        float p = fast_exp2(sc[e] * c2 + (lg2 - l4[grp][x] * kLog2e));
+        if (diag && key > 32 * qh + 8 * grp + 4 * hl + x) p = 0.0f;   // causal mask of block m
+        pv[e] = p;
+        dsv[e] = p * (dpc[e] - d4[grp][x]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 pb[2], sb[2];
@@ -952,7 +681,10 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   const int nsplit = dq_splits(a.Hq / a.Hkv);
   {
     ProfScope prof("dq", st);
-    hipLaunchKernelGGL(dq_kernel<D>, dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+    if (a.gate_out)
+      hipLaunchKernelGGL((dq_kernel<D, true>), dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+    else
+      hipLaunchKernelGGL((dq_kernel<D, false>), dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
   }
   if (nsplit > 1 && a.kcap > 0) {
     ProfScope prof("dg_reduce", st);
@@ -962,10 +694,8 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   }
   {
     ProfScope prof("dkv", st);
-    if (SAS_DKV_PIPE)
-      hipLaunchKernelGGL(dkv_pipe_kernel<D>, dim3((unsigned)nrows), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((dkv_kernel<D, SAS_DKV_NBUF, SAS_DKV_WPE>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+    if (a.gate_out) hipLaunchKernelGGL((dkv_pipe_kernel<D, true>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dkv_pipe_kernel<D, false>), dim3((unsigned)nrows), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -40,7 +40,7 @@ namespace sas {
 constexpr float kRescaleThreshold = 8.0f;   // log2 of the largest unnormalised exponential
 
 // 32 rows per wave (NTILE 1) is sized to leave room for two waves per SIMD.
-template <int D, int NTILE, int NW>
+template <int D, int NTILE, int NW, bool OUT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NTILE == 1 ? 2 : 1, NTILE == 1 ? 2 : 1)))
 void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   constexpr int NT = 64 * NW;              // threads
@@ -153,12 +153,17 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
     barrier_lds();
     const int t = tc;
     float lg2 = 0.0f;
+    bool ok = true;
     if (t > 0) {
       sel_c.ensure(t - 1, lane, load_sel);
       const int mb = sel_c.at(t - 1);
       lg2 = sel_c.gat(t - 1);
-      if (mb < 0 || mb >= j) lg2 = -INFINITY;
+      if (mb < 0 || mb >= j) { lg2 = -INFINITY; ok = false; }
     }
+    // Gate after the softmax: the logits and the normaliser are ungated (a block outside
+    // S still drops out) and the probabilities are weighted by g before the PV product.
+    const float gmul = OUT ? fast_exp2(lg2) : 1.0f;
+    if (OUT) lg2 = ok ? 0.0f : -INFINITY;
     ++tc;
     fetch(kn, vn);
     if (!active) return;   // a missing head's waves only take part in the copies
@@ -253,7 +258,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = fast_exp2(st[mt][nt][i] * c2 + off);
-          st[mt][nt][i] = p;
+          st[mt][nt][i] = OUT ? p * gmul : p;
           ls += p;
         }
       lrow[nt] += ls;
@@ -310,13 +315,19 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   }
 }
 
-template <int D, int NTILE, int NW>
-static hipError_t launch_fwd_t(const AttnArgs& a, int nsplit, int hpw, hipStream_t st) {
+template <int D, int NTILE, int NW, bool OUT>
+static hipError_t launch_fwd_o(const AttnArgs& a, int nsplit, int hpw, hipStream_t st) {
   const int NB = a.n / kBlock;
   const unsigned grid = (unsigned)(NB * a.B * a.Hkv * nsplit);
   ProfScope prof("fwd", st);
-  hipLaunchKernelGGL((fwd_kernel<D, NTILE, NW>), dim3(grid), dim3(64 * NW), 0, st, a, nsplit, hpw);
+  hipLaunchKernelGGL((fwd_kernel<D, NTILE, NW, OUT>), dim3(grid), dim3(64 * NW), 0, st, a, nsplit, hpw);
   return hipGetLastError();
+}
+
+template <int D, int NTILE, int NW>
+static hipError_t launch_fwd_t(const AttnArgs& a, int nsplit, int hpw, hipStream_t st) {
+  if (a.gate_out) return launch_fwd_o<D, NTILE, NW, true>(a, nsplit, hpw, st);
+  return launch_fwd_o<D, NTILE, NW, false>(a, nsplit, hpw, st);
 }
 
 // Heads of a KV group per workgroup: at most 4 waves of 64 rows; larger groups are split

@@ -152,16 +152,19 @@ sas_status sas_topk_select(const float* s, int B, int H, int rows, int cols, int
 
 sas_status sas_attn_fwd(const void* Q, const void* K, const void* V, const int32_t* idx,
                         const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
-                        int d, int block, int kcap, float scale, void* O, float* lse_rows,
-                        void* stream) {
+                        int d, int block, int kcap, float scale, int placement, void* O,
+                        float* lse_rows, void* stream) {
   sas_status st = check_attn(Q, K, V, idx, cnt, logg, B, Hq, Hkv, n, d, block, kcap, scale);
   if (st != SAS_OK) return st;
+  REQUIRE(placement == SAS_GATE_INSIDE || placement == SAS_GATE_OUTSIDE, SAS_ERR_INVALID_ARG,
+          "bad placement %d", placement);
   REQUIRE(O != nullptr && lse_rows != nullptr, SAS_ERR_INVALID_ARG, "O and lse_rows must be non-NULL");
   REQUIRE(aligned16(O), SAS_ERR_INVALID_ARG, "O must be 16-byte aligned");
   sas::AttnArgs a{};
   a.Q = (const uint16_t*)Q; a.K = (const uint16_t*)K; a.V = (const uint16_t*)V;
   a.idx = idx; a.cnt = cnt; a.logg = logg;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.gate_out = placement == SAS_GATE_OUTSIDE;
   a.Oout = (uint16_t*)O; a.lse_rows = lse_rows;
   return hip_result(sas::launch_fwd(a, (hipStream_t)stream), "sas_attn_fwd launch");
 }
@@ -175,10 +178,12 @@ size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int blo
 sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void* O,
                         const void* dO, const float* lse_rows, const int32_t* idx,
                         const int32_t* cnt, const float* logg, int B, int Hq, int Hkv, int n,
-                        int d, int block, int kcap, float scale, float* dQ, float* dK,
-                        float* dV, float* dg, void* ws, size_t ws_bytes, void* stream) {
+                        int d, int block, int kcap, float scale, int placement, float* dQ,
+                        float* dK, float* dV, float* dg, void* ws, size_t ws_bytes, void* stream) {
   sas_status st = check_attn(Q, K, V, idx, cnt, logg, B, Hq, Hkv, n, d, block, kcap, scale);
   if (st != SAS_OK) return st;
+  REQUIRE(placement == SAS_GATE_INSIDE || placement == SAS_GATE_OUTSIDE, SAS_ERR_INVALID_ARG,
+          "bad placement %d", placement);
   REQUIRE(O && dO && lse_rows, SAS_ERR_INVALID_ARG, "O, dO and lse_rows must be non-NULL");
   REQUIRE(dQ && dK && dV, SAS_ERR_INVALID_ARG, "dQ, dK and dV must be non-NULL");
   REQUIRE(kcap == 0 || dg != nullptr, SAS_ERR_INVALID_ARG, "dg is NULL");
@@ -195,6 +200,7 @@ sas_status sas_attn_bwd(const void* Q, const void* K, const void* V, const void*
   a.O = (const uint16_t*)O; a.dO = (const uint16_t*)dO;
   a.idx = idx; a.cnt = cnt; a.logg = logg;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.gate_out = placement == SAS_GATE_OUTSIDE;
   a.lse_rows = (float*)lse_rows; a.dQ = dQ; a.dK = dK; a.dV = dV; a.dg = dg;
   return hip_result(sas::launch_bwd(a, ws, (hipStream_t)stream), "sas_attn_bwd launch");
 }

@@ -95,6 +95,7 @@ struct AttnArgs {
   const float* logg;     // may be null
   int B, Hq, Hkv, n, d, kcap;
   float scale;
+  int gate_out;          // 1: gate after the softmax (weights p g), 0: log g inside the logits
   uint16_t* Oout;        // forward output
   float* lse_rows;       // forward output / backward input
   float* dQ;

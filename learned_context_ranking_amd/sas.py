@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsas.so")
 SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
 SCOPE = {"sparse": 0, "full": 1}
 GATE = {"softmax": 0, "softmax_selected": 1, "sigmoid": 2, "exp": 3}
+PLACEMENT = {"inside": 0, "outside": 1}
 ROWS = {"prefill": 0, "decode": 1}
 BLOCK = 64
 
@@ -38,9 +39,9 @@ SIGNATURES = {
     "sas_pool_keys": ([_P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
     "sas_decode_paged": ([_P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
     "sas_decode_select": ([_P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P, _P, _P], _I),
-    "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P], _I),
     "sas_attn_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I, _I], _SZ),
-    "sas_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+    "sas_attn_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                       _P, _P, _P, _P, _P, _SZ, _P], _I),
     "sas_decode_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "sas_decode": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
@@ -166,8 +167,9 @@ def sas_gates_bwd(s, lse, idx, cnt, dg, mode="prefill", row_valid=None, cols=Non
     return ds
 
 
-def sas_attn_fwd(Q, K, V, idx, cnt, logg, scale, out=None, lse_out=None):
+def sas_attn_fwd(Q, K, V, idx, cnt, logg, scale, out=None, lse_out=None, placement="inside"):
     """Q bf16 [B, Hq, n, d]; K, V bf16 [B, Hkv, n, d]; idx/cnt/logg from sas_topk_select.
+    placement: "inside" (log g in the logits) or "outside" (p g after the softmax).
     Returns (O bf16 [B, Hq, n, d], lse_rows fp32 [B, Hq, n])."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V")):
         _need(t, torch.bfloat16, nm)
@@ -181,7 +183,8 @@ def sas_attn_fwd(Q, K, V, idx, cnt, logg, scale, out=None, lse_out=None):
     O = torch.empty_like(Q) if out is None else out
     lse = torch.empty((B, Hq, n), dtype=torch.float32, device=Q.device) if lse_out is None else lse_out
     _check(lib().sas_attn_fwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(idx), _ptr(cnt), _ptr(logg), B, Hq, Hkv, n,
-                              d, BLOCK, kcap, float(scale), _ptr(O), _ptr(lse), _stream(Q.device)))
+                              d, BLOCK, kcap, float(scale), PLACEMENT[placement], _ptr(O), _ptr(lse),
+                              _stream(Q.device)))
     return O, lse
 
 
@@ -192,7 +195,7 @@ def bwd_workspace(B, Hq, Hkv, n, d, kcap, device):
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def sas_attn_bwd(Q, K, V, O, dO, lse_rows, idx, cnt, logg, scale, ws=None, outs=None):
+def sas_attn_bwd(Q, K, V, O, dO, lse_rows, idx, cnt, logg, scale, ws=None, outs=None, placement="inside"):
     """Returns (dQ fp32, dK fp32, dV fp32, dg fp32 [B, Hkv, n/64, kcap])."""
     for t, nm in ((Q, "Q"), (K, "K"), (V, "V"), (O, "O"), (dO, "dO")):
         _need(t, torch.bfloat16, nm)
@@ -212,7 +215,8 @@ def sas_attn_bwd(Q, K, V, O, dO, lse_rows, idx, cnt, logg, scale, ws=None, outs=
         dQ, dK, dV, dg = outs
     _check(lib().sas_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(lse_rows), _ptr(idx),
                               _ptr(cnt), _ptr(logg), B, Hq, Hkv, n, d, BLOCK, kcap, float(scale),
-                              _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(ws), ws.numel(), _stream(dev)))
+                              PLACEMENT[placement], _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dg), _ptr(ws), ws.numel(),
+                              _stream(dev)))
     return dQ, dK, dV, dg
 
 

@@ -46,11 +46,11 @@ NULL = None
 
 def _fwd(**kw):
     a = dict(Q=FAKE, K=FAKE, V=FAKE, idx=FAKE, cnt=FAKE, logg=FAKE, B=1, Hq=4, Hkv=2, n=256, d=128,
-             block=64, kcap=4, scale=0.125, O=FAKE, lse=FAKE, stream=NULL)
+             block=64, kcap=4, scale=0.125, placement=0, O=FAKE, lse=FAKE, stream=NULL)
     a.update(kw)
     return sas.lib().sas_attn_fwd(a["Q"], a["K"], a["V"], a["idx"], a["cnt"], a["logg"], a["B"], a["Hq"],
-                                  a["Hkv"], a["n"], a["d"], a["block"], a["kcap"], a["scale"], a["O"],
-                                  a["lse"], a["stream"])
+                                  a["Hkv"], a["n"], a["d"], a["block"], a["kcap"], a["scale"], a["placement"],
+                                  a["O"], a["lse"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -66,6 +66,8 @@ def _fwd(**kw):
     (dict(K=MIS), sas.SAS_ERR_INVALID_ARG),
     (dict(O=NULL), sas.SAS_ERR_INVALID_ARG),
     (dict(B=0), sas.SAS_ERR_INVALID_ARG),
+    (dict(placement=2), sas.SAS_ERR_INVALID_ARG),
+    (dict(placement=-1), sas.SAS_ERR_INVALID_ARG),
 ])
 def test_fwd_rejects(kw, code):
     assert _fwd(**kw) == code
@@ -156,7 +158,7 @@ def test_bwd_workspace_and_rejects():
     assert L.sas_attn_bwd_workspace_size(1, 4, 2, 250, 128, 64, 4) == 0
     assert L.sas_attn_bwd_workspace_size(1, 3, 2, 256, 128, 64, 4) == 0
     need = L.sas_attn_bwd_workspace_size(1, 4, 2, 256, 128, 64, 4)
-    args = [FAKE] * 9 + [1, 4, 2, 256, 128, 64, 4, 0.125] + [FAKE] * 4 + [FAKE, need - 1, NULL]
+    args = [FAKE] * 9 + [1, 4, 2, 256, 128, 64, 4, 0.125, 0] + [FAKE] * 4 + [FAKE, need - 1, NULL]
     assert L.sas_attn_bwd(*args) == sas.SAS_ERR_WORKSPACE
     args[-3] = NULL
     args[-2] = need
@@ -164,8 +166,11 @@ def test_bwd_workspace_and_rejects():
     args[-3] = FAKE
     args[4] = NULL                          # dO
     assert L.sas_attn_bwd(*args) == sas.SAS_ERR_INVALID_ARG
+    args[4] = FAKE
+    args[17] = 5                            # placement
+    assert L.sas_attn_bwd(*args) == sas.SAS_ERR_INVALID_ARG
     # one KV group's query rows must stay below 2^31 bytes: 8 heads x 2^20 rows x 128 x 2
-    big = [FAKE] * 9 + [1, 8, 1, 1 << 20, 128, 64, 4, 0.125] + [FAKE] * 4 + [FAKE, 1 << 62, NULL]
+    big = [FAKE] * 9 + [1, 8, 1, 1 << 20, 128, 64, 4, 0.125, 0] + [FAKE] * 4 + [FAKE, 1 << 62, NULL]
     assert L.sas_attn_bwd(*big) == sas.SAS_ERR_UNSUPPORTED
 
 

@@ -159,3 +159,42 @@ def test_full_size_qwen3_14b_k32():
 
 def test_full_size_long_prefill_fwd():
     _full_size(1, 32, 8, 131072, 128, 64, "planted", nsample_j=4, backward=False)
+
+
+OUT_CASES = [
+    (1, 8, 2, 1024, 128, 4, "sparse", True, "normal"),
+    (2, 8, 2, 512, 64, 3, "sparse", True, "normal"),
+    (1, 10, 2, 768, 128, 6, "sparse", True, "zipf"),
+    (1, 4, 1, 512, 128, 0, "full", True, "normal"),
+]
+
+
+@pytest.mark.parametrize("case", OUT_CASES, ids=[f"B{c[0]}H{c[1]}-{c[2]}n{c[3]}d{c[4]}K{c[5]}{c[6]}" for c in OUT_CASES])
+def test_fwd_bwd_gate_outside(case):
+    """The gate after the softmax (the alternative of the explainer's choice 1) against
+    the oracle: O, LSE of the ungated logits, dQ, dK, dV and dg = sum p dO.v. Some
+    scores are -inf, so kept blocks with gate 0 still count in the normaliser."""
+    log(f"fwd/bwd gate outside {case}")
+    B, Hq, Hkv, n, d, topk, scope, _, scores = case
+    P = Prefill(B, Hq, Hkv, n, d, seed=5, scores=scores)
+    P.s[..., ::5] = -np.inf
+    t = P.device()
+    NB = P.NB
+    kcap = NB - 1 if scope == "full" else topk
+    idx, cnt, _, logg = sas.sas_topk_select(t["s"], topk, scope=scope, kcap=kcap, cols=NB)
+    O, lse = sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx, cnt, logg, P.scale, placement="outside")
+    dQ, dK, dV, dg = sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx, cnt, logg, P.scale,
+                                      placement="outside")
+    torch.cuda.synchronize()
+    idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk, full_scope=scope == "full", kcap=kcap)
+    assert np.array_equal(host(idx), idx_r) and np.array_equal(host(cnt), cnt_r)
+    assert np.isneginf(logg_r).any()
+    Q, K, V, dO = P.f32("q"), P.f32("k"), P.f32("v"), P.f32("do")
+    O_r, lse_r = oracle.attn_fwd(Q, K, V, idx_r, cnt_r, logg_r, P.scale, placement="outside")
+    assert_close("O", host(O), O_r)
+    assert_close("LSE", host(lse), lse_r)
+    dQ_r, dK_r, dV_r, dg_r = oracle.attn_bwd(Q, K, V, dO, idx_r, cnt_r, logg_r, P.scale, placement="outside")
+    assert_close("dQ", host(dQ), dQ_r)
+    assert_close("dK", host(dK), dK_r)
+    assert_close("dV", host(dV), dV_r)
+    assert_close("dg", host(dg), dg_r)
