@@ -10,6 +10,8 @@
 // K best of those scores exactly as sas_topk_select does ([SAS-ja] "仕組み", Algorithm 2;
 // ties to the lower block index, NaN as -inf), in one workgroup per row so that rows of up
 // to 8192 blocks (512K tokens) finish in a few microseconds.
+#include <type_traits>
+
 #include "sas_common.h"
 #include "sas_kernels.h"
 
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const PoolArgs a) {
 // ------------------------------------------------------------------ Top-K per row
 
 constexpr int kSelThreads = 256;
-constexpr int kSelPer = kMaxCols / kSelThreads;   // 32 scores per thread, contiguous
+static_assert(kMaxCols == 32 * kSelThreads, "each thread owns 32 consecutive blocks of a row");
 
 // exclusive prefix sum over the workgroup and its total (all threads call it)
 __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
@@ -96,122 +98,144 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return r;
 }
 
-// Top-K of one row by one workgroup. The K-th largest order key is found digit by digit
-// (3 passes of 12, 10 and 10 bits, an LDS histogram per pass restricted to the keys that
-// match the digits fixed so far); keys above it are kept and the remaining places go to
-// the lowest-index keys equal to it. Thread t owns blocks 32 t .. 32 t + 31, so one prefix
-// sum over the threads gives every kept block its output position in ascending order.
+// Top-K of one row by one workgroup. The row's order keys are staged in LDS; the K-th
+// largest is found digit by digit (passes of 12, 10 and 10 bits over an LDS histogram of
+// the keys that match the digits fixed so far), stopping early once the chosen bin holds
+// exactly the places still open. Keys above the cut are kept and the remaining places go
+// to the lowest-index keys at the cut. Every loop runs over the row's actual length, and
+// LDS arrays are padded (one word per 32 keys, one per bin group) so the strided and the
+// per-thread-contiguous accesses are both free of bank conflicts.
+constexpr int kKeyPad = kMaxCols + kMaxCols / 32;
 struct TopkSmem {
-  int hist[4096];
+  uint32_t keys[kKeyPad];
+  int hist[4096 + 256];
   int wsum[kSelThreads / 64];
   float red[kSelThreads / 64];
-  int pick[2];
+  int pick[3];
 };
+
+__device__ __forceinline__ int kpad(int m) { return m + (m >> 5); }
+__device__ __forceinline__ float key_value(uint32_t k) {   // inverse of order_key
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 __device__ __forceinline__ void topk_row(const DecSelArgs& a, long long row, TopkSmem& sm) {
   int* hist = sm.hist;
-  int* wsum = sm.wsum;
-  float* red = sm.red;
-  int* pick = sm.pick;
   const int b = (int)(row / a.Hkv);
   const int n = min(max((a.kv_len[b] - 1) / kBlock, 0), a.C);
   const int k = min(a.topk, n);
   const int t = threadIdx.x;
-  const int m0 = t * kSelPer;
   const float* srow = a.s + (size_t)row * a.C;
   int32_t* idx = a.idx + (size_t)row * a.kcap;
   float* lg = a.logg != nullptr ? a.logg + (size_t)row * a.kcap : nullptr;
 
-  float x[kSelPer];
-  uint32_t key[kSelPer];
-#pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    const int m = m0 + i;
-    x[i] = m < n ? srow[m] : -INFINITY;
-    if (x[i] != x[i]) x[i] = -INFINITY;
-    key[i] = m < n ? order_key(x[i]) : 0u;   // valid keys are >= order_key(-inf) > 0
-  }
+#pragma unroll 8
+  for (int m = t; m < n; m += kSelThreads) sm.keys[kpad(m)] = order_key(srow[m]);   // coalesced
+  __syncthreads();
   float lse = -INFINITY;
   if (a.lse != nullptr || lg != nullptr) {
     float mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kSelPer; ++i) mx = fmaxf(mx, x[i]);
-    mx = block_reduce(mx, red, true);
+#pragma unroll 8
+    for (int m = t; m < n; m += kSelThreads) mx = fmaxf(mx, key_value(sm.keys[kpad(m)]));
+    mx = block_reduce(mx, sm.red, true);
     if (mx != -INFINITY) {
       float sum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kSelPer; ++i) sum += expf(x[i] - mx);
-      sum = block_reduce(sum, red, false);
+#pragma unroll 8
+      for (int m = t; m < n; m += kSelThreads) sum += expf(key_value(sm.keys[kpad(m)]) - mx);
+      sum = block_reduce(sum, sm.red, false);
       lse = mx + logf(sum);
     }
     if (a.lse != nullptr && t == 0) a.lse[row] = lse;
   }
 
-  int need_eq = 0;
-  uint32_t T = 0xFFFFFFFFu;   // no block kept when k == 0
+  // the cut: keys whose bits above cut_shift exceed those of T are kept, and need_eq of
+  // the keys equal to T there (lowest index first)
+  uint32_t T = 0xFFFFFFFFu;
+  int cut_shift = 0, need_eq = 0;
   if (k > 0) {
-    // Digits of 12, 10 and 10 bits from the top. Scores of one row usually share their
-    // sign and a few exponent values, so a wide first digit spreads them over many bins
-    // (few LDS atomics collide on one counter).
     uint32_t prefix = 0;
     int remaining = k;
+    // one pass over bits [SHIFT, SHIFT + log2 NB) of the keys that match prefix above HI;
+    // returns true once the chosen bin holds exactly the places still open
+    auto pass = [&](auto shift_c, auto nbins_c, auto hi_c) {
+      constexpr int SHIFT = decltype(shift_c)::value, NB = decltype(nbins_c)::value;
+      constexpr int HI = decltype(hi_c)::value, PER = NB / kSelThreads;
+      // bin b lives at b + b / PER: thread t's bins are contiguous and threads are PER + 1
+      // words apart (odd), so neither the strided zeroing nor the per-thread reads collide
 #pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-      const int nbins = pass == 0 ? 4096 : 1024;
-      const int hi = shift + (pass == 0 ? 12 : 10);   // bits >= hi are fixed by earlier passes
-      const int per = nbins / kSelThreads;             // bins owned by each thread
-      for (int i = t; i < nbins; i += kSelThreads) hist[i] = 0;
+      for (int i = 0; i < PER; ++i) hist[(PER + 1) * t + i] = 0;
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < kSelPer; ++i) {
-        const bool match = key[i] != 0u && (hi == 32 || (key[i] >> hi) == (prefix >> hi));
-        if (match) atomicAdd(&hist[(key[i] >> shift) & (nbins - 1)], 1);
-      }
-      __syncthreads();
-      // thread t owns bins per t .. per t + per - 1; above = matching keys in higher bins
-      int local = 0;
-      for (int i = 0; i < per; ++i) local += hist[per * t + i];
-      int total;
-      const int before = block_excl_scan(local, wsum, &total);
-      int above = total - before - local;
-      for (int i = per - 1; i >= 0; --i) {
-        const int c = hist[per * t + i];
-        if (above < remaining && remaining <= above + c) {
-          pick[0] = per * t + i;
-          pick[1] = above;
+#pragma unroll 8
+      for (int m = t; m < n; m += kSelThreads) {
+        const uint32_t key = sm.keys[kpad(m)];
+        if (HI == 32 || (key >> (HI & 31)) == (prefix >> (HI & 31))) {
+          const int bin = (int)((key >> SHIFT) & (uint32_t)(NB - 1));
+          atomicAdd(&hist[bin + bin / PER], 1);
         }
-        above += c;
       }
       __syncthreads();
-      prefix |= (uint32_t)pick[0] << shift;
-      remaining -= pick[1];
+      int c[PER];
+      int local = 0;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        c[i] = hist[(PER + 1) * t + i];
+        local += c[i];
+      }
+      int total;
+      const int before = block_excl_scan(local, sm.wsum, &total);
+      int above = total - before - local;   // matching keys in higher bins
+#pragma unroll
+      for (int i = PER - 1; i >= 0; --i) {
+        if (above < remaining && remaining <= above + c[i]) {
+          sm.pick[0] = PER * t + i;
+          sm.pick[1] = above;
+          sm.pick[2] = c[i];
+        }
+        above += c[i];
+      }
+      __syncthreads();
+      prefix |= (uint32_t)sm.pick[0] << SHIFT;
+      remaining -= sm.pick[1];
+      const int in_bin = sm.pick[2];
       __syncthreads();   // pick and hist are rewritten by the next pass
-    }
+      cut_shift = SHIFT;
+      return in_bin == remaining;
+    };
+    using I = int;
+    if (!pass(std::integral_constant<I, 20>{}, std::integral_constant<I, 4096>{}, std::integral_constant<I, 32>{}))
+      if (!pass(std::integral_constant<I, 10>{}, std::integral_constant<I, 1024>{}, std::integral_constant<I, 20>{}))
+        pass(std::integral_constant<I, 0>{}, std::integral_constant<I, 1024>{}, std::integral_constant<I, 10>{});
     T = prefix;
-    need_eq = remaining;   // keys equal to T still to take, lowest index first
+    need_eq = remaining;
   }
+  // thread t counts and then writes blocks 32 t .. 32 t + 31 (index order); the key reads
+  // are unrolled so they are in flight together
+  const int m0 = 32 * t;
+  uint32_t kk[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) kk[i] = (k > 0 && m0 + i < n) ? sm.keys[kpad(m0 + i)] : 0u;   // 0: no block
+  const uint32_t tc = T >> cut_shift;
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int i = 0; i < kSelPer; ++i) {
-    gt += (key[i] != 0u && key[i] > T);
-    eq += (key[i] != 0u && key[i] == T);
+  for (int i = 0; i < 32; ++i) {
+    gt += kk[i] != 0u && (kk[i] >> cut_shift) > tc;
+    eq += kk[i] != 0u && (kk[i] >> cut_shift) == tc;
   }
-  // one scan of both counts (each below 2^14): low 16 bits above-threshold, high 16 ties
+  // one scan of both counts (each below 2^14): low 16 bits above the cut, high 16 at it
   int packed_total;
-  const int packed = block_excl_scan(gt | (eq << 16), wsum, &packed_total);
+  const int packed = block_excl_scan(gt | (eq << 16), sm.wsum, &packed_total);
   int gt_before = packed & 0xFFFF, eq_before = packed >> 16;
-  if (k > 0) {
+  if (gt + eq > 0) {
 #pragma unroll
-    for (int i = 0; i < kSelPer; ++i) {
-      const bool above = key[i] != 0u && key[i] > T;
-      const bool tie = key[i] != 0u && key[i] == T;
+    for (int i = 0; i < 32; ++i) {
+      const bool above = kk[i] != 0u && (kk[i] >> cut_shift) > tc;
+      const bool tie = kk[i] != 0u && (kk[i] >> cut_shift) == tc;
       if (above || (tie && eq_before < need_eq)) {
-        // kept blocks before this one: all blocks above T, the first need_eq ties
+        // kept blocks before this one: all blocks above the cut, the first need_eq ties
         const int pos = gt_before + min(eq_before, need_eq);
-        if (pos < k) {   // always true when the threshold is right; keeps writes in the row
+        if (pos < k) {   // always true when the cut is right; keeps writes in the row
           idx[pos] = m0 + i;
-          if (lg != nullptr) lg[pos] = (lse == -INFINITY) ? -INFINITY : x[i] - lse;
+          if (lg != nullptr) lg[pos] = (lse == -INFINITY) ? -INFINITY : key_value(kk[i]) - lse;
         }
       }
       gt_before += above;
@@ -224,7 +248,6 @@ __device__ __forceinline__ void topk_row(const DecSelArgs& a, long long row, Top
   }
   if (t == 0) a.cnt[row] = k;
 }
-
 }  // namespace
 
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
