@@ -24,6 +24,8 @@
 // transposing ds_read_b64_tr_b16 from the same natural tile.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "sas_common.h"
 #include "sas_kernels.h"
 
@@ -223,13 +225,16 @@ void dq_kernel(const AttnArgs a, int nsplit) {
   const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
 
   // one block: copy the next block into (kn, vn), compute block tc from (kc, vc)
-  auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+  // DIAG: the step of block t = 0 (block j itself), the only one with a causal mask; it is
+  // peeled off the loop so the other steps carry no masking code
+  auto step = [&](auto diag_c, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+    constexpr bool DIAG = decltype(diag_c)::value;
     wait_vm();
     barrier_lds();
     const int t = tc;
     float lg2 = 0.0f;
     bool ok = true;
-    if (t > 0) {
+    if (!DIAG) {
       sel_c.ensure(t - 1, lane, load_sel);
       const int mb = sel_c.at(t - 1);
       lg2 = sel_c.gat(t - 1);
@@ -290,7 +295,7 @@ void dq_kernel(const AttnArgs a, int nsplit) {
           const int i = 8 * hh + x;
           float u = fast_exp2(st[i] * c2 - lse2);   // p~ / g = exp(scale q.k - LSE)
           const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
-          if (t == 0 && key > wrow0 + ql) u = 0.0f;   // causal mask of block j itself
+          if (DIAG && key > wrow0 + ql) u = 0.0f;   // causal mask of block j itself
           if (OUT) {
             // gate after the softmax: u is the probability itself (LSE of the ungated
             // logits); dS = u (g dP - delta), dg = sum u dP; a block outside S has u = 0
@@ -311,16 +316,19 @@ void dq_kernel(const AttnArgs a, int nsplit) {
         for (int hh = 0; hh < 2; ++hh) dq[dt] = mfma32(ka[dt][hh], dsf[hh], dq[dt]);
     }
     dgacc = wave_sum(dgacc);
-    if (lane == 0) dgp[t & 1][wave] = (t > 0 && ok) ? dgacc : 0.0f;
+    if (lane == 0) dgp[t & 1][wave] = (!DIAG && ok) ? dgacc : 0.0f;
   };
-  const int nsteps = cnt_j + 1;
-  const int nfull = nsteps & ~1;
+  const std::integral_constant<bool, true> diag_step;
+  const std::integral_constant<bool, false> plain_step;
+  const int nrest = cnt_j;   // steps after the diagonal one
+  const int nfull = nrest & ~1;
   fetch(sk0, sv0);
+  step(diag_step, sk0, sv0, sk1, sv1);
   for (int it = 0; it < nfull; it += 2) {
-    step(sk0, sv0, sk1, sv1);
-    step(sk1, sv1, sk0, sv0);
+    step(plain_step, sk1, sv1, sk0, sv0);
+    step(plain_step, sk0, sv0, sk1, sv1);
   }
-  if (nfull < nsteps) step(sk0, sv0, sk1, sv1);
+  if (nfull < nrest) step(plain_step, sk1, sv1, sk0, sv0);
   wait_vm();
   __syncthreads();
   if (tid == 0) {

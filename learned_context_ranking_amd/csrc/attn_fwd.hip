@@ -25,6 +25,8 @@
 // finite from the start (each query sees itself). The reference maximum is only moved when
 // a row's maximum grows by more than 2^8 (exponentials stay <= 256), which skips nearly
 // all rescales of the output accumulator.
+#include <type_traits>
+
 #include "sas_common.h"
 #include "sas_kernels.h"
 
@@ -148,13 +150,16 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
 
   // one block: copy the next block into (kn, vn), compute block tc from (kc, vc)
-  auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+  // DIAG: the step of block t = 0 (block j itself), the only one with a causal mask; it is
+  // peeled off the loop so the other steps carry no masking code
+  auto step = [&](auto diag_c, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+    constexpr bool DIAG = decltype(diag_c)::value;
     wait_vm();
     barrier_lds();
     const int t = tc;
     float lg2 = 0.0f;
     bool ok = true;
-    if (t > 0) {
+    if (!DIAG) {
       sel_c.ensure(t - 1, lane, load_sel);
       const int mb = sel_c.at(t - 1);
       lg2 = sel_c.gat(t - 1);
@@ -210,7 +215,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) va[dt][mt][hh] = read_va(dt, mt, hh);
     }
-    if (t == 0) {  // causal mask on the current block (key > query)
+    if (DIAG) {  // causal mask on the current block (key > query)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -282,14 +287,17 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
           for (int nt = 0; nt < NTILE; ++nt) oacc[dt][nt] = mfma32(v, pf[mt][nt][hh], oacc[dt][nt]);
         }
   };
-  const int nsteps = cnt_j + 1;
-  const int nfull = nsteps & ~1;
+  const std::integral_constant<bool, true> diag_step;
+  const std::integral_constant<bool, false> plain_step;
+  const int nrest = cnt_j;   // steps after the diagonal one
+  const int nfull = nrest & ~1;
   fetch(sk0, sv0);
+  step(diag_step, sk0, sv0, sk1, sv1);
   for (int it = 0; it < nfull; it += 2) {
-    step(sk0, sv0, sk1, sv1);
-    step(sk1, sv1, sk0, sv0);
+    step(plain_step, sk1, sv1, sk0, sv0);
+    step(plain_step, sk0, sv0, sk1, sv1);
   }
-  if (nfull < nsteps) step(sk0, sv0, sk1, sv1);
+  if (nfull < nrest) step(plain_step, sk1, sv1, sk0, sv0);
   wait_vm();   // the last (repeated) copy lands before the workgroup's LDS is released
   if (!active) return;
 
