@@ -25,6 +25,10 @@ Sources, cited by page title and section:
   2510.21270), prior art cited for one step only: sections "3." (proxy scoring) and
   "4. 実装" (block selection) estimate a block's importance by mean pooling of attention
   scores, which stands in for the undefined SAS selector in long-context decode selection.
+* [S2O-ja] "S2O: オンライン置換によるスパースアテンションの早期停止" summary (gist.science/ja/paper/
+  2602.22575), prior art cited for one rule only: section "2. 早期停止ルール" stops adding
+  blocks, taken in descending importance, once a block's marginal softmax mass falls
+  below a threshold relative to the mass accumulated so far.
 * [SAS-ko] "SAS는 언어모델 손실로 문맥 순위를 직접 학습하는 사후 어텐션 희소화다"
   (onedev.kr/papers/5). Section "어떻게 동작하나" gives o = softmax(q K_S^T + log g_S) V_S.
   Section "무엇과 다른가" gives the four design choices: (1) the gate inside the softmax and
@@ -539,3 +543,65 @@ def decode_paged(q, Kpool, Vpool, page_table, kv_len, idx, cnt, scale, block=64,
     Kc = gather_pages(Kpool, page_table, kv_len, block)
     Vc = gather_pages(Vpool, page_table, kv_len, block)
     return decode(q, Kc, Vc, kv_len, idx, cnt, scale, block, logg)
+
+
+# ---------------------------------------------------------------- early-stopped decode
+
+def decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, order, scale, tau, block=64):
+    """Decode with a mass-threshold early stop over the selected blocks, the stopping rule
+    of [S2O-ja] (gist.science/ja/paper/2602.22575), section "2. 早期停止ルール", and the
+    two-pass order of its section "3. カーネル実装" (prior art, used as a budget rule):
+
+    per query head, the online-softmax state starts from the current block (causal, as in
+    decode); the selected blocks then follow in descending ``order`` (ties to the lower
+    block index). Each block's marginal softmax mass dl = sum_i exp(z_i - M) is compared
+    with the mass l accumulated before it (both in the frame of the running maximum M
+    after the block): the block is added, and if dl < tau * l the remaining blocks are
+    skipped. tau = 0 never stops early (plain decode over every selected block).
+
+    q [B, Hq, d]; Kc, Vc [B, Hkv, Lmax, d]; idx, order [B, Hkv, kcap]; cnt [B, Hkv].
+    Returns (o [B, Hq, d], used [B, Hq]: history blocks each head attended,
+    margin: the smallest |dl / l - tau| over the comparisons made, relative to tau).
+    """
+    q = np.asarray(q, np.float64); Kc = np.asarray(Kc, np.float64); Vc = np.asarray(Vc, np.float64)
+    B, Hq, d = q.shape
+    Hkv = Kc.shape[1]
+    G = Hq // Hkv
+    o = np.zeros_like(q)
+    used = np.zeros((B, Hq), dtype=np.int32)
+    margin = np.inf
+    for b in range(B):
+        L = int(kv_len[b])
+        c = (L - 1) // block
+        for h in range(Hkv):
+            k = int(cnt[b, h])
+            sel = np.asarray(idx[b, h, :k], dtype=np.int64)
+            key = np.asarray(order[b, h, :k], dtype=np.float64)
+            seq = sel[np.lexsort((sel, -key))]          # descending order, ties to the lower index
+            for g in range(G):
+                qv = q[b, h * G + g]
+                z = scale * (Kc[b, h, c * block:L] @ qv)
+                M = z.max()
+                w = np.exp(z - M)
+                l = w.sum()
+                acc = w @ Vc[b, h, c * block:L]
+                n_used = 0
+                for m in seq:
+                    zb = scale * (Kc[b, h, m * block:(m + 1) * block] @ qv)
+                    Mn = max(M, zb.max())
+                    l *= np.exp(M - Mn)
+                    acc *= np.exp(M - Mn)
+                    M = Mn
+                    wb = np.exp(zb - M)
+                    dl = wb.sum()
+                    stop = dl < tau * l
+                    if tau > 0:
+                        margin = min(margin, abs(dl / l - tau) / tau)
+                    l += dl
+                    acc += wb @ Vc[b, h, m * block:(m + 1) * block]
+                    n_used += 1
+                    if stop:
+                        break
+                o[b, h * G + g] = acc / l
+                used[b, h * G + g] = n_used
+    return o, used, margin

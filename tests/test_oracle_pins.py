@@ -705,3 +705,72 @@ def test_pm_unit_gates_make_the_placements_equal():
                          placement="outside")
     for x, y in zip(ga[:3], gb[:3]):
         np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ P-n: early-stopped decode
+
+def test_pn_early_stop_limits_and_monotone():
+    """tau = 0 is the plain decode over every selected block; a huge tau keeps only the
+    best-scored block; the number of blocks used never grows with tau."""
+    g = np.random.default_rng(60)
+    B, Hq, Hkv, d, L, K = 2, 4, 2, 16, 64 * 12 + 5, 6
+    q = g.standard_normal((B, Hq, d))
+    Kc = g.standard_normal((B, Hkv, L, d))
+    Vc = g.standard_normal((B, Hkv, L, d))
+    kv_len = np.array([L, 64 * 7 + 1])
+    s = g.standard_normal((B * Hkv, 12)).astype(np.float32)
+    idx, cnt, _, logg = oracle.select(s, np.repeat((kv_len - 1) // 64, Hkv), K, kcap=K)
+    idx = idx.reshape(B, Hkv, K); cnt = cnt.reshape(B, Hkv); logg = logg.reshape(B, Hkv, K)
+    o0, used0, _ = oracle.decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, logg, 0.25, 0.0)
+    np.testing.assert_allclose(o0, oracle.decode(q, Kc, Vc, kv_len, idx, cnt, 0.25), rtol=1e-12, atol=1e-12)
+    assert np.array_equal(used0, np.repeat(cnt, Hq // Hkv, axis=1))
+    o1, used1, _ = oracle.decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, logg, 0.25, 1e30)
+    assert np.all(used1 == 1)
+    top = np.zeros((B, Hkv, 1), np.int32)
+    for b in range(B):
+        for h in range(Hkv):
+            k = cnt[b, h]
+            best = np.lexsort((idx[b, h, :k], -logg[b, h, :k]))[0]
+            top[b, h, 0] = idx[b, h, best]
+    np.testing.assert_allclose(o1, oracle.decode(q, Kc, Vc, kv_len, top, np.ones((B, Hkv), np.int32), 0.25),
+                               rtol=1e-12, atol=1e-12)
+    prev = used0
+    for tau in (1e-4, 1e-3, 1e-2, 0.05, 0.2, 1.0):
+        _, u, _ = oracle.decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, logg, 0.25, tau)
+        assert np.all(u <= prev)
+        prev = u
+
+
+def test_pn_early_stop_closed_form_masses():
+    """Keys constant within each block make every logit known in closed form: the current
+    block (16 tokens) has logit 0 and the four selected blocks logits 0, -1, -2, -3 (in
+    score order). The masses 64 e^-k against tau times the running sum 16 + sum 64 e^-k'
+    fix the number of blocks used for each tau."""
+    d, blk = 4, 64
+    L = 5 * blk + 16
+    Kc = np.zeros((1, 1, L, d))
+    logits = {0: 0.0, 1: -1.0, 2: -2.0, 3: -3.0}          # block -> logit (scale 1, q = e_0)
+    for m, z in logits.items():
+        Kc[0, 0, m * blk:(m + 1) * blk, 0] = z
+    Vc = np.random.default_rng(61).standard_normal((1, 1, L, d))
+    q = np.zeros((1, 1, d)); q[0, 0, 0] = 1.0
+    idx = np.array([[[0, 1, 2, 3]]], np.int32)
+    order = np.array([[[4.0, 3.0, 2.0, 1.0]]])          # descending: blocks 0, 1, 2, 3
+    cnt = np.array([[4]], np.int32)
+
+    def expected(tau):
+        lsum, n = 16.0, 0
+        for z in (0.0, -1.0, -2.0, -3.0):
+            dl = 64.0 * math.exp(z)
+            n += 1
+            stop = dl < tau * lsum
+            lsum += dl
+            if stop:
+                break
+        return n
+
+    for tau in (0.05, 0.1, 0.29, 0.3, 2.0, 5.0):
+        _, used, margin = oracle.decode_early_stop(q, Kc, Vc, np.array([L]), idx, cnt, order, 1.0, tau)
+        assert used[0, 0] == expected(tau), (tau, used, expected(tau))
+    # 0.29 separates "compared with the mass before the block" (3) from "after it" (2)
+    assert [expected(t) for t in (0.05, 0.1, 0.29, 0.3, 5.0)] == [4, 3, 3, 2, 1]
