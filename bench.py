@@ -232,12 +232,28 @@ def run_decode(steps, torch):
     torch.cuda.synchronize()
     ms_paged = float(np.median([x.elapsed_time(y) for x, y in ptimes]))
     del Kp, Vp
+    # the same step with the mass-threshold early stop (blocks in descending score order)
+    order = torch.gather(s[:, :, 0, :], -1, idx.reshape(B, Hkv, -1).clamp(min=0).long()).contiguous()
+    early = {}
+    for tau in (0.0, 0.1):
+        oe, used = sas.sas_decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, order, scale, tau)
+        torch.cuda.synchronize()
+        et = []
+        for _ in range(steps):
+            flush.sum()
+            a, c = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+            a.record(stream)
+            sas.sas_decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, order, scale, tau, out=oe, used=used)
+            c.record(stream)
+            et.append((a, c))
+        torch.cuda.synchronize()
+        early[tau] = (float(np.median([x.elapsed_time(y) for x, y in et])), float(used.float().mean()))
     cnt_h = cnt.cpu().numpy()
     # algorithmic bytes: the selected K/V blocks plus the current block, q and o
     blocks = int(cnt_h.sum()) + B * Hkv
     nbytes = blocks * 64 * d * 2 * 2 + 2 * B * Hq * d * 2
     return dict(ms=ms, ms_select=ms_sel, bytes=nbytes, gbs=nbytes / ms / 1e6, ms_paged=ms_paged,
-                gbs_paged=nbytes / ms_paged / 1e6,
+                gbs_paged=nbytes / ms_paged / 1e6, early=early,
                 workload=f"decode: B={B} sequences, Hq={Hq}, Hkv={Hkv}, d={d}, kv_len={L}, block=64, "
                          f"K={K} blocks + current block, ungated (Algorithm 2)")
 
@@ -410,6 +426,8 @@ def main():
                          "select_ms": round(dec["ms_select"], 5), "bytes": dec["bytes"],
                          "paged": {"ms": round(dec["ms_paged"], 5), "value": round(dec["gbs_paged"], 1),
                                    "unit": "GB/s", "layout": "pool of 64-token pages in random order + page table"},
+                         "early_stop": {f"tau={t}": {"ms": round(v[0], 5), "history_blocks_used": round(v[1], 2)}
+                                        for t, v in dec["early"].items()},
                          "workload": dec["workload"],
                          "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(dec["gbs"], 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",

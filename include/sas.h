@@ -252,6 +252,28 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sas_decode_early_stop - sas_decode with a mass-threshold early stop over the selected
+ * blocks, the rule of [S2O-ja] "S2O: オンライン置換によるスパースアテンションの早期停止"
+ * (section "2. 早期停止ルール"; prior art, used as a budget rule on top of Top-K).
+ * Per query head: the current block first, then the kept blocks in descending order key
+ * (ties to the lower block index); each block is attended, and the head takes no further
+ * block once the block's softmax mass is below tau times the mass accumulated before it.
+ * tau = 0 gives sas_decode (ungated) over every kept block.
+ *
+ *   q, Kc, Vc, kv_len, Lmax, idx, cnt, sizes, block, scale, o: as sas_decode.
+ *   kcap     at most 63 (the list of a (sequence, KV head) is sorted inside one wave).
+ *   order    fp32 [B][Hkv][kcap], device: the score (or log-gate) of each kept block; only
+ *            its order matters. NaN orders as -inf.
+ *   tau      finite, >= 0.
+ *   used     int32 [B][Hq], device, out, nullable: history blocks each head attended.
+ * No workspace: one workgroup walks each (sequence, KV head) list.
+ */
+sas_status sas_decode_early_stop(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                                 int Lmax, const int32_t* idx, const int32_t* cnt, const float* order,
+                                 int B, int Hq, int Hkv, int d, int block, int kcap, float scale,
+                                 float tau, void* o, int32_t* used, void* stream);
+
+/*
  * sas_decode_paged - sas_decode over a paged KV cache (serving layout).
  * Same computation as sas_decode ([SAS-ja] "仕組み", Algorithm 2); the cache is a pool of
  * pages of 64 tokens (one SAS block each) and a page table per sequence:

@@ -28,7 +28,14 @@ constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalis
 // then holds page ids, and every half block is copied through a buffer resource that
 // starts at its page and covers only its valid rows, so rows past kv_len (which a page
 // allocator leaves unwritten) read as zero rather than whatever the page holds.
-template <int D, bool PAGED>
+//
+// EARLY: the mass-threshold early stop ([S2O-ja] "S2O: オンライン置換によるスパースアテンション
+// の早期停止", section "2. 早期停止ルール"): the list (one chunk, at most 64 entries) is
+// sorted in the wave by descending order key after the current block; per query head the
+// softmax mass a block adds is compared with the mass accumulated before it, the block is
+// kept and, once the ratio falls below tau, that head takes no further block. The wave
+// stops copying when every head has stopped.
+template <int D, bool PAGED, bool EARLY>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   constexpr int HE = 32 * D;   // elements of a 32-row half tile
   __shared__ __attribute__((aligned(16))) uint16_t sk0[HE];
@@ -89,6 +96,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       v = pg;
       if (pg < 0 || pg >= a.num_pages) { v = -1; g = -INFINITY; }
     }
+    if (EARLY) {
+      // bitonic sort of the 64 entries by (order key descending, block ascending); the
+      // current block (position 0) first, unused positions last
+      float key = t == 0 ? INFINITY : -INFINITY;
+      int ord = t == 0 ? -1 : 0x7FFFFFFF;
+      if (t > 0 && t < t1) {
+        key = a.order[bh * a.kcap + t - 1];
+        if (key != key) key = -INFINITY;
+        ord = v;
+      }
+      for (int kk = 2; kk <= 64; kk <<= 1)
+        for (int j = kk >> 1; j > 0; j >>= 1) {
+          const float pk = __shfl_xor(key, j, 64);
+          const int po = __shfl_xor(ord, j, 64), pv = __shfl_xor(v, j, 64);
+          const float pg = __shfl_xor(g, j, 64);
+          const bool mine_first = key > pk || (key == pk && ord < po);
+          const bool want_first = ((lane & j) == 0) == ((lane & kk) == 0);
+          if (mine_first != want_first && !(key == pk && ord == po)) { key = pk; ord = po; v = pv; g = pg; }
+        }
+    }
   };
   LaneList lstf;   // the same list for the copies, which run ahead
   const int nhalf = 2 * (t1 - t0);
@@ -132,6 +159,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const int rx0 = ql * D + ((hl ^ Tile<D>::swz(ql)) << 3);
   const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
 
+  // early stop state per query column: stopped, history blocks taken, the block's mass
+  // so far (this lane's rows) and the column's mass before the block (same frame)
+  bool done = !EARLY || ql >= G;
+  int used = 0;
+  float dlb = 0.0f, lbefore = 0.0f;
   int uc = 0;   // half block being computed
   auto step = [&](const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     wait_vm_n<2 * PER>();   // this half block has landed; the next two may still be in flight
@@ -176,18 +208,26 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float bmax = mx * c2 + lg2;
+    const bool hist_block = EARLY && (t0 + (u >> 1)) > 0;
+    if (hist_block && (u & 1) == 0) {   // a history block starts
+      dlb = 0.0f;
+      lbefore = lrow + __shfl_xor(lrow, 32, 64);
+    }
     if (__any(bmax > mref + kDecRescaleThreshold)) {
       const float mnew = fmaxf(mref, bmax);
       const float alpha = mnew == -INFINITY ? 1.0f : fast_exp2(mref - mnew);
       mref = mnew;
       lrow *= alpha;
+      if (EARLY) { dlb *= alpha; lbefore *= alpha; }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
     }
-    // a column whose reference is still -inf has seen only masked keys: weight 0
-    const float off = mref == -INFINITY ? -INFINITY : lg2 - mref;
+    // a column whose reference is still -inf has seen only masked keys: weight 0; a
+    // stopped column takes no further block
+    const bool skip = EARLY && hist_block && done;
+    const float off = (mref == -INFINITY || skip) ? -INFINITY : lg2 - mref;
     float ls = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -196,6 +236,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       ls += p;
     }
     lrow += ls;
+    if (hist_block) {
+      dlb += ls;
+      if (u & 1) {   // the block is complete: keep it, and stop once its mass is small
+        const float dl = dlb + __shfl_xor(dlb, 32, 64);
+        if (!done) {
+          ++used;
+          if (dl < a.tau * lbefore) done = true;
+        }
+      }
+    }
     bf16x8 pf[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -212,16 +262,21 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   fetch(sk1, sv1);
   fetch(sk2, sv2);
   const int nfull = nhalf & ~3;
+  bool stopped = false;
   for (int it = 0; it < nfull; it += 4) {
     step(sk0, sv0, sk3, sv3);
     step(sk1, sv1, sk0, sv0);
     step(sk2, sv2, sk1, sv1);
     step(sk3, sv3, sk2, sv2);
+    if (EARLY && __all(done)) { stopped = true; break; }   // every head has stopped
   }
-  if (nfull < nhalf) step(sk0, sv0, sk3, sv3);
-  if (nfull + 1 < nhalf) step(sk1, sv1, sk0, sv0);
-  if (nfull + 2 < nhalf) step(sk2, sv2, sk1, sv1);
+  if (!stopped) {
+    if (nfull < nhalf) step(sk0, sv0, sk3, sv3);
+    if (nfull + 1 < nhalf) step(sk1, sv1, sk0, sv0);
+    if (nfull + 2 < nhalf) step(sk2, sv2, sk1, sv1);
+  }
   wait_vm();
+  if (EARLY && a.used != nullptr && hl == 0 && ql < G) a.used[(size_t)b * a.Hq + h * G + ql] = used;
 
   const float l = lrow + __shfl_xor(lrow, 32, 64);
   if (a.nchunk == 1) {
@@ -295,18 +350,21 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   // Enough chunks for about SAS_DEC_TARGET_WG workgroups, at least 2 blocks per chunk.
   int chunks = (int)((SAS_DEC_TARGET_WG + pairs - 1) / pairs);
   chunks = max(1, min(chunks, (nblk + 1) / 2));
+  if (a.order != nullptr) chunks = 1;   // the early stop walks one sorted list per head
   a.bpc = (nblk + chunks - 1) / chunks;
   a.nchunk = (nblk + a.bpc - 1) / a.bpc;
   const unsigned grid = (unsigned)(pairs * a.nchunk);
   {
     ProfScope prof("decode", st);
-    const bool paged = a.page_table != nullptr;
+    const bool paged = a.page_table != nullptr, early = a.order != nullptr;
     if (a.d == 128) {
-      if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true>), dim3(grid), dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((decode_split_kernel<128, false>), dim3(grid), dim3(64), 0, st, a);
+      if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<128, false, false>), dim3(grid), dim3(64), 0, st, a);
     } else {
-      if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true>), dim3(grid), dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((decode_split_kernel<64, false>), dim3(grid), dim3(64), 0, st, a);
+      if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<64, false, false>), dim3(grid), dim3(64), 0, st, a);
     }
   }
   if (a.nchunk > 1) {

@@ -239,6 +239,34 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode launch");
 }
 
+sas_status sas_decode_early_stop(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                                 int Lmax, const int32_t* idx, const int32_t* cnt, const float* order,
+                                 int B, int Hq, int Hkv, int d, int block, int kcap, float scale,
+                                 float tau, void* o, int32_t* used, void* stream) {
+  REQUIRE(q && Kc && Vc && kv_len && cnt && order && o, SAS_ERR_INVALID_ARG,
+          "q, Kc, Vc, kv_len, cnt, order, o must be non-NULL");
+  REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
+  REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && Lmax > 0, SAS_ERR_INVALID_ARG, "B, Hq, Hkv, Lmax must be > 0");
+  REQUIRE(Hq % Hkv == 0, SAS_ERR_INVALID_ARG, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  REQUIRE(Hq / Hkv <= 32, SAS_ERR_UNSUPPORTED, "decode supports Hq/Hkv <= 32 (got %d)", Hq / Hkv);
+  REQUIRE((long long)Lmax * d * 2 < (1ll << 31), SAS_ERR_UNSUPPORTED,
+          "Lmax * d * 2 bytes must be < 2^31 (one cache row range per buffer resource)");
+  REQUIRE(block == 64, SAS_ERR_UNSUPPORTED, "block must be 64 (got %d)", block);
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  REQUIRE(kcap >= 0 && kcap <= 63, SAS_ERR_UNSUPPORTED, "the early stop sorts at most 63 blocks (kcap=%d)", kcap);
+  REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  REQUIRE(isfinite(tau) && tau >= 0.0f, SAS_ERR_INVALID_ARG, "tau must be finite and >= 0");
+  REQUIRE(aligned16(q) && aligned16(Kc) && aligned16(Vc) && aligned16(o), SAS_ERR_INVALID_ARG,
+          "q, Kc, Vc, o must be 16-byte aligned");
+  sas::DecodeArgs a{};
+  a.q = (const uint16_t*)q; a.Kc = (const uint16_t*)Kc; a.Vc = (const uint16_t*)Vc;
+  a.kv_len = kv_len; a.Lmax = Lmax; a.idx = idx; a.cnt = cnt; a.logg = nullptr;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.kcap = kcap; a.scale = scale;
+  a.o = (uint16_t*)o; a.part = nullptr;
+  a.order = order; a.tau = tau; a.used = used;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_early_stop launch");
+}
+
 sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool, int num_pages,
                             const int32_t* page_table, int max_pages, const int32_t* kv_len,
                             const int32_t* idx, const int32_t* cnt, const float* logg, int B, int Hq,

@@ -132,6 +132,11 @@ struct DecodeArgs {
   // block m of sequence b lives in page page_table[b * max_pages + m]; Lmax = 64 max_pages
   const int32_t* page_table;
   int max_pages, num_pages;
+  // early stop (order != null): order key of each kept block [B][Hkv][kcap], threshold,
+  // blocks used per query head [B][Hq] (nullable)
+  const float* order;
+  float tau;
+  int32_t* used;
 };
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap);
 hipError_t launch_decode(DecodeArgs a, hipStream_t st);

@@ -37,6 +37,7 @@ SIGNATURES = {
     "sas_topk_select": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P], _I),
     "sas_gates_bwd": ([_P, _I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I, _P, _P], _I),
     "sas_pool_keys": ([_P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "sas_decode_early_stop": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _P, _P, _P], _I),
     "sas_decode_paged": ([_P, _P, _P, _I, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
     "sas_decode_select": ([_P, _P, _I, _I, _I, _I, _I, _P, _F, _I, _I, _P, _P, _P, _P, _P, _P], _I),
     "sas_attn_fwd": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _P], _I),
@@ -243,6 +244,25 @@ def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None)
                             B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
                             _stream(q.device)))
     return o
+
+
+def sas_decode_early_stop(q, Kc, Vc, kv_len, idx, cnt, order, scale, tau, out=None, used=None):
+    """q bf16 [B, Hq, d]; Kc, Vc bf16 [B, Hkv, Lmax, d]; kv_len int32 [B]; idx int32 and order
+    fp32 [B, Hkv, kcap] (kcap <= 63); cnt int32 [B, Hkv]. Returns (o bf16 [B, Hq, d],
+    used int32 [B, Hq])."""
+    for t, nm in ((q, "q"), (Kc, "Kc"), (Vc, "Vc")):
+        _need(t, torch.bfloat16, nm)
+    _need(kv_len, torch.int32, "kv_len")
+    _need(order, torch.float32, "order")
+    B, Hq, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    kcap = idx.shape[-1]
+    o = torch.empty_like(q) if out is None else out
+    u = torch.empty((B, Hq), dtype=torch.int32, device=q.device) if used is None else used
+    _check(lib().sas_decode_early_stop(_ptr(q), _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, _ptr(idx), _ptr(cnt),
+                                       _ptr(order), B, Hq, Hkv, d, BLOCK, kcap, float(scale), float(tau), _ptr(o),
+                                       _ptr(u), _stream(q.device)))
+    return o, u
 
 
 def sas_decode_paged(q, Kpool, Vpool, page_table, kv_len, idx, cnt, scale, logg=None, ws=None, out=None):

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -205,6 +205,18 @@ def test_decode_paged_rejects():
                        (11, 66, sas.SAS_ERR_UNSUPPORTED), (5, 1 << 25, sas.SAS_ERR_UNSUPPORTED)):
         bad = list(args); bad[i] = v      # Hq = 66 over Hkv = 2 is a group of 33 > 32
         assert L.sas_decode_paged(*bad) == code, (i, v)
+
+
+def test_decode_early_stop_rejects():
+    L = sas.lib()
+    # q, Kc, Vc, kv_len, Lmax, idx, cnt, order, B, Hq, Hkv, d, block, kcap, scale, tau, o, used, stream
+    args = [FAKE, FAKE, FAKE, FAKE, 1024, FAKE, FAKE, FAKE, 2, 8, 2, 128, 64, 16, 0.1, 0.01, FAKE, NULL, NULL]
+    for i, v, code in ((7, NULL, sas.SAS_ERR_INVALID_ARG), (13, 64, sas.SAS_ERR_UNSUPPORTED),
+                       (15, -0.5, sas.SAS_ERR_INVALID_ARG), (15, float("nan"), sas.SAS_ERR_INVALID_ARG),
+                       (12, 32, sas.SAS_ERR_UNSUPPORTED), (9, 7, sas.SAS_ERR_INVALID_ARG),
+                       (16, NULL, sas.SAS_ERR_INVALID_ARG), (14, 0.0, sas.SAS_ERR_INVALID_ARG)):
+        bad = list(args); bad[i] = v
+        assert L.sas_decode_early_stop(*bad) == code, (i, v)
 
 
 def test_profile_toggle_without_gpu():

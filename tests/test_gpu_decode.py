@@ -125,3 +125,63 @@ def test_decode_paged_groups_and_gated():
 def test_decode_paged_large_batch():
     """64 sequences (one chunk per (sequence, KV head), the direct-output path)."""
     _paged_case(64, 32, 8, 128, [4096 - 13 * b for b in range(64)], 16, seed=4, npages_extra=5)
+
+
+def _early_case(B, Hq, Hkv, d, Lmax, kv_len, topk, taus, seed):
+    """Early-stopped decode against the oracle: the order key is the selection score
+    itself (exact on both sides); for each tau, heads whose every stop comparison is far
+    from the threshold (the oracle reports the margin) must use the same number of
+    blocks and give the same output."""
+    log(f"early-stop decode B={B} Hq={Hq} Hkv={Hkv} d={d} K={topk} taus={taus}")
+    q_bits = synth.normal_bf16((B, Hq, 1, d), seed, synth.TID_QDEC)[:, :, 0]
+    k_bits = synth.normal_bf16((B, Hkv, Lmax, d), seed, synth.TID_K)
+    v_bits = synth.normal_bf16((B, Hkv, Lmax, d), seed, synth.TID_V)
+    C = (Lmax + 63) // 64
+    s = synth.scores_normal((B, Hkv, 1, C), seed)
+    kv_len = np.asarray(kv_len, np.int32)
+    row_valid = ((kv_len - 1) // 64).astype(np.int32)
+    kcap = min(topk, C)
+    idx_r, cnt_r, _, _ = oracle.select(s.reshape(B * Hkv, C), np.repeat(row_valid, Hkv), topk, kcap=kcap)
+    idx_r = idx_r.reshape(B, Hkv, kcap); cnt_r = cnt_r.reshape(B, Hkv)
+    order = np.zeros((B, Hkv, kcap), np.float32)
+    for b in range(B):
+        for h in range(Hkv):
+            c = cnt_r[b, h]
+            order[b, h, :c] = s[b, h, 0, idx_r[b, h, :c]]
+    Q, K, V = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits)
+    idx, cnt = dev(idx_r), dev(cnt_r)
+    scale = 1.0 / math.sqrt(d)
+    qf, Kf, Vf = (synth.bf16_bits_to_f32(x) for x in (q_bits, k_bits, v_bits))
+    for tau in taus:
+        o, used = sas.sas_decode_early_stop(Q, K, V, dev(kv_len), idx, cnt, dev(order), scale, tau)
+        torch.cuda.synchronize()
+        o_r, used_r, _ = oracle.decode_early_stop(qf, Kf, Vf, kv_len, idx_r, cnt_r, order, scale, tau)
+        ug, og = host(used), host(o)
+        # per-head margins: recompute each head alone to know whether its decisions are safe
+        safe = np.zeros((B, Hq), bool)
+        G = Hq // Hkv
+        for b in range(B):
+            for hq in range(Hq):
+                h = hq // G
+                _, _, mg = oracle.decode_early_stop(qf[b:b + 1, hq:hq + 1], Kf[b:b + 1, h:h + 1], Vf[b:b + 1, h:h + 1],
+                                                    kv_len[b:b + 1], idx_r[b:b + 1, h:h + 1], cnt_r[b:b + 1, h:h + 1],
+                                                    order[b:b + 1, h:h + 1], scale, tau)
+                safe[b, hq] = mg > 1e-3
+        cnt_q = np.repeat(cnt_r, G, axis=1)
+        assert np.all((ug >= np.minimum(cnt_q, 1)) & (ug <= cnt_q))
+        assert np.array_equal(ug[safe], used_r[safe]), tau
+        log(f"  tau={tau}: blocks used mean {ug.mean():.2f} of {cnt_q.mean():.2f}; {safe.mean():.0%} heads compared")
+        if safe.any():
+            assert_close(f"o early stop tau={tau}", og[safe], o_r[safe])
+        if tau == 0.0:
+            assert np.array_equal(ug, cnt_q)
+            assert_close("o tau=0 vs oracle decode", og, oracle.decode(qf, Kf, Vf, kv_len, idx_r, cnt_r, scale))
+
+
+def test_decode_early_stop_thresholds():
+    _early_case(4, 8, 2, 128, 4096, [4096, 1000, 65, 64 * 40 + 7], 16, [0.0, 1e-3, 0.01, 0.05, 0.5], seed=7)
+
+
+def test_decode_early_stop_groups_small_d():
+    _early_case(3, 5, 1, 64, 2048, [2048, 777, 130], 12, [0.0, 0.02], seed=8)
+    _early_case(2, 32, 8, 128, 64 * 100, [6400, 3000], 63, [0.005, 0.1], seed=9)
