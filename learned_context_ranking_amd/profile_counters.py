@@ -25,7 +25,7 @@ KERNELS = {
     "dkv": ("dkv_pipe_kernel", ["attn_bwd.hip", "sas_common.h"]),
     "dq": ("dq_kernel", ["attn_bwd.hip", "sas_common.h"]),
     "fwd": ("fwd_kernel", ["attn_fwd.hip", "sas_common.h"]),
-    "decode": ("decode_split_kernel<128, false>", ["decode.hip", "sas_common.h"]),
+    "decode": ("decode_split_kernel<128, false, false>", ["decode.hip", "sas_common.h"]),
 }
 CALIB_BYTES = 256 << 20
 
