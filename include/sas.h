@@ -181,7 +181,7 @@ sas_status sas_gates_bwd(const float* s, int B, int H, int rows, int cols, int l
  *            entries outside [0, j) are ignored. cnt is clamped to [0, min(kcap, j)].
  *            logg may be NULL: every kept block then has gate 1 (ungated sparse attention).
  *   n        multiple of 64.  d in {64, 128}.  block must be 64.  kcap >= 0.
- *   scale    finite, > 0 (typically 1/sqrt(d)).
+ *   scale    finite, >= 1e-30 (typically 1/sqrt(d)).
  *   placement sas_gate_placement. OUTSIDE: the softmax runs over the ungated logits of S
  *            (a block whose gate is 0 still counts in the normaliser) and each probability
  *            is multiplied by its block's gate before the V product.

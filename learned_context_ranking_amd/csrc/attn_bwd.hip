@@ -170,8 +170,12 @@ void dq_kernel(const AttnArgs a, int nsplit) {
     for (int e = 0; e < 8; ++e) dlt += bf2f(ov[e]) * (float)dof[ks][e];
   }
   dlt += __shfl_xor(dlt, 32, 64);
-  if (active && hl == 0) a.delta[row_off + ql] = dlt;
-  const float lse2 = a.lse_rows[row_off + ql] * kLog2e;
+  const float lse = a.lse_rows[row_off + ql];
+  if (active && hl == 0) {
+    a.ndelta[row_off + ql] = -dlt;
+    a.nlse[row_off + ql] = -lse / a.scale;
+  }
+  const float lse2 = lse * kLog2e;
 
   // per-lane byte offsets of this wave's 16-byte slots within a 64-row tile
   constexpr int NWIN = Tile<D>::CPR / NW;
@@ -370,22 +374,27 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 // registers for the whole list. The two query halves are summed through LDS at the end.
 // The items (the query blocks that selected m, then m itself, for each of the G heads)
 // stream through a ring of 4 LDS buffer sets (distinct LDS objects selected at compile
-// time, so the compiler never waits for a copy in flight before computing): item it
-// (transposed reads), item it+1 (row reads), item it+2 (copy in flight), and the ring
-// receives item it+3. The copies are buffer loads into LDS addressed by a per-lane
-// constant offset plus a scalar per-item offset; in the swizzled Tile layout each operand
-// read is a laundered lane base XORed with a constant plus an immediate.
-// The pass is software-pipelined across items: with one wave per SIMD the matrix and
-// vector pipes only overlap when the instruction stream interleaves them, so step it
-// issues each S / dP product of item it+1 followed by one element of item it's softmax
-// (scheduling barriers keep that order), then item it's dV / dK products.
+// time, so the compiler never waits for a copy in flight before computing). The copies
+// are buffer loads into LDS addressed by a per-lane constant offset plus a scalar
+// per-item offset; in the swizzled Tile layout each operand read is a laundered lane base
+// XORed with a constant plus an immediate.
+//
+// Each item t is handled in two halves, software-pipelined so that with one wave per SIMD
+// the matrix pipe always has independent work next to the vector, LDS and copy work:
+//   A(t): the S / dP products of item t+1, each followed by one element of item t's
+//         softmax, with the transposed reads of item t's Q and dO spread over them;
+//   B(t): item t's dV / dK products, with the wait for item t+2's copy, the barrier, the
+//         copy of item t+4 into item t's buffers and the row reads of item t+2 between them.
+// The S and dP accumulators start from -LSE / scale and -delta of their rows (written by
+// the query-major pass), so the softmax element is exp2(c S' + log2 g) and dS = P dP';
+// the causal mask of the diagonal items is folded into the same start value.
 template <int D, bool OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void dkv_pipe_kernel(const AttnArgs a) {
+void dkv_kernel(const AttnArgs a) {
   constexpr int NW = 4;
   constexpr int TE = Tile<D>::ELEMS;
-  // Q tile + lse / delta rows: every wave copies one 64-float row behind the tile
-  // (wave 1 delta, the others lse; rows 2 and 3 are spare copies)
+  // Q tile + two 64-float rows (-LSE / scale copied by wave 0, -delta by wave 1; waves 2
+  // and 3 copy spare rows so that every wave issues the same number of copies)
   constexpr int TQ = TE + 4 * 128;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
@@ -420,12 +429,18 @@ void dkv_pipe_kernel(const AttnArgs a) {
   for (int ks = 0; ks < D / 16; ++ks) {
     kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 16 * ks + 8 * hl));
     vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 16 * ks + 8 * hl));
+    // K / V fragments and the dK / dV accumulators only ever feed the matrix cores: keep
+    // them in AGPRs, which leaves the VGPRs to the values the vector ALU touches (fewer
+    // copies between the two files per item)
+    asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
   }
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+    asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+  }
   const float c2 = a.scale * kLog2e;
   const int g16 = lane >> 4, lp = lane & 15;
   const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
@@ -436,12 +451,13 @@ void dkv_pipe_kernel(const AttnArgs a) {
   const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
   const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
   const int nitems = (nlist + 1) * G;
+  const int ndiag0 = nlist * G;   // items from here on are the diagonal block m itself
 
   const size_t head0 = (size_t)(b * a.Hq + h * G) * a.n;
   const int qbytes = G * a.n * D * 2, rbytes = G * a.n * 4;
   const uint16_t* qbase = a.Q + head0 * D;
   const uint16_t* obase = a.dO + head0 * D;
-  const float* rbase = (wave == 1 ? a.delta : a.lse_rows) + head0;
+  const float* rbase = (wave == 1 ? a.ndelta : a.nlse) + head0;
   constexpr int NWIN = Tile<D>::CPR / NW;
   uint32_t voff[NWIN];
 #pragma unroll
@@ -461,84 +477,105 @@ void dkv_pipe_kernel(const AttnArgs a) {
     }
   };
   LaneList lst_c, lst_f;
-  int ec = 0, gc = 0, ef = 0, gf = 0;   // item being finished; next item to copy
-  auto fetch = [&](uint16_t* qb, uint16_t* ob) {
+  int ec = 0, gc = 0, ef = 0, gf = 0;   // item whose softmax is next; next item to copy
+  // The copy of one item is PER buffer loads per wave: NWIN windows of Q, NWIN of dO and
+  // one row of per-row values. fetch_row() returns the item's first global row (and
+  // advances to the next item); fetch_part() issues loads [c0, c1) of it.
+  constexpr int PER = 2 * NWIN + 1;
+  static_assert(2 * PER < 64, "copies in flight exceed the vmcnt range");
+  auto fetch_row = [&]() -> uint32_t {
     int jj = m;
     if (ef < nlist) {
       lst_f.ensure(ef, lane, load_lst);
       jj = lst_f.at(ef);
     }
     const uint32_t row = (uint32_t)(gf * a.n + jj * kBlock);
-    const uint32_t so = row * (uint32_t)(D * 2);
-#pragma unroll
-    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(qbase, qbytes, qb + 512 * (wave + NW * i), voff[i], so);
-#pragma unroll
-    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(obase, qbytes, ob + 512 * (wave + NW * i), voff[i], so);
-    buffer_load_lds4(rbase, rbytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
     if (!(ef == nlist && gf == G - 1)) {
       if (++gf == G) { gf = 0; ++ef; }
     }
+    return row;
   };
-  constexpr int PER = 2 * NWIN + 1;
-  static_assert(2 * PER < 64, "copies in flight exceed the vmcnt range");
+  auto fetch_part = [&](uint16_t* qb, uint16_t* ob, uint32_t row, int c0, int c1) {
+    const uint32_t so = row * (uint32_t)(D * 2);
+#pragma unroll
+    for (int c = c0; c < c1; ++c) {
+      if (c < NWIN) buffer_load_lds16(qbase, qbytes, qb + 512 * (wave + NW * c), voff[c], so);
+      else if (c < 2 * NWIN) buffer_load_lds16(obase, qbytes, ob + 512 * (wave + NW * (c - NWIN)), voff[c - NWIN], so);
+      else buffer_load_lds4(rbase, rbytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
+    }
+  };
+  auto fetch = [&](uint16_t* qb, uint16_t* ob) { fetch_part(qb, ob, fetch_row(), 0, PER); };
 
-  // row reads of the item in (qn, on) for its S^T and dP^T products
-  auto row_reads = [&](const uint16_t* qn, const uint16_t* on, bf16x8 (&qr)[D / 16], bf16x8 (&orw)[D / 16]) {
+  // Row operands of the item two ahead: Q / dO rows of this wave's queries and the start
+  // values of its S / dP accumulators (rows 32 qh + 8 grp + 4 hl + x, element 4 grp + x).
+  bf16x8 qr[D / 16], orw[D / 16];
+  f32x4 cl[4], cd[4];
+  auto row_reads_c = [&](const uint16_t* qn) {
+    const float* lr = reinterpret_cast<const float*>(qn + TE);
+    const float* dr = reinterpret_cast<const float*>(qn + TE + 128);
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      cl[grp] = *reinterpret_cast<const f32x4*>(&lr[32 * qh + 8 * grp + 4 * hl]);
+      if (!OUT) cd[grp] = *reinterpret_cast<const f32x4*>(&dr[32 * qh + 8 * grp + 4 * hl]);
+    }
+  };
+  auto row_reads_q = [&](const uint16_t* qn, const uint16_t* on, int k0, int k1) {
     int rx = rx0;
     asm volatile("" : "+v"(rx));
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int ks = k0; ks < k1; ++ks) {
       qr[ks] = as_bf16x8(ld16(&qn[rx ^ (ks << 4)]));
       orw[ks] = as_bf16x8(ld16(&on[rx ^ (ks << 4)]));
     }
   };
-  // step: item it in (qc, oc) with S^T / dP^T in (sc, dpc); item it+1 in (qn, on), whose
-  // products go to (sn, dpn); the next copy goes to (qf, of)
-  auto step = [&](const uint16_t* qc, const uint16_t* oc, const uint16_t* qn, const uint16_t* on,
-                  uint16_t* qf, uint16_t* of, const f32x16& sc, const f32x16& dpc, f32x16& sn,
-                  f32x16& dpn) {
-    wait_vm_n<PER>();   // item it+1 has landed; item it+2 may be in flight
-    barrier_lds();
-    int jj = m;
+  auto cat16 = [](const f32x4 (&c)[4]) -> f32x16 {
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    const f32x8 lo = __builtin_shufflevector(c[0], c[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const f32x8 hi = __builtin_shufflevector(c[2], c[3], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  };
+  // start values of S and dP for the item whose rows are in (cl, cd); diagonal items
+  // start masked entries (key after query) at -1e30, so their softmax weight is exactly 0
+  auto start = [&](int t, f32x16& s0, f32x16& dp0) {
+    s0 = cat16(cl);
+    dp0 = OUT ? f32x16{} : cat16(cd);
+    if (t >= ndiag0) {
+      int kk = key;
+      asm volatile("" : "+v"(kk));   // a branch, not a select, on this uniform condition
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (kk > 32 * qh + 8 * (i >> 2) + 4 * hl + (i & 3)) s0[i] = -1e30f;
+    }
+  };
+
+  // A(t) and B(t) for one item. (qx, ox): item t's buffers (transposed reads, then the copy
+  // of item t+4); (qy, oy): item t+2's buffers (row reads). (sc, dpc): S' / dP' of item t;
+  // (sn, dpn) receive those of item t+1.
+  auto step = [&](int t, uint16_t* qx, uint16_t* ox, const uint16_t* qy, const uint16_t* oy,
+                  const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
+    // every read of the previous B has landed (its row operands feed the products below)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
     float lg2 = 0.0f;
     if (ec < nlist) {
       lst_c.ensure(ec, lane, load_lst);
-      jj = lst_c.at(ec);
       lg2 = lst_c.gat(ec);
     }
-    const bool diag = ec == nlist;
     const float gmul = OUT ? fast_exp2(lg2) : 1.0f;   // the item's gate (1 on the diagonal)
     if (++gc == G) { gc = 0; ++ec; }
-    fetch(qf, of);
-    // lse / delta rows of item it first (the softmax waits on them), then the row reads
-    f32x4 l4[4], d4[4];
-    const float* lc = reinterpret_cast<const float*>(qc + TE);
-    const float* dc = reinterpret_cast<const float*>(qc + TE + 128);
+    f32x4 nd4[4];
+    if (OUT) {
+      const float* dc = reinterpret_cast<const float*>(qx + TE + 128);
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {   // rows 32 qh + 8 grp + 4 hl + x
-      l4[grp] = *reinterpret_cast<const f32x4*>(&lc[32 * qh + 8 * grp + 4 * hl]);
-      d4[grp] = *reinterpret_cast<const f32x4*>(&dc[32 * qh + 8 * grp + 4 * hl]);
+      for (int grp = 0; grp < 4; ++grp) nd4[grp] = *reinterpret_cast<const f32x4*>(&dc[32 * qh + 8 * grp + 4 * hl]);
     }
-    bf16x8 qr[D / 16], orw[D / 16];
-    row_reads(qn, on, qr, orw);
-    // transposed operands of item it
-    bf16x8 da[D / 32][2], qa[D / 32][2];
+    start(t + 1, sn, dpn);
+    // transposed operands of item t, two reads per softmax element
+    i16x4 trv[D / 32][2][2][2];   // [dt][hh][dO / Q][row half]
     int tx = tx0;
     asm volatile("" : "+v"(tx));
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int r0 = 32 * qh + 16 * hh;
-        const int o0 = r0 * D + (tx ^ ((4 * dt) << 3)), o1 = (r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3));
-        da[dt][hh] = join_tr16(lds_tr16(&oc[o0]), lds_tr16(&oc[o1]));
-        qa[dt][hh] = join_tr16(lds_tr16(&qc[o0]), lds_tr16(&qc[o1]));
-      }
-    // S / dP products of item it+1 interleaved with item it's softmax, one element each
-    sn = f32x16{};
-    dpn = f32x16{};
     float pv[16], dsv[16];
     constexpr int NM = 2 * (D / 16);   // S and dP products, spread evenly over the 16 elements
+    constexpr int NTR = (D / 32) * 8;  // transposed reads
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       if ((e * NM) % 16 == 0) {
@@ -546,19 +583,25 @@ void dkv_pipe_kernel(const AttnArgs a) {
         if ((j & 1) == 0) sn = mfma32(qr[ks], kf[ks], sn);
         else dpn = mfma32(orw[ks], vf[ks], dpn);
       }
+#pragma unroll
+      for (int u = 0; u < NTR / 16; ++u) {
+        const int r = e * (NTR / 16) + u;   // (dt, hh, src, half) = r in mixed radix
+        const int half = r & 1, src = (r >> 1) & 1, hh = (r >> 2) & 1, dt = r >> 3;
+        const int r0 = 32 * qh + 16 * hh + 8 * half;
+        const int o = r0 * D + (tx ^ (((4 * dt) ^ (2 * half)) << 3));
+        trv[dt][hh][src][half] = lds_tr16(src == 0 ? &ox[o] : &qx[o]);
+      }
       const int grp = e >> 2, x = e & 3;
       if (OUT) {
         // gate after the softmax: p~ from the ungated LSE, weights p~ g for dV,
         // dS = p~ (g dP - delta)
-        float p = fast_exp2(sc[e] * c2 - l4[grp][x] * kLog2e);
-        if (diag && key > 32 * qh + 8 * grp + 4 * hl + x) p = 0.0f;   // causal mask of block m
+        const float p = fast_exp2(sc[e] * c2);
         pv[e] = p * gmul;
-        dsv[e] = p * (gmul * dpc[e] - d4[grp][x]);
+        dsv[e] = p * (gmul * dpc[e] + nd4[grp][x]);
       } else {
-        float p = fast_exp2(sc[e] * c2 + (lg2 - l4[grp][x] * kLog2e));
-        if (diag && key > 32 * qh + 8 * grp + 4 * hl + x) p = 0.0f;   // causal mask of block m
+        const float p = fast_exp2(fmaf(sc[e], c2, lg2));
         pv[e] = p;
-        dsv[e] = p * (dpc[e] - d4[grp][x]);
+        dsv[e] = p * dpc[e];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -569,44 +612,69 @@ void dkv_pipe_kernel(const AttnArgs a) {
       pb[hh] = pack8(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5], pv[o + 6], pv[o + 7]);
       sb[hh] = pack8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS for item it
+    // materialise the softmax here, next to its products (left alone, the compiler sinks it
+    // past the copy's branch into B)
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(sb[0]), "+v"(sb[1]));
+    __builtin_amdgcn_sched_barrier(0);
+    // B(t): dV^T += dO^T P and dK^T += Q^T dS for item t, two products per slot. The
+    // copy of item t+4 (into item t's buffers, after the barrier) and the row reads of item
+    // t+2 are spread over the slots: issued back to back, the copy's loads stall the wave
+    // on the vector memory queue for several products' worth of cycles.
+    constexpr int NQ = 2 * (D / 32);
+    static_assert(NQ >= 4, "slots for the barrier, the copy and the row reads");
+    constexpr int CPS = (PER + NQ - 2) / (NQ - 1);   // copies per slot from slot 1 on
+    uint32_t frow = 0;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        dv[dt] = mfma32(da[dt][hh], pb[hh], dv[dt]);
-        dk[dt] = mfma32(qa[dt][hh], sb[hh], dk[dt]);
+    for (int q = 0; q < NQ; ++q) {
+      const int hh = q / (D / 32), dt = q % (D / 32);
+      dv[dt] = mfma32(join_tr16(trv[dt][hh][0][0], trv[dt][hh][0][1]), pb[hh], dv[dt]);
+      dk[dt] = mfma32(join_tr16(trv[dt][hh][1][0], trv[dt][hh][1][1]), sb[hh], dk[dt]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q == 0) {
+        wait_vm_n<PER>();   // item t+2 has landed (this wave's share) ...
+        barrier_lds();      // ... everyone's, and every read of item t is done
+      } else {
+        if (q == 1) frow = fetch_row();
+        fetch_part(qx, ox, frow, min(PER, (q - 1) * CPS), min(PER, q * CPS));
+        if (q == 1) row_reads_c(qy);
+        else row_reads_q(qy, oy, (q - 2) * (D / 16) / (NQ - 2), (q - 1) * (D / 16) / (NQ - 2));
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
-  // prologue: items 0, 1, 2 in flight; S / dP of item 0
+  // prologue: copy items 0 and 1; B(-2): item 0's rows, copy of item 2; S / dP of item 0;
+  // B(-1): item 1's rows, copy of item 3
   fetch(sq0, so0);
   fetch(sq1, so1);
-  fetch(sq2, so2);
-  wait_vm_n<2 * PER>();
+  wait_vm_n<PER>();
   barrier_lds();
+  fetch(sq2, so2);
+  row_reads_c(sq0);
+  row_reads_q(sq0, so0, 0, D / 16);
   f32x16 sA, dpA, sB, dpB;
-  {
-    bf16x8 qr[D / 16], orw[D / 16];
-    row_reads(sq0, so0, qr, orw);
-    sA = f32x16{};
-    dpA = f32x16{};
+  start(0, sA, dpA);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      sA = mfma32(qr[ks], kf[ks], sA);
-      dpA = mfma32(orw[ks], vf[ks], dpA);
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    sA = mfma32(qr[ks], kf[ks], sA);
+    dpA = mfma32(orw[ks], vf[ks], dpA);
   }
-  const int nfull = nitems & ~3;
-  for (int it = 0; it < nfull; it += 4) {
-    step(sq0, so0, sq1, so1, sq3, so3, sA, dpA, sB, dpB);
-    step(sq1, so1, sq2, so2, sq0, so0, sB, dpB, sA, dpA);
-    step(sq2, so2, sq3, so3, sq1, so1, sA, dpA, sB, dpB);
-    step(sq3, so3, sq0, so0, sq2, so2, sB, dpB, sA, dpA);
+  wait_vm_n<PER>();
+  barrier_lds();
+  fetch(sq3, so3);
+  row_reads_c(sq1);
+  row_reads_q(sq1, so1, 0, D / 16);
+
+  int t = 0;
+  for (; t + 4 <= nitems; t += 4) {
+    step(t, sq0, so0, sq2, so2, sA, dpA, sB, dpB);
+    step(t + 1, sq1, so1, sq3, so3, sB, dpB, sA, dpA);
+    step(t + 2, sq2, so2, sq0, so0, sA, dpA, sB, dpB);
+    step(t + 3, sq3, so3, sq1, so1, sB, dpB, sA, dpA);
   }
-  if (nfull < nitems) step(sq0, so0, sq1, so1, sq3, so3, sA, dpA, sB, dpB);
-  if (nfull + 1 < nitems) step(sq1, so1, sq2, so2, sq0, so0, sB, dpB, sA, dpA);
-  if (nfull + 2 < nitems) step(sq2, so2, sq3, so3, sq1, so1, sA, dpA, sB, dpB);
+  if (t < nitems) step(t, sq0, so0, sq2, so2, sA, dpA, sB, dpB);
+  if (t + 1 < nitems) step(t + 1, sq1, so1, sq3, so3, sB, dpB, sA, dpA);
+  if (t + 2 < nitems) step(t + 2, sq2, so2, sq0, so0, sA, dpA, sB, dpB);
 
   // sum the two query halves through LDS (key half 0 uses sq0 / sq1, key half 1 so0 / so1)
   constexpr int PERW = (D / 32) * 16 * 64;
@@ -660,7 +728,7 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap) {
   const size_t bh = (size_t)B * Hkv;
   const size_t kc = (size_t)(kcap > 0 ? kcap : 1);
   const int ns = dq_splits(Hq / Hkv);
-  return al256((size_t)B * Hq * n * sizeof(float))            // delta
+  return 2 * al256((size_t)B * Hq * n * sizeof(float))        // -delta, -LSE / scale
          + al256(bh * NB * sizeof(int32_t))                    // counts
          + al256(bh * (NB + 1) * sizeof(int32_t))              // offsets
          + al256(bh * NB * kc * sizeof(int32_t))               // lists
@@ -702,8 +770,8 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   }
   {
     ProfScope prof("dkv", st);
-    if (a.gate_out) hipLaunchKernelGGL((dkv_pipe_kernel<D, true>), dim3((unsigned)nrows), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dkv_pipe_kernel<D, false>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+    if (a.gate_out) hipLaunchKernelGGL((dkv_kernel<D, true>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dkv_kernel<D, false>), dim3((unsigned)nrows), dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -713,7 +781,9 @@ hipError_t launch_bwd(AttnArgs a, void* ws, hipStream_t st) {
   const size_t bh = (size_t)a.B * a.Hkv;
   const size_t kc = (size_t)(a.kcap > 0 ? a.kcap : 1);
   char* p = (char*)ws;
-  a.delta = (float*)p;
+  a.ndelta = (float*)p;
+  p += al256((size_t)a.B * a.Hq * a.n * sizeof(float));
+  a.nlse = (float*)p;
   p += al256((size_t)a.B * a.Hq * a.n * sizeof(float));
   a.inv_cnt = (int32_t*)p;
   p += al256(bh * NB * sizeof(int32_t));

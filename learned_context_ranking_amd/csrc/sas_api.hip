@@ -71,7 +71,8 @@ sas_status check_attn(const void* Q, const void* K, const void* V, const int32_t
   REQUIRE(n % 64 == 0, SAS_ERR_INVALID_ARG, "n=%d is not a multiple of 64", n);
   REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
   REQUIRE(kcap >= 0 && kcap <= 8192, SAS_ERR_INVALID_ARG, "kcap=%d out of [0, 8192]", kcap);
-  REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
+  // the backward keeps -LSE / scale per row, finite for every finite LSE when scale >= 1e-30
+  REQUIRE(isfinite(scale) && scale >= 1e-30f, SAS_ERR_INVALID_ARG, "scale must be finite and >= 1e-30");
   REQUIRE(aligned16(Q) && aligned16(K) && aligned16(V), SAS_ERR_INVALID_ARG, "Q, K, V must be 16-byte aligned");
   REQUIRE((long long)B * Hq * n * d < (1ll << 40), SAS_ERR_UNSUPPORTED, "tensor too large");
   REQUIRE((long long)B * Hkv * (n / 64) < (1ll << 31) / 4, SAS_ERR_UNSUPPORTED, "too many blocks");

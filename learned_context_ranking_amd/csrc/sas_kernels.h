@@ -103,7 +103,8 @@ struct AttnArgs {
   float* dV;
   float* dg;
   // backward workspace pieces
-  float* delta;
+  float* ndelta;         // -delta_t = -dO_t . o_t per query row
+  float* nlse;           // -LSE_t / scale per query row (the score offset of the key-major pass)
   float* dg_part;        // [nsplit][rows][kcap] per-split gate-gradient partials
   int32_t* inv_cnt;
   int32_t* inv_off;

@@ -22,9 +22,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # kernel short name -> (substring of the device symbol, the sources its code comes from)
 KERNELS = {
-    "dkv": ("dkv_pipe_kernel", ["attn_bwd.hip", "sas_common.h"]),
-    "dq": ("dq_kernel", ["attn_bwd.hip", "sas_common.h"]),
-    "fwd": ("fwd_kernel", ["attn_fwd.hip", "sas_common.h"]),
+    "dkv": ("dkv_kernel<128, false>", ["attn_bwd.hip", "sas_common.h"]),
+    "dq": ("dq_kernel<128, false>", ["attn_bwd.hip", "sas_common.h"]),
+    "fwd": ("fwd_kernel<128, 1, 4, false>", ["attn_fwd.hip", "sas_common.h"]),
     "decode": ("decode_split_kernel<128, false, false>", ["decode.hip", "sas_common.h"]),
 }
 CALIB_BYTES = 256 << 20

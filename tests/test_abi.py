@@ -63,6 +63,7 @@ def _fwd(**kw):
     (dict(kcap=-1), sas.SAS_ERR_INVALID_ARG),
     (dict(scale=0.0), sas.SAS_ERR_INVALID_ARG),
     (dict(scale=float("nan")), sas.SAS_ERR_INVALID_ARG),
+    (dict(scale=1e-35), sas.SAS_ERR_INVALID_ARG),
     (dict(K=MIS), sas.SAS_ERR_INVALID_ARG),
     (dict(O=NULL), sas.SAS_ERR_INVALID_ARG),
     (dict(B=0), sas.SAS_ERR_INVALID_ARG),
