@@ -548,11 +548,20 @@ void dkv_kernel(const AttnArgs a) {
     }
   };
 
+  // The copy of an item is issued in two parts: loads [0, CB) in B right after the barrier
+  // that frees its buffers, loads [CB, PER) in the next A, one every few softmax elements.
+  // Issued together, the four waves' loads queue on the vector-memory path and stall each
+  // wave's instruction stream (and its matrix products) for several hundred cycles.
+  constexpr int CB = PER / 2;
+  constexpr int CA = PER - CB;
+  uint32_t crow = 0;   // global row of the item whose copy A finishes
+
   // A(t) and B(t) for one item. (qx, ox): item t's buffers (transposed reads, then the copy
-  // of item t+4); (qy, oy): item t+2's buffers (row reads). (sc, dpc): S' / dP' of item t;
-  // (sn, dpn) receive those of item t+1.
-  auto step = [&](int t, uint16_t* qx, uint16_t* ox, const uint16_t* qy, const uint16_t* oy,
-                  const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
+  // of item t+4); (qp, op): item t-1's buffers, receiving the rest of item t+3's copy;
+  // (qy, oy): item t+2's buffers (row reads). (sc, dpc): S' / dP' of item t; (sn, dpn)
+  // receive those of item t+1.
+  auto step = [&](int t, uint16_t* qx, uint16_t* ox, uint16_t* qp, uint16_t* op, const uint16_t* qy,
+                  const uint16_t* oy, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
     // every read of the previous B has landed (its row operands feed the products below)
     __builtin_amdgcn_s_waitcnt(0xC07F);
     float lg2 = 0.0f;
@@ -591,6 +600,10 @@ void dkv_kernel(const AttnArgs a) {
         const int o = r0 * D + (tx ^ (((4 * dt) ^ (2 * half)) << 3));
         trv[dt][hh][src][half] = lds_tr16(src == 0 ? &ox[o] : &qx[o]);
       }
+      if (e % (16 / CA) == 1 && e / (16 / CA) < CA) {
+        const int c = CB + e / (16 / CA);
+        fetch_part(qp, op, crow, c, c + 1);
+      }
       const int grp = e >> 2, x = e & 3;
       if (OUT) {
         // gate after the softmax: p~ from the ungated LSE, weights p~ g for dV,
@@ -616,14 +629,12 @@ void dkv_kernel(const AttnArgs a) {
     // past the copy's branch into B)
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(sb[0]), "+v"(sb[1]));
     __builtin_amdgcn_sched_barrier(0);
-    // B(t): dV^T += dO^T P and dK^T += Q^T dS for item t, two products per slot. The
-    // copy of item t+4 (into item t's buffers, after the barrier) and the row reads of item
-    // t+2 are spread over the slots: issued back to back, the copy's loads stall the wave
-    // on the vector memory queue for several products' worth of cycles.
+    // B(t): dV^T += dO^T P and dK^T += Q^T dS for item t, two products per slot, with the
+    // barrier, the row reads of item t+2 and the first part of item t+4's copy (into item
+    // t's buffers) between them
     constexpr int NQ = 2 * (D / 32);
-    static_assert(NQ >= 4, "slots for the barrier, the copy and the row reads");
-    constexpr int CPS = (PER + NQ - 2) / (NQ - 1);   // copies per slot from slot 1 on
-    uint32_t frow = 0;
+    constexpr int NR = NQ / 2;   // slots 1 .. NR carry the row reads
+    static_assert(NQ >= 4 && CB <= 2 * (NQ - 2), "slots for the barrier, the rows and the copy");
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
       const int hh = q / (D / 32), dt = q % (D / 32);
@@ -634,10 +645,12 @@ void dkv_kernel(const AttnArgs a) {
         wait_vm_n<PER>();   // item t+2 has landed (this wave's share) ...
         barrier_lds();      // ... everyone's, and every read of item t is done
       } else {
-        if (q == 1) frow = fetch_row();
-        fetch_part(qx, ox, frow, min(PER, (q - 1) * CPS), min(PER, q * CPS));
-        if (q == 1) row_reads_c(qy);
-        else row_reads_q(qy, oy, (q - 2) * (D / 16) / (NQ - 2), (q - 1) * (D / 16) / (NQ - 2));
+        if (q == 1) {
+          crow = fetch_row();
+          row_reads_c(qy);
+        }
+        if (q <= NR) row_reads_q(qy, oy, (q - 1) * (D / 16) / NR, q * (D / 16) / NR);
+        if (q >= 2) fetch_part(qx, ox, crow, min(CB, 2 * (q - 2)), min(CB, 2 * (q - 1)));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -661,20 +674,21 @@ void dkv_kernel(const AttnArgs a) {
   }
   wait_vm_n<PER>();
   barrier_lds();
-  fetch(sq3, so3);
+  crow = fetch_row();   // item 3: its first part here, the rest in A(0)
+  fetch_part(sq3, so3, crow, 0, CB);
   row_reads_c(sq1);
   row_reads_q(sq1, so1, 0, D / 16);
 
   int t = 0;
   for (; t + 4 <= nitems; t += 4) {
-    step(t, sq0, so0, sq2, so2, sA, dpA, sB, dpB);
-    step(t + 1, sq1, so1, sq3, so3, sB, dpB, sA, dpA);
-    step(t + 2, sq2, so2, sq0, so0, sA, dpA, sB, dpB);
-    step(t + 3, sq3, so3, sq1, so1, sB, dpB, sA, dpA);
+    step(t, sq0, so0, sq3, so3, sq2, so2, sA, dpA, sB, dpB);
+    step(t + 1, sq1, so1, sq0, so0, sq3, so3, sB, dpB, sA, dpA);
+    step(t + 2, sq2, so2, sq1, so1, sq0, so0, sA, dpA, sB, dpB);
+    step(t + 3, sq3, so3, sq2, so2, sq1, so1, sB, dpB, sA, dpA);
   }
-  if (t < nitems) step(t, sq0, so0, sq2, so2, sA, dpA, sB, dpB);
-  if (t + 1 < nitems) step(t + 1, sq1, so1, sq3, so3, sB, dpB, sA, dpA);
-  if (t + 2 < nitems) step(t + 2, sq2, so2, sq0, so0, sA, dpA, sB, dpB);
+  if (t < nitems) step(t, sq0, so0, sq3, so3, sq2, so2, sA, dpA, sB, dpB);
+  if (t + 1 < nitems) step(t + 1, sq1, so1, sq0, so0, sq3, so3, sB, dpB, sA, dpA);
+  if (t + 2 < nitems) step(t + 2, sq2, so2, sq1, so1, sq0, so0, sA, dpA, sB, dpB);
 
   // sum the two query halves through LDS (key half 0 uses sq0 / sq1, key half 1 so0 / so1)
   constexpr int PERW = (D / 32) * 16 * 64;
