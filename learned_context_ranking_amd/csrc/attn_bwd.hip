@@ -14,7 +14,8 @@
 //   2. query-major pass, one workgroup per (b, KV head, j, pair of query heads): delta_t =
 //      dO_t . o_t for its rows, dQ, and the workgroup's share of dg. Each dg_jm is owned by
 //      the workgroups of query block j; their per-split partials are summed in a fixed
-//      order by a small reduction kernel
+//      order by a small reduction kernel. Per row it also stores -delta_t and
+//      -LSE_t / scale, the start values of the key-major pass's dP and S accumulators
 //   3. key-major pass, one workgroup per (b, KV head, m): dK and dV over the current block
 //      m itself plus every query block that selected m, for all G heads
 //
