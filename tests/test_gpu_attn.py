@@ -28,12 +28,15 @@ CASES = [
     (1, 4, 1, 512, 128, 0, "full", True, "normal"),         # full scope
     (1, 4, 2, 512, 128, 4, "sparse", False, "normal"),      # ungated (logg = NULL)
     (3, 4, 1, 512, 128, 4, "sparse", True, "normal"),       # 3 (batch, KV head) pairs: odd launch phase
+    (1, 4, 1, 512, 128, 0, "sparse", True, "normal"),       # budget 0: the causal current block only
 ]
 
 
-def _run(case, seed=0):
+def _run(case, seed=0, scale=None):
     B, Hq, Hkv, n, d, topk, scope, gated, scores = case
     P = Prefill(B, Hq, Hkv, n, d, seed=seed, scores=scores)
+    if scale is not None:
+        P.scale = scale
     t = P.device()
     NB = P.NB
     kcap = NB - 1 if scope == "full" else topk
@@ -47,9 +50,9 @@ def _run(case, seed=0):
 
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}-{c[2]}n{c[3]}d{c[4]}K{c[5]}{c[6]}{'' if c[7] else '-ungated'}"
                                              for c in CASES])
-def test_fwd_bwd_parity(case):
-    log(f"fwd/bwd parity {case}")
-    P, g, gated, scope, topk = _run(case)
+def test_fwd_bwd_parity(case, scale=None):
+    log(f"fwd/bwd parity {case}" + ("" if scale is None else f" scale={scale}"))
+    P, g, gated, scope, topk = _run(case, scale=scale)
     idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk, full_scope=scope == "full",
                                                     kcap=g["idx"].shape[-1])
     assert np.array_equal(host(g["idx"]), idx_r) and np.array_equal(host(g["cnt"]), cnt_r)
@@ -63,6 +66,13 @@ def test_fwd_bwd_parity(case):
     assert_close("dK", host(g["dK"]), dK_r)
     assert_close("dV", host(g["dV"]), dV_r)
     assert_close("dg", host(g["dg"]), dg_r)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.02])
+def test_fwd_bwd_other_scales(scale):
+    """Logit scales other than 1/sqrt(d): the backward's key-major pass starts its score
+    accumulators at -LSE/scale, which grows as the scale shrinks."""
+    test_fwd_bwd_parity((1, 8, 2, 512, 128, 4, "sparse", True, "normal"), scale=scale)
 
 
 def test_deterministic_reruns():
