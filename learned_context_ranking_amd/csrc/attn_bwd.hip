@@ -383,9 +383,11 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 // Each item t is handled in two halves, software-pipelined so that with one wave per SIMD
 // the matrix pipe always has independent work next to the vector, LDS and copy work:
 //   A(t): the S / dP products of item t+1, each followed by one element of item t's
-//         softmax, with the transposed reads of item t's Q and dO spread over them;
+//         softmax, with the transposed reads of item t's Q and dO and the second part of
+//         item t+3's copy spread over them;
 //   B(t): item t's dV / dK products, with the wait for item t+2's copy, the barrier, the
-//         copy of item t+4 into item t's buffers and the row reads of item t+2 between them.
+//         row reads of item t+2 and the first part of item t+4's copy (into item t's
+//         buffers) between them.
 // The S and dP accumulators start from -LSE / scale and -delta of their rows (written by
 // the query-major pass), so the softmax element is exp2(c S' + log2 g) and dS = P dP';
 // the causal mask of the diagonal items is folded into the same start value.

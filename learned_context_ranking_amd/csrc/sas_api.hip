@@ -75,6 +75,8 @@ sas_status check_attn(const void* Q, const void* K, const void* V, const int32_t
   REQUIRE(isfinite(scale) && scale >= 1e-30f, SAS_ERR_INVALID_ARG, "scale must be finite and >= 1e-30");
   REQUIRE(aligned16(Q) && aligned16(K) && aligned16(V), SAS_ERR_INVALID_ARG, "Q, K, V must be 16-byte aligned");
   REQUIRE((long long)B * Hq * n * d < (1ll << 40), SAS_ERR_UNSUPPORTED, "tensor too large");
+  // one (batch, head) slice of K / V is addressed by a 31-bit buffer resource
+  REQUIRE((long long)n * d * 2 < (1ll << 31), SAS_ERR_UNSUPPORTED, "n * d * 2 bytes must be < 2^31");
   REQUIRE((long long)B * Hkv * (n / 64) < (1ll << 31) / 4, SAS_ERR_UNSUPPORTED, "too many blocks");
   REQUIRE((long long)(n / 64) * (kcap > 0 ? kcap : 1) < (1ll << 31), SAS_ERR_UNSUPPORTED, "n/64 * kcap too large");
   (void)logg;

@@ -30,11 +30,30 @@ KERNELS = {
 CALIB_BYTES = 256 << 20
 
 
+def _code_lines(text: str):
+    """The source's code without // comments, whitespace-trimmed, blank lines dropped: a
+    comment edit does not change what the counters describe."""
+    out = []
+    for line in text.splitlines():
+        cut = len(line)
+        pos = line.find("//")
+        while pos != -1:
+            if line[:pos].count('"') % 2 == 0:   # not inside a string literal
+                cut = pos
+                break
+            pos = line.find("//", pos + 2)
+        code = line[:cut].strip()
+        if code:
+            out.append(code)
+    return out
+
+
 def source_digest(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNELS[kernel][1]:
-        with open(os.path.join(ROOT, "learned_context_ranking_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "learned_context_ranking_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update("\n".join(_code_lines(fh.read())).encode())
+            h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -64,6 +64,7 @@ def _fwd(**kw):
     (dict(scale=0.0), sas.SAS_ERR_INVALID_ARG),
     (dict(scale=float("nan")), sas.SAS_ERR_INVALID_ARG),
     (dict(scale=1e-35), sas.SAS_ERR_INVALID_ARG),
+    (dict(n=1 << 24), sas.SAS_ERR_UNSUPPORTED),          # n * d * 2 bytes >= 2^31
     (dict(K=MIS), sas.SAS_ERR_INVALID_ARG),
     (dict(O=NULL), sas.SAS_ERR_INVALID_ARG),
     (dict(B=0), sas.SAS_ERR_INVALID_ARG),
