@@ -486,25 +486,40 @@ void dkv_kernel(const AttnArgs a) {
   // advances to the next item); fetch_part() issues loads [c0, c1) of it.
   constexpr int PER = 2 * NWIN + 1;
   static_assert(2 * PER < 64, "copies in flight exceed the vmcnt range");
+  // the copies only need the query block of an entry (no gate: one dependent load less
+  // before the first copy)
+  auto load_blk = [&](int e, int& v, float& g) {
+    v = m;
+    g = 0.0f;
+    if (e < nlist) v = list[nlist - 1 - e] / a.kcap;
+  };
+  // Past the last item (the ring keeps issuing copies so that every step waits for the
+  // same count) a copy goes through an empty buffer range: it writes zeros and reads no
+  // memory, so the final wait does not sit on redundant traffic.
+  constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+  int nf = 0;   // items whose copy has been issued
   auto fetch_row = [&]() -> uint32_t {
+    if (nf >= nitems) return kNoRow;
+    ++nf;
     int jj = m;
     if (ef < nlist) {
-      lst_f.ensure(ef, lane, load_lst);
+      lst_f.ensure(ef, lane, load_blk);
       jj = lst_f.at(ef);
     }
     const uint32_t row = (uint32_t)(gf * a.n + jj * kBlock);
-    if (!(ef == nlist && gf == G - 1)) {
-      if (++gf == G) { gf = 0; ++ef; }
-    }
+    if (++gf == G) { gf = 0; ++ef; }
     return row;
   };
   auto fetch_part = [&](uint16_t* qb, uint16_t* ob, uint32_t row, int c0, int c1) {
-    const uint32_t so = row * (uint32_t)(D * 2);
+    const bool none = row == kNoRow;
+    const int qb_bytes = none ? 0 : qbytes, rb_bytes = none ? 0 : rbytes;
+    const uint32_t r = none ? 0u : row;
+    const uint32_t so = r * (uint32_t)(D * 2);
 #pragma unroll
     for (int c = c0; c < c1; ++c) {
-      if (c < NWIN) buffer_load_lds16(qbase, qbytes, qb + 512 * (wave + NW * c), voff[c], so);
-      else if (c < 2 * NWIN) buffer_load_lds16(obase, qbytes, ob + 512 * (wave + NW * (c - NWIN)), voff[c - NWIN], so);
-      else buffer_load_lds4(rbase, rbytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
+      if (c < NWIN) buffer_load_lds16(qbase, qb_bytes, qb + 512 * (wave + NW * c), voff[c], so);
+      else if (c < 2 * NWIN) buffer_load_lds16(obase, qb_bytes, ob + 512 * (wave + NW * (c - NWIN)), voff[c - NWIN], so);
+      else buffer_load_lds4(rbase, rb_bytes, qb + TE + 128 * wave, 4u * lane, r * 4u);
     }
   };
   auto fetch = [&](uint16_t* qb, uint16_t* ob) { fetch_part(qb, ob, fetch_row(), 0, PER); };
