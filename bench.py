@@ -17,7 +17,9 @@ while the kernel's sources match the digest taken with the counters. The decode 
 reported alongside as HBM GB/s of the decode kernel, with L2 / Infinity Cache evicted by
 a 1 GiB read before each launch. The long-context decode object times one decode step's
 selection (block scores over the pooled-key cache + Top-K) against its sparse attention
-at 32K-512K cached tokens.
+at 32K-512K cached tokens. The sweep object times the other prefill configurations (the
+128K-token long prefill forward and the Qwen3-14B-shaped budgets 16 / 32 / 64) by the same
+FLOP counting.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 3]
 """
@@ -312,6 +314,58 @@ def run_long_decode(torch, reps=20):
     return out
 
 
+def run_sweep(torch, steps):
+    """The other prefill configurations, each timed over `steps` steps after 2 warmup
+    steps: the 128K-token long prefill (selection + forward, planted scores) and the
+    Qwen3-14B-shaped sweep over budgets 16 / 32 / 64 blocks (selection + forward +
+    backward with dg, Zipf scores). Q/K/V/dO ~ N(0,1) drawn on the device (seeded)."""
+    from learned_context_ranking_amd import sas, synth
+    dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
+    out = []
+    for name in ("long_prefill", "qwen3_14b_k16", "qwen3_14b_k32", "qwen3_14b_k64"):
+        w = synth.WORKLOADS[name]
+        log(f"[bench] sweep: {name} (generating inputs)")
+        g = torch.Generator(device=dev)
+        g.manual_seed(99)
+        mk = lambda shape: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        Q, K, V = mk((w.B, w.Hq, w.n, w.d)), mk((w.B, w.Hkv, w.n, w.d)), mk((w.B, w.Hkv, w.n, w.d))
+        dO = mk((w.B, w.Hq, w.n, w.d)) if w.backward else None
+        s = torch.from_numpy(synth.prefill_scores(w)).to(dev)
+        scale = 1.0 / math.sqrt(w.d)
+        O = torch.empty_like(Q)
+        lse = torch.empty((w.B, w.Hq, w.n), dtype=torch.float32, device=dev)
+        if w.backward:
+            ws = sas.bwd_workspace(w.B, w.Hq, w.Hkv, w.n, w.d, w.topk, dev)
+            outs = (torch.empty(Q.shape, dtype=torch.float32, device=dev),
+                    torch.empty(K.shape, dtype=torch.float32, device=dev),
+                    torch.empty(V.shape, dtype=torch.float32, device=dev),
+                    torch.empty((w.B, w.Hkv, w.NB, w.topk), dtype=torch.float32, device=dev))
+        marks = []
+        for r in range(steps + 2):
+            a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            idx, cnt, _, logg = sas.sas_topk_select(s, w.topk, kcap=w.topk, cols=w.NB)
+            sas.sas_attn_fwd(Q, K, V, idx, cnt, logg, scale, out=O, lse_out=lse)
+            if w.backward:
+                sas.sas_attn_bwd(Q, K, V, O, dO, lse, idx, cnt, logg, scale, ws=ws, outs=outs)
+            b_.record(stream)
+            if r >= 2:
+                marks.append((a, b_))
+        torch.cuda.synchronize()
+        ms = float(np.mean([x.elapsed_time(y) for x, y in marks]))
+        pairs = pair_count(cnt.cpu().numpy(), w.G)
+        flop = (12.0 if w.backward else 4.0) * w.d * pairs
+        tf = flop / (ms * 1e-3) / 1e12
+        out.append({"workload": f"{name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, n={w.n}, Top-K={w.topk}, "
+                                f"{w.scores} scores, " + ("select+fwd+bwd with dg" if w.backward else "select+fwd"),
+                    "ms": round(ms, 4), "tflops": round(tf, 1), "attended_pairs": pairs,
+                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+        log(f"[bench]   {name}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
+        del Q, K, V, dO, O, s
+    return out
+
+
 def cpu_baseline(w, host, cnt, budget_s=20.0):
     """The oracle (NumPy, float64) on a sample of query blocks of the same workload; FLOPs
     of the sampled blocks over their wall time. Threads = the BLAS pool's size."""
@@ -353,6 +407,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long-decode", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the long-prefill and 14B-sweep configurations")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the step without the per-kernel events (no roofline figures)")
@@ -439,6 +495,8 @@ def main():
                         "sparse attention (sas_decode); Hq=32, Hkv=8, d=128, K=16 blocks + current block; "
                         "select GB/s counts pooled keys read and scores written",
             "points": run_long_decode(torch)}
+    if not args.no_sweep:
+        out["sweep"] = run_sweep(torch, args.steps)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, tr["host"], tr["cnt"], args.cpu_seconds)

@@ -10,14 +10,19 @@
 // Passes (no atomics, deterministic):
 //   1. inverse index: for every key block m, the ascending list of (j, slot) with
 //      idx[j][slot] = m, found by binary search in the ascending idx rows; the lists of
-//      one (b, KV head) live in its own NB * kcap slice of the list buffer
+//      one (b, KV head) live in its own NB * kcap slice of the list buffer. The scan of
+//      the list lengths also plans pass 3: lists too long for one workgroup (with skewed
+//      scores some key blocks are selected by nearly every later query block) are cut
+//      into segments, and the segments are ordered longest first
 //   2. query-major pass, one workgroup per (b, KV head, j, pair of query heads): delta_t =
 //      dO_t . o_t for its rows, dQ, and the workgroup's share of dg. Each dg_jm is owned by
 //      the workgroups of query block j; their per-split partials are summed in a fixed
 //      order by a small reduction kernel. Per row it also stores -delta_t and
 //      -LSE_t / scale, the start values of the key-major pass's dP and S accumulators
-//   3. key-major pass, one workgroup per (b, KV head, m): dK and dV over the current block
-//      m itself plus every query block that selected m, for all G heads
+//   3. key-major pass, one workgroup per planned segment of (b, KV head, m): dK and dV over
+//      the current block m itself plus every query block that selected m, for all G heads.
+//      The first segment of a block writes its rows of dK / dV, later ones a partial slot;
+//      a small kernel adds the partials in segment order
 //
 // All 64-row operand tiles live in LDS in the swizzled layout of Tile<D>, copied straight
 // from global memory (global_load_lds) one block ahead of use. Operands whose contraction
@@ -39,6 +44,8 @@
 #endif
 
 namespace sas {
+
+constexpr int kDkvMinSeg = 64;   // shortest segment (items) a key block's list is cut into
 
 // ---------------------------------------------------------------- small kernels
 
@@ -88,31 +95,153 @@ __global__ __launch_bounds__(256) void inv_kernel(const int32_t* idx, const int3
   if (list == nullptr && lane == 0) counts[w] = base;
 }
 
-// Exclusive scan of the per-block counts of one (b, h): off[0..NB].
-__global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, int NB, int32_t* off) {
-  __shared__ int32_t part[256];
+// Exclusive scan of one value per thread of a 256-thread block; part[256] receives the total.
+__device__ __forceinline__ int scan256(int32_t* part, int v) {
+  part[threadIdx.x] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int x = part[i];
+      part[i] = run;
+      run += x;
+    }
+    part[256] = run;
+  }
+  __syncthreads();
+  const int r = part[threadIdx.x];
+  __syncthreads();
+  return r;
+}
+
+// Per (b, h), one workgroup: the exclusive scan of the per-block counts, off[0..NB], and
+// the key-major pass's work plan. Key block m has items_m = (count_m + 1) * G (its list and
+// itself, for each of the G heads). A long list is cut into nseg_m segments of at most T
+// items, T the smallest length (>= kDkvMinSeg) for which the extra segments fit the
+// budget of partial-result slots; every segment is one workgroup. seg_tab lists the
+// segments of (b, h) in key-block order as {m, s, nseg_m, partial slot (-1 for s = 0)},
+// then {-1, ...} up to NB + budget entries; red_tab lists the split blocks as {m, nseg_m,
+// first partial slot, 0}, then {-1, ...} up to budget entries.
+__global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, int NB, int G, int budget,
+                                                       int32_t* off, int4* seg_tab, int4* red_tab) {
+  __shared__ int32_t part[257];
   const long long bh = blockIdx.x;
   const int per = (NB + 255) / 256;
   const int t = threadIdx.x;
-  int s = 0;
-  for (int i = t * per; i < min(NB, (t + 1) * per); ++i) s += counts[bh * NB + i];
-  part[t] = s;
+  const int i0 = min(NB, t * per), i1 = min(NB, (t + 1) * per);
+  const int32_t* cnt = counts + bh * NB;
+  int s = 0, mx = 0;
+  for (int i = i0; i < i1; ++i) {
+    s += cnt[i];
+    mx = max(mx, (cnt[i] + 1) * G);
+  }
+  int run = scan256(part, s);
+  for (int i = i0; i < i1; ++i) {
+    off[bh * (NB + 1) + i] = run;
+    run += cnt[i];
+  }
+  if (t == 255) off[bh * (NB + 1) + NB] = run;
+
+  // the largest item count, then the segment length by bisection
+  part[t] = mx;
+  __syncthreads();
+  if (t == 0) {
+    int m2 = 0;
+    for (int i = 0; i < 256; ++i) m2 = max(m2, part[i]);
+    part[256] = m2;
+  }
+  __syncthreads();
+  const int maxItems = part[256];
+  __syncthreads();
+  int lo = kDkvMinSeg, hi = max(kDkvMinSeg, maxItems);
+  while (lo < hi) {   // uniform: every thread sees the same totals
+    const int mid = lo + (hi - lo) / 2;
+    int ex = 0;
+    for (int i = i0; i < i1; ++i) ex += ((cnt[i] + 1) * G + mid - 1) / mid - 1;
+    scan256(part, ex);
+    const int total = part[256];
+    __syncthreads();
+    if (total <= budget) hi = mid; else lo = mid + 1;
+  }
+  const int T = lo;
+  auto nseg_of = [&](int i) { return ((cnt[i] + 1) * G + T - 1) / T; };
+  int ns = 0, nx = 0, nr = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int q = nseg_of(i);
+    ns += q;
+    nx += q - 1;
+    nr += q > 1;
+  }
+  int so = scan256(part, ns);
+  const int nsegs = part[256];
+  __syncthreads();
+  int xo = scan256(part, nx);
+  int ro = scan256(part, nr);
+  const int nred = part[256];
+  __syncthreads();
+  // Segments are listed longest first (log-spaced length classes, counting sort), so the
+  // long ones start early and the short ones fill in at the end. The order only decides
+  // the schedule: each segment writes its own rows or its own partial slot.
+  constexpr int NBKT = 64;
+  __shared__ int hist[NBKT], cur[NBKT];
+  auto bucket = [](int len) {   // 4 classes per octave, descending order = larger class first
+    const int lg = 31 - __clz(max(len, 4));
+    return min(NBKT - 1, 4 * lg + ((len >> (lg - 2)) & 3));
+  };
+  auto seg_len = [&](int i, int q, int k) {
+    const int tot = (cnt[i] + 1) * G, ts = (tot + q - 1) / q;
+    return k < q - 1 ? ts : tot - (q - 1) * ts;
+  };
+  if (t < NBKT) hist[t] = 0;
+  __syncthreads();
+  for (int i = i0; i < i1; ++i) {
+    const int q = nseg_of(i);
+    for (int k = 0; k < q; ++k) atomicAdd(&hist[bucket(seg_len(i, q, k))], 1);
+  }
   __syncthreads();
   if (t == 0) {
     int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int v = part[i];
-      part[i] = run;
-      run += v;
+    for (int k = NBKT - 1; k >= 0; --k) {
+      cur[k] = run;
+      run += hist[k];
     }
   }
   __syncthreads();
-  int run = part[t];
-  for (int i = t * per; i < min(NB, (t + 1) * per); ++i) {
-    off[bh * (NB + 1) + i] = run;
-    run += counts[bh * NB + i];
+  (void)so;
+  const int slots = NB + budget;
+  int4* st = seg_tab + bh * slots;
+  int4* rt = red_tab + bh * budget;
+  const int pbase = (int)bh * budget;
+  for (int i = i0; i < i1; ++i) {
+    const int q = nseg_of(i);
+    for (int k = 0; k < q; ++k)
+      st[atomicAdd(&cur[bucket(seg_len(i, q, k))], 1)] = make_int4(i, k, q, k == 0 ? -1 : pbase + xo + k - 1);
+    if (q > 1) rt[ro++] = make_int4(i, q, pbase + xo, 0);
+    xo += q - 1;
   }
-  if (t == 255) off[bh * (NB + 1) + NB] = run;
+  for (int k = nsegs + t; k < slots; k += 256) st[k] = make_int4(-1, 0, 0, 0);
+  for (int k = nred + t; k < budget; k += 256) rt[k] = make_int4(-1, 0, 0, 0);
+}
+
+// Sum of the partial dK / dV of the split key blocks, in segment order: the first segment
+// wrote the block's rows of dK / dV directly; segments 1 .. nseg - 1 their partial slots.
+template <int D>
+__global__ __launch_bounds__(256) void dkv_reduce_kernel(const int4* red_tab, int budget, int n,
+                                                         const float* part, float* dK, float* dV) {
+  const long long bh = blockIdx.x / budget;
+  const int4 e = red_tab[blockIdx.x];
+  if (e.x < 0) return;
+  const size_t rows = ((size_t)bh * n + (size_t)e.x * kBlock) * D;
+  for (int i = threadIdx.x; i < kBlock * D; i += 256) {
+    float k = dK[rows + i], v = dV[rows + i];
+    for (int sgm = 1; sgm < e.y; ++sgm) {
+      const float* p = part + (size_t)(e.z + sgm - 1) * (2 * kBlock * D);
+      k += p[i];
+      v += p[kBlock * D + i];
+    }
+    dK[rows + i] = k;
+    dV[rows + i] = v;
+  }
 }
 
 // ---------------------------------------------------------------- query-major: dQ, dg
@@ -413,17 +542,22 @@ void dkv_kernel(const AttnArgs a) {
   const int kh = wave & 1, qh = wave >> 1;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
   // Launch order: the (batch, KV head) pairs in phases of SAS_DKV_ORDER pairs (0: one
-  // phase), key blocks ascending within a phase (the earliest blocks have the longest
-  // lists), the pairs of a phase interleaved so each pair's workgroups spread over the XCDs.
+  // phase), the work plan's segments (key blocks ascending; the earliest blocks have the
+  // longest lists) within a phase, the pairs of a phase interleaved so each pair's
+  // workgroups spread over the XCDs. Slots past a pair's last segment exit at once.
   const int BHp = a.B * a.Hkv;
   const int P = SAS_DKV_ORDER > 0 ? min(SAS_DKV_ORDER, BHp) : BHp;
-  const int phase = (int)(blockIdx.x / ((unsigned)P * NB));
+  const int S = NB + a.dkv_budget;   // plan slots per pair
+  const int phase = (int)(blockIdx.x / ((unsigned)P * S));
   const int np = min(P, BHp - phase * P);
-  const int rem = (int)(blockIdx.x - (unsigned)phase * P * NB);
-  const int m = rem / np;
+  const int rem = (int)(blockIdx.x - (unsigned)phase * P * S);
+  const int slot = rem / np;
   const int rr = phase * P + rem % np;
   const int h = rr % a.Hkv, b = rr / a.Hkv;
   const long long bh = (long long)b * a.Hkv + h;
+  const int4 seg = a.seg_tab[bh * S + slot];
+  if (seg.x < 0) return;   // uniform: the whole workgroup leaves before any barrier
+  const int m = seg.x, sgm = seg.y, nseg = seg.z, pslot = seg.w;
 
   const size_t kv_off = ((size_t)bh * a.n + (size_t)m * kBlock) * D;
   const int key = 32 * kh + ql;
@@ -453,8 +587,12 @@ void dkv_kernel(const AttnArgs a) {
   const int off0 = a.inv_off[bh * (NB + 1) + m];
   const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
   const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
-  const int nitems = (nlist + 1) * G;
-  const int ndiag0 = nlist * G;   // items from here on are the diagonal block m itself
+  // this segment's items [it0, it0 + nitems) of the block's (nlist + 1) * G, e-major
+  const int ntot = (nlist + 1) * G;
+  const int tseg = (ntot + nseg - 1) / nseg;
+  const int it0 = min(sgm * tseg, ntot);
+  const int nitems = min(tseg, ntot - it0);
+  const int ndiag0 = nlist * G - it0;   // local items from here on are the diagonal block m
 
   const size_t head0 = (size_t)(b * a.Hq + h * G) * a.n;
   const int qbytes = G * a.n * D * 2, rbytes = G * a.n * 4;
@@ -480,7 +618,8 @@ void dkv_kernel(const AttnArgs a) {
     }
   };
   LaneList lst_c, lst_f;
-  int ec = 0, gc = 0, ef = 0, gf = 0;   // item whose softmax is next; next item to copy
+  // item whose softmax is next (list position ec, head gc); next item to copy (ef, gf)
+  int ec = it0 / G, gc = it0 - (it0 / G) * G, ef = ec, gf = gc;
   // The copy of one item is PER buffer loads per wave: NWIN windows of Q, NWIN of dO and
   // one row of per-row values. fetch_row() returns the item's first global row (and
   // advances to the next item); fetch_part() issues loads [c0, c1) of it.
@@ -726,8 +865,9 @@ void dkv_kernel(const AttnArgs a) {
   }
   __syncthreads();
   if (qh == 0) {
-    float* dKp = a.dK + kv_off + key * D;
-    float* dVp = a.dV + kv_off + key * D;
+    // the block's rows of dK / dV, or (segments 1.. of a split block) its partial slot
+    float* dKp = sgm == 0 ? a.dK + kv_off + key * D : a.dkv_part + (size_t)pslot * (2 * kBlock * D) + key * D;
+    float* dVp = sgm == 0 ? a.dV + kv_off + key * D : dKp + kBlock * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -754,16 +894,23 @@ static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static int dq_splits(int G) { return (G + 1) / 2; }
 
+// Partial-result slots of the key-major pass per (b, KV head): enough to cut the longest
+// lists of a few pairs into pieces, at most 2048 slots in all.
+static int dkv_budget(long long BH) { return (int)std::max<long long>(4, std::min<long long>(64, 2048 / std::max<long long>(BH, 1))); }
+
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap) {
-  (void)d;
   const size_t NB = (size_t)n / kBlock;
   const size_t bh = (size_t)B * Hkv;
   const size_t kc = (size_t)(kcap > 0 ? kcap : 1);
   const int ns = dq_splits(Hq / Hkv);
+  const size_t bud = (size_t)dkv_budget((long long)bh);
   return 2 * al256((size_t)B * Hq * n * sizeof(float))        // -delta, -LSE / scale
          + al256(bh * NB * sizeof(int32_t))                    // counts
          + al256(bh * (NB + 1) * sizeof(int32_t))              // offsets
          + al256(bh * NB * kc * sizeof(int32_t))               // lists
+         + al256(bh * (NB + bud) * sizeof(int4))               // key-major work plan
+         + al256(bh * bud * sizeof(int4))                      // split key blocks
+         + al256(bh * bud * 2 * kBlock * (size_t)d * sizeof(float))   // their partial dK / dV
          + (ns > 1 ? al256((size_t)ns * bh * NB * kc * sizeof(float)) : 0);  // dg partials
 }
 
@@ -779,7 +926,7 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   {
     ProfScope prof("inv_scan", st);
     hipLaunchKernelGGL(inv_scan_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, st, a.inv_cnt, NB,
-                       a.inv_off);
+                       a.Hq / a.Hkv, a.dkv_budget, a.inv_off, a.seg_tab, a.red_tab);
   }
   {
     ProfScope prof("inv_fill", st);
@@ -802,8 +949,14 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   }
   {
     ProfScope prof("dkv", st);
-    if (a.gate_out) hipLaunchKernelGGL((dkv_kernel<D, true>), dim3((unsigned)nrows), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dkv_kernel<D, false>), dim3((unsigned)nrows), dim3(256), 0, st, a);
+    const unsigned grid = (unsigned)((long long)a.B * a.Hkv * (NB + a.dkv_budget));
+    if (a.gate_out) hipLaunchKernelGGL((dkv_kernel<D, true>), dim3(grid), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dkv_kernel<D, false>), dim3(grid), dim3(256), 0, st, a);
+  }
+  {
+    ProfScope prof("dkv_reduce", st);
+    hipLaunchKernelGGL((dkv_reduce_kernel<D>), dim3((unsigned)((long long)a.B * a.Hkv * a.dkv_budget)), dim3(256), 0,
+                       st, (const int4*)a.red_tab, a.dkv_budget, a.n, (const float*)a.dkv_part, a.dK, a.dV);
   }
   return hipGetLastError();
 }
@@ -823,6 +976,14 @@ hipError_t launch_bwd(AttnArgs a, void* ws, hipStream_t st) {
   p += al256(bh * (NB + 1) * sizeof(int32_t));
   a.inv_list = (int32_t*)p;
   p += al256(bh * NB * kc * sizeof(int32_t));
+  a.dkv_budget = dkv_budget((long long)bh);
+  const size_t bud = (size_t)a.dkv_budget;
+  a.seg_tab = (int4*)p;
+  p += al256(bh * (NB + bud) * sizeof(int4));
+  a.red_tab = (int4*)p;
+  p += al256(bh * bud * sizeof(int4));
+  a.dkv_part = (float*)p;
+  p += al256(bh * bud * 2 * kBlock * (size_t)a.d * sizeof(float));
   a.dg_part = (float*)p;
   if (a.d == 128) return launch_bwd_d<128>(a, st);
   return launch_bwd_d<64>(a, st);

@@ -109,6 +109,10 @@ struct AttnArgs {
   int32_t* inv_cnt;
   int32_t* inv_off;
   int32_t* inv_list;
+  int4* seg_tab;         // key-major work plan: per (b, KV head) NB + dkv_budget segments
+  int4* red_tab;         // split key blocks, per (b, KV head) dkv_budget entries
+  float* dkv_part;       // partial dK / dV of segments 1.. of split blocks
+  int dkv_budget;        // partial slots per (b, KV head)
 };
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap);

@@ -29,7 +29,35 @@ CASES = [
     (1, 4, 2, 512, 128, 4, "sparse", False, "normal"),      # ungated (logg = NULL)
     (3, 4, 1, 512, 128, 4, "sparse", True, "normal"),       # 3 (batch, KV head) pairs: odd launch phase
     (1, 4, 1, 512, 128, 0, "sparse", True, "normal"),       # budget 0: the causal current block only
+    (1, 8, 2, 4096, 64, 8, "sparse", True, "zipf"),         # popular key blocks: split key-major lists
+    (1, 5, 1, 4096, 128, 8, "sparse", True, "zipf"),        # the same with G = 5
 ]
+
+
+def _key_major_splits(idx_r, cnt_r, G):
+    """Whether the key-major pass cuts some key block's list into several workgroups, by
+    its planning rule: items_m = (uses_m + 1) * G; the segment length T is the smallest
+    length >= 64 whose extra segments fit min(64, max(4, 2048 // (B * Hkv))) partial slots
+    per (batch, KV head)."""
+    B, Hkv, NB = cnt_r.shape
+    budget = max(4, min(64, 2048 // (B * Hkv)))
+    split = False
+    for b in range(B):
+        for h in range(Hkv):
+            uses = np.zeros(NB, np.int64)
+            for j in range(NB):
+                for m in idx_r[b, h, j, :cnt_r[b, h, j]]:
+                    uses[m] += 1
+            items = (uses + 1) * G
+            lo, hi = 64, max(64, int(items.max()))
+            while lo < hi:
+                mid = (lo + hi) // 2
+                if int(((items + mid - 1) // mid - 1).sum()) <= budget:
+                    hi = mid
+                else:
+                    lo = mid + 1
+            split |= bool((items > lo).any())
+    return split
 
 
 def _run(case, seed=0, scale=None):
@@ -56,6 +84,8 @@ def test_fwd_bwd_parity(case, scale=None):
     idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk, full_scope=scope == "full",
                                                     kcap=g["idx"].shape[-1])
     assert np.array_equal(host(g["idx"]), idx_r) and np.array_equal(host(g["cnt"]), cnt_r)
+    if case[8] == "zipf" and case[3] >= 4096:
+        assert _key_major_splits(idx_r, cnt_r, case[1] // case[2]), "case meant to split key-major lists"
     lg = logg_r if gated else np.zeros_like(logg_r)
     Q, K, V, dO = P.f32("q"), P.f32("k"), P.f32("v"), P.f32("do")
     O_r, lse_r = oracle.attn_fwd(Q, K, V, idx_r, cnt_r, lg, P.scale)
@@ -101,7 +131,7 @@ def test_kernel_timing_records_each_launch():
     assert sas.profile_collect() == {}
 
 
-def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backward=True):
+def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backward=True, most_used=False):
     log(f"full size B={B} Hq={Hq} Hkv={Hkv} n={n} d={d} K={topk} scores={scores}")
     P = Prefill(B, Hq, Hkv, n, d, seed=0, scores=scores, backward=backward)
     t = P.device()
@@ -137,8 +167,15 @@ def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backwar
     if not backward:
         return
     dKh, dVh = host(dK), host(dV)
-    for m in [0] + list(g.integers(1, NB, nsample_m)):
-        h = int(g.integers(0, Hkv))
+    picks = [(0, int(g.integers(0, Hkv)))] + [(int(mm), int(g.integers(0, Hkv))) for mm in g.integers(1, NB, nsample_m)]
+    if most_used:
+        # for one head, also the key block with the most users: with skewed scores its
+        # list is cut into several key-major workgroups whose partials are summed
+        hm = int(g.integers(0, Hkv))
+        uses = np.bincount(np.concatenate([idx_r[0, hm, j, :cnt_r[0, hm, j]] for j in range(NB)]).astype(np.int64),
+                           minlength=NB)
+        picks.append((int(np.argmax(uses)), hm))
+    for m, h in picks:
         users = [j for j in range(m + 1, NB) if m in idx_r[0, h, j, :cnt_r[0, h, j]]]
         dk_r = np.zeros((64, d)); dv_r = np.zeros((64, d))
         for j in [m] + users:
@@ -165,6 +202,18 @@ def test_full_size_qwen3_4b_train():
 
 def test_full_size_qwen3_14b_k32():
     _full_size(1, 40, 8, 32768, 128, 32, "zipf", nsample_j=4, nsample_m=2)
+
+
+def test_key_major_split_lists():
+    """Zipf scores over 128 query blocks: the top-ranked key blocks are selected by nearly
+    every later query block, so the key-major pass cuts their lists into several
+    workgroups and sums the partial dK / dV. The most-used block is checked against the
+    oracle with sampled others, plus the gradient invariants on every element."""
+    B, Hq, Hkv, n, d, topk = 1, 10, 2, 8192, 128, 8
+    P = Prefill(B, Hq, Hkv, n, d, seed=0, scores="zipf")
+    idx_r, cnt_r, _, _ = oracle.select_prefill(P.s, topk)
+    assert _key_major_splits(idx_r, cnt_r, Hq // Hkv)
+    _full_size(B, Hq, Hkv, n, d, topk, "zipf", nsample_j=2, nsample_m=2, most_used=True)
 
 
 def test_full_size_long_prefill_fwd():
