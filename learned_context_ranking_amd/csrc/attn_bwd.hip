@@ -95,36 +95,66 @@ __global__ __launch_bounds__(256) void inv_kernel(const int32_t* idx, const int3
   if (list == nullptr && lane == 0) counts[w] = base;
 }
 
-// Exclusive scan of one value per thread of a 256-thread block; part[256] receives the total.
-__device__ __forceinline__ int scan256(int32_t* part, int v) {
-  part[threadIdx.x] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int x = part[i];
-      part[i] = run;
-      run += x;
-    }
-    part[256] = run;
+// Exclusive scan of one value per thread of a 256-thread block (4 waves); *total receives
+// the sum. red4 is 4 ints of LDS.
+__device__ __forceinline__ int scan256(int32_t* red4, int v, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
+  if (lane == 63) red4[w] = x;
   __syncthreads();
-  const int r = part[threadIdx.x];
+  int before = 0;
+  for (int u = 0; u < w; ++u) before += red4[u];
+  *total = (red4[0] + red4[1]) + (red4[2] + red4[3]);
+  __syncthreads();
+  return before + x - v;
+}
+
+// Sum / maximum over a 256-thread block (every thread gets the result).
+__device__ __forceinline__ int block_sum256(int32_t* red4, int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int r = (red4[0] + red4[1]) + (red4[2] + red4[3]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ int block_max256(int32_t* red4, int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const int r = max(max(red4[0], red4[1]), max(red4[2], red4[3]));
   __syncthreads();
   return r;
 }
 
+// Length class of a segment for the longest-first order: 4 classes per octave.
+__device__ __forceinline__ int len_class(int len) {
+  len = max(len, 1);
+  const int lg = 31 - __clz(len);
+  return min(63, lg < 2 ? len : 4 * lg + ((len >> (lg - 2)) & 3));
+}
+
 // Per (b, h), one workgroup: the exclusive scan of the per-block counts, off[0..NB], and
 // the key-major pass's work plan. Key block m has items_m = (count_m + 1) * G (its list and
-// itself, for each of the G heads). A long list is cut into nseg_m segments of at most T
-// items, T the smallest length (>= kDkvMinSeg) for which the extra segments fit the
-// budget of partial-result slots; every segment is one workgroup. seg_tab lists the
-// segments of (b, h) in key-block order as {m, s, nseg_m, partial slot (-1 for s = 0)},
-// then {-1, ...} up to NB + budget entries; red_tab lists the split blocks as {m, nseg_m,
-// first partial slot, 0}, then {-1, ...} up to budget entries.
+// itself, for each of the G heads). A list longer than the segment length T is cut into
+// nseg_m = ceil(items_m / T) segments, one workgroup each; T is the smallest length >=
+// kDkvMinSeg for which the extra segments fit the budget of partial-result slots. seg_tab
+// lists the segments of (b, h) as {m, s, nseg_m, partial slot (-1 for s = 0)}, longest first
+// by length class and in key-block order within a class (a fixed order: the plan does not
+// depend on timing), then {-1, ...} up to NB + budget entries; red_tab lists the split
+// blocks as {m, nseg_m, first partial slot, 0}, then {-1, ...} up to budget entries.
 __global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, int NB, int G, int budget,
                                                        int32_t* off, int4* seg_tab, int4* red_tab) {
-  __shared__ int32_t part[257];
+  constexpr int NCLS = 64, PITCH = 260;   // hist row: one column per thread, padded
+  __shared__ int32_t red4[4];
+  __shared__ int32_t hist[NCLS * PITCH];   // [class][thread]: segments, then positions
   const long long bh = blockIdx.x;
   const int per = (NB + 255) / 256;
   const int t = threadIdx.x;
@@ -135,92 +165,72 @@ __global__ __launch_bounds__(256) void inv_scan_kernel(const int32_t* counts, in
     s += cnt[i];
     mx = max(mx, (cnt[i] + 1) * G);
   }
-  int run = scan256(part, s);
+  int tot;
+  int run = scan256(red4, s, &tot);
   for (int i = i0; i < i1; ++i) {
     off[bh * (NB + 1) + i] = run;
     run += cnt[i];
   }
   if (t == 255) off[bh * (NB + 1) + NB] = run;
 
-  // the largest item count, then the segment length by bisection
-  part[t] = mx;
-  __syncthreads();
-  if (t == 0) {
-    int m2 = 0;
-    for (int i = 0; i < 256; ++i) m2 = max(m2, part[i]);
-    part[256] = m2;
-  }
-  __syncthreads();
-  const int maxItems = part[256];
-  __syncthreads();
+  // segment length by bisection (uniform: every thread sees the same sums)
+  const int maxItems = block_max256(red4, mx);
   int lo = kDkvMinSeg, hi = max(kDkvMinSeg, maxItems);
-  while (lo < hi) {   // uniform: every thread sees the same totals
+  while (lo < hi) {
     const int mid = lo + (hi - lo) / 2;
     int ex = 0;
     for (int i = i0; i < i1; ++i) ex += ((cnt[i] + 1) * G + mid - 1) / mid - 1;
-    scan256(part, ex);
-    const int total = part[256];
-    __syncthreads();
-    if (total <= budget) hi = mid; else lo = mid + 1;
+    if (block_sum256(red4, ex) <= budget) hi = mid; else lo = mid + 1;
   }
   const int T = lo;
   auto nseg_of = [&](int i) { return ((cnt[i] + 1) * G + T - 1) / T; };
-  int ns = 0, nx = 0, nr = 0;
+  auto seg_len = [&](int i, int q, int k) {
+    const int all = (cnt[i] + 1) * G, ts = (all + q - 1) / q;
+    return k < q - 1 ? ts : all - (q - 1) * ts;
+  };
+  // position of each segment: classes from the longest down, then thread (key block) order
+  for (int c = 0; c < NCLS; ++c) hist[c * PITCH + t] = 0;
+  int nx = 0, nr = 0;
   for (int i = i0; i < i1; ++i) {
     const int q = nseg_of(i);
-    ns += q;
     nx += q - 1;
     nr += q > 1;
-  }
-  int so = scan256(part, ns);
-  const int nsegs = part[256];
-  __syncthreads();
-  int xo = scan256(part, nx);
-  int ro = scan256(part, nr);
-  const int nred = part[256];
-  __syncthreads();
-  // Segments are listed longest first (log-spaced length classes, counting sort), so the
-  // long ones start early and the short ones fill in at the end. The order only decides
-  // the schedule: each segment writes its own rows or its own partial slot.
-  constexpr int NBKT = 64;
-  __shared__ int hist[NBKT], cur[NBKT];
-  auto bucket = [](int len) {   // 4 classes per octave, descending order = larger class first
-    const int lg = 31 - __clz(max(len, 4));
-    return min(NBKT - 1, 4 * lg + ((len >> (lg - 2)) & 3));
-  };
-  auto seg_len = [&](int i, int q, int k) {
-    const int tot = (cnt[i] + 1) * G, ts = (tot + q - 1) / q;
-    return k < q - 1 ? ts : tot - (q - 1) * ts;
-  };
-  if (t < NBKT) hist[t] = 0;
-  __syncthreads();
-  for (int i = i0; i < i1; ++i) {
-    const int q = nseg_of(i);
-    for (int k = 0; k < q; ++k) atomicAdd(&hist[bucket(seg_len(i, q, k))], 1);
+    for (int k = 0; k < q; ++k) ++hist[(NCLS - 1 - len_class(seg_len(i, q, k))) * PITCH + t];
   }
   __syncthreads();
-  if (t == 0) {
-    int run = 0;
-    for (int k = NBKT - 1; k >= 0; --k) {
-      cur[k] = run;
-      run += hist[k];
+  {
+    // thread t scans the 64 entries [64 t, 64 t + 64) of the class-major order in place
+    const int c = t >> 2, u0 = (t & 3) * 64;
+    int32_t* h = hist + c * PITCH + u0;
+    int sum = 0;
+    for (int u = 0; u < 64; ++u) sum += h[u];
+    int nsegs;
+    int base = scan256(red4, sum, &nsegs);
+    for (int u = 0; u < 64; ++u) {
+      const int x = h[u];
+      h[u] = base;
+      base += x;
     }
+    __syncthreads();
+    const int slots = NB + budget;
+    int4* st = seg_tab + bh * slots;
+    int4* rt = red_tab + bh * budget;
+    int nred;
+    int xo = scan256(red4, nx, &tot);
+    int ro = scan256(red4, nr, &nred);
+    const int pbase = (int)bh * budget;
+    for (int i = i0; i < i1; ++i) {
+      const int q = nseg_of(i);
+      for (int k = 0; k < q; ++k) {
+        const int pos = hist[(NCLS - 1 - len_class(seg_len(i, q, k))) * PITCH + t]++;
+        st[pos] = make_int4(i, k, q, k == 0 ? -1 : pbase + xo + k - 1);
+      }
+      if (q > 1) rt[ro++] = make_int4(i, q, pbase + xo, 0);
+      xo += q - 1;
+    }
+    for (int k = nsegs + t; k < slots; k += 256) st[k] = make_int4(-1, 0, 0, 0);
+    for (int k = nred + t; k < budget; k += 256) rt[k] = make_int4(-1, 0, 0, 0);
   }
-  __syncthreads();
-  (void)so;
-  const int slots = NB + budget;
-  int4* st = seg_tab + bh * slots;
-  int4* rt = red_tab + bh * budget;
-  const int pbase = (int)bh * budget;
-  for (int i = i0; i < i1; ++i) {
-    const int q = nseg_of(i);
-    for (int k = 0; k < q; ++k)
-      st[atomicAdd(&cur[bucket(seg_len(i, q, k))], 1)] = make_int4(i, k, q, k == 0 ? -1 : pbase + xo + k - 1);
-    if (q > 1) rt[ro++] = make_int4(i, q, pbase + xo, 0);
-    xo += q - 1;
-  }
-  for (int k = nsegs + t; k < slots; k += 256) st[k] = make_int4(-1, 0, 0, 0);
-  for (int k = nred + t; k < budget; k += 256) rt[k] = make_int4(-1, 0, 0, 0);
 }
 
 // Sum of the partial dK / dV of the split key blocks, in segment order: the first segment
@@ -893,6 +903,7 @@ static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 
 static int dq_splits(int G) { return (G + 1) / 2; }
+
 
 // Partial-result slots of the key-major pass per (b, KV head): enough to cut the longest
 // lists of a few pairs into pieces, at most 2048 slots in all.
