@@ -314,7 +314,7 @@ def run_long_decode(torch, reps=20):
     return out
 
 
-def run_sweep(torch, steps):
+def run_sweep(torch, steps, kernel_timing=True):
     """The other prefill configurations, each timed over `steps` steps after 2 warmup
     steps: the 128K-token long prefill (selection + forward, planted scores) and the
     Qwen3-14B-shaped sweep over budgets 16 / 32 / 64 blocks (selection + forward +
@@ -343,6 +343,10 @@ def run_sweep(torch, steps):
                     torch.empty((w.B, w.Hkv, w.NB, w.topk), dtype=torch.float32, device=dev))
         marks = []
         for r in range(steps + 2):
+            if r == 2:
+                torch.cuda.synchronize()
+                sas.profile_collect()
+                sas.profile_enable(kernel_timing)
             a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             idx, cnt, _, logg = sas.sas_topk_select(s, w.topk, kcap=w.topk, cols=w.NB)
@@ -353,6 +357,8 @@ def run_sweep(torch, steps):
             if r >= 2:
                 marks.append((a, b_))
         torch.cuda.synchronize()
+        sas.profile_enable(False)
+        prof = sas.profile_collect()
         ms = float(np.mean([x.elapsed_time(y) for x, y in marks]))
         pairs = pair_count(cnt.cpu().numpy(), w.G)
         flop = (12.0 if w.backward else 4.0) * w.d * pairs
@@ -360,7 +366,8 @@ def run_sweep(torch, steps):
         out.append({"workload": f"{name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, n={w.n}, Top-K={w.topk}, "
                                 f"{w.scores} scores, " + ("select+fwd+bwd with dg" if w.backward else "select+fwd"),
                     "ms": round(ms, 4), "tflops": round(tf, 1), "attended_pairs": pairs,
-                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
+                    "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "kernels_ms": {f"kernel:{k}": round(tot / n, 4) for k, (n, tot) in prof.items()}})
         log(f"[bench]   {name}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
         del Q, K, V, dO, O, s
     return out
@@ -423,7 +430,7 @@ def main():
 
     import torch
     from learned_context_ranking_amd import sas, synth
-    from learned_context_ranking_amd.profile_counters import profiled_traffic
+    from learned_context_ranking_amd.profile_counters import profiled_mfma, profiled_traffic
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     sas.lib()
@@ -452,6 +459,13 @@ def main():
         roof["achieved"] = fl / (kms[dom] * 1e-3) / 1e12
         roof["frac"] = roof["achieved"] / PEAK_BF16_TFLOPS
     roof["traffic"] = profiled_traffic(dom)
+    # matrix-core counters of the same kernel (rocprofv3 MfmaFlopsBF16 / MfmaUtil): the FLOPs
+    # it executes (its design recomputes q.k and dO.v) over this run's launch time
+    mc = profiled_mfma(dom)
+    if mc is not None and dom in kms:
+        mc["executed_tflops"] = mc["executed_flop_per_launch"] / (kms[dom] * 1e-3) / 1e12
+        mc = {k: round(v, 3) if k != "executed_flop_per_launch" else v for k, v in mc.items()}
+    roof["mfma_counters"] = mc
     out = {
         "metric": "gated block-sparse attn TFLOP/s fwd+bwd @n=32K,K=32; decode KV GB/s",
         "value": round(value, 3),
@@ -496,7 +510,7 @@ def main():
                         "select GB/s counts pooled keys read and scores written",
             "points": run_long_decode(torch)}
     if not args.no_sweep:
-        out["sweep"] = run_sweep(torch, args.steps)
+        out["sweep"] = run_sweep(torch, args.steps, kernel_timing=not args.no_kernel_timing)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, tr["host"], tr["cnt"], args.cpu_seconds)

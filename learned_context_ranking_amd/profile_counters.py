@@ -1,4 +1,4 @@
-"""HBM traffic of the library's kernels from rocprofv3 counter runs.
+"""HBM traffic and matrix-core use of the library's kernels from rocprofv3 counter runs.
 
 Two counter passes over the same command (``bench.py --calib-copy``), one collecting
 FETCH_SIZE and one WRITE_SIZE (KiB per dispatch), are reduced to bytes per launch for each
@@ -8,6 +8,20 @@ kernel, each counter scaled by what it reads for a plain copy of known size (the
 later run can tell whether the counters still describe the code:
 
     python3 -m learned_context_ranking_amd.profile_counters FETCH_DIR WRITE_DIR OUT_DIR "COMMAND"
+
+A third run collecting the derived counters MfmaFlopsBF16 (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+and MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE x SIMDs) is reduced to the bf16
+matrix FLOPs each attention kernel executes per launch, its duration under the counters
+and the matrix-core busy fraction, written as ``profiles/mfma_train_step.txt``:
+
+    python3 -m learned_context_ranking_amd.profile_counters --mfma MFMA_DIR OUT_DIR "COMMAND"
+
+A kernel trace (``rocprofv3 --kernel-trace --stats``, its ``*_results.db``) is summarised as a
+markdown table per kernel; with ``--by-workload`` the dispatches are also split into the
+bench's workloads (each begins with its input generation, torch's random-number kernels)
+and the library's kernels listed per workload:
+
+    python3 -m learned_context_ranking_amd.profile_counters --trace DB TITLE "COMMAND" [--by-workload NAME ...]
 """
 from __future__ import annotations
 
@@ -79,6 +93,30 @@ def profiled_traffic(kernel: str, profiles_dir: str | None = None):
         return None
 
 
+def profiled_mfma(kernel: str, profiles_dir: str | None = None):
+    """{executed bf16 matrix FLOPs per launch, matrix-core busy %} recorded for an attention
+    kernel in profiles/mfma_train_step.txt, or None when missing or the sources changed."""
+    path = os.path.join(profiles_dir or os.path.join(ROOT, "profiles"), "mfma_train_step.txt")
+    if kernel not in MFMA_PER_PAIR_D or not os.path.exists(path):
+        return None
+    kv, sec = {}, None
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("[") and "]" in line:
+                sec = line[1:line.index("]")]
+            elif sec == kernel and "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest(kernel):
+        return None
+    try:
+        return {"executed_flop_per_launch": float(kv["mfma_bf16_flops_per_launch"]),
+                "mfma_util_pct": float(kv["mfma_util_pct"])}
+    except (KeyError, ValueError):
+        return None
+
+
 def _per_dispatch(d: str, counter: str):
     """{kernel name: [value per dispatch]} for one counter from a rocprofv3 csv directory."""
     rows = defaultdict(float)
@@ -106,7 +144,116 @@ def _calibration(per: dict) -> float:
     return cands[0]
 
 
+def _per_dispatch_timed(d: str, counter: str):
+    """{kernel name: [(value, duration ns)]} for one counter from a rocprofv3 csv directory."""
+    rows = defaultdict(float)
+    meta = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (f, r["Dispatch_Id"])
+                rows[key] += float(r["Counter_Value"])
+                meta[key] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = defaultdict(list)
+    for key, v in rows.items():
+        name, dur = meta[key]
+        out[name].append((v, dur))
+    return out
+
+
+# executed bf16 matrix FLOPs per (query, key) pair of each attention kernel, by its design
+MFMA_PER_PAIR_D = {"fwd": 4, "dq": 6, "dkv": 8}
+
+
+def main_mfma(argv):
+    mfma_dir, out_dir, command = argv[0], argv[1], argv[2]
+    flops = _per_dispatch_timed(mfma_dir, "MfmaFlopsBF16")
+    util = _per_dispatch_timed(mfma_dir, "MfmaUtil")
+    path = os.path.join(out_dir, "mfma_train_step.txt")
+    with open(path, "w") as fh:
+        fh.write("# bf16 matrix-core use of the attention kernels per launch, from one rocprofv3 counter run of:\n")
+        fh.write(f"#   {command}\n")
+        fh.write("# MfmaFlopsBF16 = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (FLOPs the matrix cores executed);\n")
+        fh.write("# MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) in %; durations are the\n")
+        fh.write("# dispatches' own timestamps under counter collection (kernels serialised). Executed\n")
+        fh.write("# TFLOP/s = MfmaFlopsBF16 / duration, against the 2500 TFLOP/s dense bf16 peak. The\n")
+        fh.write("# design executes 4 d (fwd), 6 d (dq) and 8 d (dkv) FLOPs per attended (query, key) pair.\n")
+        for short in ("fwd", "dq", "dkv"):
+            sym = KERNELS[short][0]
+            fv = [x for n, vals in flops.items() if sym in n for x in vals]
+            uv = [x for n, vals in util.items() if sym in n for x in vals]
+            if not fv:
+                continue
+            f_mean = sum(v for v, _ in fv) / len(fv)
+            d_min = min(t for _, t in fv)
+            d_mean = sum(t for _, t in fv) / len(fv)
+            u_mean = sum(v for v, _ in uv) / len(uv) if uv else float("nan")
+            fh.write(f"[{short}] {sym}\n")
+            fh.write(f"dispatches = {len(fv)}\n")
+            fh.write(f"mfma_bf16_flops_per_launch = {f_mean:.6g}\n")
+            fh.write(f"attended_pairs_x_d_implied = {f_mean / MFMA_PER_PAIR_D[short]:.6g}\n")
+            fh.write(f"duration_us_mean = {d_mean / 1e3:.1f}\n")
+            fh.write(f"duration_us_min = {d_min / 1e3:.1f}\n")
+            fh.write(f"executed_tflops_at_mean = {f_mean / d_mean / 1e3:.1f}\n")
+            fh.write(f"executed_frac_of_bf16_peak = {f_mean / d_mean / 1e3 / 2500.0:.3f}\n")
+            fh.write(f"mfma_util_pct = {u_mean:.1f}\n")
+            fh.write(f"source_sha256 = {source_digest(short)}\n")
+            print(f"{short}: {f_mean:.4g} bf16 MFMA FLOPs/launch, {d_mean / 1e3:.0f} us, "
+                  f"{f_mean / d_mean / 1e3:.0f} TFLOP/s executed, MfmaUtil {u_mean:.1f} %")
+    print("->", path)
+
+
+def _short(name: str) -> str:
+    if name.startswith("void at::") or "rocclr" in name:
+        return "(torch) " + name[:60]
+    return name[:90]
+
+
+def main_trace(argv):
+    import sqlite3
+    db, title, command = argv[0], argv[1], argv[2]
+    names = argv[4:] if len(argv) > 3 and argv[3] == "--by-workload" else []
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, start, duration, grid_x from kernels order by start").fetchall()
+    print(f"# {title}\n\nCommand (run from /tmp on the MI355X box, repository at $R):\n\n    {command}\n")
+    agg = defaultdict(list)
+    for n, _, d, _ in rows:
+        agg[n].append(d)
+    print("| kernel | calls | avg us | min us | max us | total ms |\n|---|---:|---:|---:|---:|---:|")
+    for n, ds in sorted(agg.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{_short(n)}` | {len(ds)} | {sum(ds) / len(ds) / 1e3:.1f} | {min(ds) / 1e3:.1f} | "
+              f"{max(ds) / 1e3:.1f} | {sum(ds) / 1e6:.3f} |")
+    if not names:
+        return
+    # workloads: runs of dispatches that start with torch's random-number kernels; the last
+    # len(names) runs that launch library kernels are the named workloads, in order
+    runs, cur, prev_rand = [], [], False
+    for n, st, d, g in rows:
+        rand = "distribution_elementwise" in n or "normal_kernel" in n
+        if rand and not prev_rand and cur:
+            runs.append(cur)
+            cur = []
+        cur.append((n, d, g))
+        prev_rand = rand
+    runs.append(cur)
+    runs = [r for r in runs if any("sas::" in n for n, _, _ in r)][-len(names):]
+    for wname, run in zip(names, runs):
+        print(f"\n## {wname}\n\n| kernel | grid | calls | avg us | min us |\n|---|---:|---:|---:|---:|")
+        per = defaultdict(list)
+        for n, d, g in run:
+            if "sas::" in n:
+                per[(n, g)].append(d)
+        for (n, g), ds in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+            print(f"| `{_short(n)}` | {g} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.1f} | {min(ds) / 1e3:.1f} |")
+
+
 def main(argv):
+    if argv[1] == "--mfma":
+        return main_mfma(argv[2:])
+    if argv[1] == "--trace":
+        return main_trace(argv[2:])
     fetch_dir, write_dir, out_dir, command = argv[1], argv[2], argv[3], argv[4]
     fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _per_dispatch(write_dir, "WRITE_SIZE")
