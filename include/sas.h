@@ -349,8 +349,9 @@ sas_status sas_decode_select(const void* q, const void* kbar, int B, int Hq, int
  *   launches  int[max], out (may be NULL): launches of each kernel,
  *   total_ms  double[max], out (may be NULL): summed event time of each kernel.
  * Returns the number of entries written, or -1 if an event query failed. The record is
- * cleared either way. Kernel names: select, fwd, inv_count, inv_scan, inv_fill, dq,
- * dg_reduce, dkv, decode, decode_merge.
+ * cleared either way. Kernel names: select, fwd, inv_count, inv_scan (the inverse-index
+ * offsets and the key-major pass's work plan), inv_fill, dq, dg_reduce, dkv, dkv_reduce,
+ * gates_bwd, decode, decode_merge, pool, block_scores, topk_rows.
  */
 sas_status sas_profile_enable(int on);
 int sas_profile_collect(int max, char* names, int name_len, int* launches, double* total_ms);
