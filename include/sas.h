@@ -213,7 +213,10 @@ size_t sas_attn_bwd_workspace_size(int B, int Hq, int Hkv, int n, int d, int blo
  *   dQ fp32 [B][Hq][n][d], dK, dV fp32 [B][Hkv][n][d], out (overwritten, not accumulated).
  *   dg fp32 [B][Hkv][n/64][kcap], out: aligned with idx, 0 on padding slots.
  *   ws, ws_bytes  device workspace of at least sas_attn_bwd_workspace_size() bytes,
- *            16-byte aligned; its contents need no initialisation.
+ *            16-byte aligned; its contents need no initialisation. It holds the inverse
+ *            index, the key-major pass's work plan, the partial dK / dV of key blocks whose
+ *            lists are split over several workgroups and per-row delta / LSE values, so
+ *            calls that may run at the same time (other streams) need separate workspaces.
  * Returns SAS_ERR_UNSUPPORTED when (Hq / Hkv) * n * d * 2 >= 2^31 (the key-major pass
  * addresses the query rows of one KV group with 31-bit offsets).
  */
