@@ -246,7 +246,9 @@ size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap);
  *            pointer adds the log-gates as in training (useful to check decode against the
  *            training forward).
  *   o        bf16 [B][Hq][d], out.
- *   ws       workspace of sas_decode_workspace_size() bytes, 16-byte aligned.
+ *   ws       workspace of sas_decode_workspace_size() bytes, 16-byte aligned; it holds the
+ *            partial softmax states of split block lists (no initialisation needed), so
+ *            calls that may run at the same time need separate workspaces.
  * Returns SAS_ERR_UNSUPPORTED when Hq / Hkv > 32 or Lmax * d * 2 >= 2^31.
  */
 sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
