@@ -2,8 +2,13 @@
 
 Tolerance (floating outputs, bf16 GPU path against the fp64 oracle on the same
 bf16-rounded inputs), applied per tensor; both parts must hold:
-  * max |got - ref| <= 2e-2 * max(1, max |ref|)      (scale-aware max-abs)
+  * max |got - ref| <= 2e-2                           (O, LSE, dQ, dK, dV, decode o)
+    max |got - ref| <= 2e-2 * max(1, max |ref|)       (dg only: scale_aware=True)
   * sum |got - ref| / sum |ref| <= 1e-2               (mean relative error)
+The scale-aware bound is for the gate gradient alone: dg_jm sums G * 64 * 64 terms of
+p~/g * dO.(v - o), so its magnitude (tens to ~100 on N(0,1) inputs) grows with the rows
+that share a selection, and a fixed 2e-2 would ask bf16 operands for ~1e-4 relative
+accuracy. Every other output is O(1) and takes the fixed bound.
 Indices and counts are compared bit for bit.
 """
 from __future__ import annotations
@@ -39,13 +44,15 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-def assert_close(name, got, ref, max_abs=MAX_ABS, mean_rel=MEAN_REL):
+def assert_close(name, got, ref, max_abs=MAX_ABS, mean_rel=MEAN_REL, scale_aware=False):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite output"
     diff = np.abs(got - ref)
-    bound = max_abs * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
+    bound = max_abs
+    if scale_aware:
+        bound = max_abs * max(1.0, float(np.max(np.abs(ref))) if ref.size else 1.0)
     mx = float(diff.max()) if diff.size else 0.0
     den = float(np.abs(ref).sum())
     rel = float(diff.sum()) / den if den > 0 else float(diff.sum())

@@ -78,7 +78,7 @@ def _run(case, seed=0, scale=None):
 
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}-{c[2]}n{c[3]}d{c[4]}K{c[5]}{c[6]}{'' if c[7] else '-ungated'}"
                                              for c in CASES])
-def test_fwd_bwd_parity(case, scale=None):
+def test_fwd_bwd_parity(case, scale=None, grad_scale_aware=False):
     log(f"fwd/bwd parity {case}" + ("" if scale is None else f" scale={scale}"))
     P, g, gated, scope, topk = _run(case, scale=scale)
     idx_r, cnt_r, _, logg_r = oracle.select_prefill(P.s, topk, full_scope=scope == "full",
@@ -92,10 +92,10 @@ def test_fwd_bwd_parity(case, scale=None):
     assert_close("O", host(g["O"]), O_r)
     assert_close("LSE", host(g["lse"]), lse_r)
     dQ_r, dK_r, dV_r, dg_r = oracle.attn_bwd(Q, K, V, dO, idx_r, cnt_r, lg, P.scale)
-    assert_close("dQ", host(g["dQ"]), dQ_r)
-    assert_close("dK", host(g["dK"]), dK_r)
-    assert_close("dV", host(g["dV"]), dV_r)
-    assert_close("dg", host(g["dg"]), dg_r)
+    assert_close("dQ", host(g["dQ"]), dQ_r, scale_aware=grad_scale_aware)
+    assert_close("dK", host(g["dK"]), dK_r, scale_aware=grad_scale_aware)
+    assert_close("dV", host(g["dV"]), dV_r, scale_aware=grad_scale_aware)
+    assert_close("dg", host(g["dg"]), dg_r, scale_aware=True)
 
 
 def test_key_major_small_budget():
@@ -107,14 +107,20 @@ def test_key_major_small_budget():
     idx_r, cnt_r, _, _ = oracle.select_prefill(P.s, case[5])
     assert max(4, min(64, 2048 // (case[0] * case[2]))) == 16
     assert _key_major_splits(idx_r, cnt_r, case[1] // case[2])
-    test_fwd_bwd_parity(case)
+    # G = 8 and Zipf-popular key blocks: a block's dK / dV sum ~7,700 query rows, so the
+    # reference reaches |dK| ~ 9, |dV| ~ 15 (bf16 operands give ~0.3 % of that); the
+    # gradients take the bound relative to their magnitude here
+    test_fwd_bwd_parity(case, grad_scale_aware=True)
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.02])
 def test_fwd_bwd_other_scales(scale):
     """Logit scales other than 1/sqrt(d): the backward's key-major pass starts its score
-    accumulators at -LSE/scale, which grows as the scale shrinks."""
-    test_fwd_bwd_parity((1, 8, 2, 512, 128, 4, "sparse", True, "normal"), scale=scale)
+    accumulators at -LSE/scale, which grows as the scale shrinks. At scale 1 (11x the
+    standard 1/sqrt(128)) the reference gradients reach |dQ| ~ 54, |dK| ~ 46, so they take
+    the bound relative to their magnitude; at 0.02 the fixed bound."""
+    test_fwd_bwd_parity((1, 8, 2, 512, 128, 4, "sparse", True, "normal"), scale=scale,
+                        grad_scale_aware=scale > 0.1)
 
 
 def test_deterministic_reruns():
@@ -175,7 +181,7 @@ def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backwar
                                                          logg_r[0, h, j], P.scale)
             assert_close(f"dQ[j={j},h={h}]", dQh[0, h * G:(h + 1) * G, rows], dq_r)
             if cnt_r[0, h, j] > 0:
-                assert_close(f"dg[j={j},h={h}]", dgh[0, h, j, :cnt_r[0, h, j]], dg_r)
+                assert_close(f"dg[j={j},h={h}]", dgh[0, h, j, :cnt_r[0, h, j]], dg_r, scale_aware=True)
     if not backward:
         return
     dKh, dVh = host(dK), host(dV)
@@ -205,7 +211,8 @@ def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backwar
     assert bool((sk <= 1e-2 * sa).all()), float((sk / sa).max())
     sv = host(dV.double().sum(dim=2))
     sdo = dO.reshape(B, Hkv, G, n, d).sum(axis=(2, 3))
-    assert_close("sum dV", sv, sdo)
+    # a sum over n * G rows (magnitude ~sqrt(n G), hundreds here): relative bound
+    assert_close("sum dV", sv, sdo, scale_aware=True)
 
 
 def test_full_size_qwen3_4b_train():
@@ -214,6 +221,36 @@ def test_full_size_qwen3_4b_train():
 
 def test_full_size_qwen3_14b_k32():
     _full_size(1, 40, 8, 32768, 128, 32, "zipf", nsample_j=4, nsample_m=2)
+
+
+def test_full_size_qwen3_14b_k16():
+    _full_size(1, 40, 8, 32768, 128, 16, "zipf", nsample_j=4, nsample_m=2, most_used=True)
+
+
+def test_full_size_qwen3_14b_k64():
+    _full_size(1, 40, 8, 32768, 128, 64, "zipf", nsample_j=4, nsample_m=2, most_used=True)
+
+
+LONG_LIST_CASES = [
+    # selection rows longer than the 64 entries a wave holds at once: the kernels reload
+    # their lane-held window of the list (query-major passes) and walk inverse lists of
+    # more than 64 query blocks (key-major pass)
+    (1, 2, 1, 8320, 64, 0, "full", True, "normal"),        # full scope, 130 blocks: rows up to 129 entries
+    (1, 2, 1, 8192, 128, 96, "sparse", True, "normal"),    # sparse scope, K = 96
+    (1, 4, 1, 8192, 64, 80, "sparse", True, "zipf"),       # K = 80, G = 4, popular blocks split key-major lists
+]
+
+
+@pytest.mark.parametrize("case", LONG_LIST_CASES, ids=[f"B{c[0]}H{c[1]}-{c[2]}n{c[3]}d{c[4]}K{c[5]}{c[6]}"
+                                                        for c in LONG_LIST_CASES])
+def test_fwd_bwd_long_lists(case):
+    """Every output against the oracle, element by element, with lists of more than 64
+    blocks (the longest list of each case is asserted to exceed 64)."""
+    B, Hq, Hkv, n, d, topk, scope, gated, scores = case
+    NB = n // 64
+    longest = NB - 1 if scope == "full" else min(topk, NB - 1)
+    assert longest > 64
+    test_fwd_bwd_parity(case)
 
 
 def test_key_major_split_lists():
@@ -268,4 +305,4 @@ def test_fwd_bwd_gate_outside(case):
     assert_close("dQ", host(dQ), dQ_r)
     assert_close("dK", host(dK), dK_r)
     assert_close("dV", host(dV), dV_r)
-    assert_close("dg", host(dg), dg_r)
+    assert_close("dg", host(dg), dg_r, scale_aware=True)

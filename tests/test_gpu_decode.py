@@ -57,6 +57,21 @@ def test_decode_budget_exceeds_history():
     _decode_case(2, 4, 1, 128, 512, [200, 512], 16)
 
 
+def test_decode_long_list_one_chunk():
+    """Lists of 80 blocks + the current one at 512 (sequence, KV head) pairs: the launch
+    gives every pair one chunk, so a wave walks 81 list entries and reloads its lane-held
+    window of the list after the first 64."""
+    B, Hkv = 128, 4
+    Lmax = 82 * 64
+    kv_len = [Lmax - (b % 7) * 13 for b in range(B)]
+    _decode_case(B, 8, Hkv, 64, Lmax, kv_len, 80, seed=3, check=[0, 1, 63, 127])
+
+
+def test_decode_long_list_small_batch():
+    """The same budget at 4 pairs: the lists are split over many chunks and merged."""
+    _decode_case(2, 8, 2, 128, 8192, [8192, 5000], 100, seed=4)
+
+
 def test_decode_full_size():
     """64 sequences, 32 query / 8 KV heads, 32,768 cached tokens, 16 blocks + the current
     one; the oracle checks 4 sampled sequences, the selection is checked on all."""

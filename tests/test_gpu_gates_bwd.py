@@ -127,7 +127,8 @@ def test_gates_bwd_score_gradient_chain():
     Q, K, V, dO = P.f32("q"), P.f32("k"), P.f32("v"), P.f32("do")
     _, _, _, dg_r = oracle.attn_bwd(Q, K, V, dO, idx_r, cnt_r, logg_r, P.scale)
     ds_r = oracle.gates_bwd_prefill(P.s, idx_r, cnt_r, dg_r)
-    assert_close("ds (chain)", host(ds), ds_r)
+    # ds = g (dg - c) carries dg's magnitude and rounding, hence dg's scale-aware bound
+    assert_close("ds (chain)", host(ds), ds_r, scale_aware=True)
 
 
 def test_gates_bwd_full_size_train_scores():
@@ -176,4 +177,4 @@ def test_gates_bwd_variant_score_gradient_chain():
     Q, K, V, dO = P.f32("q"), P.f32("k"), P.f32("v"), P.f32("do")
     _, _, _, dg_r = oracle.attn_bwd(Q, K, V, dO, idx_r, cnt_r, logg_r, P.scale)
     ds_r = oracle.gates_bwd_prefill(P.s, idx_r, cnt_r, dg_r, gate="sigmoid")
-    assert_close("ds (sigmoid chain)", host(ds), ds_r)
+    assert_close("ds (sigmoid chain)", host(ds), ds_r, scale_aware=True)
