@@ -39,9 +39,6 @@
 #ifndef SAS_DQ_WPE
 #define SAS_DQ_WPE 2
 #endif
-#ifndef SAS_DKV_ORDER
-#define SAS_DKV_ORDER 2  // (batch, KV head) pairs per launch phase; 0: all pairs interleaved
-#endif
 
 namespace sas {
 
@@ -509,54 +506,50 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 
 // ---------------------------------------------------------------- key-major: dK, dV
 
-// 4 waves per (b, KV head, key block m): wave w owns keys 32 (w & 1) .. + 31 and query rows
-// 32 (w >> 1) .. + 31 of every (query block, head) item; K and V of its keys stay in
-// registers for the whole list. The two query halves are summed through LDS at the end.
-// The items (the query blocks that selected m, then m itself, for each of the G heads)
-// stream through a ring of 4 LDS buffer sets (distinct LDS objects selected at compile
-// time, so the compiler never waits for a copy in flight before computing). The copies
-// are buffer loads into LDS addressed by a per-lane constant offset plus a scalar
-// per-item offset; in the swizzled Tile layout each operand read is a laundered lane base
-// XORed with a constant plus an immediate.
+// Key-major pass, four waves per (b, KV head, key block m) segment and two workgroups per
+// CU: wave w owns keys 16 w .. 16 w + 15 of block m and every one of the 64 query rows of
+// each item, so its dK / dV rows are complete when the list ends (no reduction across
+// waves) and its registers stay within the budget of two waves per SIMD. The two
+// workgroups on a CU run independent items: one wave's softmax overlaps the other's
+// matrix products.
 //
-// Each item t is handled in two halves, software-pipelined so that with one wave per SIMD
-// the matrix pipe always has independent work next to the vector, LDS and copy work:
-//   A(t): the S / dP products of item t+1, each followed by one element of item t's
-//         softmax, with the transposed reads of item t's Q and dO and the second part of
-//         item t+3's copy spread over them;
-//   B(t): item t's dV / dK products, with the wait for item t+2's copy, the barrier, the
-//         row reads of item t+2 and the first part of item t+4's copy (into item t's
-//         buffers) between them.
+// Products (16x16x32 bf16 MFMAs, fp32 accumulate), per item and wave:
+//   S  = Q K^T   (64 rows x 16 keys): A = Q rows from LDS, B = K from registers
+//   dP = dO V^T  (64 rows x 16 keys): A = dO rows from LDS, B = V from registers
+//   dV^T += dO^T P, dK^T += Q^T dS   (d x 16 keys, contraction over the 64 rows)
+// A lane of the S / dP accumulators holds one key and 16 rows {16 rt + 4 u + i}; for the
+// contraction over rows the MFMA's k order is taken as a permutation of the rows
+// (position 8 u + x of a 32-row step is row 16 (x >> 2) + 4 u + (x & 3)), so P and dS
+// feed the dV / dK products straight from registers, and the dO^T / Q^T operands are
+// read in the same permuted order with the transposing LDS read.
 // The S and dP accumulators start from -LSE / scale and -delta of their rows (written by
-// the query-major pass), so the softmax element is exp2(c S' + log2 g) and dS = P dP';
-// the causal mask of the diagonal items is folded into the same start value.
+// the query-major pass), so a softmax element is one FMA, one exp2 and one multiply;
+// the causal mask of the diagonal items starts masked entries at -inf.
+// Items stream through two LDS slots: the copy of item t + 1 (buffer loads into LDS) is
+// issued right after the barrier that opens item t, and item t is computed meanwhile.
 template <int D, bool OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkv_kernel(const AttnArgs a) {
   constexpr int NW = 4;
   constexpr int TE = Tile<D>::ELEMS;
-  // Q tile + two 64-float rows (-LSE / scale copied by wave 0, -delta by wave 1; waves 2
+  constexpr int KS = D / 32;         // 32-wide k steps of the S / dP products
+  constexpr int DT = D / 16;         // 16-wide d tiles of dK^T / dV^T
+  // Q tile + four 64-float rows (-LSE / scale copied by wave 0, -delta by wave 1; waves 2
   // and 3 copy spare rows so that every wave issues the same number of copies)
   constexpr int TQ = TE + 4 * 128;
   __shared__ __attribute__((aligned(16))) uint16_t sq0[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t sq1[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sq2[TQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sq3[TQ];
   __shared__ __attribute__((aligned(16))) uint16_t so0[TE];
   __shared__ __attribute__((aligned(16))) uint16_t so1[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t so2[TE];
-  __shared__ __attribute__((aligned(16))) uint16_t so3[TE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5, ql = lane & 31;
-  const int kh = wave & 1, qh = wave >> 1;
+  const int u = lane >> 4, lq = lane & 15;
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
-  // Launch order: the (batch, KV head) pairs in phases of SAS_DKV_ORDER pairs (0: one
-  // phase), the work plan's segments (key blocks ascending; the earliest blocks have the
-  // longest lists) within a phase, the pairs of a phase interleaved so each pair's
-  // workgroups spread over the XCDs. Slots past a pair's last segment exit at once.
+  // Launch order: the (batch, KV head) pairs in phases of two, the work plan's segments
+  // (longest first) within a phase, the two pairs of a phase interleaved so that each
+  // pair's workgroups spread over the XCDs. Slots past a pair's last segment exit at once.
   const int BHp = a.B * a.Hkv;
-  const int P = SAS_DKV_ORDER > 0 ? min(SAS_DKV_ORDER, BHp) : BHp;
+  const int P = min(2, BHp);
   const int S = NB + a.dkv_budget;   // plan slots per pair
   const int phase = (int)(blockIdx.x / ((unsigned)P * S));
   const int np = min(P, BHp - phase * P);
@@ -570,34 +563,34 @@ void dkv_kernel(const AttnArgs a) {
   const int m = seg.x, sgm = seg.y, nseg = seg.z, pslot = seg.w;
 
   const size_t kv_off = ((size_t)bh * a.n + (size_t)m * kBlock) * D;
-  const int key = 32 * kh + ql;
-  bf16x8 kf[D / 16], vf[D / 16];
+  const int key = 16 * wave + lq;            // this lane's key within block m
+  // K / V as the B operands of S and dP: key `key`, d = 32 ks + 8 u .. + 7
+  bf16x8 kf[KS], vf[KS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 16 * ks + 8 * hl));
-    vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 16 * ks + 8 * hl));
-    // K / V fragments and the dK / dV accumulators only ever feed the matrix cores: keep
-    // them in AGPRs, which leaves the VGPRs to the values the vector ALU touches (fewer
-    // copies between the two files per item)
-    asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));
+  for (int ks = 0; ks < KS; ++ks) {
+    kf[ks] = as_bf16x8(ld16(a.K + kv_off + key * D + 32 * ks + 8 * u));
+    vf[ks] = as_bf16x8(ld16(a.V + kv_off + key * D + 32 * ks + 8 * u));
+    asm volatile("" : "+a"(kf[ks]), "+a"(vf[ks]));   // only the matrix cores read them
   }
-  f32x16 dk[D / 32], dv[D / 32];
+  f32x4 dk[DT], dv[DT];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
+  for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
+    for (int i = 0; i < 4; ++i) { dk[dt][i] = 0.0f; dv[dt][i] = 0.0f; }
     asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
   }
   const float c2 = a.scale * kLog2e;
-  const int g16 = lane >> 4, lp = lane & 15;
-  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
-  const int rrow = 32 * qh + ql;
-  const int rx0 = rrow * D + ((hl ^ Tile<D>::swz(rrow)) << 3);
-  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
+  // lane bases (elements) in the Tile layout: row read of rows 16 rt + lq at d = 32 ks + 8 u
+  // sits at 16 rt D + (rx0 ^ (ks << 5)); the transposing read of rows 32 q + 4 u + lq / 4
+  // (+ 16 for the second half of the k step) at d = 16 dt + 4 (lq % 4) at
+  // 32 q D + (tx0 ^ (dt << 4)) (+ 16 D)
+  const int rx0 = lq * D + ((u ^ Tile<D>::swz(lq)) << 3);
+  const int r0 = 4 * u + (lq >> 2);
+  const int tx0 = r0 * D + ((((lq & 3) >> 1) ^ Tile<D>::swz(r0)) << 3) + 4 * (lq & 1);
   const int off0 = a.inv_off[bh * (NB + 1) + m];
   const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
   const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
-  // this segment's items [it0, it0 + nitems) of the block's (nlist + 1) * G, e-major
+  // this segment's items [it0, it0 + nitems) of the block's (nlist + 1) * G, entry-major
   const int ntot = (nlist + 1) * G;
   const int tseg = (ntot + nseg - 1) / nseg;
   const int it0 = min(sgm * tseg, ntot);
@@ -617,282 +610,162 @@ void dkv_kernel(const AttnArgs a) {
     const int r = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
     voff[i] = (uint32_t)(r * D + ((c ^ Tile<D>::swz(r)) << 3)) * 2u;
   }
+  // list entry e (descending query block; e == nlist is block m itself): query block and
+  // base-2 log-gate of the entry's slot
   auto load_lst = [&](int e, int& v, float& g) {
     v = m;
     g = 0.0f;
     if (e < nlist) {
       const int p = list[nlist - 1 - e];
       v = p / a.kcap;
-      const int slot = p - v * a.kcap;
-      g = a.logg != nullptr ? a.logg[((size_t)bh * NB + v) * a.kcap + slot] * kLog2e : 0.0f;
+      const int sl = p - v * a.kcap;
+      g = a.logg != nullptr ? a.logg[((size_t)bh * NB + v) * a.kcap + sl] * kLog2e : 0.0f;
     }
   };
-  LaneList lst_c, lst_f;
-  // item whose softmax is next (list position ec, head gc); next item to copy (ef, gf)
-  int ec = it0 / G, gc = it0 - (it0 / G) * G, ef = ec, gf = gc;
-  // The copy of one item is PER buffer loads per wave: NWIN windows of Q, NWIN of dO and
-  // one row of per-row values. fetch_row() returns the item's first global row (and
-  // advances to the next item); fetch_part() issues loads [c0, c1) of it.
-  constexpr int PER = 2 * NWIN + 1;
-  static_assert(2 * PER < 64, "copies in flight exceed the vmcnt range");
-  // the copies only need the query block of an entry (no gate: one dependent load less
-  // before the first copy)
   auto load_blk = [&](int e, int& v, float& g) {
     v = m;
     g = 0.0f;
     if (e < nlist) v = list[nlist - 1 - e] / a.kcap;
   };
-  // Past the last item (the ring keeps issuing copies so that every step waits for the
-  // same count) a copy goes through an empty buffer range: it writes zeros and reads no
-  // memory, so the final wait does not sit on redundant traffic.
-  constexpr uint32_t kNoRow = 0xFFFFFFFFu;
-  int nf = 0;   // items whose copy has been issued
-  auto fetch_row = [&]() -> uint32_t {
-    if (nf >= nitems) return kNoRow;
-    ++nf;
-    int jj = m;
-    if (ef < nlist) {
-      lst_f.ensure(ef, lane, load_blk);
-      jj = lst_f.at(ef);
+  LaneList lst_c, lst_f;
+  int ef = it0 / G, gf = it0 - (it0 / G) * G;    // next item to copy
+  int ec = ef, gc = gf;                          // item to compute
+  int nf = 0;
+  // Past the last item a copy goes through an empty buffer range: it writes zeros and
+  // reads no memory (every step issues the same copies, so the waits stay uniform).
+  auto fetch = [&](uint16_t* qb, uint16_t* ob) {
+    uint32_t row = 0;
+    int qb_bytes = 0, rb_bytes = 0;
+    if (nf < nitems) {
+      ++nf;
+      int jj = m;
+      if (ef < nlist) {
+        lst_f.ensure(ef, lane, load_blk);
+        jj = lst_f.at(ef);
+      }
+      row = (uint32_t)(gf * a.n + jj * kBlock);
+      qb_bytes = qbytes;
+      rb_bytes = rbytes;
+      if (++gf == G) { gf = 0; ++ef; }
     }
-    const uint32_t row = (uint32_t)(gf * a.n + jj * kBlock);
-    if (++gf == G) { gf = 0; ++ef; }
-    return row;
-  };
-  auto fetch_part = [&](uint16_t* qb, uint16_t* ob, uint32_t row, int c0, int c1) {
-    const bool none = row == kNoRow;
-    const int qb_bytes = none ? 0 : qbytes, rb_bytes = none ? 0 : rbytes;
-    const uint32_t r = none ? 0u : row;
-    const uint32_t so = r * (uint32_t)(D * 2);
+    const uint32_t so = row * (uint32_t)(D * 2);
 #pragma unroll
-    for (int c = c0; c < c1; ++c) {
-      if (c < NWIN) buffer_load_lds16(qbase, qb_bytes, qb + 512 * (wave + NW * c), voff[c], so);
-      else if (c < 2 * NWIN) buffer_load_lds16(obase, qb_bytes, ob + 512 * (wave + NW * (c - NWIN)), voff[c - NWIN], so);
-      else buffer_load_lds4(rbase, rb_bytes, qb + TE + 128 * wave, 4u * lane, r * 4u);
-    }
-  };
-  auto fetch = [&](uint16_t* qb, uint16_t* ob) { fetch_part(qb, ob, fetch_row(), 0, PER); };
-
-  // Row operands of the item two ahead: Q / dO rows of this wave's queries and the start
-  // values of its S / dP accumulators (rows 32 qh + 8 grp + 4 hl + x, element 4 grp + x).
-  bf16x8 qr[D / 16], orw[D / 16];
-  f32x4 cl[4], cd[4];
-  auto row_reads_c = [&](const uint16_t* qn) {
-    const float* lr = reinterpret_cast<const float*>(qn + TE);
-    const float* dr = reinterpret_cast<const float*>(qn + TE + 128);
+    for (int c = 0; c < NWIN; ++c) buffer_load_lds16(qbase, qb_bytes, qb + 512 * (wave + NW * c), voff[c], so);
 #pragma unroll
-    for (int grp = 0; grp < 4; ++grp) {
-      cl[grp] = *reinterpret_cast<const f32x4*>(&lr[32 * qh + 8 * grp + 4 * hl]);
-      if (!OUT) cd[grp] = *reinterpret_cast<const f32x4*>(&dr[32 * qh + 8 * grp + 4 * hl]);
-    }
-  };
-  auto row_reads_q = [&](const uint16_t* qn, const uint16_t* on, int k0, int k1) {
-    int rx = rx0;
-    asm volatile("" : "+v"(rx));
-#pragma unroll
-    for (int ks = k0; ks < k1; ++ks) {
-      qr[ks] = as_bf16x8(ld16(&qn[rx ^ (ks << 4)]));
-      orw[ks] = as_bf16x8(ld16(&on[rx ^ (ks << 4)]));
-    }
-  };
-  auto cat16 = [](const f32x4 (&c)[4]) -> f32x16 {
-    typedef float f32x8 __attribute__((ext_vector_type(8)));
-    const f32x8 lo = __builtin_shufflevector(c[0], c[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    const f32x8 hi = __builtin_shufflevector(c[2], c[3], 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-  };
-  // start values of S and dP for the item whose rows are in (cl, cd); diagonal items
-  // start masked entries (key after query) at -1e30, so their softmax weight is exactly 0
-  auto start = [&](int t, f32x16& s0, f32x16& dp0) {
-    s0 = cat16(cl);
-    dp0 = OUT ? f32x16{} : cat16(cd);
-    if (t >= ndiag0) {
-      int kk = key;
-      asm volatile("" : "+v"(kk));   // a branch, not a select, on this uniform condition
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (kk > 32 * qh + 8 * (i >> 2) + 4 * hl + (i & 3)) s0[i] = -1e30f;
-    }
+    for (int c = 0; c < NWIN; ++c) buffer_load_lds16(obase, qb_bytes, ob + 512 * (wave + NW * c), voff[c], so);
+    buffer_load_lds4(rbase, rb_bytes, qb + TE + 128 * wave, 4u * lane, row * 4u);
   };
 
-  // The copy of an item is issued in two parts: loads [0, CB) in B right after the barrier
-  // that frees its buffers, loads [CB, PER) in the next A, one every few softmax elements.
-  // Issued together, the four waves' loads queue on the vector-memory path and stall each
-  // wave's instruction stream (and its matrix products) for several hundred cycles.
-  constexpr int CB = PER / 2;
-  constexpr int CA = PER - CB;
-  uint32_t crow = 0;   // global row of the item whose copy A finishes
-
-  // A(t) and B(t) for one item. (qx, ox): item t's buffers (transposed reads, then the copy
-  // of item t+4); (qp, op): item t-1's buffers, receiving the rest of item t+3's copy;
-  // (qy, oy): item t+2's buffers (row reads). (sc, dpc): S' / dP' of item t; (sn, dpn)
-  // receive those of item t+1.
-  auto step = [&](int t, uint16_t* qx, uint16_t* ox, uint16_t* qp, uint16_t* op, const uint16_t* qy,
-                  const uint16_t* oy, const f32x16& sc, const f32x16& dpc, f32x16& sn, f32x16& dpn) {
-    // every read of the previous B has landed (its row operands feed the products below)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+  auto compute = [&](int t, const uint16_t* qc, const uint16_t* oc) {
     float lg2 = 0.0f;
     if (ec < nlist) {
       lst_c.ensure(ec, lane, load_lst);
       lg2 = lst_c.gat(ec);
     }
-    const float gmul = OUT ? fast_exp2(lg2) : 1.0f;   // the item's gate (1 on the diagonal)
     if (++gc == G) { gc = 0; ++ec; }
-    f32x4 nd4[4];
-    if (OUT) {
-      const float* dc = reinterpret_cast<const float*>(qx + TE + 128);
+    const float gmul = OUT ? fast_exp2(lg2) : 1.0f;   // the item's gate (1 on the diagonal)
+    const float* lr = reinterpret_cast<const float*>(qc + TE);
+    const float* dr = reinterpret_cast<const float*>(qc + TE + 128);
+    // S' and dP' start from -LSE / scale and -delta of rows 16 rt + 4 u + i
+    f32x4 sacc[4], pacc[4], nd[4];
 #pragma unroll
-      for (int grp = 0; grp < 4; ++grp) nd4[grp] = *reinterpret_cast<const f32x4*>(&dc[32 * qh + 8 * grp + 4 * hl]);
+    for (int rt = 0; rt < 4; ++rt) {
+      sacc[rt] = *reinterpret_cast<const f32x4*>(&lr[16 * rt + 4 * u]);
+      nd[rt] = *reinterpret_cast<const f32x4*>(&dr[16 * rt + 4 * u]);
+      pacc[rt] = OUT ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : nd[rt];
     }
-    start(t + 1, sn, dpn);
-    // transposed operands of item t, two reads per softmax element
-    i16x4 trv[D / 32][2][2][2];   // [dt][hh][dO / Q][row half]
-    int tx = tx0;
-    asm volatile("" : "+v"(tx));
-    float pv[16], dsv[16];
-    constexpr int NM = 2 * (D / 16);   // S and dP products, spread evenly over the 16 elements
-    constexpr int NTR = (D / 32) * 8;  // transposed reads
+    if (t >= ndiag0) {   // block m itself: keys after the query row carry no weight
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if ((e * NM) % 16 == 0) {
-        const int j = e * NM / 16, ks = j >> 1;
-        if ((j & 1) == 0) sn = mfma32(qr[ks], kf[ks], sn);
-        else dpn = mfma32(orw[ks], vf[ks], dpn);
-      }
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int u = 0; u < NTR / 16; ++u) {
-        const int r = e * (NTR / 16) + u;   // (dt, hh, src, half) = r in mixed radix
-        const int half = r & 1, src = (r >> 1) & 1, hh = (r >> 2) & 1, dt = r >> 3;
-        const int r0 = 32 * qh + 16 * hh + 8 * half;
-        const int o = r0 * D + (tx ^ (((4 * dt) ^ (2 * half)) << 3));
-        trv[dt][hh][src][half] = lds_tr16(src == 0 ? &ox[o] : &qx[o]);
-      }
-      if (e % (16 / CA) == 1 && e / (16 / CA) < CA) {
-        const int c = CB + e / (16 / CA);
-        fetch_part(qp, op, crow, c, c + 1);
-      }
-      const int grp = e >> 2, x = e & 3;
-      if (OUT) {
-        // gate after the softmax: p~ from the ungated LSE, weights p~ g for dV,
-        // dS = p~ (g dP - delta)
-        const float p = fast_exp2(sc[e] * c2);
-        pv[e] = p * gmul;
-        dsv[e] = p * (gmul * dpc[e] + nd4[grp][x]);
-      } else {
-        const float p = fast_exp2(fmaf(sc[e], c2, lg2));
-        pv[e] = p;
-        dsv[e] = p * dpc[e];
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i)
+          if (key > 16 * rt + 4 * u + i) sacc[rt][i] = -INFINITY;
     }
+    int rx = rx0;
+    asm volatile("" : "+v"(rx));   // keeps per-(buffer, read) addresses unhoisted
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      bf16x8 qa[KS], oa[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qa[ks] = as_bf16x8(ld16(&qc[16 * rt * D + (rx ^ (ks << 5))]));
+        oa[ks] = as_bf16x8(ld16(&oc[16 * rt * D + (rx ^ (ks << 5))]));
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        sacc[rt] = mfma16(qa[ks], kf[ks], sacc[rt]);
+        pacc[rt] = mfma16(oa[ks], vf[ks], pacc[rt]);
+      }
+    }
+    // softmax weights and dS, packed as the B operands of the two 32-row k steps
     bf16x8 pb[2], sb[2];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int o = 8 * hh;
-      pb[hh] = pack8(pv[o], pv[o + 1], pv[o + 2], pv[o + 3], pv[o + 4], pv[o + 5], pv[o + 6], pv[o + 7]);
-      sb[hh] = pack8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
-    }
-    // materialise the softmax here, next to its products (left alone, the compiler sinks it
-    // past the copy's branch into B)
-    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(sb[0]), "+v"(sb[1]));
-    __builtin_amdgcn_sched_barrier(0);
-    // B(t): dV^T += dO^T P and dK^T += Q^T dS for item t, two products per slot, with the
-    // barrier, the row reads of item t+2 and the first part of item t+4's copy (into item
-    // t's buffers) between them
-    constexpr int NQ = 2 * (D / 32);
-    constexpr int NR = NQ / 2;   // slots 1 .. NR carry the row reads
-    static_assert(NQ >= 4 && CB <= 2 * (NQ - 2), "slots for the barrier, the rows and the copy");
+    for (int q = 0; q < 2; ++q) {
+      float pv[8], dsv[8];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const int hh = q / (D / 32), dt = q % (D / 32);
-      dv[dt] = mfma32(join_tr16(trv[dt][hh][0][0], trv[dt][hh][0][1]), pb[hh], dv[dt]);
-      dk[dt] = mfma32(join_tr16(trv[dt][hh][1][0], trv[dt][hh][1][1]), sb[hh], dk[dt]);
-      __builtin_amdgcn_sched_barrier(0);
-      if (q == 0) {
-        wait_vm_n<PER>();   // item t+2 has landed (this wave's share) ...
-        barrier_lds();      // ... everyone's, and every read of item t is done
-      } else {
-        if (q == 1) {
-          crow = fetch_row();
-          row_reads_c(qy);
+      for (int x = 0; x < 8; ++x) {
+        const int rt = 2 * q + (x >> 2), i = x & 3;
+        if (OUT) {
+          // gate after the softmax: p~ from the ungated LSE, weights p~ g for dV,
+          // dS = p~ (g dP - delta)
+          const float p = fast_exp2(sacc[rt][i] * c2);
+          pv[x] = p * gmul;
+          dsv[x] = p * (gmul * pacc[rt][i] + nd[rt][i]);
+        } else {
+          const float p = fast_exp2(fmaf(sacc[rt][i], c2, lg2));
+          pv[x] = p;
+          dsv[x] = p * pacc[rt][i];
         }
-        if (q <= NR) row_reads_q(qy, oy, (q - 1) * (D / 16) / NR, q * (D / 16) / NR);
-        if (q >= 2) fetch_part(qx, ox, crow, min(CB, 2 * (q - 2)), min(CB, 2 * (q - 1)));
       }
-      __builtin_amdgcn_sched_barrier(0);
+      pb[q] = pack8(pv[0], pv[1], pv[2], pv[3], pv[4], pv[5], pv[6], pv[7]);
+      sb[q] = pack8(dsv[0], dsv[1], dsv[2], dsv[3], dsv[4], dsv[5], dsv[6], dsv[7]);
+    }
+    int tx = tx0;
+    asm volatile("" : "+v"(tx));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int o = 32 * q * D + (tx ^ (dt << 4));
+        const bf16x8 ot = join_tr16(lds_tr16(&oc[o]), lds_tr16(&oc[o + 16 * D]));
+        const bf16x8 qt = join_tr16(lds_tr16(&qc[o]), lds_tr16(&qc[o + 16 * D]));
+        dv[dt] = mfma16(ot, pb[q], dv[dt]);
+        dk[dt] = mfma16(qt, sb[q], dk[dt]);
+      }
     }
   };
 
-  // prologue: copy items 0 and 1; B(-2): item 0's rows, copy of item 2; S / dP of item 0;
-  // B(-1): item 1's rows, copy of item 3
   fetch(sq0, so0);
-  fetch(sq1, so1);
-  wait_vm_n<PER>();
-  barrier_lds();
-  fetch(sq2, so2);
-  row_reads_c(sq0);
-  row_reads_q(sq0, so0, 0, D / 16);
-  f32x16 sA, dpA, sB, dpB;
-  start(0, sA, dpA);
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    sA = mfma32(qr[ks], kf[ks], sA);
-    dpA = mfma32(orw[ks], vf[ks], dpA);
-  }
-  wait_vm_n<PER>();
-  barrier_lds();
-  crow = fetch_row();   // item 3: its first part here, the rest in A(0)
-  fetch_part(sq3, so3, crow, 0, CB);
-  row_reads_c(sq1);
-  row_reads_q(sq1, so1, 0, D / 16);
-
   int t = 0;
-  for (; t + 4 <= nitems; t += 4) {
-    step(t, sq0, so0, sq3, so3, sq2, so2, sA, dpA, sB, dpB);
-    step(t + 1, sq1, so1, sq0, so0, sq3, so3, sB, dpB, sA, dpA);
-    step(t + 2, sq2, so2, sq1, so1, sq0, so0, sA, dpA, sB, dpB);
-    step(t + 3, sq3, so3, sq2, so2, sq1, so1, sB, dpB, sA, dpA);
+  for (; t + 2 <= nitems; t += 2) {
+    wait_vm();
+    barrier_lds();   // item t has landed for every wave; item t - 1 is done everywhere
+    fetch(sq1, so1);
+    compute(t, sq0, so0);
+    wait_vm();
+    barrier_lds();
+    fetch(sq0, so0);
+    compute(t + 1, sq1, so1);
   }
-  if (t < nitems) step(t, sq0, so0, sq3, so3, sq2, so2, sA, dpA, sB, dpB);
-  if (t + 1 < nitems) step(t + 1, sq1, so1, sq0, so0, sq3, so3, sB, dpB, sA, dpA);
-  if (t + 2 < nitems) step(t + 2, sq2, so2, sq1, so1, sq0, so0, sA, dpA, sB, dpB);
+  if (t < nitems) {
+    wait_vm();
+    barrier_lds();
+    fetch(sq1, so1);
+    compute(t, sq0, so0);
+  }
+  wait_vm();   // the last (empty) copies land before the workgroup's LDS is released
 
-  // sum the two query halves through LDS (key half 0 uses sq0 / sq1, key half 1 so0 / so1)
-  constexpr int PERW = (D / 32) * 16 * 64;
-  static_assert(PERW * sizeof(float) <= sizeof(so0), "reduction buffer");
-  wait_vm();
-  __syncthreads();
-  float* rk = reinterpret_cast<float*>(kh == 0 ? sq0 : so0);
-  float* rv = reinterpret_cast<float*>(kh == 0 ? sq1 : so1);
-  if (qh == 1) {
+  // this wave's 16 keys: the block's rows of dK / dV, or (segments 1.. of a split block)
+  // its partial slot. dK^T / dV^T element i of lane (u, lq) in d tile dt is d = 16 dt + 4 u + i
+  float* dKp = sgm == 0 ? a.dK + kv_off + key * D : a.dkv_part + (size_t)pslot * (2 * kBlock * D) + key * D;
+  float* dVp = sgm == 0 ? a.dV + kv_off + key * D : dKp + kBlock * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < DT; ++dt) {
+    f32x4 kv = dk[dt], vv = dv[dt];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        rk[(dt * 16 + i) * 64 + lane] = dk[dt][i];
-        rv[(dt * 16 + i) * 64 + lane] = dv[dt][i];
-      }
-  }
-  __syncthreads();
-  if (qh == 0) {
-    // the block's rows of dK / dV, or (segments 1.. of a split block) its partial slot
-    float* dKp = sgm == 0 ? a.dK + kv_off + key * D : a.dkv_part + (size_t)pslot * (2 * kBlock * D) + key * D;
-    float* dVp = sgm == 0 ? a.dV + kv_off + key * D : dKp + kBlock * D;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int d0 = 32 * dt + 8 * g4 + 4 * hl;
-        f32x4 kv, vv;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i = 4 * g4 + x;
-          kv[x] = (dk[dt][i] + rk[(dt * 16 + i) * 64 + lane]) * a.scale;
-          vv[x] = dv[dt][i] + rv[(dt * 16 + i) * 64 + lane];
-        }
-        *reinterpret_cast<f32x4*>(dKp + d0) = kv;
-        *reinterpret_cast<f32x4*>(dVp + d0) = vv;
-      }
+    for (int i = 0; i < 4; ++i) kv[i] *= a.scale;
+    *reinterpret_cast<f32x4*>(dKp + 16 * dt + 4 * u) = kv;
+    *reinterpret_cast<f32x4*>(dVp + 16 * dt + 4 * u) = vv;
   }
 }
 
