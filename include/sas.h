@@ -257,6 +257,28 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sas_decode_noalloc - sas_decode for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that forbid allocation.
+ * Same computation, arguments, results and launches as sas_decode, without the workspace
+ * arguments: the partial softmax states of split block lists go to a 16 MiB scratch array
+ * that the library holds on each device it runs on (until the process ends). The call
+ * itself allocates nothing (no hipMalloc, hipFree or allocating library routine); its
+ * first call on a device looks up that device's scratch address (hipGetSymbolAddress) and
+ * keeps it.
+ * The scratch needs B * Hkv * chunks * (Hq / Hkv) * (d + 2) * 4 bytes, where the launch
+ * splits each (sequence, KV head) list into chunks only when B * Hkv < 512 (then about
+ * 512 workgroups in all): at most ~17 MB for Hq / Hkv = 32, d = 128. Sizes whose launch
+ * would need more than the 16 MiB are rejected with SAS_ERR_UNSUPPORTED and nothing is
+ * enqueued. The scratch needs no initialisation (every chunk writes its whole partial).
+ * Every call on one device shares that device's scratch: calls that may overlap on one
+ * device (other streams, other threads) race and must be serialised by the caller.
+ */
+sas_status sas_decode_noalloc(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                              int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
+                              int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
+                              void* stream);
+
+/*
  * sas_decode_early_stop - sas_decode with a mass-threshold early stop over the selected
  * blocks, the rule of [S2O-ja] "S2O: オンライン置換によるスパースアテンションの早期停止"
  * (section "2. 早期停止ルール"; prior art, used as a budget rule on top of Top-K).

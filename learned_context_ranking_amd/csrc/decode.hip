@@ -340,19 +340,29 @@ size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap) {
   return (size_t)B * Hkv * (size_t)(kcap + 1) * G * (d + 2) * sizeof(float);
 }
 
-#ifndef SAS_DEC_TARGET_WG
-#define SAS_DEC_TARGET_WG 512    // aim for about this many single-wave workgroups
-#endif
+constexpr long long kDecTargetWG = 512;   // aim for about this many single-wave workgroups
+
+// Chunking of the block lists: enough chunks for about kDecTargetWG workgroups, at least 2
+// blocks per chunk; the early stop walks one sorted list per head (one chunk).
+void decode_plan(DecodeArgs& a) {
+  const long long pairs = (long long)a.B * a.Hkv;
+  const int nblk = a.kcap + 1;
+  int chunks = (int)((kDecTargetWG + pairs - 1) / pairs);
+  chunks = max(1, min(chunks, (nblk + 1) / 2));
+  if (a.order != nullptr) chunks = 1;
+  a.bpc = (nblk + chunks - 1) / chunks;
+  a.nchunk = (nblk + a.bpc - 1) / a.bpc;
+}
+
+size_t decode_part_bytes(const DecodeArgs& a) {
+  if (a.nchunk <= 1) return 0;
+  const size_t G = (size_t)a.Hq / a.Hkv;
+  return (size_t)a.B * a.Hkv * (size_t)a.nchunk * G * (a.d + 2) * sizeof(float);
+}
 
 hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   const long long pairs = (long long)a.B * a.Hkv;
-  const int nblk = a.kcap + 1;
-  // Enough chunks for about SAS_DEC_TARGET_WG workgroups, at least 2 blocks per chunk.
-  int chunks = (int)((SAS_DEC_TARGET_WG + pairs - 1) / pairs);
-  chunks = max(1, min(chunks, (nblk + 1) / 2));
-  if (a.order != nullptr) chunks = 1;   // the early stop walks one sorted list per head
-  a.bpc = (nblk + chunks - 1) / chunks;
-  a.nchunk = (nblk + a.bpc - 1) / a.bpc;
+  decode_plan(a);
   const unsigned grid = (unsigned)(pairs * a.nchunk);
   {
     ProfScope prof("decode", st);

@@ -6,6 +6,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/sas.h"
@@ -213,10 +214,11 @@ size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap) {
   return sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
 }
 
-sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
-                      int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
-                      int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
-                      void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+sas_status check_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len, int Lmax,
+                        const int32_t* idx, const int32_t* cnt, int B, int Hq, int Hkv, int d, int block,
+                        int kcap, float scale, const void* o) {
   REQUIRE(q && Kc && Vc && kv_len && cnt && o, SAS_ERR_INVALID_ARG, "q, Kc, Vc, kv_len, cnt, o must be non-NULL");
   REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
   REQUIRE(B > 0 && Hq > 0 && Hkv > 0 && Lmax > 0, SAS_ERR_INVALID_ARG, "B, Hq, Hkv, Lmax must be > 0");
@@ -231,15 +233,81 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
   REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
   REQUIRE(aligned16(q) && aligned16(Kc) && aligned16(Vc) && aligned16(o), SAS_ERR_INVALID_ARG,
           "q, Kc, Vc, o must be 16-byte aligned");
-  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
-  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  return SAS_OK;
+}
+
+sas::DecodeArgs decode_args(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len, int Lmax,
+                            const int32_t* idx, const int32_t* cnt, const float* logg, int B, int Hq, int Hkv,
+                            int d, int kcap, float scale, void* o) {
   sas::DecodeArgs a{};
   a.q = (const uint16_t*)q; a.Kc = (const uint16_t*)Kc; a.Vc = (const uint16_t*)Vc;
   a.kv_len = kv_len; a.Lmax = Lmax; a.idx = idx; a.cnt = cnt; a.logg = logg;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.kcap = kcap; a.scale = scale;
-  a.o = (uint16_t*)o; a.part = (float*)ws;
+  a.o = (uint16_t*)o;
+  return a;
+}
+
+// Scratch of sas_decode_noalloc: the partial softmax states of block lists split over
+// several workgroups. Each device the library runs on holds its own copy until the process
+// ends; in host code `scratch` only names the symbol, its device address comes from
+// hipGetSymbolAddress, looked up once per device and kept.
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sas_status decode_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SAS_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  REQUIRE(dev >= 0 && dev < kMaxDevices, SAS_ERR_UNSUPPORTED, "device %d beyond the %d this library tracks", dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(SAS_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SAS_OK;
+}
+
+}  // namespace
+
+sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                      int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
+                      int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
+                      void* ws, size_t ws_bytes, void* stream) {
+  const sas_status chk = check_decode(q, Kc, Vc, kv_len, Lmax, idx, cnt, B, Hq, Hkv, d, block, kcap, scale, o);
+  if (chk != SAS_OK) return chk;
+  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  sas::DecodeArgs a = decode_args(q, Kc, Vc, kv_len, Lmax, idx, cnt, logg, B, Hq, Hkv, d, kcap, scale, o);
+  a.part = (float*)ws;
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode launch");
+}
+
+sas_status sas_decode_noalloc(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                              int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
+                              int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,
+                              void* stream) {
+  const sas_status chk = check_decode(q, Kc, Vc, kv_len, Lmax, idx, cnt, B, Hq, Hkv, d, block, kcap, scale, o);
+  if (chk != SAS_OK) return chk;
+  sas::DecodeArgs a = decode_args(q, Kc, Vc, kv_len, Lmax, idx, cnt, logg, B, Hq, Hkv, d, kcap, scale, o);
+  sas::decode_plan(a);
+  const size_t need = sas::decode_part_bytes(a);
+  REQUIRE(need <= kDecodeScratchBytes, SAS_ERR_UNSUPPORTED,
+          "these sizes need %zu bytes of partial states, beyond the %zu-byte device scratch of sas_decode_noalloc",
+          need, kDecodeScratchBytes);
+  void* ptr = nullptr;
+  const sas_status sst = decode_scratch(&ptr);
+  if (sst != SAS_OK) return sst;
+  a.part = (float*)ptr;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_noalloc launch");
 }
 
 sas_status sas_decode_early_stop(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,

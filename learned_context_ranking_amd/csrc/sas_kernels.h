@@ -144,6 +144,10 @@ struct DecodeArgs {
   int32_t* used;
 };
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap);
+// sets a.bpc and a.nchunk as launch_decode will
+void decode_plan(DecodeArgs& a);
+// bytes of partial states the planned launch writes (0 when every list is one chunk)
+size_t decode_part_bytes(const DecodeArgs& a);
 hipError_t launch_decode(DecodeArgs a, hipStream_t st);
 
 }  // namespace sas

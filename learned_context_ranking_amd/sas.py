@@ -46,6 +46,7 @@ SIGNATURES = {
                       _P, _P, _P, _P, _P, _SZ, _P], _I),
     "sas_decode_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "sas_decode": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
+    "sas_decode_noalloc": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P], _I),
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
 }
@@ -243,6 +244,23 @@ def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None)
     _check(lib().sas_decode(_ptr(q), _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, _ptr(idx), _ptr(cnt), _ptr(logg),
                             B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
                             _stream(q.device)))
+    return o
+
+
+def sas_decode_noalloc(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, out=None):
+    """sas_decode without a workspace (the library's per-device scratch holds the partial
+    states; calls that overlap on one device race). `out` must be given where the caller
+    cannot allocate. Returns o bf16 [B, Hq, d]."""
+    for t, nm in ((q, "q"), (Kc, "Kc"), (Vc, "Vc")):
+        _need(t, torch.bfloat16, nm)
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hq, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    kcap = idx.shape[-1]
+    o = torch.empty_like(q) if out is None else out
+    _check(lib().sas_decode_noalloc(_ptr(q), _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, _ptr(idx), _ptr(cnt),
+                                    _ptr(logg), B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o),
+                                    _stream(q.device)))
     return o
 
 

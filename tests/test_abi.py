@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -191,6 +191,27 @@ def test_decode_rejects():
     assert L.sas_decode(*bad) == sas.SAS_ERR_INVALID_ARG
     bad = list(args); bad[12] = 128               # block
     assert L.sas_decode(*bad) == sas.SAS_ERR_UNSUPPORTED
+
+
+def test_decode_noalloc_rejects():
+    """The allocation-free decode shares sas_decode's checks and rejects sizes whose launch
+    would need more partial-state bytes than its 16 MiB per-device scratch (before any HIP
+    call)."""
+    L = sas.lib()
+    # q, Kc, Vc, kv_len, Lmax, idx, cnt, logg, B, Hq, Hkv, d, block, kcap, scale, o, stream
+    args = [FAKE, FAKE, FAKE, FAKE, 4096, FAKE, FAKE, NULL, 2, 8, 2, 128, 64, 16, 0.1, FAKE, NULL]
+    for i, v, code in ((0, NULL, sas.SAS_ERR_INVALID_ARG), (3, NULL, sas.SAS_ERR_INVALID_ARG),
+                       (12, 128, sas.SAS_ERR_UNSUPPORTED), (11, 96, sas.SAS_ERR_UNSUPPORTED),
+                       (9, 7, sas.SAS_ERR_INVALID_ARG), (15, MIS, sas.SAS_ERR_INVALID_ARG),
+                       (14, 0.0, sas.SAS_ERR_INVALID_ARG)):
+        bad = list(args); bad[i] = v
+        assert L.sas_decode_noalloc(*bad) == code, (i, v)
+    # 511 pairs x 32 heads x d = 128 split in 2 chunks: 511 * 2 * 32 * 130 * 4 B > 16 MiB
+    big = list(args); big[8] = 511; big[9] = 32; big[10] = 1; big[13] = 3
+    assert L.sas_decode_noalloc(*big) == sas.SAS_ERR_UNSUPPORTED
+    assert b"scratch" in L.sas_last_error()
+    # 512 pairs keep one chunk per list: no partial states, accepted by the checks (the
+    # call then needs a device, so it is not made here)
 
 
 def test_decode_paged_rejects():
