@@ -56,6 +56,63 @@ def calibration_copy(torch, nbytes=256 << 20):
     log(f"[bench] calibration copy: {nbytes} bytes read, {nbytes} bytes written")
 
 
+def stats(samples) -> dict:
+    """mean / median / p10 / p90 (ms) of a list of per-launch or per-step times."""
+    a = np.asarray(samples, np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "p10": round(float(np.percentile(a, 10)), 5), "p90": round(float(np.percentile(a, 90)), 5),
+            "n": int(a.size)}
+
+
+def select_bytes(NB: int, rows_per_head: int, H: int, kcap: int) -> int:
+    """Algorithmic bytes of one prefill selection launch: the valid scores read (row j has
+    j of them) and idx, logg (kcap each), cnt and lse written per row."""
+    valid = NB * (NB - 1) // 2 * H
+    return 4 * valid + rows_per_head * H * (8 * kcap + 8)
+
+
+def measure_peaks(torch, reps=5):
+    """Measured ceilings on this machine: the bf16 MFMA rate of an MFMA-loop microkernel (with
+    the shader clock under that load, from the in-kernel cycle and 100 MHz counters) and
+    the rate of a streaming read of 2 GiB (L2 / Infinity Cache hold a small part of it)."""
+    from learned_context_ranking_amd import sas
+    dev = torch.device("cuda", 0)
+    wgs, iters = 2048, 2000
+    clocks = torch.zeros(2 * wgs, dtype=torch.int64, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    flop = wgs * 4 * iters * 8 * 32768.0
+    sas.measure_mfma(wgs, iters, clocks, sink)
+    mf, rd = [], []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sas.measure_mfma(wgs, iters, clocks, sink)
+        b.record(stream)
+        b.synchronize()
+        mf.append(a.elapsed_time(b))
+    c = clocks.reshape(-1, 2).double().cpu().numpy()
+    sclk_mhz = float(np.median(c[:, 0] / np.maximum(c[:, 1], 1)) * 100.0)
+    buf = torch.ones((1 << 29,), dtype=torch.float32, device=dev)   # 2 GiB
+    sas.measure_read(buf, sink)
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sas.measure_read(buf, sink)
+        b.record(stream)
+        b.synchronize()
+        rd.append(a.elapsed_time(b))
+    del buf
+    tf = flop / (float(np.median(mf)) * 1e-3) / 1e12
+    gbs = (1 << 31) / (float(np.median(rd)) * 1e-3) / 1e9
+    return {"mfma_bf16_tflops": round(tf, 1), "sclk_mhz_under_mfma_load": round(sclk_mhz, 1),
+            "stream_read_gbs": round(gbs, 1),
+            "method": "sas_measure_mfma: 2048 workgroups x 4 waves x 2000 rounds of 8 independent bf16 "
+                      "32x32x16 MFMAs, median of 5 launches; clock = s_memtime cycles / s_memrealtime "
+                      "ticks x 100 MHz over wave 0 of each workgroup; sas_measure_read: 2 GiB streamed "
+                      "with 16-byte loads, median of 5"}
+
+
 def pair_count(cnt: np.ndarray, G: int, block: int = 64) -> int:
     """Attended (query row, key) pairs: causal current block plus cnt_j full history
     blocks for every query block, times the G query heads of each KV head."""
@@ -100,6 +157,8 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
     stream = torch.cuda.current_stream()
     ev = {k: [] for k in ("sel", "fwd", "bwd", "gates_bwd")}
 
+    ev["step"] = []
+
     def step(record):
         marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
         if record:
@@ -122,6 +181,7 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
             ev["fwd"].append((marks[1], marks[2]))
             ev["bwd"].append((marks[2], marks[3]))
             ev["gates_bwd"].append((marks[3], marks[4]))
+            ev["step"].append((marks[0], marks[4]))
         return cnt_
 
     log(f"[bench] warmup {warmup}")
@@ -144,10 +204,15 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sas.profile_enable(False)
-    prof = sas.profile_collect()
+    launches = sas.profile_collect_launches()
     ms_step = (t1 - t0) * 1e3 / steps
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
-    kern_ms = {k: tot / n for k, (n, tot) in prof.items()}
+    ev_stats = {k: stats([a.elapsed_time(b) for a, b in v]) for k, v in ev.items()}
+    per_kernel = {}
+    for name, t_ms in launches:
+        per_kernel.setdefault(name, []).append(t_ms)
+    kern_ms = {k: float(np.mean(v)) for k, v in per_kernel.items()}
+    kern_stats = {k: stats(v) for k, v in per_kernel.items()}
     # the same forward + backward with the gate placed after the softmax (the design
     # alternative the method is compared with), on the same selection
     idx_, cnt_, _, logg_ = sas.sas_topk_select(t["s"], w.topk, kcap=w.topk, cols=NB)
@@ -164,7 +229,7 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
     torch.cuda.synchronize()
     ms["fwd_bwd_gate_outside"] = float(np.mean([a_.elapsed_time(b_) for a_, b_ in outside]))
     return dict(ms_step=ms_step, ms=ms, kern_ms=kern_ms, pairs=pairs, flop_fwd=flop_fwd,
-                flop_bwd=flop_bwd, host=host, cnt=cnt_h)
+                flop_bwd=flop_bwd, host=host, cnt=cnt_h, ev_stats=ev_stats, kern_stats=kern_stats)
 
 
 def run_decode(steps, torch):
@@ -207,8 +272,11 @@ def run_decode(steps, torch):
         times.append((b, c))
         sel_times.append((a, b))
     torch.cuda.synchronize()
-    ms = float(np.median([x.elapsed_time(y) for x, y in times]))
-    ms_sel = float(np.median([x.elapsed_time(y) for x, y in sel_times]))
+    dec_samples = [x.elapsed_time(y) for x, y in times]
+    sel_samples = [x.elapsed_time(y) for x, y in sel_times]
+    e2e_samples = [x[0].elapsed_time(y[1]) for x, y in zip(sel_times, times)]
+    ms = float(np.median(dec_samples))
+    ms_sel = float(np.median(sel_samples))
     # the same step over a paged cache: the sequences' blocks scattered over a pool of
     # 64-token pages in random order, read through a page table
     C = L // 64
@@ -232,7 +300,8 @@ def run_decode(steps, torch):
         c.record(stream)
         ptimes.append((a, c))
     torch.cuda.synchronize()
-    ms_paged = float(np.median([x.elapsed_time(y) for x, y in ptimes]))
+    paged_samples = [x.elapsed_time(y) for x, y in ptimes]
+    ms_paged = float(np.median(paged_samples))
     del Kp, Vp
     # the same step with the mass-threshold early stop (blocks in descending score order)
     order = torch.gather(s[:, :, 0, :], -1, idx.reshape(B, Hkv, -1).clamp(min=0).long()).contiguous()
@@ -254,8 +323,14 @@ def run_decode(steps, torch):
     # algorithmic bytes: the selected K/V blocks plus the current block, q and o
     blocks = int(cnt_h.sum()) + B * Hkv
     nbytes = blocks * 64 * d * 2 * 2 + 2 * B * Hq * d * 2
+    # selection: the row's valid scores read, idx (kcap), cnt and lse written
+    sel_bytes = B * Hkv * ((L - 1) // 64) * 4 + B * Hkv * (4 * K + 8)
+    ms_e2e = float(np.median(e2e_samples))
     return dict(ms=ms, ms_select=ms_sel, bytes=nbytes, gbs=nbytes / ms / 1e6, ms_paged=ms_paged,
-                gbs_paged=nbytes / ms_paged / 1e6, early=early,
+                gbs_paged=nbytes / ms_paged / 1e6, early=early, stats=stats(dec_samples),
+                sel_stats=stats(sel_samples), paged_stats=stats(paged_samples), sel_bytes=sel_bytes,
+                sel_gbs=sel_bytes / ms_sel / 1e6, ms_e2e=ms_e2e, e2e_stats=stats(e2e_samples),
+                e2e_gbs=(nbytes + sel_bytes) / ms_e2e / 1e6,
                 workload=f"decode: B={B} sequences, Hq={Hq}, Hkv={Hkv}, d={d}, kv_len={L}, block=64, "
                          f"K={K} blocks + current block, ungated (Algorithm 2)")
 
@@ -359,14 +434,20 @@ def run_sweep(torch, steps, kernel_timing=True):
         torch.cuda.synchronize()
         sas.profile_enable(False)
         prof = sas.profile_collect()
-        ms = float(np.mean([x.elapsed_time(y) for x, y in marks]))
+        samples = [x.elapsed_time(y) for x, y in marks]
+        ms = float(np.mean(samples))
         pairs = pair_count(cnt.cpu().numpy(), w.G)
+        sel_b = select_bytes(w.NB, w.NB, w.B * w.Hkv, w.topk)
+        sel_ms = prof["select"][1] / prof["select"][0] if "select" in prof else None
         flop = (12.0 if w.backward else 4.0) * w.d * pairs
         tf = flop / (ms * 1e-3) / 1e12
         out.append({"workload": f"{name}: B={w.B}, Hq={w.Hq}, Hkv={w.Hkv}, d={w.d}, n={w.n}, Top-K={w.topk}, "
                                 f"{w.scores} scores, " + ("select+fwd+bwd with dg" if w.backward else "select+fwd"),
                     "ms": round(ms, 4), "tflops": round(tf, 1), "attended_pairs": pairs,
                     "frac_of_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                    "ms_stats": stats(samples),
+                    "select": {"bytes": sel_b, "ms": round(sel_ms, 5) if sel_ms else None,
+                               "gbs": round(sel_b / (sel_ms * 1e-3) / 1e9, 1) if sel_ms else None},
                     "kernels_ms": {f"kernel:{k}": round(tot / n, 4) for k, (n, tot) in prof.items()}})
         log(f"[bench]   {name}: {ms:.3f} ms, {tf:.1f} TFLOP/s")
         del Q, K, V, dO, O, s
@@ -378,11 +459,24 @@ def cpu_baseline(w, host, cnt, budget_s=20.0):
     of the sampled blocks over their wall time. Threads = the BLAS pool's size."""
     import oracle
     from learned_context_ranking_amd import synth
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in info] or [1])
+        if info:
+            blas = f"{info[0].get('internal_api', '?')} {info[0].get('version', '')}".strip()
     except Exception:   # threadpoolctl missing: report the affinity mask
         cores = len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     f = synth.bf16_bits_to_f32
     Q, K, V, dO = f(host["q"]), f(host["k"]), f(host["v"]), f(host["do"])
     idx_r, cnt_r, _, logg_r = oracle.select_prefill(host["s"], w.topk)
@@ -403,7 +497,10 @@ def cpu_baseline(w, host, cnt, budget_s=20.0):
     dt = time.perf_counter() - t0
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample=f"{nblk} random (KV head, query block) tiles of the training workload, fwd+bwd "
-                       f"with dg, float64 NumPy, {dt:.1f} s wall")
+                       f"with dg, float64 NumPy, {dt:.1f} s wall",
+                cpu_model=cpu_model, blas=blas, dtype="f64",
+                dtype_reason="the oracle is timed as it stands: it computes in float64 by design (it is "
+                             "the parity reference; a float32 run would be a different program)")
 
 
 def main():
@@ -417,6 +514,9 @@ def main():
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the long-prefill and 14B-sweep configurations")
     ap.add_argument("--cpu-seconds", type=float, default=20.0)
+    ap.add_argument("--decode-reps", type=int, default=200,
+                    help="timed decode launches (each after a 1 GiB cache-evicting read)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured MFMA / read peaks")
     ap.add_argument("--no-kernel-timing", action="store_true",
                     help="time the step without the per-kernel events (no roofline figures)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -436,6 +536,9 @@ def main():
     sas.lib()
     if args.calib_copy:
         calibration_copy(torch)
+    peaks = None if args.no_peaks else measure_peaks(torch)
+    if peaks:
+        log(f"[bench] measured peaks: {peaks}")
     w = synth.WORKLOADS["qwen3_4b_train"]
     tr = run_train(w, args.steps, args.warmup, torch, kernel_timing=not args.no_kernel_timing)
     flop_step = tr["flop_fwd"] + tr["flop_bwd"]
@@ -458,6 +561,11 @@ def main():
         roof["flop_per_launch"] = fl
         roof["achieved"] = fl / (kms[dom] * 1e-3) / 1e12
         roof["frac"] = roof["achieved"] / PEAK_BF16_TFLOPS
+        if peaks:
+            roof["measured_peak"] = peaks["mfma_bf16_tflops"]
+            roof["frac_of_measured_peak"] = roof["achieved"] / peaks["mfma_bf16_tflops"]
+        if dom in tr["kern_stats"]:
+            roof["launch_ms_stats"] = tr["kern_stats"][dom]
     roof["traffic"] = profiled_traffic(dom)
     # matrix-core counters of the same kernel (rocprofv3 MfmaFlopsBF16 / MfmaUtil): the FLOPs
     # it executes (its design recomputes q.k and dO.v) over this run's launch time
@@ -486,15 +594,31 @@ def main():
             "attended_pairs": tr["pairs"], "flop_per_step": flop_step,
         },
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "step_ms_stats": tr["ev_stats"]["step"],
+        "call_ms_stats": {k: v for k, v in tr["ev_stats"].items() if k != "step"},
+        "kernel_ms_stats": tr["kern_stats"],
+        "select": {"bytes": select_bytes(w.NB, w.NB, w.B * w.Hkv, w.topk),
+                   "ms": round(ms["sel"], 5),
+                   "gbs": round(select_bytes(w.NB, w.NB, w.B * w.Hkv, w.topk) / (ms["sel"] * 1e-3) / 1e9, 1),
+                   "counts": "valid scores read (row j: j of them) + idx/logg (kcap each), cnt, lse written"},
+        "measured_peaks": peaks,
+        "fwd_bwd_frac_of_measured_mfma": (round(value / peaks["mfma_bf16_tflops"], 4) if peaks else None),
         "fwd_tflops": round(fwd_tf, 2),
         "bwd_tflops": round(bwd_tf, 2),
         "roofline": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in roof.items()},
     }
     if not args.no_decode:
-        dec = run_decode(max(args.steps, 20), torch)
+        dec = run_decode(max(args.steps, args.decode_reps), torch)
         out["decode"] = {"value": round(dec["gbs"], 1), "unit": "GB/s", "ms": round(dec["ms"], 5),
-                         "select_ms": round(dec["ms_select"], 5), "bytes": dec["bytes"],
-                         "paged": {"ms": round(dec["ms_paged"], 5), "value": round(dec["gbs_paged"], 1),
+                         "ms_stats": dec["stats"], "bytes": dec["bytes"],
+                         "select_ms": round(dec["ms_select"], 5), "select_ms_stats": dec["sel_stats"],
+                         "select_bytes": dec["sel_bytes"], "select_gbs": round(dec["sel_gbs"], 1),
+                         "end_to_end": {"ms": round(dec["ms_e2e"], 5), "ms_stats": dec["e2e_stats"],
+                                        "value": round(dec["e2e_gbs"], 1), "unit": "GB/s",
+                                        "counts": "decode bytes + the scores read and idx/cnt/lse written by the "
+                                                  "selection, over select + decode time (one step, L2/MALL evicted)"},
+                         "paged": {"ms": round(dec["ms_paged"], 5), "ms_stats": dec["paged_stats"],
+                                   "value": round(dec["gbs_paged"], 1),
                                    "unit": "GB/s", "layout": "pool of 64-token pages in random order + page table"},
                          "early_stop": {f"tau={t}": {"ms": round(v[0], 5), "history_blocks_used": round(v[1], 2)}
                                         for t, v in dec["early"].items()},
@@ -502,6 +626,8 @@ def main():
                          "roofline": {"kernel": "decode", "bound": "hbm", "achieved": round(dec["gbs"], 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(dec["gbs"] / PEAK_HBM_GBS, 4),
+                                      "frac_of_measured_read": (round(dec["gbs"] / peaks["stream_read_gbs"], 4)
+                                                                if peaks else None),
                                       "traffic": profiled_traffic("decode")}}
     if not args.no_long_decode:
         out["long_decode"] = {

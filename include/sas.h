@@ -383,6 +383,34 @@ sas_status sas_decode_select(const void* q, const void* kbar, int B, int Hq, int
 sas_status sas_profile_enable(int on);
 int sas_profile_collect(int max, char* names, int name_len, int* launches, double* total_ms);
 
+/*
+ * sas_profile_collect_launches: like sas_profile_collect, but one entry per recorded launch
+ * in launch order (names as above, ms[i] its event time), for medians and percentiles. At
+ * most `max` entries are written; the record is cleared either way. Returns the count, or
+ * -1 if an event query failed.
+ */
+int sas_profile_collect_launches(int max, char* names, int name_len, double* ms);
+
+/*
+ * Measurement microkernels (not part of the pages' method): what the chip delivers, so
+ * achieved rates can be quoted against measured peaks beside the vendor's.
+ *
+ * sas_measure_mfma: `workgroups` workgroups of 4 waves, each wave running `iters` rounds of
+ * 8 independent bf16 32x32x16 MFMAs (32768 FLOP each), i.e. workgroups * 4 * iters * 8 *
+ * 32768 FLOP in all; the caller times the launch with events on `stream`. clocks: device
+ * uint64 [2 * workgroups], out: per workgroup, the shader-clock cycles (s_memtime) and the
+ * constant 100 MHz counter ticks (s_memrealtime) of wave 0's loop, so clock = cycles /
+ * ticks * 100 MHz. sink: device float[1], never written in practice.
+ *
+ * sas_measure_read: one streaming read of `bytes` (a multiple of 16; buf 16-byte aligned)
+ * with 16-byte loads from 4096 workgroups; sink as above.
+ *
+ * Both return SAS_ERR_INVALID_ARG on a NULL pointer or a non-positive size, SAS_ERR_HIP on
+ * a launch failure.
+ */
+sas_status sas_measure_mfma(int workgroups, int iters, unsigned long long* clocks, float* sink, void* stream);
+sas_status sas_measure_read(const void* buf, size_t bytes, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

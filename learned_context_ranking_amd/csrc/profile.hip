@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "../../include/sas.h"
+#include "sas_common.h"
 #include "sas_kernels.h"
 
 namespace sas {
@@ -105,6 +106,101 @@ int sas_profile_collect(int max, char* names, int name_len, int* launches, doubl
     ++n;
   }
   return n;
+}
+
+int sas_profile_collect_launches(int max, char* names, int name_len, double* ms) {
+  using namespace sas;
+  std::lock_guard<std::mutex> lk(g_mu);
+  int rc = 0, n = 0;
+  for (const Rec& r : g_recs) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) rc = -1;
+    if (n < max) {
+      if (names != nullptr && name_len > 0) {
+        strncpy(names + (size_t)n * name_len, r.name, (size_t)name_len - 1);
+        names[(size_t)n * name_len + name_len - 1] = '\0';
+      }
+      if (ms != nullptr) ms[n] = t;
+      ++n;
+    }
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return rc != 0 ? -1 : n;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- measurement kernels
+// Not part of the method: microkernels that measure what the chip delivers, so that
+// achieved rates can be quoted against measured peaks as well as the vendor's.
+
+namespace sas {
+namespace {
+
+// Independent chains of bf16 32x32x16 MFMAs (8 accumulators per wave, so no product
+// waits on the previous one), one wave per SIMD. Wave 0 of each workgroup records the
+// shader-clock and the constant-rate (100 MHz) counters around its loop.
+__global__ __launch_bounds__(256) void mfma_loop_kernel(int iters, unsigned long long* clocks, float* sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(1.0f + 0.001f * (lane + e));
+    b[e] = (__bf16)(0.5f - 0.001f * (lane - e));
+  }
+  f32x16 acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if (threadIdx.x == 0) {
+    clocks[2 * blockIdx.x] = t1 - t0;
+    clocks[2 * blockIdx.x + 1] = r1 - r0;
+  }
+  if (s == 1234.5678f) sink[0] = s;   // keeps the products (never true for these inputs)
+}
+
+// Streaming read of a buffer with 16-byte loads, grid-stride; the sum is written only
+// under a condition that is never true, so the loads are not removed.
+__global__ __launch_bounds__(256) void read_kernel(const f32x4* p, size_t n4, float* sink) {
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) acc += p[i];
+  if (acc[0] + acc[1] + acc[2] + acc[3] == 1234.5678f) sink[0] = acc[0];
+}
+
+}  // namespace
+}  // namespace sas
+
+extern "C" {
+
+sas_status sas_measure_mfma(int workgroups, int iters, unsigned long long* clocks, float* sink, void* stream) {
+  if (workgroups <= 0 || iters <= 0 || clocks == nullptr || sink == nullptr) return SAS_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(sas::mfma_loop_kernel, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream, iters,
+                     clocks, sink);
+  return hipGetLastError() == hipSuccess ? SAS_OK : SAS_ERR_HIP;
+}
+
+sas_status sas_measure_read(const void* buf, size_t bytes, float* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr || bytes < 16 || ((uintptr_t)buf & 15u) != 0) return SAS_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(sas::read_kernel, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const sas::f32x4*)buf,
+                     bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? SAS_OK : SAS_ERR_HIP;
 }
 
 }  // extern "C"

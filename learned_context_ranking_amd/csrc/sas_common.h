@@ -199,6 +199,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
 
 // Position of key k within its 16-key group when a transposed operand is staged in LDS
 // so that each lane's 8 MFMA k-values are contiguous: a 32x32x16 accumulator gives lane

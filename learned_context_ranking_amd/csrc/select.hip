@@ -5,12 +5,14 @@
 // history blocks are attended. Selection compares the fp32 scores themselves; ties go to
 // the lower block index, -0 equals +0 and NaN ranks as -inf.
 //
-// Each lane holds PL scores (element m = lane + 64 i, so loads are coalesced). The K-th
-// largest order-preserving key is found by fixing its 32 bits from the top: a candidate
-// bit stays set when at least K keys are >= the candidate, counted with one ballot per
-// register. Blocks strictly above the threshold are kept; among the blocks equal to it the
-// lowest indices fill the remaining places. A ballot prefix count writes the kept indices
-// in ascending order without any sort.
+// Each lane holds PL scores (element m = lane + 64 i, so loads are coalesced); only the
+// registers that hold valid scores of the row take part (rows of a prefill have j valid
+// scores). The K-th largest order-preserving key is found by fixing its 32 bits from the
+// top: a candidate bit stays set when at least K keys are >= the candidate, counted with
+// one ballot per register; the search stops as soon as a candidate admits exactly K keys
+// (they are the kept set). Otherwise blocks strictly above the threshold are kept and,
+// among the blocks equal to it, the lowest indices fill the remaining places. A ballot
+// prefix count writes the kept indices in ascending order without any sort.
 #include "sas_common.h"
 #include "sas_kernels.h"
 
@@ -32,9 +34,17 @@ __device__ __forceinline__ float log_gate(int gate, float x, float norm) {
   return norm == -INFINITY ? -INFINITY : x - norm;
 }
 
-template <int PL>
+// GATE: the activation whose log g is written (a compile-time choice, so each launch
+// carries only its own code path: the per-register walks below are fully unrolled)
+constexpr int kStageCap = 256;   // rows with kcap up to this stage their output in LDS
+
+template <int PL, int GATE>
 __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
+  // kept (index, log g) of each wave's row, written out with coalesced stores at the end
+  __shared__ int s_idx[4][kStageCap];
+  __shared__ float s_lg[4][kStageCap];
   const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.R) return;  // uniform per wave
   int valid;
@@ -47,17 +57,18 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   valid = min(max(valid, 0), a.cols);
   const float* srow = a.s + row * a.ld;
 
+  // Loads without branches (the index clamped into the valid columns, which are the only
+  // ones read), so all PL loads are in flight together; masks are applied afterwards.
   float x[PL];
+  if (valid > 0) {
+#pragma unroll
+    for (int i = 0; i < PL; ++i) x[i] = srow[min(lane + 64 * i, valid - 1)];
+  }
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
-    const int m = lane + 64 * i;
-    float v = -INFINITY;
-    if (m < valid) {
-      v = srow[m];
-      if (v != v) v = -INFINITY;  // NaN ranks as -inf
-      if (v == 0.0f) v = 0.0f;    // -0 -> +0
-    }
-    x[i] = v;
+    float v = valid > 0 ? x[i] : -INFINITY;
+    v = (lane + 64 * i < valid && v == v) ? v : -INFINITY;   // NaN ranks as -inf
+    x[i] = v == 0.0f ? 0.0f : v;                             // -0 -> +0
   }
 
   // LSE over the valid scores.
@@ -73,7 +84,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     sum = wave_sum(sum);
     lse = mx + logf(sum);
   }
-  if (a.lse != nullptr && lane == 0 && (!a.do_select || a.gate == kGateSoftmax)) a.lse[row] = lse;
+  if (a.lse != nullptr && lane == 0 && (!a.do_select || GATE == kGateSoftmax)) a.lse[row] = lse;
   if (a.g != nullptr) {
     float* grow = a.g + row * a.ld;
 #pragma unroll
@@ -88,22 +99,37 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   int32_t* idx_row = a.idx + row * a.kcap;
   float* lg_row = a.logg != nullptr ? a.logg + row * a.kcap : nullptr;
   if (k > 0) {
+    const int nreg = (valid + 63) >> 6;   // registers holding valid scores (uniform)
     uint32_t key[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i < valid) ? order_key(x[i]) : 0u;
     // Valid keys are >= order_key(-inf) = 0x007FFFFF > 0, so padding (key 0) never reaches
     // the threshold.
     uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int c = 0;
+    if (k < valid) {
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        // per-lane counts on the vector ALUs, one wave reduction per bit (a ballot and a
+        // scalar popcount per register would queue on the CU's single scalar unit)
+        int cl = 0;
 #pragma unroll
-      for (int i = 0; i < PL; ++i) c += __popcll(__ballot(key[i] >= cand));
-      if (c >= k) T = cand;
+        for (int i = 0; i < PL; ++i)
+          if (i < nreg) cl += key[i] >= cand ? 1 : 0;
+        const int c = wave_sum_i(cl);
+        if (c >= k) {
+          T = cand;
+          // exactly K keys are >= cand: they are the kept set, whatever the lower bits
+          // (selected below as the keys > cand - 1, with no ties to break)
+          if (c == k) { T = cand - 1u; break; }
+        }
+      }
     }
-    int n_gt = 0;
+    // (k == valid keeps every valid block: T = 0 is below every valid key)
+    int gl = 0;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) n_gt += __popcll(__ballot(key[i] > T));
+    for (int i = 0; i < PL; ++i)
+      if (i < nreg) gl += key[i] > T ? 1 : 0;
+    const int n_gt = wave_sum_i(gl);
     const int need_eq = k - n_gt;
     const unsigned long long lt = (1ull << lane) - 1ull;
     // calls f(i, pos) for every kept register i of this lane, pos = its output slot
@@ -111,6 +137,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
       int base = 0, eq_before = 0;
 #pragma unroll
       for (int i = 0; i < PL; ++i) {
+        if (i >= nreg) break;
         const bool eq = key[i] == T;
         const unsigned long long beq = __ballot(eq);
         const int eq_rank = eq_before + __popcll(beq & lt);
@@ -122,7 +149,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
       }
     };
     float norm = lse;   // the gate's normaliser (reported as lse)
-    if (a.gate == kGateSoftmaxSelected) {
+    if (GATE == kGateSoftmaxSelected) {
       float m = -INFINITY, sum = 0.0f;   // online LSE over the kept scores
       walk([&](int i, int) {
         if (x[i] > m) { sum = sum * expf(m - x[i]) + 1.0f; m = x[i]; }
@@ -131,36 +158,66 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
       const float wm = wave_max(m);
       sum = wave_sum(m == -INFINITY ? 0.0f : sum * expf(m - wm));
       norm = wm == -INFINITY ? -INFINITY : wm + logf(sum);
-    } else if (a.gate != kGateSoftmax) {
+    } else if (GATE != kGateSoftmax) {
       norm = 0.0f;
     }
-    if (a.lse != nullptr && lane == 0 && a.gate != kGateSoftmax) a.lse[row] = norm;
-    walk([&](int i, int pos) {
-      idx_row[pos] = lane + 64 * i;
-      if (lg_row != nullptr) lg_row[pos] = log_gate(a.gate, x[i], norm);
-    });
-  } else if (a.lse != nullptr && lane == 0 && a.gate != kGateSoftmax) {
-    a.lse[row] = a.gate == kGateSoftmaxSelected ? -INFINITY : 0.0f;
+    if (a.lse != nullptr && lane == 0 && GATE != kGateSoftmax) a.lse[row] = norm;
+    if (a.kcap <= kStageCap) {
+      // a row's kept entries are few per register (one or two lanes): gather them in LDS
+      walk([&](int i, int pos) {
+        s_idx[wv][pos] = lane + 64 * i;
+        s_lg[wv][pos] = log_gate(GATE, x[i], norm);
+      });
+    } else {
+      walk([&](int i, int pos) {
+        idx_row[pos] = lane + 64 * i;
+        if (lg_row != nullptr) lg_row[pos] = log_gate(GATE, x[i], norm);
+      });
+    }
+  } else if (a.lse != nullptr && lane == 0 && GATE != kGateSoftmax) {
+    a.lse[row] = GATE == kGateSoftmaxSelected ? -INFINITY : 0.0f;
   }
-  for (int p = k + lane; p < a.kcap; p += 64) {
-    idx_row[p] = -1;
-    if (lg_row != nullptr) lg_row[p] = 0.0f;
+  if (a.kcap <= kStageCap) {
+    // the row's LDS entries were written by this wave's own lanes: make them visible to
+    // the other lanes (LDS accesses of one wave complete in order once issued)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int p = lane; p < a.kcap; p += 64) {
+      const bool kept = p < k;
+      idx_row[p] = kept ? s_idx[wv][p] : -1;
+      if (lg_row != nullptr) lg_row[p] = kept ? s_lg[wv][p] : 0.0f;
+    }
+  } else {
+    for (int p = k + lane; p < a.kcap; p += 64) {
+      idx_row[p] = -1;
+      if (lg_row != nullptr) lg_row[p] = 0.0f;
+    }
   }
   if (lane == 0) a.cnt[row] = k;
+}
+
+template <int PL>
+static void launch_select_pl(const SelectArgs& a, dim3 grid, dim3 block, hipStream_t st) {
+  const int gate = a.do_select ? a.gate : kGateSoftmax;   // gates only: the softmax normaliser
+  if (gate == kGateSoftmaxSelected) hipLaunchKernelGGL((select_kernel<PL, kGateSoftmaxSelected>), grid, block, 0, st, a);
+  else if (gate == kGateSigmoid) hipLaunchKernelGGL((select_kernel<PL, kGateSigmoid>), grid, block, 0, st, a);
+  else if (gate == kGateExp) hipLaunchKernelGGL((select_kernel<PL, kGateExp>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((select_kernel<PL, kGateSoftmax>), grid, block, 0, st, a);
 }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)((a.R + 3) / 4)), block(256);
   const int c = a.cols;
   ProfScope prof("select", st);
-  if (c <= 64) hipLaunchKernelGGL(select_kernel<1>, grid, block, 0, st, a);
-  else if (c <= 128) hipLaunchKernelGGL(select_kernel<2>, grid, block, 0, st, a);
-  else if (c <= 256) hipLaunchKernelGGL(select_kernel<4>, grid, block, 0, st, a);
-  else if (c <= 512) hipLaunchKernelGGL(select_kernel<8>, grid, block, 0, st, a);
-  else if (c <= 1024) hipLaunchKernelGGL(select_kernel<16>, grid, block, 0, st, a);
-  else if (c <= 2048) hipLaunchKernelGGL(select_kernel<32>, grid, block, 0, st, a);
-  else if (c <= 4096) hipLaunchKernelGGL(select_kernel<64>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(select_kernel<128>, grid, block, 0, st, a);
+  if (c <= 64) launch_select_pl<1>(a, grid, block, st);
+  else if (c <= 128) launch_select_pl<2>(a, grid, block, st);
+  else if (c <= 256) launch_select_pl<4>(a, grid, block, st);
+  else if (c <= 512) launch_select_pl<8>(a, grid, block, st);
+  else if (c <= 1024) launch_select_pl<16>(a, grid, block, st);
+  else if (c <= 2048) launch_select_pl<32>(a, grid, block, st);
+  else if (c <= 4096) launch_select_pl<64>(a, grid, block, st);
+  else launch_select_pl<128>(a, grid, block, st);
   return hipGetLastError();
 }
 

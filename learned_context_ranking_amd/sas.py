@@ -49,6 +49,9 @@ SIGNATURES = {
     "sas_decode_noalloc": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P], _I),
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
+    "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
+    "sas_measure_mfma": ([_I, _I, _P, _P, _P], _I),
+    "sas_measure_read": ([_P, _SZ, _P, _P], _I),
 }
 
 
@@ -364,3 +367,28 @@ def profile_collect(max_kernels: int = 32, name_len: int = 32):
         nm = names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode()
         out[nm] = (int(launches[i]), float(total[i]))
     return out
+
+
+def profile_collect_launches(max_launches: int = 4096, name_len: int = 32):
+    """Every launch recorded since the last collect, in launch order: [(name, ms)]. Waits
+    for the recorded events."""
+    names = ctypes.create_string_buffer(max_launches * name_len)
+    ms = (ctypes.c_double * max_launches)()
+    n = lib().sas_profile_collect_launches(max_launches, names, name_len, ctypes.cast(ms, ctypes.c_void_p))
+    if n < 0:
+        raise RuntimeError("sas_profile_collect_launches: an event query failed")
+    return [(names.raw[i * name_len:(i + 1) * name_len].split(b"\0", 1)[0].decode(), float(ms[i]))
+            for i in range(n)]
+
+
+def measure_mfma(workgroups, iters, clocks, sink, stream=None):
+    """Launch the bf16 MFMA loop (sas_measure_mfma) on the current stream; clocks is a
+    device int64 tensor of 2 * workgroups entries, sink a device float tensor."""
+    dev = clocks.device
+    _check(lib().sas_measure_mfma(int(workgroups), int(iters), _ptr(clocks), _ptr(sink),
+                                  _stream(dev) if stream is None else stream))
+
+
+def measure_read(buf, sink):
+    """One streaming read of the whole of `buf` (sas_measure_read) on the current stream."""
+    _check(lib().sas_measure_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf.device)))
