@@ -228,8 +228,20 @@ def run_train(w, steps, warmup, torch, kernel_timing=True):
             outside.append((a_, b_))
     torch.cuda.synchronize()
     ms["fwd_bwd_gate_outside"] = float(np.mean([a_.elapsed_time(b_) for a_, b_ in outside]))
+    # score-gradient norm under the method's gate (softmax over the history) against the
+    # kept-set normalisation of a binary Top-K mask ([SAS-ko] choice 3), same inputs
+    gnorm = {}
+    for gate in ("softmax", "softmax_selected"):
+        idx_, cnt_, lse_s, logg_ = sas.sas_topk_select(t["s"], w.topk, kcap=w.topk, cols=NB, gate=gate)
+        sas.sas_attn_fwd(t["Q"], t["K"], t["V"], idx_, cnt_, logg_, scale, out=O, lse_out=lse)
+        sas.sas_attn_bwd(t["Q"], t["K"], t["V"], O, t["dO"], lse, idx_, cnt_, logg_, scale, ws=ws,
+                         outs=(dQ, dK, dV, dg))
+        sas.sas_gates_bwd(t["s"], lse_s, idx_, cnt_, dg, cols=NB, out=ds, gate=gate)
+        gnorm[gate] = float(torch.linalg.vector_norm(ds.double()))
+    gnorm["ratio"] = gnorm["softmax_selected"] / gnorm["softmax"]
     return dict(ms_step=ms_step, ms=ms, kern_ms=kern_ms, pairs=pairs, flop_fwd=flop_fwd,
-                flop_bwd=flop_bwd, host=host, cnt=cnt_h, ev_stats=ev_stats, kern_stats=kern_stats)
+                flop_bwd=flop_bwd, host=host, cnt=cnt_h, ev_stats=ev_stats, kern_stats=kern_stats,
+                gate_grad_norm=gnorm)
 
 
 def run_decode(steps, torch):
@@ -602,6 +614,10 @@ def main():
                    "gbs": round(select_bytes(w.NB, w.NB, w.B * w.Hkv, w.topk) / (ms["sel"] * 1e-3) / 1e9, 1),
                    "counts": "valid scores read (row j: j of them) + idx/logg (kcap each), cnt, lse written"},
         "measured_peaks": peaks,
+        "score_grad_norm": {**{k: round(v, 4) for k, v in tr["gate_grad_norm"].items()},
+                            "what": "|ds| over the whole score tensor after select -> fwd -> bwd -> gates_bwd "
+                                    "with the history softmax gate vs the kept-set softmax (binary Top-K "
+                                    "mask normalisation), same N(0,1) inputs"},
         "fwd_bwd_frac_of_measured_mfma": (round(value / peaks["mfma_bf16_tflops"], 4) if peaks else None),
         "fwd_tflops": round(fwd_tf, 2),
         "bwd_tflops": round(bwd_tf, 2),

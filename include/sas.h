@@ -392,6 +392,17 @@ int sas_profile_collect(int max, char* names, int name_len, int* launches, doubl
 int sas_profile_collect_launches(int max, char* names, int name_len, double* ms);
 
 /*
+ * sas_debug_workgroup_order - a debugging aid (not part of the pages' method): with seed != 0,
+ * the attention forward, both backward passes and decode take their work items in a
+ * permuted order (work item = (workgroup * mul + add) mod grid, mul coprime with the grid
+ * size, both derived from the seed); seed 0 (the default) restores the natural order.
+ * Results do not depend on the order (every output element has one producer and a fixed
+ * reduction order), which the determinism tests check with it. Library-wide setting,
+ * read at each launch; returns SAS_OK.
+ */
+sas_status sas_debug_workgroup_order(unsigned long long seed);
+
+/*
  * Measurement microkernels (not part of the pages' method): what the chip delivers, so
  * achieved rates can be quoted against measured peaks beside the vendor's.
  *

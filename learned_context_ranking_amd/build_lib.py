@@ -54,5 +54,40 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libsas_asan.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime shipped with ROCm's LLVM (for LD_PRELOAD)."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not hits:
+        raise RuntimeError("no libclang_rt.asan-x86_64.so under /opt/rocm/llvm")
+    return hits[-1]
+
+
+def build_asan(verbose: bool = False) -> str:
+    """The same library with AddressSanitizer on its host code only (the device code is
+    built as usual): checks the C ABI layer's argument checks, error strings, workspace
+    queries and measurement bookkeeping for host memory errors. Written to _build/asan/."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    flags = [f for f in FLAGS if f != "-O3"] + ["-O1", "-g", "-fno-omit-frame-pointer",
+                                                "-Xarch_host", "-fsanitize=address"]
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(ASAN_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(min(len(cmds), os.cpu_count() or 1, 8)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address",
+          "-shared-libasan", *objs, "-o", ASAN_LIB], verbose)
+    return ASAN_LIB
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -35,11 +35,6 @@
 #include "sas_common.h"
 #include "sas_kernels.h"
 
-// Build-time tuning knobs (defaults are the measured best on gfx950)
-#ifndef SAS_DQ_WPE
-#define SAS_DQ_WPE 2
-#endif
-
 namespace sas {
 
 constexpr int kDkvMinSeg = 64;   // shortest segment (items) a key block's list is cut into
@@ -239,15 +234,32 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const int4* red_tab, in
   const int4 e = red_tab[blockIdx.x];
   if (e.x < 0) return;
   const size_t rows = ((size_t)bh * n + (size_t)e.x * kBlock) * D;
-  for (int i = threadIdx.x; i < kBlock * D; i += 256) {
-    float k = dK[rows + i], v = dV[rows + i];
-    for (int sgm = 1; sgm < e.y; ++sgm) {
-      const float* p = part + (size_t)(e.z + sgm - 1) * (2 * kBlock * D);
-      k += p[i];
-      v += p[kBlock * D + i];
+  // 16-byte accesses; the partials of four segments are loaded together, then added in
+  // segment order (the result does not depend on the grouping)
+  constexpr int N4 = kBlock * D / 4;
+  const f32x4* pp = reinterpret_cast<const f32x4*>(part) + (size_t)e.z * (2 * N4);
+  for (int i = threadIdx.x; i < N4; i += 256) {
+    f32x4 k = reinterpret_cast<const f32x4*>(dK + rows)[i];
+    f32x4 v = reinterpret_cast<const f32x4*>(dV + rows)[i];
+    int sgm = 1;
+    for (; sgm + 4 <= e.y; sgm += 4) {
+      f32x4 pk[4], pv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4* p = pp + (size_t)(sgm - 1 + u) * (2 * N4);
+        pk[u] = p[i];
+        pv[u] = p[N4 + i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { k += pk[u]; v += pv[u]; }
     }
-    dK[rows + i] = k;
-    dV[rows + i] = v;
+    for (; sgm < e.y; ++sgm) {
+      const f32x4* p = pp + (size_t)(sgm - 1) * (2 * N4);
+      k += p[i];
+      v += p[N4 + i];
+    }
+    reinterpret_cast<f32x4*>(dK + rows)[i] = k;
+    reinterpret_cast<f32x4*>(dV + rows)[i] = v;
   }
 }
 
@@ -261,7 +273,7 @@ __global__ __launch_bounds__(256) void dkv_reduce_kernel(const int4* red_tab, in
 // while block t is computed. The copy is issued on every step, past the end of the list it
 // repeats the last block, so the compiler's wait tracking stays exact.
 template <int D, bool OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SAS_DQ_WPE, SAS_DQ_WPE)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(const AttnArgs a, int nsplit) {
   constexpr int NW = 4;
   __shared__ __attribute__((aligned(16))) uint16_t sk0[Tile<D>::ELEMS];
@@ -275,8 +287,9 @@ void dq_kernel(const AttnArgs a, int nsplit) {
   const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
   const int BH = a.B * a.Hkv;
   const int per_j = BH * nsplit;
-  const int j = NB - 1 - (int)(blockIdx.x / per_j);
-  const int r = blockIdx.x % per_j;
+  const unsigned bid = wg_index(a.wg);
+  const int j = NB - 1 - (int)(bid / per_j);
+  const int r = bid % per_j;
   const int split = r / BH;
   const int h = (r % BH) % a.Hkv, b = (r % BH) / a.Hkv;
   const int head0 = split * 2;
@@ -551,9 +564,10 @@ void dkv_kernel(const AttnArgs a) {
   const int BHp = a.B * a.Hkv;
   const int P = min(2, BHp);
   const int S = NB + a.dkv_budget;   // plan slots per pair
-  const int phase = (int)(blockIdx.x / ((unsigned)P * S));
+  const unsigned bid = wg_index(a.wg);
+  const int phase = (int)(bid / ((unsigned)P * S));
   const int np = min(P, BHp - phase * P);
-  const int rem = (int)(blockIdx.x - (unsigned)phase * P * S);
+  const int rem = (int)(bid - (unsigned)phase * P * S);
   const int slot = rem / np;
   const int rr = phase * P + rem % np;
   const int h = rr % a.Hkv, b = rr / a.Hkv;
@@ -779,8 +793,9 @@ static int dq_splits(int G) { return (G + 1) / 2; }
 
 
 // Partial-result slots of the key-major pass per (b, KV head): enough to cut the longest
-// lists of a few pairs into pieces, at most 2048 slots in all.
-static int dkv_budget(long long BH) { return (int)std::max<long long>(4, std::min<long long>(64, 2048 / std::max<long long>(BH, 1))); }
+// lists of a few pairs into pieces (two key-major workgroups share a CU, so a long segment
+// runs at about half a CU's rate), at most 4096 slots in all.
+static int dkv_budget(long long BH) { return (int)std::max<long long>(4, std::min<long long>(128, 4096 / std::max<long long>(BH, 1))); }
 
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap) {
   const size_t NB = (size_t)n / kBlock;
@@ -820,10 +835,12 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   const int nsplit = dq_splits(a.Hq / a.Hkv);
   {
     ProfScope prof("dq", st);
+    const unsigned grid = (unsigned)(nrows * nsplit);
+    a.wg = wg_order(grid);
     if (a.gate_out)
-      hipLaunchKernelGGL((dq_kernel<D, true>), dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+      hipLaunchKernelGGL((dq_kernel<D, true>), dim3(grid), dim3(256), 0, st, a, nsplit);
     else
-      hipLaunchKernelGGL((dq_kernel<D, false>), dim3((unsigned)(nrows * nsplit)), dim3(256), 0, st, a, nsplit);
+      hipLaunchKernelGGL((dq_kernel<D, false>), dim3(grid), dim3(256), 0, st, a, nsplit);
   }
   if (nsplit > 1 && a.kcap > 0) {
     ProfScope prof("dg_reduce", st);
@@ -834,6 +851,7 @@ static hipError_t launch_bwd_d(AttnArgs& a, hipStream_t st) {
   {
     ProfScope prof("dkv", st);
     const unsigned grid = (unsigned)((long long)a.B * a.Hkv * (NB + a.dkv_budget));
+    a.wg = wg_order(grid);
     if (a.gate_out) hipLaunchKernelGGL((dkv_kernel<D, true>), dim3(grid), dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dkv_kernel<D, false>), dim3(grid), dim3(256), 0, st, a);
   }

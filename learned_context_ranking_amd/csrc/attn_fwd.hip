@@ -32,13 +32,6 @@
 
 namespace sas {
 
-#ifndef SAS_FWD_KBATCH
-#define SAS_FWD_KBATCH 0   // K operand reads in batches ahead of their products
-#endif
-#ifndef SAS_FWD_VBATCH
-#define SAS_FWD_VBATCH 1   // V^T operand reads issued before the softmax
-#endif
-
 constexpr float kRescaleThreshold = 8.0f;   // log2 of the largest unnormalised exponential
 
 // 32 rows per wave (NTILE 1) is sized to leave room for two waves per SIMD.
@@ -63,8 +56,9 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   // and all its query-head splits stay on one XCD (one L2) when B * Hkv is a multiple of 8.
   const int BH = a.B * a.Hkv;
   const int per_j = BH * nsplit;
-  const int j = NB - 1 - (int)(blockIdx.x / per_j);
-  const int r = blockIdx.x % per_j;
+  const unsigned bid = wg_index(a.wg);
+  const int j = NB - 1 - (int)(bid / per_j);
+  const int r = bid % per_j;
   const int split = r / BH;             // splits of one (b, h) are BH workgroups apart: same XCD when BH % 8 == 0
   const int h = (r % BH) % a.Hkv, b = (r % BH) / a.Hkv;
   const int head0 = split * hpw;
@@ -189,9 +183,6 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) kr[u][mt] = as_bf16x8(ld16(&kc[32 * mt * D + (rx ^ ((k0 + u) << 4))]));
-#if SAS_FWD_KBATCH
-      __builtin_amdgcn_sched_barrier(0);
-#endif
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -207,7 +198,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
                        lds_tr16(&vc[(r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3))]));
     };
     bf16x8 va[D / 32][2][2];   // [dt][mt][hh]
-    if constexpr (NTILE == 1 && SAS_FWD_VBATCH) {
+    if constexpr (NTILE == 1) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -282,7 +273,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const bf16x8 v = (NTILE == 1 && SAS_FWD_VBATCH) ? va[dt][mt][hh] : read_va(dt, mt, hh);
+          const bf16x8 v = NTILE == 1 ? va[dt][mt][hh] : read_va(dt, mt, hh);
 #pragma unroll
           for (int nt = 0; nt < NTILE; ++nt) oacc[dt][nt] = mfma32(v, pf[mt][nt][hh], oacc[dt][nt]);
         }
@@ -327,8 +318,10 @@ template <int D, int NTILE, int NW, bool OUT>
 static hipError_t launch_fwd_o(const AttnArgs& a, int nsplit, int hpw, hipStream_t st) {
   const int NB = a.n / kBlock;
   const unsigned grid = (unsigned)(NB * a.B * a.Hkv * nsplit);
+  AttnArgs b = a;
+  b.wg = wg_order(grid);
   ProfScope prof("fwd", st);
-  hipLaunchKernelGGL((fwd_kernel<D, NTILE, NW, OUT>), dim3(grid), dim3(64 * NW), 0, st, a, nsplit, hpw);
+  hipLaunchKernelGGL((fwd_kernel<D, NTILE, NW, OUT>), dim3(grid), dim3(64 * NW), 0, st, b, nsplit, hpw);
   return hipGetLastError();
 }
 
@@ -346,25 +339,14 @@ void head_split(int G, int* nsplit, int* hpw, int* nw) {
   *nw = *hpw <= 1 ? 1 : (*hpw <= 2 ? 2 : 4);
 }
 
-#ifndef SAS_FWD_ROWS
-#define SAS_FWD_ROWS 32   // query rows per wave: 64 (1 wave per head) or 32 (2 waves per head)
-#endif
-#ifndef SAS_FWD_HPW32
-#define SAS_FWD_HPW32 2   // heads per workgroup with 32-row waves (2 -> 4 waves, 4 -> 8 waves)
-#endif
-
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   int nsplit, hpw, nw;
   head_split(G, &nsplit, &hpw, &nw);
-  if (SAS_FWD_ROWS == 32 && G >= 2) {
-    // two waves per head, SAS_FWD_HPW32 heads per workgroup (split evenly)
-    nsplit = (G + SAS_FWD_HPW32 - 1) / SAS_FWD_HPW32;
+  if (G >= 2) {
+    // 32 rows per wave (two waves per head), two heads per workgroup (split evenly)
+    nsplit = (G + 1) / 2;
     hpw = (G + nsplit - 1) / nsplit;
-    if (hpw > 2) {
-      if (a.d == 128) return launch_fwd_t<128, 1, 8>(a, nsplit, hpw, st);
-      return launch_fwd_t<64, 1, 8>(a, nsplit, hpw, st);
-    }
     if (a.d == 128) return launch_fwd_t<128, 1, 4>(a, nsplit, hpw, st);
     return launch_fwd_t<64, 1, 4>(a, nsplit, hpw, st);
   }

@@ -49,8 +49,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const int lane = threadIdx.x;
   const int hl = lane >> 5, ql = lane & 31;
   const int G = a.Hq / a.Hkv;
-  const int chunk = blockIdx.x % a.nchunk;
-  const long long bh = blockIdx.x / a.nchunk;
+  const unsigned bid = wg_index(a.wg);
+  const int chunk = bid % a.nchunk;
+  const long long bh = bid / a.nchunk;
   const int h = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
   const int L = min(max(a.kv_len[b], 1), (int)a.Lmax);
   const int cur = (L - 1) / kBlock;
@@ -364,6 +365,7 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   const long long pairs = (long long)a.B * a.Hkv;
   decode_plan(a);
   const unsigned grid = (unsigned)(pairs * a.nchunk);
+  a.wg = wg_order(grid);
   {
     ProfScope prof("decode", st);
     const bool paged = a.page_table != nullptr, early = a.order != nullptr;

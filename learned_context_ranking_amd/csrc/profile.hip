@@ -63,9 +63,44 @@ ProfScope::~ProfScope() {
   g_recs.push_back(Rec{name_, (hipEvent_t)a_, b});
 }
 
+namespace {
+
+std::atomic<unsigned long long> g_order_seed{0};
+
+unsigned gcd_u(unsigned a, unsigned b) {
+  while (b != 0) {
+    const unsigned t = a % b;
+    a = b;
+    b = t;
+  }
+  return a;
+}
+
+}  // namespace
+
+WgOrder wg_order(unsigned grid) {
+  WgOrder o;
+  const unsigned long long seed = g_order_seed.load(std::memory_order_relaxed);
+  if (seed == 0 || grid <= 1) return o;
+  // an odd multiplier near grid / phi (a large stride through the grid), nudged until it
+  // is coprime with the grid size; a seed-dependent offset
+  unsigned long long m = (unsigned long long)grid * 1000003ull / 1618034ull + (seed % 97ull) * 2ull + 1ull;
+  m %= grid;
+  if (m < 2) m = 2;
+  while (gcd_u((unsigned)m, grid) != 1) m = (m + 1) % grid == 0 ? 1 : m + 1;
+  o.mul = (uint32_t)m;
+  o.add = (uint32_t)((seed * 0x9E3779B97F4A7C15ull) % grid);
+  return o;
+}
+
 }  // namespace sas
 
 extern "C" {
+
+sas_status sas_debug_workgroup_order(unsigned long long seed) {
+  sas::g_order_seed.store(seed, std::memory_order_relaxed);
+  return SAS_OK;
+}
 
 sas_status sas_profile_enable(int on) {
   sas::g_on.store(on != 0, std::memory_order_relaxed);

@@ -22,6 +22,18 @@ class ProfScope {
   void* a_;
 };
 
+// Order in which a launch's workgroups take their work items (a debugging aid, see
+// sas_debug_workgroup_order): work item = (blockIdx.x * mul + add) mod gridDim.x, a
+// bijection when mul and the grid size are coprime. The natural order is mul = 1, add = 0.
+struct WgOrder {
+  uint32_t mul = 1, add = 0;
+};
+// the order for a launch of `grid` workgroups under the library's current debug seed
+WgOrder wg_order(unsigned grid);
+__device__ __forceinline__ unsigned wg_index(WgOrder o) {
+  return (unsigned)(((unsigned long long)blockIdx.x * o.mul + o.add) % gridDim.x);
+}
+
 // gate activations (sas_gate in include/sas.h)
 constexpr int kGateSoftmax = 0, kGateSoftmaxSelected = 1, kGateSigmoid = 2, kGateExp = 3;
 
@@ -113,6 +125,7 @@ struct AttnArgs {
   int4* red_tab;         // split key blocks, per (b, KV head) dkv_budget entries
   float* dkv_part;       // partial dK / dV of segments 1.. of split blocks
   int dkv_budget;        // partial slots per (b, KV head)
+  WgOrder wg;            // workgroup order of the launch (set by the launcher)
 };
 hipError_t launch_fwd(const AttnArgs& a, hipStream_t st);
 size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int n, int d, int kcap);
@@ -142,6 +155,7 @@ struct DecodeArgs {
   const float* order;
   float tau;
   int32_t* used;
+  WgOrder wg;            // workgroup order of the decode launch (set by the launcher)
 };
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap);
 // sets a.bpc and a.nchunk as launch_decode will

@@ -13,7 +13,9 @@ import os
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsas.so")
+# SAS_LIB names another build of the same library (e.g. the AddressSanitizer build of
+# the host layer that the CPU tests load); there is no fallback either way.
+LIB_PATH = os.environ.get("SAS_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsas.so")
 
 SAS_OK, SAS_ERR_INVALID_ARG, SAS_ERR_UNSUPPORTED, SAS_ERR_WORKSPACE, SAS_ERR_HIP = range(5)
 SCOPE = {"sparse": 0, "full": 1}
@@ -50,6 +52,7 @@ SIGNATURES = {
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
     "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
+    "sas_debug_workgroup_order": ([ctypes.c_ulonglong], _I),
     "sas_measure_mfma": ([_I, _I, _P, _P, _P], _I),
     "sas_measure_read": ([_P, _SZ, _P, _P], _I),
 }
@@ -392,3 +395,9 @@ def measure_mfma(workgroups, iters, clocks, sink, stream=None):
 def measure_read(buf, sink):
     """One streaming read of the whole of `buf` (sas_measure_read) on the current stream."""
     _check(lib().sas_measure_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(buf.device)))
+
+
+def debug_workgroup_order(seed: int = 0):
+    """Permute the order in which the attention and decode kernels take their work items
+    (seed != 0), or restore the natural order (seed 0). A debugging aid."""
+    _check(lib().sas_debug_workgroup_order(int(seed)))

@@ -200,3 +200,25 @@ def test_decode_early_stop_thresholds():
 def test_decode_early_stop_groups_small_d():
     _early_case(3, 5, 1, 64, 2048, [2048, 777, 130], 12, [0.0, 0.02], seed=8)
     _early_case(2, 32, 8, 128, 64 * 100, [6400, 3000], 63, [0.005, 0.1], seed=9)
+
+
+def test_decode_permuted_workgroup_order():
+    """Decode output is bit-identical when the workgroups take their chunks in a permuted
+    order (split lists are merged in chunk order)."""
+    B, Hq, Hkv, d, Lmax, topk = 3, 8, 2, 128, 4096, 24
+    q_bits = synth.normal_bf16((B, Hq, 1, d), 5, synth.TID_QDEC)[:, :, 0]
+    k_bits = synth.normal_bf16((B, Hkv, Lmax, d), 5, synth.TID_K)
+    v_bits = synth.normal_bf16((B, Hkv, Lmax, d), 5, synth.TID_V)
+    s = synth.scores_normal((B, Hkv, 1, Lmax // 64), 5)
+    kv_len = np.array([4096, 2500, 700], np.int32)
+    rv = ((kv_len - 1) // 64).astype(np.int32)
+    idx, cnt, _, _ = sas.sas_topk_select(dev(s), topk, mode="decode", row_valid=dev(rv), kcap=topk)
+    q, K, V, L = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits), dev(kv_len)
+    o0 = sas.sas_decode(q, K, V, L, idx, cnt, 1.0 / math.sqrt(d))
+    try:
+        sas.debug_workgroup_order(99)
+        o1 = sas.sas_decode(q, K, V, L, idx, cnt, 1.0 / math.sqrt(d))
+    finally:
+        sas.debug_workgroup_order(0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1)
