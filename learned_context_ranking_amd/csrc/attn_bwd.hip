@@ -540,6 +540,20 @@ __global__ void dg_reduce_kernel(const float* part, float* dg, long long n, int 
 // the causal mask of the diagonal items starts masked entries at -inf.
 // Items stream through two LDS slots: the copy of item t + 1 (buffer loads into LDS) is
 // issued right after the barrier that opens item t, and item t is computed meanwhile.
+// Chunk swizzle of the key-major pass's Q / dO tiles: 16-byte chunk c of row r sits at
+// chunk c ^ kv_swz(r). LDS has 64 banks of 4 bytes. Measured with the bank-conflict
+// counter (address patterns replayed over 160 swizzles): an 8-byte (transposing) read is
+// served in groups of 32 consecutive lanes; a 16-byte read in groups of 16 lanes, each
+// half wave split by the parity of lane bits 2..4 (lanes 0-3, 12-15, 20-23, 24-27 form
+// one group). Here a transposing group reads 8 rows x 32 bytes and a 16-byte group
+// 8 rows x 2 chunks; the common tile swizzle, laid out for the forward's patterns, gives
+// both a 2-way conflict. (r mod 8) * 2 (128-element rows) and r & 6 (64-element rows, two
+// to a bank row) put every group of either read on distinct banks.
+template <int D>
+__device__ __forceinline__ int kv_swz(int r) {
+  return D == 128 ? ((r & 7) << 1) : (r & 6);
+}
+
 template <int D, bool OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void dkv_kernel(const AttnArgs a) {
@@ -594,13 +608,13 @@ void dkv_kernel(const AttnArgs a) {
     asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
   }
   const float c2 = a.scale * kLog2e;
-  // lane bases (elements) in the Tile layout: row read of rows 16 rt + lq at d = 32 ks + 8 u
+  // lane bases (elements) in the kv_swz tile layout: row read of rows 16 rt + lq at d = 32 ks + 8 u
   // sits at 16 rt D + (rx0 ^ (ks << 5)); the transposing read of rows 32 q + 4 u + lq / 4
   // (+ 16 for the second half of the k step) at d = 16 dt + 4 (lq % 4) at
   // 32 q D + (tx0 ^ (dt << 4)) (+ 16 D)
-  const int rx0 = lq * D + ((u ^ Tile<D>::swz(lq)) << 3);
+  const int rx0 = lq * D + ((u ^ kv_swz<D>(lq)) << 3);
   const int r0 = 4 * u + (lq >> 2);
-  const int tx0 = r0 * D + ((((lq & 3) >> 1) ^ Tile<D>::swz(r0)) << 3) + 4 * (lq & 1);
+  const int tx0 = r0 * D + ((((lq & 3) >> 1) ^ kv_swz<D>(r0)) << 3) + 4 * (lq & 1);
   const int off0 = a.inv_off[bh * (NB + 1) + m];
   const int nlist = a.inv_off[bh * (NB + 1) + m + 1] - off0;
   const int32_t* list = a.inv_list + bh * NB * a.kcap + off0;
@@ -622,7 +636,7 @@ void dkv_kernel(const AttnArgs a) {
   for (int i = 0; i < NWIN; ++i) {
     const int sidx = 64 * (wave + NW * i) + lane;
     const int r = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
-    voff[i] = (uint32_t)(r * D + ((c ^ Tile<D>::swz(r)) << 3)) * 2u;
+    voff[i] = (uint32_t)(r * D + ((c ^ kv_swz<D>(r)) << 3)) * 2u;
   }
   // list entry e (descending query block; e == nlist is block m itself): query block and
   // base-2 log-gate of the entry's slot
