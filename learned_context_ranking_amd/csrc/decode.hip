@@ -53,14 +53,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const int chunk = bid % a.nchunk;
   const long long bh = bid / a.nchunk;
   const int h = (int)(bh % a.Hkv), b = (int)(bh / a.Hkv);
+  const int t0 = chunk * a.bpc;
+  const int32_t* idx_row = a.idx + bh * a.kcap;
+  const float* lg_row = a.logg != nullptr ? a.logg + bh * a.kcap : nullptr;
+  // The raw entries of the chunk's first list window (lane i: position t0 + i) depend on
+  // neither kv_len nor cnt: loaded together with them, the first copies need one memory
+  // latency less. Which of them count is decided once cnt and kv_len are in.
+  int pre_v = 0;
+  float pre_g = 0.0f;
+  if (t0 + lane > 0 && t0 + lane <= a.kcap) {
+    pre_v = idx_row[t0 + lane - 1];
+    if (lg_row != nullptr) pre_g = lg_row[t0 + lane - 1];
+  }
   const int L = min(max(a.kv_len[b], 1), (int)a.Lmax);
   const int cur = (L - 1) / kBlock;
   const int cnt = min(max(a.cnt[bh], 0), min(a.kcap, cur));
   // list position t: 0 is the current block, t >= 1 the selected block idx[t - 1]
   // (a chunk past the end of a short list is empty: t1 == t0)
-  const int t0 = chunk * a.bpc, t1 = max(t0, min(t0 + a.bpc, cnt + 1));
-  const int32_t* idx_row = a.idx + bh * a.kcap;
-  const float* lg_row = a.logg != nullptr ? a.logg + bh * a.kcap : nullptr;
+  const int t1 = max(t0, min(t0 + a.bpc, cnt + 1));
   const uint16_t* Kh = a.Kc + (size_t)bh * a.Lmax * D;
   const uint16_t* Vh = a.Vc + (size_t)bh * a.Lmax * D;
   const int cbytes = (int)(a.Lmax * D * 2);   // checked on the host to fit 31 bits
@@ -88,8 +98,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     v = cur;
     g = 0.0f;
     if (t > 0 && t < t1) {
-      v = idx_row[t - 1];
-      g = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
+      if (i < 64) {   // the first window, loaded at the start
+        v = pre_v;
+        g = pre_g * kLog2e;
+      } else {
+        v = idx_row[t - 1];
+        g = lg_row != nullptr ? lg_row[t - 1] * kLog2e : 0.0f;
+      }
       if (v < 0 || v >= cur) { v = 0; g = -INFINITY; }
     }
     if (PAGED) {   // logical block -> page; a page id out of range reads nothing
