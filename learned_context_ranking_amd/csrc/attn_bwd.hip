@@ -469,7 +469,7 @@ void dq_kernel(const AttnArgs a, int nsplit) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) dq[dt] = mfma32(ka[dt][hh], dsf[hh], dq[dt]);
     }
-    dgacc = wave_sum(dgacc);
+    dgacc = dpp_sum(dgacc);
     if (lane == 0) dgp[t & 1][wave] = (!DIAG && ok) ? dgacc : 0.0f;
   };
   const std::integral_constant<bool, true> diag_step;

@@ -88,7 +88,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
 }
 
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  v = is_max ? wave_max(v) : wave_sum(v);
+  v = is_max ? dpp_max(v) : dpp_sum(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) red[w] = v;
   __syncthreads();

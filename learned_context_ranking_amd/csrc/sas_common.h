@@ -189,20 +189,32 @@ struct LaneList {
 // flush to zero, which is harmless for softmax weights relative to a maximum >= 1/256).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+// Wave-wide reductions through DPP lane moves, register to register (a butterfly of
+// __shfl_xor compiles to LDS permutes, one round trip each). An inclusive scan within each
+// row of 16 lanes by row shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row
+// contribute the identity), then the row totals carried forward by the broadcasts of lane
+// 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3): lane 63 ends with the total,
+// which is returned as a wave-uniform value. All 64 lanes must be active.
+template <class Op>
+__device__ __forceinline__ int dpp_reduce(int v, int identity, Op op) {
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x111, 0xf, 0xf, false));   // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x112, 0xf, 0xf, false));   // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x114, 0xf, 0xf, false));   // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x118, 0xf, 0xf, false));   // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  v = op(v, __builtin_amdgcn_update_dpp(identity, v, 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+__device__ __forceinline__ int dpp_sum_i(int v) {
+  return dpp_reduce(v, 0, [](int x, int y) { return x + y; });
 }
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+__device__ __forceinline__ float dpp_sum(float v) {
+  return __int_as_float(dpp_reduce(__float_as_int(v), 0,
+                                   [](int x, int y) { return __float_as_int(__int_as_float(x) + __int_as_float(y)); }));
+}
+__device__ __forceinline__ float dpp_max(float v) {
+  return __int_as_float(dpp_reduce(__float_as_int(v), __float_as_int(-INFINITY),
+                                   [](int x, int y) { return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y))); }));
 }
 
 // Position of key k within its 16-key group when a transposed operand is staged in LDS

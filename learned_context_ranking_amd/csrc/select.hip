@@ -75,13 +75,13 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < PL; ++i) mx = fmaxf(mx, x[i]);
-  mx = wave_max(mx);
+  mx = dpp_max(mx);
   float lse = -INFINITY;
   if (mx != -INFINITY) {
     float sum = 0.0f;
 #pragma unroll
     for (int i = 0; i < PL; ++i) sum += expf(x[i] - mx);
-    sum = wave_sum(sum);
+    sum = dpp_sum(sum);
     lse = mx + logf(sum);
   }
   if (a.lse != nullptr && lane == 0 && (!a.do_select || GATE == kGateSoftmax)) a.lse[row] = lse;
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 #pragma unroll
         for (int i = 0; i < PL; ++i)
           if (i < nreg) cl += key[i] >= cand ? 1 : 0;
-        const int c = wave_sum_i(cl);
+        const int c = dpp_sum_i(cl);
         if (c >= k) {
           T = cand;
           // exactly K keys are >= cand: they are the kept set, whatever the lower bits
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 #pragma unroll
     for (int i = 0; i < PL; ++i)
       if (i < nreg) gl += key[i] > T ? 1 : 0;
-    const int n_gt = wave_sum_i(gl);
+    const int n_gt = dpp_sum_i(gl);
     const int need_eq = k - n_gt;
     const unsigned long long lt = (1ull << lane) - 1ull;
     // calls f(i, pos) for every kept register i of this lane, pos = its output slot
@@ -155,8 +155,8 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
         if (x[i] > m) { sum = sum * expf(m - x[i]) + 1.0f; m = x[i]; }
         else if (x[i] != -INFINITY) sum += expf(x[i] - m);
       });
-      const float wm = wave_max(m);
-      sum = wave_sum(m == -INFINITY ? 0.0f : sum * expf(m - wm));
+      const float wm = dpp_max(m);
+      sum = dpp_sum(m == -INFINITY ? 0.0f : sum * expf(m - wm));
       norm = wm == -INFINITY ? -INFINITY : wm + logf(sum);
     } else if (GATE != kGateSoftmax) {
       norm = 0.0f;
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
       if (softmax_like) c += gate(m) * grow[t];
     }
   }
-  c = wave_sum(c);
+  c = dpp_sum(c);
   __syncthreads();
   if (!live) return;  // uniform per wave; no barrier follows
   for (int m = lane; m < a.ld; m += 64) {
