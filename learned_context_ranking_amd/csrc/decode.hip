@@ -58,10 +58,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const float* lg_row = a.logg != nullptr ? a.logg + bh * a.kcap : nullptr;
   // The raw entries of the chunk's first list window (lane i: position t0 + i) depend on
   // neither kv_len nor cnt: loaded together with them, the first copies need one memory
-  // latency less. Which of them count is decided once cnt and kv_len are in.
+  // latency less. Which of them count is decided once cnt and kv_len are in. (Not in the
+  // early-stop form: its in-wave sort leaves no registers for them, and the compiler
+  // then moves state to scratch memory, which costs far more than the latency.)
   int pre_v = 0;
   float pre_g = 0.0f;
-  if (t0 + lane > 0 && t0 + lane <= a.kcap) {
+  if (!EARLY && t0 + lane > 0 && t0 + lane <= a.kcap) {
     pre_v = idx_row[t0 + lane - 1];
     if (lg_row != nullptr) pre_g = lg_row[t0 + lane - 1];
   }
@@ -98,7 +100,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     v = cur;
     g = 0.0f;
     if (t > 0 && t < t1) {
-      if (i < 64) {   // the first window, loaded at the start
+      if (!EARLY && i < 64) {   // the first window, loaded at the start
         v = pre_v;
         g = pre_g * kLog2e;
       } else {

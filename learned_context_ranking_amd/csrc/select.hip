@@ -22,6 +22,10 @@ __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// inverse of order_key (exact for every key order_key produces)
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 // log g of a kept block with score x (NaN already read as -inf) under each activation;
 // norm is the softmax normaliser (LSE over the history or over the kept set)
@@ -133,9 +137,11 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     const int need_eq = k - n_gt;
     const unsigned long long lt = (1ull << lane) - 1ull;
     // calls f(i, pos) for every kept register i of this lane, pos = its output slot
+    // (fully unrolled whatever its size: a rolled loop would index the key registers and
+    // put them in scratch memory)
     auto walk = [&](auto&& f) {
       int base = 0, eq_before = 0;
-#pragma unroll
+#pragma clang loop unroll(full)
       for (int i = 0; i < PL; ++i) {
         if (i >= nreg) break;
         const bool eq = key[i] == T;
@@ -148,12 +154,15 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
         eq_before += __popcll(beq);
       }
     };
+    // The walks take each kept score back from its key (exact), so that x[] is no longer
+    // live: that leaves the widest rows registers to spare.
     float norm = lse;   // the gate's normaliser (reported as lse)
     if (GATE == kGateSoftmaxSelected) {
       float m = -INFINITY, sum = 0.0f;   // online LSE over the kept scores
       walk([&](int i, int) {
-        if (x[i] > m) { sum = sum * expf(m - x[i]) + 1.0f; m = x[i]; }
-        else if (x[i] != -INFINITY) sum += expf(x[i] - m);
+        const float xi = key_score(key[i]);
+        if (xi > m) { sum = sum * expf(m - xi) + 1.0f; m = xi; }
+        else if (xi != -INFINITY) sum += expf(xi - m);
       });
       const float wm = dpp_max(m);
       sum = dpp_sum(m == -INFINITY ? 0.0f : sum * expf(m - wm));
@@ -166,12 +175,12 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
       // a row's kept entries are few per register (one or two lanes): gather them in LDS
       walk([&](int i, int pos) {
         s_idx[wv][pos] = lane + 64 * i;
-        s_lg[wv][pos] = log_gate(GATE, x[i], norm);
+        s_lg[wv][pos] = log_gate(GATE, key_score(key[i]), norm);
       });
     } else {
       walk([&](int i, int pos) {
         idx_row[pos] = lane + 64 * i;
-        if (lg_row != nullptr) lg_row[pos] = log_gate(GATE, x[i], norm);
+        if (lg_row != nullptr) lg_row[pos] = log_gate(GATE, key_score(key[i]), norm);
       });
     }
   } else if (a.lse != nullptr && lane == 0 && GATE != kGateSoftmax) {
