@@ -319,7 +319,7 @@ void dq_kernel(const AttnArgs a, int nsplit) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) dlt += bf2f(ov[e]) * (float)dof[ks][e];
   }
-  dlt += __shfl_xor(dlt, 32, 64);
+  dlt = half_sum(dlt);
   const float lse = a.lse_rows[row_off + ql];
   if (active && hl == 0) {
     a.ndelta[row_off + ql] = -dlt;

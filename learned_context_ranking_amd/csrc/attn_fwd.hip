@@ -227,7 +227,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mt][nt][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = half_max(mx);
       bmax[nt] = mx * c2 + lg2;
       grow |= bmax[nt] > mref[nt] + kRescaleThreshold;
     }
@@ -295,7 +295,7 @@ void fwd_kernel(const AttnArgs a, int nsplit, int hpw) {
   const size_t lse_off = (size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock + wrow0;
 #pragma unroll
   for (int nt = 0; nt < NTILE; ++nt) {
-    const float l = lrow[nt] + __shfl_xor(lrow[nt], 32, 64);
+    const float l = half_sum(lrow[nt]);
     const float inv = 1.0f / l;
     if (hl == 0) a.lse_rows[lse_off + 32 * nt + ql] = (mref[nt] + log2f(l)) * kLn2;
     const int qrow = 32 * nt + ql;

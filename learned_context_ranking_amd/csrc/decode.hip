@@ -224,12 +224,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = half_max(mx);
     const float bmax = mx * c2 + lg2;
     const bool hist_block = EARLY && (t0 + (u >> 1)) > 0;
     if (hist_block && (u & 1) == 0) {   // a history block starts
       dlb = 0.0f;
-      lbefore = lrow + __shfl_xor(lrow, 32, 64);
+      lbefore = half_sum(lrow);
     }
     if (__any(bmax > mref + kDecRescaleThreshold)) {
       const float mnew = fmaxf(mref, bmax);
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     if (hist_block) {
       dlb += ls;
       if (u & 1) {   // the block is complete: keep it, and stop once its mass is small
-        const float dl = dlb + __shfl_xor(dlb, 32, 64);
+        const float dl = half_sum(dlb);
         if (!done) {
           ++used;
           if (dl < a.tau * lbefore) done = true;
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   wait_vm();
   if (EARLY && a.used != nullptr && hl == 0 && ql < G) a.used[(size_t)b * a.Hq + h * G + ql] = used;
 
-  const float l = lrow + __shfl_xor(lrow, 32, 64);
+  const float l = half_sum(lrow);
   if (a.nchunk == 1) {
     // the whole list in one chunk: write the normalised output directly
     if (ql < G) {

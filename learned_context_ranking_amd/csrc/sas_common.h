@@ -189,6 +189,19 @@ struct LaneList {
 // flush to zero, which is harmless for softmax weights relative to a maximum >= 1/256).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max / sum of a lane's value and that of lane l ^ 32, in every lane. v_permlane32_swap
+// exchanges the two 32-lane halves between two copies of the value (a vector-ALU
+// instruction; __shfl_xor(v, 32) is an LDS permute), so each lane then holds the pair
+// {v_l, v_(l^32)}, and both halves get the same result.
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Wave-wide reductions through DPP lane moves, register to register (a butterfly of
 // __shfl_xor compiles to LDS permutes, one round trip each). An inclusive scan within each
 // row of 16 lanes by row shifts of 1, 2, 4 and 8 (lanes shifted in from outside the row
