@@ -257,6 +257,31 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sas_decode_topk - one decode step with its block selection in the same launch
+ * ([SAS-ja] "仕組み", Algorithm 2: Top-K of the history scores, then ungated attention
+ * over the current block and the kept blocks). Per (sequence, KV head) the kept blocks are
+ * exactly those sas_topk_select picks in mode DECODE (rows = 1, row_valid[b] =
+ * (kv_len[b] - 1) / 64, K = topk: ties to the lower index, -0 equal to +0, NaN ranked as
+ * -inf), and o is bit-identical to sas_topk_select followed by sas_decode. The selection
+ * overlaps the copies of the current block and saves the selection launch.
+ *
+ *   s        fp32 [B][Hkv][ld]: history block scores; row (b, h) reads its first
+ *            (kv_len[b] - 1) / 64 entries.
+ *   ld       row pitch of s, >= (Lmax - 1) / 64.
+ *   topk     K, 1 <= K <= 64.
+ *   idx, cnt int32 [B][Hkv][topk] and [B][Hkv], out, nullable (both or neither): the kept
+ *            blocks as sas_topk_select writes them (ascending, -1 padded) and their number.
+ *   q, Kc, Vc, kv_len, Lmax, B, Hq, Hkv, d, block, scale, o: as for sas_decode.
+ *   ws       workspace of sas_decode_workspace_size(B, Hq, Hkv, d, topk) bytes.
+ * Returns SAS_ERR_UNSUPPORTED for topk > 64 or (Lmax - 1) / 64 > 1024 (rows of more than
+ * 1024 history blocks); sas_topk_select and sas_decode cover those.
+ */
+sas_status sas_decode_topk(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                           int Lmax, const float* s, int ld, int topk, int B, int Hq, int Hkv,
+                           int d, int block, float scale, void* o, int32_t* idx, int32_t* cnt,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
  * sas_decode_noalloc - sas_decode for callers that cannot allocate device memory: code
  * being captured into a HIP graph, tight serving loops, harnesses that forbid allocation.
  * Same computation, arguments, results and launches as sas_decode, without the workspace

@@ -35,7 +35,13 @@ constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalis
 // softmax mass a block adds is compared with the mass accumulated before it, the block is
 // kept and, once the ratio falls below tau, that head takes no further block. The wave
 // stops copying when every head has stopped.
-template <int D, bool PAGED, bool EARLY>
+//
+// SEL: the block selection in the same launch (sas_decode_topk). The wave loads its row
+// of history scores, issues the copies of its current block (they depend on kv_len only),
+// then finds the row's Top-K exactly as the selection kernel does (topk_cut / topk_walk,
+// decode mode: the valid scores are the row's first (kv_len - 1) / 64) while those copies
+// are in flight, and keeps the kept block indices, ascending, in LDS for the block list.
+template <int D, bool PAGED, bool EARLY, bool SEL>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   constexpr int HE = 32 * D;   // elements of a 32-row half tile
   __shared__ __attribute__((aligned(16))) uint16_t sk0[HE];
@@ -46,6 +52,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sv1[HE];
   __shared__ __attribute__((aligned(16))) uint16_t sv2[HE];
   __shared__ __attribute__((aligned(16))) uint16_t sv3[HE];
+  __shared__ int s_sel[SEL ? kDecSelMax : 1];   // (SEL) the kept blocks, ascending
   const int lane = threadIdx.x;
   const int hl = lane >> 5, ql = lane & 31;
   const int G = a.Hq / a.Hkv;
@@ -63,27 +70,15 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   // then moves state to scratch memory, which costs far more than the latency.)
   int pre_v = 0;
   float pre_g = 0.0f;
-  if (!EARLY && t0 + lane > 0 && t0 + lane <= a.kcap) {
+  if (!EARLY && !SEL && t0 + lane > 0 && t0 + lane <= a.kcap) {
     pre_v = idx_row[t0 + lane - 1];
     if (lg_row != nullptr) pre_g = lg_row[t0 + lane - 1];
   }
   const int L = min(max(a.kv_len[b], 1), (int)a.Lmax);
   const int cur = (L - 1) / kBlock;
-  const int cnt = min(max(a.cnt[bh], 0), min(a.kcap, cur));
-  // list position t: 0 is the current block, t >= 1 the selected block idx[t - 1]
-  // (a chunk past the end of a short list is empty: t1 == t0)
-  const int t1 = max(t0, min(t0 + a.bpc, cnt + 1));
   const uint16_t* Kh = a.Kc + (size_t)bh * a.Lmax * D;
   const uint16_t* Vh = a.Vc + (size_t)bh * a.Lmax * D;
   const int cbytes = (int)(a.Lmax * D * 2);   // checked on the host to fit 31 bits
-
-  // the G query heads as the B operand of S^T = K Q^T: lane holds query column ql,
-  // d = 16 ks + 8 hl + e; columns ql >= G are zero
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qf[ks] = ql < G ? as_bf16x8(ld16(a.q + ((size_t)b * a.Hq + h * G + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
-
   constexpr int NWIN = Tile<D>::CPR / 2;   // 1 KB windows per half tile (one wave copies all)
   uint32_t voff[NWIN];
 #pragma unroll
@@ -92,6 +87,71 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     const int rr = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
     voff[i] = (uint32_t)(rr * D + ((c ^ Tile<D>::swz(rr)) << 3)) * 2u;
   }
+  int cnt = 0;
+  bool early_cur = false;   // (SEL) the current block's copies were issued before the selection
+  if constexpr (SEL) {
+    constexpr int PL = kDecSelMaxCols / 64;
+    const int valid = cur;   // the row's history blocks
+    const int k = min(a.topk, valid);
+    const int nreg = __builtin_amdgcn_readfirstlane((valid + 63) >> 6);
+    const float* srow = a.s + bh * a.s_ld;
+    float x[PL];
+    if (k > 0) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (i < nreg) x[i] = srow[min(lane + 64 * i, valid - 1)];   // loads first: then the
+    }                                                                // copies do not delay them
+    if (t0 == 0) {
+      // the current block's two halves into the first two ring slots
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t so = ((uint32_t)cur * kBlock + 32u * u) * (uint32_t)(D * 2);
+        uint16_t* kb = u == 0 ? sk0 : sk1;
+        uint16_t* vb = u == 0 ? sv0 : sv1;
+#pragma unroll
+        for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, cbytes, kb + 512 * i, voff[i], so);
+#pragma unroll
+        for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, cbytes, vb + 512 * i, voff[i], so);
+      }
+      early_cur = true;
+    }
+    if (k > 0) {
+      uint32_t key[PL];
+#pragma unroll
+      for (int i = 0; i < PL; ++i) {
+        float v = -INFINITY;
+        if (i < nreg) v = x[i];
+        v = (lane + 64 * i < valid && v == v) ? v : -INFINITY;   // NaN ranks as -inf
+        v = v == 0.0f ? 0.0f : v;                                 // -0 -> +0
+        key[i] = lane + 64 * i < valid ? order_key(v) : 0u;
+      }
+      uint32_t T;
+      int need_eq;
+      topk_cut(key, nreg, valid, k, T, need_eq);
+      topk_walk(key, nreg, T, need_eq, [&](int i, int pos) { s_sel[pos] = lane + 64 * i; });
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the list, for every lane
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    cnt = max(k, 0);
+    if (a.idx_out != nullptr && chunk == 0) {
+      for (int p = lane; p < a.kcap; p += 64) a.idx_out[bh * a.kcap + p] = p < cnt ? s_sel[p] : -1;
+      if (lane == 0) a.cnt_out[bh] = cnt;
+    }
+  } else {
+    cnt = min(max(a.cnt[bh], 0), min(a.kcap, cur));
+  }
+  // list position t: 0 is the current block, t >= 1 the selected block idx[t - 1]
+  // (a chunk past the end of a short list is empty: t1 == t0)
+  const int t1 = max(t0, min(t0 + a.bpc, cnt + 1));
+
+  // the G query heads as the B operand of S^T = K Q^T: lane holds query column ql,
+  // d = 16 ks + 8 hl + e; columns ql >= G are zero
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = ql < G ? as_bf16x8(ld16(a.q + ((size_t)b * a.Hq + h * G + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
+
   // The chunk's list positions, one per lane (lane i: position t0 + i): block and base-2
   // log-gate; an ignored entry reads block 0 with weight 0.
   LaneList lst;
@@ -100,7 +160,10 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     v = cur;
     g = 0.0f;
     if (t > 0 && t < t1) {
-      if (!EARLY && i < 64) {   // the first window, loaded at the start
+      if (SEL) {   // the list selected above (at most kDecSelMax entries: one window)
+        v = s_sel[t - 1];
+        g = 0.0f;
+      } else if (!EARLY && i < 64) {   // the first window, loaded at the start
         v = pre_v;
         g = pre_g * kLog2e;
       } else {
@@ -276,8 +339,12 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       for (int hh = 0; hh < 2; ++hh) oacc[dt] = mfma32(va[dt][hh], pf[hh], oacc[dt]);
   };
   // whole rounds of 4 half blocks without conditions inside, then the remainder
-  fetch(sk0, sv0);
-  fetch(sk1, sv1);
+  if (early_cur) {
+    uf = 2;   // (SEL) the current block's halves are already on their way
+  } else {
+    fetch(sk0, sv0);
+    fetch(sk1, sv1);
+  }
   fetch(sk2, sv2);
   const int nfull = nhalf & ~3;
   bool stopped = false;
@@ -385,15 +452,17 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   a.wg = wg_order(grid);
   {
     ProfScope prof("decode", st);
-    const bool paged = a.page_table != nullptr, early = a.order != nullptr;
+    const bool paged = a.page_table != nullptr, early = a.order != nullptr, sel = a.s != nullptr;
     if (a.d == 128) {
-      if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true>), dim3(grid), dim3(64), 0, st, a);
-      else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false>), dim3(grid), dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((decode_split_kernel<128, false, false>), dim3(grid), dim3(64), 0, st, a);
+      if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true, false>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false, false>), dim3(grid), dim3(64), 0, st, a);
+      else if (sel) hipLaunchKernelGGL((decode_split_kernel<128, false, false, true>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<128, false, false, false>), dim3(grid), dim3(64), 0, st, a);
     } else {
-      if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true>), dim3(grid), dim3(64), 0, st, a);
-      else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false>), dim3(grid), dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((decode_split_kernel<64, false, false>), dim3(grid), dim3(64), 0, st, a);
+      if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true, false>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false, false>), dim3(grid), dim3(64), 0, st, a);
+      else if (sel) hipLaunchKernelGGL((decode_split_kernel<64, false, false, true>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<64, false, false, false>), dim3(grid), dim3(64), 0, st, a);
     }
   }
   if (a.nchunk > 1) {

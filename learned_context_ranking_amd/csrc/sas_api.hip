@@ -291,6 +291,37 @@ sas_status sas_decode(const void* q, const void* Kc, const void* Vc, const int32
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode launch");
 }
 
+sas_status sas_decode_topk(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
+                           int Lmax, const float* s, int ld, int topk, int B, int Hq, int Hkv,
+                           int d, int block, float scale, void* o, int32_t* idx, int32_t* cnt,
+                           void* ws, size_t ws_bytes, void* stream) {
+  REQUIRE(s != nullptr, SAS_ERR_INVALID_ARG, "s must be non-NULL");
+  REQUIRE((idx == nullptr) == (cnt == nullptr), SAS_ERR_INVALID_ARG, "idx and cnt must both be given or both NULL");
+  REQUIRE(topk >= 1, SAS_ERR_INVALID_ARG, "topk=%d must be >= 1", topk);
+  REQUIRE(topk <= sas::kDecSelMax, SAS_ERR_UNSUPPORTED, "topk=%d above %d: use sas_topk_select and sas_decode", topk,
+          sas::kDecSelMax);
+  REQUIRE(Lmax > 0 && (Lmax - 1) / 64 <= sas::kDecSelMaxCols, SAS_ERR_UNSUPPORTED,
+          "Lmax=%d: more than %d history blocks per row; use sas_topk_select and sas_decode", Lmax,
+          sas::kDecSelMaxCols);
+  REQUIRE(ld >= (Lmax - 1) / 64, SAS_ERR_INVALID_ARG, "ld=%d below the %d history blocks of Lmax=%d", ld,
+          (Lmax - 1) / 64, Lmax);
+  // cnt is an output here: check_decode's input checks are met with a stand-in pointer
+  const int32_t dummy = 0;
+  const sas_status chk = check_decode(q, Kc, Vc, kv_len, Lmax, &dummy, &dummy, B, Hq, Hkv, d, block, topk, scale, o);
+  if (chk != SAS_OK) return chk;
+  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, topk);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  sas::DecodeArgs a = decode_args(q, Kc, Vc, kv_len, Lmax, nullptr, nullptr, nullptr, B, Hq, Hkv, d, topk, scale, o);
+  a.part = (float*)ws;
+  a.s = s;
+  a.s_ld = ld;
+  a.topk = topk;
+  a.idx_out = idx;
+  a.cnt_out = cnt;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_topk launch");
+}
+
 sas_status sas_decode_noalloc(const void* q, const void* Kc, const void* Vc, const int32_t* kv_len,
                               int Lmax, const int32_t* idx, const int32_t* cnt, const float* logg,
                               int B, int Hq, int Hkv, int d, int block, int kcap, float scale, void* o,

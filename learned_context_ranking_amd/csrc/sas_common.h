@@ -189,6 +189,52 @@ struct LaneList {
 // flush to zero, which is harmless for softmax weights relative to a maximum >= 1/256).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- Top-K of a wave's keys
+// Selection compares fp32 scores through an order-preserving key (ties go to the lower
+// block index, -0 equals +0 and NaN ranks as -inf before the key is formed). Lane l holds
+// the keys of elements l + 64 i, i < nreg; padding keys are 0, below every valid key
+// (order_key(-inf) = 0x007FFFFF).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// inverse of order_key (exact for every key order_key produces)
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// The cut of the k largest of `valid` keys (0 < k <= valid): keys above T are kept, and of
+// the keys equal to T the need_eq lowest-index ones. T's 32 bits are fixed from the top: a
+// candidate bit stays set when at least k keys are >= the candidate (per-lane counts on the
+// vector ALUs, one wave reduction per bit: a ballot and a scalar popcount per register
+// would queue on the CU's single scalar unit); the search stops once a candidate admits
+// exactly k keys (then they are the kept set, whatever the lower bits). Whole wave.
+template <int PL>
+__device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
+                                         int& need_eq);
+// Calls f(i, pos) for every kept register i of this lane, pos its slot in index order
+// (ascending element index: a ballot prefix count, no sort). Fully unrolled whatever its
+// size: a rolled loop would index the key registers and put them in scratch memory.
+template <int PL, class F>
+__device__ __forceinline__ void topk_walk(const uint32_t (&key)[PL], int nreg, uint32_t T, int need_eq, F&& f) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int base = 0, eq_before = 0;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < PL; ++i) {
+    if (i < nreg) {   // (a guard, not a break: a constant trip count unrolls in full)
+      const bool eq = key[i] == T;
+      const unsigned long long beq = __ballot(eq);
+      const int eq_rank = eq_before + __popcll(beq & lt);
+      const bool sel = key[i] > T || (eq && eq_rank < need_eq);
+      const unsigned long long bsel = __ballot(sel);
+      if (sel) f(i, base + __popcll(bsel & lt));
+      base += __popcll(bsel);
+      eq_before += __popcll(beq);
+    }
+  }
+}
+
 // Max / sum of a lane's value and that of lane l ^ 32, in every lane. v_permlane32_swap
 // exchanges the two 32-lane halves between two copies of the value (a vector-ALU
 // instruction; __shfl_xor(v, 32) is an LDS permute), so each lane then holds the pair
@@ -228,6 +274,32 @@ __device__ __forceinline__ float dpp_sum(float v) {
 __device__ __forceinline__ float dpp_max(float v) {
   return __int_as_float(dpp_reduce(__float_as_int(v), __float_as_int(-INFINITY),
                                    [](int x, int y) { return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y))); }));
+}
+
+template <int PL>
+__device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
+                                         int& need_eq) {
+  T = 0;
+  if (k < valid) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cl = 0;
+#pragma clang loop unroll(full)
+      for (int i = 0; i < PL; ++i)
+        if (i < nreg) cl += key[i] >= cand ? 1 : 0;
+      const int c = dpp_sum_i(cl);
+      if (c >= k) {
+        T = cand;
+        if (c == k) { T = cand - 1u; break; }   // the kept set: the keys > cand - 1, no ties
+      }
+    }
+  }
+  // (k == valid keeps every valid key: T = 0 is below all of them)
+  int gl = 0;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < PL; ++i)
+    if (i < nreg) gl += key[i] > T ? 1 : 0;
+  need_eq = k - dpp_sum_i(gl);
 }
 
 // Position of key k within its 16-key group when a transposed operand is staged in LDS

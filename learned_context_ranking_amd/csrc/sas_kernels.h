@@ -155,8 +155,17 @@ struct DecodeArgs {
   const float* order;
   float tau;
   int32_t* used;
+  // selection in the same launch (s != null): history scores [B][Hkv][s_ld], K = topk
+  // (kcap = topk); the kept blocks written to idx_out [B][Hkv][kcap] / cnt_out [B][Hkv]
+  // when idx_out is not null
+  const float* s;
+  int s_ld, topk;
+  int32_t* idx_out;
+  int32_t* cnt_out;
   WgOrder wg;            // workgroup order of the decode launch (set by the launcher)
 };
+constexpr int kDecSelMax = 64;        // largest K of the decode with its own selection
+constexpr int kDecSelMaxCols = 1024;  // largest number of history blocks it ranks
 size_t decode_workspace_bytes(int B, int Hq, int Hkv, int d, int kcap);
 // sets a.bpc and a.nchunk as launch_decode will
 void decode_plan(DecodeArgs& a);

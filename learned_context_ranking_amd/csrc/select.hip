@@ -8,24 +8,15 @@
 // Each lane holds PL scores (element m = lane + 64 i, so loads are coalesced); only the
 // registers that hold valid scores of the row take part (rows of a prefill have j valid
 // scores). The K-th largest order-preserving key is found by fixing its 32 bits from the
-// top: a candidate bit stays set when at least K keys are >= the candidate, counted with
-// one ballot per register; the search stops as soon as a candidate admits exactly K keys
-// (they are the kept set). Otherwise blocks strictly above the threshold are kept and,
-// among the blocks equal to it, the lowest indices fill the remaining places. A ballot
-// prefix count writes the kept indices in ascending order without any sort.
+// top (topk_cut): a candidate bit stays set when at least K keys are >= the candidate; the
+// search stops as soon as a candidate admits exactly K keys (they are the kept set).
+// Otherwise blocks strictly above the threshold are kept and, among the blocks equal to it,
+// the lowest indices fill the remaining places. A ballot prefix count (topk_walk) writes
+// the kept indices in ascending order without any sort.
 #include "sas_common.h"
 #include "sas_kernels.h"
 
 namespace sas {
-
-__device__ __forceinline__ uint32_t order_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-// inverse of order_key (exact for every key order_key produces)
-__device__ __forceinline__ float key_score(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
 
 // log g of a kept block with score x (NaN already read as -inf) under each activation;
 // norm is the softmax normaliser (LSE over the history or over the kept set)
@@ -107,53 +98,10 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     uint32_t key[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i < valid) ? order_key(x[i]) : 0u;
-    // Valid keys are >= order_key(-inf) = 0x007FFFFF > 0, so padding (key 0) never reaches
-    // the threshold.
-    uint32_t T = 0;
-    if (k < valid) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = T | (1u << bit);
-        // per-lane counts on the vector ALUs, one wave reduction per bit (a ballot and a
-        // scalar popcount per register would queue on the CU's single scalar unit)
-        int cl = 0;
-#pragma unroll
-        for (int i = 0; i < PL; ++i)
-          if (i < nreg) cl += key[i] >= cand ? 1 : 0;
-        const int c = dpp_sum_i(cl);
-        if (c >= k) {
-          T = cand;
-          // exactly K keys are >= cand: they are the kept set, whatever the lower bits
-          // (selected below as the keys > cand - 1, with no ties to break)
-          if (c == k) { T = cand - 1u; break; }
-        }
-      }
-    }
-    // (k == valid keeps every valid block: T = 0 is below every valid key)
-    int gl = 0;
-#pragma unroll
-    for (int i = 0; i < PL; ++i)
-      if (i < nreg) gl += key[i] > T ? 1 : 0;
-    const int n_gt = dpp_sum_i(gl);
-    const int need_eq = k - n_gt;
-    const unsigned long long lt = (1ull << lane) - 1ull;
-    // calls f(i, pos) for every kept register i of this lane, pos = its output slot
-    // (fully unrolled whatever its size: a rolled loop would index the key registers and
-    // put them in scratch memory)
-    auto walk = [&](auto&& f) {
-      int base = 0, eq_before = 0;
-#pragma clang loop unroll(full)
-      for (int i = 0; i < PL; ++i) {
-        if (i >= nreg) break;
-        const bool eq = key[i] == T;
-        const unsigned long long beq = __ballot(eq);
-        const int eq_rank = eq_before + __popcll(beq & lt);
-        const bool sel = key[i] > T || (eq && eq_rank < need_eq);
-        const unsigned long long bsel = __ballot(sel);
-        if (sel) f(i, base + __popcll(bsel & lt));
-        base += __popcll(bsel);
-        eq_before += __popcll(beq);
-      }
-    };
+    uint32_t T;
+    int need_eq;
+    topk_cut(key, nreg, valid, k, T, need_eq);
+    auto walk = [&](auto&& f) { topk_walk(key, nreg, T, need_eq, f); };
     // The walks take each kept score back from its key (exact), so that x[] is no longer
     // live: that leaves the widest rows registers to spare.
     float norm = lse;   // the gate's normaliser (reported as lse)

@@ -49,6 +49,7 @@ SIGNATURES = {
     "sas_decode_workspace_size": ([_I, _I, _I, _I, _I], _SZ),
     "sas_decode": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
     "sas_decode_noalloc": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P], _I),
+    "sas_decode_topk": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
     "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
@@ -251,6 +252,32 @@ def sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, ws=None, out=None)
                             B, Hq, Hkv, d, BLOCK, kcap, float(scale), _ptr(o), _ptr(ws), ws.numel(),
                             _stream(q.device)))
     return o
+
+
+def sas_decode_topk(q, Kc, Vc, kv_len, s, topk, scale, ws=None, out=None, want_idx=False):
+    """One decode step with its Top-K selection in the same launch. q bf16 [B, Hq, d];
+    Kc/Vc bf16 [B, Hkv, Lmax, d]; kv_len int32 [B]; s fp32 [B, Hkv, ld] history block
+    scores (or [B, Hkv, 1, ld]). Returns o bf16 [B, Hq, d], and with want_idx also the kept
+    blocks idx int32 [B, Hkv, topk] and cnt int32 [B, Hkv]."""
+    for t, nm in ((q, "q"), (Kc, "Kc"), (Vc, "Vc")):
+        _need(t, torch.bfloat16, nm)
+    _need(kv_len, torch.int32, "kv_len")
+    _need(s, torch.float32, "s")
+    B, Hq, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    ld = s.shape[-1]
+    dev = q.device
+    if ws is None:
+        ws = decode_workspace(B, Hq, Hkv, d, topk, dev)
+    o = torch.empty_like(q) if out is None else out
+    idx = cnt = None
+    if want_idx:
+        idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _check(lib().sas_decode_topk(_ptr(q), _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, _ptr(s), ld, int(topk), B, Hq,
+                                 Hkv, d, 64, float(scale), _ptr(o), _ptr(idx), _ptr(cnt), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(dev)))
+    return (o, idx, cnt) if want_idx else o
 
 
 def sas_decode_noalloc(q, Kc, Vc, kv_len, idx, cnt, scale, logg=None, out=None):

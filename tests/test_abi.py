@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -212,6 +212,26 @@ def test_decode_noalloc_rejects():
     assert b"scratch" in L.sas_last_error()
     # 512 pairs keep one chunk per list: no partial states, accepted by the checks (the
     # call then needs a device, so it is not made here)
+
+
+def test_decode_topk_rejects():
+    """The decode with its own selection checks its sizes before any HIP call: K above 64
+    and rows of more than 1024 history blocks are left to sas_topk_select + sas_decode."""
+    L = sas.lib()
+    need = L.sas_decode_workspace_size(2, 8, 2, 128, 16)
+    # q, Kc, Vc, kv_len, Lmax, s, ld, topk, B, Hq, Hkv, d, block, scale, o, idx, cnt, ws, ws_bytes, stream
+    args = [FAKE, FAKE, FAKE, FAKE, 4096, FAKE, 64, 16, 2, 8, 2, 128, 64, 0.1, FAKE, NULL, NULL, FAKE, need, NULL]
+    for i, v, code in ((5, NULL, sas.SAS_ERR_INVALID_ARG),         # no scores
+                       (7, 0, sas.SAS_ERR_INVALID_ARG),            # K = 0
+                       (7, 65, sas.SAS_ERR_UNSUPPORTED),           # K above 64
+                       (4, 65665, sas.SAS_ERR_UNSUPPORTED),        # 1025 history blocks
+                       (6, 62, sas.SAS_ERR_INVALID_ARG),           # ld below (Lmax - 1) / 64
+                       (15, FAKE, sas.SAS_ERR_INVALID_ARG),        # idx without cnt
+                       (0, NULL, sas.SAS_ERR_INVALID_ARG),         # no q
+                       (12, 32, sas.SAS_ERR_UNSUPPORTED),          # block != 64
+                       (18, need - 1, sas.SAS_ERR_WORKSPACE)):     # workspace too small
+        bad = list(args); bad[i] = v
+        assert L.sas_decode_topk(*bad) == code, (i, v)
 
 
 def test_decode_paged_rejects():
