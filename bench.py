@@ -365,6 +365,31 @@ def run_decode(steps, torch):
             et.append((a, c))
         torch.cuda.synchronize()
         early[tau] = (float(np.median([x.elapsed_time(y) for x, y in et])), float(used.float().mean()))
+    # the same step with the selection inside the decode launch (sas_decode_topk): one
+    # isolated launch after the flush, and steps back to back over the 4 score draws
+    of = torch.empty_like(q)
+    sas.sas_decode_topk(q, Kc, Vc, kv_len, s, K, scale, ws=ws, out=of)
+    torch.cuda.synchronize()
+    assert torch.equal(of, o), "fused decode differs from select + decode"
+    ftimes = []
+    for _ in range(steps):
+        flush.sum()
+        a, c = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record(stream)
+        sas.sas_decode_topk(q, Kc, Vc, kv_len, s, K, scale, ws=ws, out=of)
+        c.record(stream)
+        ftimes.append((a, c))
+    torch.cuda.synchronize()
+    fused_samples = [x.elapsed_time(y) for x, y in ftimes]
+    s_draws = [torch.from_numpy(synth.scores_normal((B, Hkv, 1, C), w.seed + 101 + r)).to(dev) for r in range(4)]
+    fmarks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    fmarks[0].record(stream)
+    for i in range(steps):
+        sas.sas_decode_topk(q, Kc, Vc, kv_len, s_draws[i % 4], K, scale, ws=ws, out=of)
+        fmarks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    fss_samples = [fmarks[i].elapsed_time(fmarks[i + 1]) for i in range(steps)]
     cnt_h = cnt.cpu().numpy()
     # algorithmic bytes: the selected K/V blocks plus the current block, q and o
     blocks = int(cnt_h.sum()) + B * Hkv
@@ -372,12 +397,16 @@ def run_decode(steps, torch):
     # selection: the row's valid scores read, idx (kcap), cnt and lse written
     sel_bytes = B * Hkv * ((L - 1) // 64) * 4 + B * Hkv * (4 * K + 8)
     ms_e2e = float(np.median(e2e_samples))
+    # fused: the decode bytes plus the scores each row's workgroup reads (no idx/cnt written)
+    fused_bytes = nbytes + B * Hkv * ((L - 1) // 64) * 4
     return dict(ms=ms, ms_select=ms_sel, bytes=nbytes, gbs=nbytes / ms / 1e6, ms_paged=ms_paged,
                 gbs_paged=nbytes / ms_paged / 1e6, early=early, stats=stats(dec_samples),
                 sel_stats=stats(sel_samples), paged_stats=stats(paged_samples), sel_bytes=sel_bytes,
                 sel_gbs=sel_bytes / ms_sel / 1e6, ms_e2e=ms_e2e, e2e_stats=stats(e2e_samples),
                 ss_stats=stats(ss_samples), ss_bytes=ss_bytes, dispatch_ms=dispatch_ms,
                 ss_gbs=ss_bytes / float(np.median(ss_samples)) / 1e6,
+                ms_fused=float(np.median(fused_samples)), fused_stats=stats(fused_samples), fused_bytes=fused_bytes,
+                fss_stats=stats(fss_samples), fss_ms=float(np.median(fss_samples)),
                 e2e_gbs=(nbytes + sel_bytes) / ms_e2e / 1e6,
                 workload=f"decode: B={B} sequences, Hq={Hq}, Hkv={Hkv}, d={d}, kv_len={L}, block=64, "
                          f"K={K} blocks + current block, ungated (Algorithm 2)")
@@ -679,6 +708,17 @@ def main():
                                                  "event to event; includes the dispatch latency that a trivial "
                                                  "kernel also shows between two events on this stream",
                          "trivial_kernel_event_ms": round(dec["dispatch_ms"], 5),
+                         "fused_select": {
+                             "ms": round(dec["ms_fused"], 5), "ms_stats": dec["fused_stats"],
+                             "bytes": dec["fused_bytes"],
+                             "value": round(dec["fused_bytes"] / dec["ms_fused"] / 1e6, 1),
+                             "unit": "GB/s",
+                             "steady_state_ms_stats": dec["fss_stats"],
+                             "steady_state_value": round((dec["ss_bytes"] + dec["fused_bytes"] - dec["bytes"])
+                                                         / dec["fss_ms"] / 1e6, 1),
+                             "how": "sas_decode_topk: the Top-K selection inside the decode launch; one launch "
+                                    "after the cache-evicting read (compare end_to_end), and steps back to back "
+                                    "over 4 score draws (compare steady_state); bytes: the decode's plus the scores read"},
                          "paged": {"ms": round(dec["ms_paged"], 5), "ms_stats": dec["paged_stats"],
                                    "value": round(dec["gbs_paged"], 1),
                                    "unit": "GB/s", "layout": "pool of 64-token pages in random order + page table"},

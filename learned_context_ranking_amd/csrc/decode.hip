@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sv1[HE];
   __shared__ __attribute__((aligned(16))) uint16_t sv2[HE];
   __shared__ __attribute__((aligned(16))) uint16_t sv3[HE];
-  __shared__ int s_sel[SEL ? kDecSelMax : 1];   // (SEL) the kept blocks, ascending
+  __shared__ int s_sel[SEL ? kDecSelMax + 1 : 1];   // (SEL) the kept blocks, ascending; a spare slot
   const int lane = threadIdx.x;
   const int hl = lane >> 5, ql = lane & 31;
   const int G = a.Hq / a.Hkv;
@@ -74,6 +74,20 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     pre_v = idx_row[t0 + lane - 1];
     if (lg_row != nullptr) pre_g = lg_row[t0 + lane - 1];
   }
+  // (SEL) The row's scores likewise: every column a sequence of this cache can have as
+  // history ((Lmax - 1) / 64, at most kDecSelMaxCols, and the row holds s_ld >= that many),
+  // so the loads need not wait for kv_len; the columns past the sequence's own history are
+  // masked once it is known.
+  constexpr int PL = SEL ? kDecSelMaxCols / 64 : 1;
+  float x[PL];
+  int nld = 0;
+  if constexpr (SEL) {
+    const int ncol = min(a.s_ld, (int)((a.Lmax - 1) / kBlock));
+    nld = (ncol + 63) >> 6;
+    const float* srow = a.s + bh * a.s_ld;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) x[i] = i < nld ? srow[min(lane + 64 * i, ncol - 1)] : -INFINITY;
+  }
   const int L = min(max(a.kv_len[b], 1), (int)a.Lmax);
   const int cur = (L - 1) / kBlock;
   const uint16_t* Kh = a.Kc + (size_t)bh * a.Lmax * D;
@@ -87,22 +101,36 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     const int rr = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
     voff[i] = (uint32_t)(rr * D + ((c ^ Tile<D>::swz(rr)) << 3)) * 2u;
   }
+  // the G query heads as the B operand of S^T = K Q^T: lane holds query column ql,
+  // d = 16 ks + 8 hl + e; columns ql >= G are zero (loaded before the selection, whose
+  // wavefront fences would keep them behind it)
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = ql < G ? as_bf16x8(ld16(a.q + ((size_t)b * a.Hq + h * G + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
+
   int cnt = 0;
   bool early_cur = false;   // (SEL) the current block's copies were issued before the selection
   if constexpr (SEL) {
-    constexpr int PL = kDecSelMaxCols / 64;
-    const int valid = cur;   // the row's history blocks
+    const int valid = cur;   // the row's history blocks (valid <= 64 nld)
     const int k = min(a.topk, valid);
     const int nreg = __builtin_amdgcn_readfirstlane((valid + 63) >> 6);
-    const float* srow = a.s + bh * a.s_ld;
-    float x[PL];
-    if (k > 0) {
+    // The scores (and q) are awaited before the current block's copies are issued: the
+    // memory counter drains in issue order, so a wait for them after the copies would be a
+    // wait for the copies too, and the search would start only once those had landed.
+    wait_vm();
+    uint32_t key[PL];
 #pragma unroll
-      for (int i = 0; i < PL; ++i)
-        if (i < nreg) x[i] = srow[min(lane + 64 * i, valid - 1)];   // loads first: then the
-    }                                                                // copies do not delay them
+    for (int i = 0; i < PL; ++i) {
+      float v = -INFINITY;
+      if (i < nreg) v = x[i];
+      v = (lane + 64 * i < valid && v == v) ? v : -INFINITY;   // NaN ranks as -inf
+      v = v == 0.0f ? 0.0f : v;                                 // -0 -> +0
+      key[i] = lane + 64 * i < valid ? order_key(v) : 0u;
+    }
     if (t0 == 0) {
-      // the current block's two halves into the first two ring slots
+      // the current block's two halves into the first two ring slots, in flight during
+      // the search
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const uint32_t so = ((uint32_t)cur * kBlock + 32u * u) * (uint32_t)(D * 2);
@@ -116,19 +144,16 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       early_cur = true;
     }
     if (k > 0) {
-      uint32_t key[PL];
-#pragma unroll
-      for (int i = 0; i < PL; ++i) {
-        float v = -INFINITY;
-        if (i < nreg) v = x[i];
-        v = (lane + 64 * i < valid && v == v) ? v : -INFINITY;   // NaN ranks as -inf
-        v = v == 0.0f ? 0.0f : v;                                 // -0 -> +0
-        key[i] = lane + 64 * i < valid ? order_key(v) : 0u;
-      }
       uint32_t T;
       int need_eq;
-      topk_cut(key, nreg, valid, k, T, need_eq);
-      topk_walk(key, nreg, T, need_eq, [&](int i, int pos) { s_sel[pos] = lane + 64 * i; });
+      topk_cut<PL, true>(key, nreg, valid, k, T, need_eq);   // the wave has its SIMD to itself
+      if (need_eq == 0) {   // no tie at the cut: every lane writes, the unkept ones to a spare slot
+        auto put = [&](int i, int pos, bool kept) { s_sel[kept ? pos : kDecSelMax] = lane + 64 * i; };
+        if (nreg <= PL / 2) topk_walk_gt<PL / 2>(key, T, put);
+        else topk_walk_gt<PL>(key, T, put);
+      } else {
+        topk_walk(key, nreg, T, need_eq, [&](int i, int pos) { s_sel[pos] = lane + 64 * i; });
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the list, for every lane
     __builtin_amdgcn_wave_barrier();
@@ -144,13 +169,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   // list position t: 0 is the current block, t >= 1 the selected block idx[t - 1]
   // (a chunk past the end of a short list is empty: t1 == t0)
   const int t1 = max(t0, min(t0 + a.bpc, cnt + 1));
-
-  // the G query heads as the B operand of S^T = K Q^T: lane holds query column ql,
-  // d = 16 ks + 8 hl + e; columns ql >= G are zero
-  bf16x8 qf[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    qf[ks] = ql < G ? as_bf16x8(ld16(a.q + ((size_t)b * a.Hq + h * G + ql) * D + 16 * ks + 8 * hl)) : bf16x8{};
 
   // The chunk's list positions, one per lane (lane i: position t0 + i): block and base-2
   // log-gate; an ignored entry reads block 0 with weight 0.
@@ -451,8 +469,8 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   const unsigned grid = (unsigned)(pairs * a.nchunk);
   a.wg = wg_order(grid);
   {
-    ProfScope prof("decode", st);
     const bool paged = a.page_table != nullptr, early = a.order != nullptr, sel = a.s != nullptr;
+    ProfScope prof(early ? "decode_early_stop" : paged ? "decode_paged" : sel ? "decode_topk" : "decode", st);
     if (a.d == 128) {
       if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true, false>), dim3(grid), dim3(64), 0, st, a);
       else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false, false>), dim3(grid), dim3(64), 0, st, a);

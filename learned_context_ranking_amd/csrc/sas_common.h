@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sas {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -205,11 +207,16 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 // The cut of the k largest of `valid` keys (0 < k <= valid): keys above T are kept, and of
 // the keys equal to T the need_eq lowest-index ones. T's 32 bits are fixed from the top: a
-// candidate bit stays set when at least k keys are >= the candidate (per-lane counts on the
-// vector ALUs, one wave reduction per bit: a ballot and a scalar popcount per register
-// would queue on the CU's single scalar unit); the search stops once a candidate admits
-// exactly k keys (then they are the kept set, whatever the lower bits). Whole wave.
-template <int PL>
+// candidate bit stays set when at least k keys are >= the candidate; the search stops once
+// a candidate admits exactly k keys (then they are the kept set, whatever the lower bits).
+// Whole wave. Two ways to count, same result:
+//  * BALLOT = false: per-lane counts on the vector ALUs and one DPP wave reduction per bit,
+//    for kernels that keep several waves on each SIMD (a ballot and a scalar popcount per
+//    register would queue them all on the CU's single scalar unit);
+//  * BALLOT = true: one compare mask per register, summed by scalar popcounts, for a wave
+//    that has its SIMD to itself (no reduction chain: the latency of each bit is a few
+//    issue slots). The registers past nreg must hold 0.
+template <int PL, bool BALLOT = false>
 __device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
                                          int& need_eq);
 // Calls f(i, pos) for every kept register i of this lane, pos its slot in index order
@@ -220,6 +227,18 @@ __device__ __forceinline__ void topk_walk(const uint32_t (&key)[PL], int nreg, u
   const int lane = threadIdx.x & 63;
   const unsigned long long lt = (1ull << lane) - 1ull;
   int base = 0, eq_before = 0;
+  if (need_eq == 0) {   // no key equal to T is kept (the usual case): one ballot per register
+#pragma clang loop unroll(full)
+    for (int i = 0; i < PL; ++i) {
+      if (i < nreg) {
+        const bool sel = key[i] > T;
+        const unsigned long long bsel = __ballot(sel);
+        if (sel) f(i, base + __popcll(bsel & lt));
+        base += __popcll(bsel);
+      }
+    }
+    return;
+  }
 #pragma clang loop unroll(full)
   for (int i = 0; i < PL; ++i) {
     if (i < nreg) {   // (a guard, not a break: a constant trip count unrolls in full)
@@ -232,6 +251,23 @@ __device__ __forceinline__ void topk_walk(const uint32_t (&key)[PL], int nreg, u
       base += __popcll(bsel);
       eq_before += __popcll(beq);
     }
+  }
+}
+
+// The walk for a cut that keeps no key equal to T (need_eq == 0), without branches: calls
+// f(i, pos, kept) for every register i < NR of this lane, pos the key's slot in index order
+// when kept (the compare's lane mask, counted below the lane and carried across registers
+// by scalar popcounts). The registers past nreg must hold 0.
+template <int NR, int PL, class F>
+__device__ __forceinline__ void topk_walk_gt(const uint32_t (&key)[PL], uint32_t T, F&& f) {
+  constexpr int kUGT = 34;   // integer compare predicate: unsigned >
+  int base = 0;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < NR; ++i) {
+    const unsigned long long m = __builtin_amdgcn_uicmp(key[i], T, kUGT);
+    const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    f(i, base + below, key[i] > T);
+    base += __builtin_popcountll(m);
   }
 }
 
@@ -276,18 +312,41 @@ __device__ __forceinline__ float dpp_max(float v) {
                                    [](int x, int y) { return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y))); }));
 }
 
-template <int PL>
-__device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
-                                         int& need_eq) {
+// Number of keys >= c (GE) or > c over the wave's registers i < nreg: per-lane counts on
+// the vector ALUs and one DPP wave reduction.
+template <int PL, bool GE>
+__device__ __forceinline__ int topk_count_dpp(const uint32_t (&key)[PL], int nreg, uint32_t c) {
+  int cl = 0;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < PL; ++i)
+    if (i < nreg) cl += (GE ? key[i] >= c : key[i] > c) ? 1 : 0;
+  return dpp_sum_i(cl);
+}
+// The same over the first NR registers, each compare's lane mask (v_cmp into a scalar
+// register pair) summed by scalar popcounts. No guard per register (it would be a branch
+// each): registers i >= nreg must hold 0, which is never > c and never >= a candidate
+// (candidates have a bit set).
+template <int NR, int PL, bool GE>
+__device__ __forceinline__ int topk_count_mask(const uint32_t (&key)[PL], uint32_t c) {
+  constexpr int kUGE = 35, kUGT = 34;   // integer compare predicates (unsigned >=, >)
+  int n = 0;
+#pragma clang loop unroll(full)
+  for (int i = 0; i < NR; ++i) n += __builtin_popcountll(__builtin_amdgcn_uicmp(key[i], c, GE ? kUGE : kUGT));
+  return n;
+}
+
+template <int PL, int NR, bool BALLOT>
+__device__ __forceinline__ void topk_cut_n(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
+                                           int& need_eq) {
+  auto count = [&](uint32_t c, auto ge) {
+    if constexpr (BALLOT) return topk_count_mask<NR, PL, decltype(ge)::value>(key, c);
+    else return topk_count_dpp<PL, decltype(ge)::value>(key, nreg, c);
+  };
   T = 0;
   if (k < valid) {
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = T | (1u << bit);
-      int cl = 0;
-#pragma clang loop unroll(full)
-      for (int i = 0; i < PL; ++i)
-        if (i < nreg) cl += key[i] >= cand ? 1 : 0;
-      const int c = dpp_sum_i(cl);
+      const int c = count(cand, std::true_type{});
       if (c >= k) {
         T = cand;
         if (c == k) { T = cand - 1u; break; }   // the kept set: the keys > cand - 1, no ties
@@ -295,11 +354,18 @@ __device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, in
     }
   }
   // (k == valid keeps every valid key: T = 0 is below all of them)
-  int gl = 0;
-#pragma clang loop unroll(full)
-  for (int i = 0; i < PL; ++i)
-    if (i < nreg) gl += key[i] > T ? 1 : 0;
-  need_eq = k - dpp_sum_i(gl);
+  need_eq = k - count(T, std::false_type{});
+}
+
+template <int PL, bool BALLOT>
+__device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
+                                         int& need_eq) {
+  if constexpr (BALLOT && PL >= 2) {   // count over half the registers when the rest are padding
+    if (nreg <= PL / 2) topk_cut_n<PL, PL / 2, true>(key, nreg, valid, k, T, need_eq);
+    else topk_cut_n<PL, PL, true>(key, nreg, valid, k, T, need_eq);
+  } else {
+    topk_cut_n<PL, PL, BALLOT>(key, nreg, valid, k, T, need_eq);
+  }
 }
 
 // Position of key k within its 16-key group when a transposed operand is staged in LDS
