@@ -73,9 +73,13 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   mx = dpp_max(mx);
   float lse = -INFINITY;
   if (mx != -INFINITY) {
+    // sum of e^(x - mx) as 2^((x - mx) log2 e) on the hardware exp2 (one instruction, where
+    // expf's full-range version takes about a dozen): every term is <= 1, the largest is
+    // 1, and a term the hardware flushes (below 2^-126) changes no fp32 sum that holds it
+    const float mxl = mx * kLog2e;
     float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) sum += expf(x[i] - mx);
+    for (int i = 0; i < PL; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mxl));
     sum = dpp_sum(sum);
     lse = mx + logf(sum);
   }

@@ -2,10 +2,10 @@
 
 Each call only launches kernels on the caller's stream: no allocation, no memset and no
 host synchronisation inside the library, so a whole training step (select, forward,
-backward) or decode step (select, decode, chunk merge) can be captured once. The kernels
-are deterministic, so every replay must reproduce the eager results bit for bit; the
-outputs are overwritten with garbage before each replay, and unrelated eager work and
-synchronisations run between replays.
+backward) or decode step (select, decode, chunk merge; or the decode with its selection) can
+be captured once. The kernels are deterministic, so every replay must reproduce the eager
+results bit for bit; the outputs are overwritten with garbage before each replay, and
+unrelated eager work and synchronisations run between replays.
 """
 import math
 
@@ -79,6 +79,32 @@ def test_decode_step_graph_replay(B, Hkv, Lmax):
     def step():
         idx, cnt, _, logg = sas.sas_topk_select(s, topk, mode="decode", row_valid=row_valid, kcap=topk)
         o = sas.sas_decode(q, Kc, Vc, kv_len, idx, cnt, scale, logg=logg, ws=ws)
+        return dict(idx=idx, cnt=cnt, o=o)
+
+    ref = {k: v.clone() for k, v in step().items()}
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step()
+    _replays(g, out, ref)
+
+
+@pytest.mark.parametrize("B,Hkv,Lmax", [(2, 2, 4096), (64, 8, 1024)], ids=["merged-chunks", "one-chunk"])
+def test_decode_topk_graph_replay(B, Hkv, Lmax):
+    """The decode with its selection in the launch, captured and replayed: kept blocks
+    (idx_out / cnt_out) and output."""
+    Hq, d, topk = 4 * Hkv, 128, 16
+    log(f"graph: decode_topk B={B} Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} K={topk}")
+    q = dev_bf16(synth.normal_bf16((B, Hq, 1, d), 3, synth.TID_QDEC)[:, :, 0])
+    Kc = dev_bf16(synth.normal_bf16((B, Hkv, Lmax, d), 3, synth.TID_K))
+    Vc = dev_bf16(synth.normal_bf16((B, Hkv, Lmax, d), 3, synth.TID_V))
+    s = dev(synth.scores_normal((B, Hkv, 1, Lmax // 64), 3))
+    kv_len = dev(np.linspace(100, Lmax, B).astype(np.int32))
+    scale = 1.0 / math.sqrt(d)
+    ws = sas.decode_workspace(B, Hq, Hkv, d, topk, q.device)
+
+    def step():
+        o, idx, cnt = sas.sas_decode_topk(q, Kc, Vc, kv_len, s, topk, scale, ws=ws, want_idx=True)
         return dict(idx=idx, cnt=cnt, o=o)
 
     ref = {k: v.clone() for k, v in step().items()}
