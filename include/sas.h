@@ -237,6 +237,8 @@ size_t sas_decode_workspace_size(int B, int Hq, int Hkv, int d, int kcap);
  *
  *   q        bf16 [B][Hq][d]: the new token's queries.
  *   Kc, Vc   bf16 [B][Hkv][Lmax][d]: the caches, already holding the new token's K/V.
+ *            Rows at or past kv_len[b] are never used (they read as zero), so they may
+ *            hold anything, NaN included.
  *   kv_len   int32 [B], device: tokens in each cache (1 <= kv_len <= Lmax, clamped). The
  *            query is token kv_len - 1; its current block is tokens
  *            [64 * floor((kv_len - 1) / 64), kv_len).

@@ -92,7 +92,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   const int cur = (L - 1) / kBlock;
   const uint16_t* Kh = a.Kc + (size_t)bh * a.Lmax * D;
   const uint16_t* Vh = a.Vc + (size_t)bh * a.Lmax * D;
-  const int cbytes = (int)(a.Lmax * D * 2);   // checked on the host to fit 31 bits
+  // The copies' byte range is the sequence's own tokens: cache rows at or past kv_len (in
+  // the current block) read as zero, whatever the cache holds there. Their keys are masked
+  // anyway, but a weight of zero times a NaN value row would still be NaN.
+  // (L * D * 2 <= Lmax * D * 2, checked on the host to fit 31 bits.)
+  const int cbytes = L * D * 2;
   constexpr int NWIN = Tile<D>::CPR / 2;   // 1 KB windows per half tile (one wave copies all)
   uint32_t voff[NWIN];
 #pragma unroll

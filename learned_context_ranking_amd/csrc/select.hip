@@ -207,6 +207,7 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
   const float* srow = a.s + row * a.ld;
   float* drow = a.ds + row * a.ld;
   const float lse = (live && a.lse != nullptr) ? a.lse[row] : -INFINITY;
+  const float lse2 = lse * kLog2e;
   const int cnt = live ? min(max(a.cnt[row], 0), a.kcap) : 0;
   const int32_t* irow = a.idx + row * a.kcap;
   const float* grow = a.dg + row * a.kcap;
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256) void gates_bwd_kernel(const GatesBwdArgs a) {
     if (a.gate == kGateSigmoid) return 1.0f / (1.0f + expf(-v));
     if (a.gate == kGateExp) return expf(v);
     if (!(lse > -INFINITY)) return 0.0f;
-    return expf(v - lse);
+    return __builtin_amdgcn_exp2f(fmaf(v, kLog2e, -lse2));   // e^(v - lse) <= 1 on the hardware exp2
   };
   const bool softmax_like = a.gate == kGateSoftmax || a.gate == kGateSoftmaxSelected;
   for (int i = lane; i < kMaxCols / 32; i += 64) sel_bits[w][i] = 0u;

@@ -1,7 +1,8 @@
 """GPU parity of sas_decode (inference form, Algorithm 2) against the oracle, including
 partial current blocks, a sequence with a single token, rows whose budget exceeds their
 history, GQA groups of 1, 4, 5 and 8, d = 64 and 128, the gated check variant, and the
-full decode workload (64 sequences x 32,768 cached tokens) on sampled sequences."""
+full decode workload (64 sequences x 32,768 cached tokens) on sampled sequences, and caches
+whose rows past kv_len hold NaN."""
 import math
 
 import numpy as np
@@ -222,3 +223,37 @@ def test_decode_permuted_workgroup_order():
         sas.debug_workgroup_order(0)
     torch.cuda.synchronize()
     assert torch.equal(o0, o1)
+
+
+def test_decode_ignores_rows_past_kv_len():
+    """Cache rows at or past kv_len (the rest of the current block and beyond) hold NaN:
+    they are never used, so decode, early-stopped decode (tau = 0: every kept block) and
+    the decode with its selection all match the oracle, which reads only the valid rows."""
+    B, Hq, Hkv, d, Lmax, topk = 4, 8, 2, 128, 2048, 8
+    kv_len = np.array([2048, 1000, 65, 1], np.int32)
+    log(f"decode with NaN past kv_len B={B} Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} K={topk}")
+    q_bits = synth.normal_bf16((B, Hq, 1, d), 7, synth.TID_QDEC)[:, :, 0]
+    k_bits = synth.normal_bf16((B, Hkv, Lmax, d), 7, synth.TID_K)
+    v_bits = synth.normal_bf16((B, Hkv, Lmax, d), 7, synth.TID_V)
+    for b in range(B):
+        k_bits[b, :, kv_len[b]:] = 0x7FC0   # bf16 quiet NaN
+        v_bits[b, :, kv_len[b]:] = 0x7FC0
+    C = Lmax // 64
+    s = synth.scores_normal((B, Hkv, 1, C), 7)
+    row_valid = ((kv_len - 1) // 64).astype(np.int32)
+    scale = 1.0 / math.sqrt(d)
+    q, Kc, Vc, kvl, sd = dev_bf16(q_bits), dev_bf16(k_bits), dev_bf16(v_bits), dev(kv_len), dev(s)
+    idx, cnt, _, _ = sas.sas_topk_select(sd, topk, mode="decode", row_valid=dev(row_valid), kcap=topk)
+    idx3, cnt3 = idx.reshape(B, Hkv, topk), cnt.reshape(B, Hkv)
+    o = sas.sas_decode(q, Kc, Vc, kvl, idx, cnt, scale)
+    of = sas.sas_decode_topk(q, Kc, Vc, kvl, sd, topk, scale)
+    order = torch.gather(sd[:, :, 0, :], -1, idx3.clamp(min=0).long()).contiguous()
+    oe, _ = sas.sas_decode_early_stop(q, Kc, Vc, kvl, idx3.contiguous(), cnt3.contiguous(), order, scale, 0.0)
+    torch.cuda.synchronize()
+    idx_r, cnt_r, _, _ = oracle.select(s.reshape(B * Hkv, C), np.repeat(row_valid, Hkv), topk, kcap=topk)
+    ref = oracle.decode(synth.bf16_bits_to_f32(q_bits), synth.bf16_bits_to_f32(k_bits),
+                        synth.bf16_bits_to_f32(v_bits), kv_len, idx_r.reshape(B, Hkv, topk),
+                        cnt_r.reshape(B, Hkv), scale)
+    assert_close("o (decode)", host(o), ref)
+    assert_close("o (decode_topk)", host(of), ref)
+    assert_close("o (early stop, tau 0)", host(oe), ref)

@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 
 def _scores(B, Hkv, C, seed, kind):
     s = synth.scores_normal((B, Hkv, 1, C), seed)
+    if kind == "const":
+        s = np.full_like(s, 0.25)                      # every key equal: the K lowest indices
     if kind == "ties":
         s = np.round(s * 2.0) / 2.0                    # few distinct values: many ties at the cut
         s[..., 3::7] = np.nan
@@ -87,3 +89,8 @@ def test_decode_topk_ties_nan():
 def test_decode_topk_budget_above_history():
     """K = 32 over 16 history blocks at most: every history block is kept, -1 padded."""
     _case(2, 4, 1, 128, 1024, [1024, 300], 32, seed=5)
+
+
+def test_decode_topk_all_equal():
+    """Every score equal: the cut is that key, and the walk keeps its K lowest indices."""
+    _case(3, 8, 2, 64, 4096, [4096, 2000, 700], 20, seed=6, kind="const")
