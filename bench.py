@@ -348,6 +348,21 @@ def run_decode(steps, torch):
     torch.cuda.synchronize()
     paged_samples = [x.elapsed_time(y) for x, y in ptimes]
     ms_paged = float(np.median(paged_samples))
+    # the paged step with its selection in the launch
+    opf = torch.empty_like(q)
+    sas.sas_decode_paged_topk(q, Kp, Vp, page_table, kv_len, s, K, scale, ws=ws, out=opf)
+    torch.cuda.synchronize()
+    assert torch.equal(opf, o), "paged fused decode differs from select + decode"
+    pftimes = []
+    for _ in range(steps):
+        flush.sum()
+        a, c = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        a.record(stream)
+        sas.sas_decode_paged_topk(q, Kp, Vp, page_table, kv_len, s, K, scale, ws=ws, out=opf)
+        c.record(stream)
+        pftimes.append((a, c))
+    torch.cuda.synchronize()
+    paged_fused_samples = [x.elapsed_time(y) for x, y in pftimes]
     del Kp, Vp
     # the same step with the mass-threshold early stop (blocks in descending score order)
     order = torch.gather(s[:, :, 0, :], -1, idx.reshape(B, Hkv, -1).clamp(min=0).long()).contiguous()
@@ -407,6 +422,7 @@ def run_decode(steps, torch):
                 ss_gbs=ss_bytes / float(np.median(ss_samples)) / 1e6,
                 ms_fused=float(np.median(fused_samples)), fused_stats=stats(fused_samples), fused_bytes=fused_bytes,
                 fss_stats=stats(fss_samples), fss_ms=float(np.median(fss_samples)),
+                paged_fused_stats=stats(paged_fused_samples), ms_paged_fused=float(np.median(paged_fused_samples)),
                 e2e_gbs=(nbytes + sel_bytes) / ms_e2e / 1e6,
                 workload=f"decode: B={B} sequences, Hq={Hq}, Hkv={Hkv}, d={d}, kv_len={L}, block=64, "
                          f"K={K} blocks + current block, ungated (Algorithm 2)")
@@ -721,7 +737,12 @@ def main():
                                     "over 4 score draws (compare steady_state); bytes: the decode's plus the scores read"},
                          "paged": {"ms": round(dec["ms_paged"], 5), "ms_stats": dec["paged_stats"],
                                    "value": round(dec["gbs_paged"], 1),
-                                   "unit": "GB/s", "layout": "pool of 64-token pages in random order + page table"},
+                                   "unit": "GB/s", "layout": "pool of 64-token pages in random order + page table",
+                                   "fused_select": {"ms": round(dec["ms_paged_fused"], 5),
+                                                    "ms_stats": dec["paged_fused_stats"],
+                                                    "value": round(dec["fused_bytes"] / dec["ms_paged_fused"] / 1e6, 1),
+                                                    "unit": "GB/s", "how": "sas_decode_paged_topk, one launch after "
+                                                    "the cache-evicting read; bytes as decode.fused_select"}},
                          "early_stop": {f"tau={t}": {"ms": round(v[0], 5), "history_blocks_used": round(v[1], 2)}
                                         for t, v in dec["early"].items()},
                          "workload": dec["workload"],

@@ -348,6 +348,31 @@ sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool,
                             size_t ws_bytes, void* stream);
 
 /*
+ * sas_decode_paged_topk - sas_decode_topk over a paged KV cache: one decode step with its
+ * block selection in the same launch ([SAS-ja] "仕組み", Algorithm 2), the caches laid out
+ * as for sas_decode_paged. The kept blocks are those sas_topk_select picks in mode DECODE
+ * (rows = 1, row_valid[b] = (kv_len[b] - 1) / 64, K = topk), and o is bit-identical to
+ * sas_topk_select followed by sas_decode_paged.
+ *
+ *   s        fp32 [B][Hkv][ld]: history block scores (logical block order); row (b, h)
+ *            reads its first (kv_len[b] - 1) / 64 entries.
+ *   ld       row pitch of s, >= max_pages - 1.
+ *   topk     K, 1 <= K <= 64.
+ *   idx, cnt int32 [B][Hkv][topk] and [B][Hkv], out, nullable (both or neither): the kept
+ *            logical blocks (ascending, -1 padded) and their number.
+ *   Kpool, Vpool, num_pages, page_table, max_pages, kv_len: as for sas_decode_paged.
+ *   q, B, Hq, Hkv, d, block, scale, o: as for sas_decode.
+ *   ws       workspace of sas_decode_workspace_size(B, Hq, Hkv, d, topk) bytes.
+ * Returns SAS_ERR_UNSUPPORTED for topk > 64 or max_pages > 1025 (rows of more than 1024
+ * history blocks); sas_topk_select and sas_decode_paged cover those.
+ */
+sas_status sas_decode_paged_topk(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                                 const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                                 const float* s, int ld, int topk, int B, int Hq, int Hkv, int d,
+                                 int block, float scale, void* o, int32_t* idx, int32_t* cnt, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
  * sas_pool_keys - block means of a decode key cache, the input of sas_decode_select.
  * kbar_m = (1/64) sum of the 64 keys of block m, summed in fp32 and rounded to bf16
  * (nearest even). In serving, call it with first_block = the first block completed since

@@ -36,11 +36,12 @@ constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalis
 // kept and, once the ratio falls below tau, that head takes no further block. The wave
 // stops copying when every head has stopped.
 //
-// SEL: the block selection in the same launch (sas_decode_topk). The wave loads its row
-// of history scores, issues the copies of its current block (they depend on kv_len only),
-// then finds the row's Top-K exactly as the selection kernel does (topk_cut / topk_walk,
-// decode mode: the valid scores are the row's first (kv_len - 1) / 64) while those copies
-// are in flight, and keeps the kept block indices, ascending, in LDS for the block list.
+// SEL: the block selection in the same launch (sas_decode_topk, and with PAGED
+// sas_decode_paged_topk). The wave loads its row of history scores, issues the copies of
+// its current block (they depend on kv_len, and paged on its page, only), then finds the
+// row's Top-K exactly as the selection kernel does (topk_cut / topk_walk, decode mode: the
+// valid scores are the row's first (kv_len - 1) / 64) while those copies are in flight,
+// and keeps the kept block indices, ascending, in LDS for the block list.
 template <int D, bool PAGED, bool EARLY, bool SEL>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   constexpr int HE = 32 * D;   // elements of a 32-row half tile
@@ -134,16 +135,31 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     }
     if (t0 == 0) {
       // the current block's two halves into the first two ring slots, in flight during
-      // the search
+      // the search (paged: its page, rows at or past kv_len read as zero; a page id out of
+      // range reads nothing)
+      int pg = 0;
+      if constexpr (PAGED) {
+        pg = a.page_table[(size_t)b * a.max_pages + cur];
+        if (pg < 0 || pg >= a.num_pages) pg = -1;
+      }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const uint32_t so = ((uint32_t)cur * kBlock + 32u * u) * (uint32_t)(D * 2);
         uint16_t* kb = u == 0 ? sk0 : sk1;
         uint16_t* vb = u == 0 ? sv0 : sv1;
+        if constexpr (PAGED) {
+          const size_t off = ((size_t)max(pg, 0) * a.Hkv + h) * (size_t)(kBlock * D) + (size_t)(32 * u) * D;
+          const int pbytes = pg < 0 ? 0 : min(max(L - cur * kBlock - 32 * u, 0), 32) * D * 2;
 #pragma unroll
-        for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, cbytes, kb + 512 * i, voff[i], so);
+          for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Kc + off, pbytes, kb + 512 * i, voff[i], 0u);
 #pragma unroll
-        for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, cbytes, vb + 512 * i, voff[i], so);
+          for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Vc + off, pbytes, vb + 512 * i, voff[i], 0u);
+        } else {
+          const uint32_t so = ((uint32_t)cur * kBlock + 32u * u) * (uint32_t)(D * 2);
+#pragma unroll
+          for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, cbytes, kb + 512 * i, voff[i], so);
+#pragma unroll
+          for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, cbytes, vb + 512 * i, voff[i], so);
+        }
       }
       early_cur = true;
     }
@@ -474,14 +490,16 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   a.wg = wg_order(grid);
   {
     const bool paged = a.page_table != nullptr, early = a.order != nullptr, sel = a.s != nullptr;
-    ProfScope prof(early ? "decode_early_stop" : paged ? "decode_paged" : sel ? "decode_topk" : "decode", st);
+    ProfScope prof(early ? "decode_early_stop" : paged ? (sel ? "decode_paged_topk" : "decode_paged") : sel ? "decode_topk" : "decode", st);
     if (a.d == 128) {
       if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true, false>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<128, true, false, true>), dim3(grid), dim3(64), 0, st, a);
       else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false, false>), dim3(grid), dim3(64), 0, st, a);
       else if (sel) hipLaunchKernelGGL((decode_split_kernel<128, false, false, true>), dim3(grid), dim3(64), 0, st, a);
       else hipLaunchKernelGGL((decode_split_kernel<128, false, false, false>), dim3(grid), dim3(64), 0, st, a);
     } else {
       if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true, false>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<64, true, false, true>), dim3(grid), dim3(64), 0, st, a);
       else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false, false>), dim3(grid), dim3(64), 0, st, a);
       else if (sel) hipLaunchKernelGGL((decode_split_kernel<64, false, false, true>), dim3(grid), dim3(64), 0, st, a);
       else hipLaunchKernelGGL((decode_split_kernel<64, false, false, false>), dim3(grid), dim3(64), 0, st, a);

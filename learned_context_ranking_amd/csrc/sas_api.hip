@@ -369,11 +369,10 @@ sas_status sas_decode_early_stop(const void* q, const void* Kc, const void* Vc, 
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_early_stop launch");
 }
 
-sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool, int num_pages,
-                            const int32_t* page_table, int max_pages, const int32_t* kv_len,
-                            const int32_t* idx, const int32_t* cnt, const float* logg, int B, int Hq,
-                            int Hkv, int d, int block, int kcap, float scale, void* o, void* ws,
-                            size_t ws_bytes, void* stream) {
+static sas_status check_decode_paged(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                                     const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                                     const int32_t* idx, const int32_t* cnt, int B, int Hq, int Hkv, int d,
+                                     int block, int kcap, float scale, const void* o) {
   REQUIRE(q && Kpool && Vpool && page_table && kv_len && cnt && o, SAS_ERR_INVALID_ARG,
           "q, Kpool, Vpool, page_table, kv_len, cnt, o must be non-NULL");
   REQUIRE(kcap == 0 || idx != nullptr, SAS_ERR_INVALID_ARG, "idx is NULL");
@@ -388,16 +387,69 @@ sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool,
   REQUIRE(isfinite(scale) && scale > 0.0f, SAS_ERR_INVALID_ARG, "scale must be finite and > 0");
   REQUIRE(aligned16(q) && aligned16(Kpool) && aligned16(Vpool) && aligned16(o), SAS_ERR_INVALID_ARG,
           "q, Kpool, Vpool, o must be 16-byte aligned");
-  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
-  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
-  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  return SAS_OK;
+}
+
+static sas::DecodeArgs decode_paged_args(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                                         const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                                         const int32_t* idx, const int32_t* cnt, const float* logg, int B,
+                                         int Hq, int Hkv, int d, int kcap, float scale, void* o, void* ws) {
   sas::DecodeArgs a{};
   a.q = (const uint16_t*)q; a.Kc = (const uint16_t*)Kpool; a.Vc = (const uint16_t*)Vpool;
   a.kv_len = kv_len; a.Lmax = (long long)max_pages * 64; a.idx = idx; a.cnt = cnt; a.logg = logg;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.kcap = kcap; a.scale = scale;
   a.o = (uint16_t*)o; a.part = (float*)ws;
   a.page_table = page_table; a.max_pages = max_pages; a.num_pages = num_pages;
+  return a;
+}
+
+sas_status sas_decode_paged(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                            const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                            const int32_t* idx, const int32_t* cnt, const float* logg, int B, int Hq,
+                            int Hkv, int d, int block, int kcap, float scale, void* o, void* ws,
+                            size_t ws_bytes, void* stream) {
+  const sas_status chk = check_decode_paged(q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, idx, cnt, B,
+                                            Hq, Hkv, d, block, kcap, scale, o);
+  if (chk != SAS_OK) return chk;
+  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, kcap);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const sas::DecodeArgs a = decode_paged_args(q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, idx, cnt,
+                                              logg, B, Hq, Hkv, d, kcap, scale, o, ws);
   return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_paged launch");
+}
+
+sas_status sas_decode_paged_topk(const void* q, const void* Kpool, const void* Vpool, int num_pages,
+                                 const int32_t* page_table, int max_pages, const int32_t* kv_len,
+                                 const float* s, int ld, int topk, int B, int Hq, int Hkv, int d,
+                                 int block, float scale, void* o, int32_t* idx, int32_t* cnt, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  REQUIRE(s != nullptr, SAS_ERR_INVALID_ARG, "s must be non-NULL");
+  REQUIRE((idx == nullptr) == (cnt == nullptr), SAS_ERR_INVALID_ARG, "idx and cnt must both be given or both NULL");
+  REQUIRE(topk >= 1, SAS_ERR_INVALID_ARG, "topk=%d must be >= 1", topk);
+  REQUIRE(topk <= sas::kDecSelMax, SAS_ERR_UNSUPPORTED, "topk=%d above %d: use sas_topk_select and sas_decode_paged",
+          topk, sas::kDecSelMax);
+  REQUIRE(max_pages > 0 && max_pages - 1 <= sas::kDecSelMaxCols, SAS_ERR_UNSUPPORTED,
+          "max_pages=%d: more than %d history blocks per row; use sas_topk_select and sas_decode_paged", max_pages,
+          sas::kDecSelMaxCols);
+  REQUIRE(ld >= max_pages - 1, SAS_ERR_INVALID_ARG, "ld=%d below the %d history blocks of max_pages=%d", ld,
+          max_pages - 1, max_pages);
+  // cnt is an output here: the input checks are met with a stand-in pointer
+  const int32_t dummy = 0;
+  const sas_status chk = check_decode_paged(q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, &dummy,
+                                            &dummy, B, Hq, Hkv, d, block, topk, scale, o);
+  if (chk != SAS_OK) return chk;
+  const size_t need = sas::decode_workspace_bytes(B, Hq, Hkv, d, topk);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  sas::DecodeArgs a = decode_paged_args(q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, nullptr, nullptr,
+                                        nullptr, B, Hq, Hkv, d, topk, scale, o, ws);
+  a.s = s;
+  a.s_ld = ld;
+  a.topk = topk;
+  a.idx_out = idx;
+  a.cnt_out = cnt;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_paged_topk launch");
 }
 
 sas_status sas_pool_keys(const void* Kc, int B, int Hkv, int Lmax, int d, const int32_t* kv_len,

@@ -50,6 +50,8 @@ SIGNATURES = {
     "sas_decode": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _SZ, _P], _I),
     "sas_decode_noalloc": ([_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P], _I),
     "sas_decode_topk": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
+    "sas_decode_paged_topk": ([_P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
+                               _P], _I),
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
     "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
@@ -337,6 +339,37 @@ def sas_decode_paged(q, Kpool, Vpool, page_table, kv_len, idx, cnt, scale, logg=
                                   _ptr(kv_len), _ptr(idx), _ptr(cnt), _ptr(logg), B, Hq, Hkv, d, BLOCK, kcap,
                                   float(scale), _ptr(o), _ptr(ws), ws.numel(), _stream(q.device)))
     return o
+
+
+def sas_decode_paged_topk(q, Kpool, Vpool, page_table, kv_len, s, topk, scale, ws=None, out=None, want_idx=False):
+    """sas_decode_topk over a paged cache: q bf16 [B, Hq, d]; Kpool, Vpool bf16
+    [num_pages, Hkv, 64, d]; page_table int32 [B, max_pages]; kv_len int32 [B]; s fp32
+    [B, Hkv, ld] history block scores (or [B, Hkv, 1, ld]). Returns o bf16 [B, Hq, d], and
+    with want_idx also idx int32 [B, Hkv, topk] and cnt int32 [B, Hkv]."""
+    for t, nm in ((q, "q"), (Kpool, "Kpool"), (Vpool, "Vpool")):
+        _need(t, torch.bfloat16, nm)
+    _need(page_table, torch.int32, "page_table")
+    _need(kv_len, torch.int32, "kv_len")
+    _need(s, torch.float32, "s")
+    B, Hq, d = q.shape
+    num_pages, Hkv = Kpool.shape[0], Kpool.shape[1]
+    if Kpool.shape[2] != BLOCK or tuple(Vpool.shape) != tuple(Kpool.shape):
+        raise ValueError(f"pools must be [num_pages, Hkv, {BLOCK}, d] (got {tuple(Kpool.shape)}, {tuple(Vpool.shape)})")
+    max_pages = page_table.shape[1]
+    ld = s.shape[-1]
+    dev = q.device
+    if ws is None:
+        ws = decode_workspace(B, Hq, Hkv, d, topk, dev)
+    o = torch.empty_like(q) if out is None else out
+    idx = cnt = None
+    if want_idx:
+        idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _check(lib().sas_decode_paged_topk(_ptr(q), _ptr(Kpool), _ptr(Vpool), num_pages, _ptr(page_table), max_pages,
+                                       _ptr(kv_len), _ptr(s), ld, int(topk), B, Hq, Hkv, d, BLOCK, float(scale),
+                                       _ptr(o), _ptr(idx), _ptr(cnt), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(dev)))
+    return (o, idx, cnt) if want_idx else o
 
 
 def sas_pool_keys(Kc, kv_len, first_block=0, out=None):

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 24, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -248,6 +248,33 @@ def test_decode_paged_rejects():
                        (11, 66, sas.SAS_ERR_UNSUPPORTED), (5, 1 << 25, sas.SAS_ERR_UNSUPPORTED)):
         bad = list(args); bad[i] = v      # Hq = 66 over Hkv = 2 is a group of 33 > 32
         assert L.sas_decode_paged(*bad) == code, (i, v)
+
+
+def test_decode_paged_topk_rejects():
+    """The paged decode with its own selection: the paged checks plus those of the
+    selection (K in [1, 64], at most 1024 history blocks, ld, idx and cnt together)."""
+    L = sas.lib()
+    need = L.sas_decode_workspace_size(2, 8, 2, 128, 16)
+    # q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, s, ld, topk, B, Hq, Hkv, d,
+    # block, scale, o, idx, cnt, ws, ws_bytes, stream
+    args = [FAKE, FAKE, FAKE, 100, FAKE, 64, FAKE, FAKE, 64, 16, 2, 8, 2, 128, 64, 0.1, FAKE, NULL, NULL, FAKE,
+            need, NULL]
+    for i, v, code in ((7, NULL, sas.SAS_ERR_INVALID_ARG),         # no scores
+                       (9, 0, sas.SAS_ERR_INVALID_ARG),            # K = 0
+                       (9, 65, sas.SAS_ERR_UNSUPPORTED),           # K above 64
+                       (5, 1026, sas.SAS_ERR_UNSUPPORTED),         # 1025 history blocks
+                       (8, 62, sas.SAS_ERR_INVALID_ARG),           # ld below max_pages - 1
+                       (17, FAKE, sas.SAS_ERR_INVALID_ARG),        # idx without cnt
+                       (4, NULL, sas.SAS_ERR_INVALID_ARG),         # no page table
+                       (3, 0, sas.SAS_ERR_INVALID_ARG),            # no pages
+                       (14, 32, sas.SAS_ERR_UNSUPPORTED),          # block != 64
+                       (1, MIS, sas.SAS_ERR_INVALID_ARG),          # misaligned pool
+                       (20, need - 1, sas.SAS_ERR_WORKSPACE)):     # workspace too small
+        bad = list(args); bad[i] = v
+        assert L.sas_decode_paged_topk(*bad) == code, (i, v)
+    ok = list(args); ok[5] = 1025; ok[8] = 1024          # 1024 history blocks: accepted up to the launch
+    ok[0] = NULL                                        # (then stopped by the missing q, before any HIP call)
+    assert L.sas_decode_paged_topk(*ok) == sas.SAS_ERR_INVALID_ARG
 
 
 def test_decode_early_stop_rejects():
