@@ -471,13 +471,35 @@ def run_long_decode(torch, reps=20):
             torch.cuda.synchronize()
             ms_sel = float(np.median([x.elapsed_time(y) for x, y in sel_t]))
             ms_att = float(np.median([x.elapsed_time(y) for x, y in att_t]))
+            ms_two = float(np.median([x[0].elapsed_time(y[1]) for x, y in zip(sel_t, att_t)]))
+            # the same step in two launches (sas_decode_long: scores with per-chunk
+            # candidates, then the decode ranking them); same output
+            wl = sas.decode_long_workspace(B, Hq, Hkv, d, C, K, dev)
+            ol = torch.empty_like(o)
+            sas.sas_decode_long(q[:B], kbar[:B], Kc[:B], Vc[:B], kv_len, K, scale, ws=wl, out=ol)
+            torch.cuda.synchronize()
+            assert torch.equal(ol, o), "sas_decode_long differs from sas_decode_select + sas_decode"
+            lt = []
+            for r in range(reps + 3):
+                flush.sum()
+                a, c = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+                a.record(stream)
+                sas.sas_decode_long(q[:B], kbar[:B], Kc[:B], Vc[:B], kv_len, K, scale, ws=wl, out=ol)
+                c.record(stream)
+                if r >= 3:
+                    lt.append((a, c))
+            torch.cuda.synchronize()
+            ms_long = float(np.median([x.elapsed_time(y) for x, y in lt]))
             hist = (L - 1) // 64
             sel_bytes = B * Hkv * hist * (d * 2 + 4)
             out.append({"context": L, "batch": B, "select_us": round(ms_sel * 1e3, 2),
                         "attn_us": round(ms_att * 1e3, 2),
                         "select_share": round(ms_sel / (ms_sel + ms_att), 3),
-                        "select_gbs": round(sel_bytes / ms_sel / 1e6, 1)})
-            log(f"[bench]   B={B} L={L}: select {ms_sel * 1e3:.1f} us, attention {ms_att * 1e3:.1f} us")
+                        "select_gbs": round(sel_bytes / ms_sel / 1e6, 1),
+                        "step_us": round(ms_two * 1e3, 2),
+                        "decode_long_us": round(ms_long * 1e3, 2)})
+            log(f"[bench]   B={B} L={L}: select {ms_sel * 1e3:.1f} us, attention {ms_att * 1e3:.1f} us, "
+                f"step {ms_two * 1e3:.1f} us; sas_decode_long {ms_long * 1e3:.1f} us")
     del Kc, Vc, kbar
     return out
 
@@ -756,7 +778,8 @@ def main():
         out["long_decode"] = {
             "workload": "one decode step: block scores over pooled keys + Top-K (sas_decode_select), then "
                         "sparse attention (sas_decode); Hq=32, Hkv=8, d=128, K=16 blocks + current block; "
-                        "select GB/s counts pooled keys read and scores written",
+                        "select GB/s counts pooled keys read and scores written; step_us: both, event to "
+                        "event; decode_long_us: the same step as sas_decode_long (two launches, same output)",
             "points": run_long_decode(torch)}
     if not args.no_sweep:
         out["sweep"] = run_sweep(torch, args.steps, kernel_timing=not args.no_kernel_timing)

@@ -415,6 +415,34 @@ sas_status sas_decode_select(const void* q, const void* kbar, int B, int Hq, int
                              const int32_t* kv_len, float scale, int topk, int kcap, float* s,
                              int32_t* idx, int32_t* cnt, float* lse, float* logg, void* stream);
 
+/* Bytes of device workspace sas_decode_long needs (0 on invalid or unsupported sizes). */
+size_t sas_decode_long_workspace_size(int B, int Hq, int Hkv, int d, int C, int topk);
+
+/*
+ * sas_decode_long - one decode step over a long context in two launches: the block scores
+ * of sas_decode_select with their Top-K, and the decode of sas_decode ([SAS-ja] "仕組み",
+ * Algorithm 2; the scores as in sas_decode_select, [PBS-ja] sections 3 and 4). The kept
+ * blocks and o are identical to sas_decode_select (kcap = topk) followed by sas_decode.
+ * The first launch scores the pooled keys in chunks and keeps each chunk's min(topk,
+ * blocks) best (every block of the row's Top-K is among its chunk's best); the decode
+ * ranks those candidates in its own prologue, beside the copies of the current block,
+ * instead of a row-wide selection launch.
+ *
+ *   q, Kc, Vc, kv_len, Lmax, B, Hq, Hkv, d, block, scale, o: as for sas_decode.
+ *   kbar     bf16 [B][Hkv][C][d] from sas_pool_keys, 16-byte aligned; C in [(Lmax - 1) / 64,
+ *            8192].
+ *   topk     K, 1 <= K <= 64.
+ *   idx, cnt int32 [B][Hkv][topk] and [B][Hkv], out, nullable (both or neither): the kept
+ *            blocks (ascending, -1 padded) and their number, as sas_decode_select writes them.
+ *   ws       workspace of sas_decode_long_workspace_size(B, Hq, Hkv, d, C, topk) bytes,
+ *            16-byte aligned (partial states and candidates; no initialisation needed).
+ * Returns SAS_ERR_UNSUPPORTED for topk > 64 or C > 8192.
+ */
+sas_status sas_decode_long(const void* q, const void* kbar, int C, const void* Kc, const void* Vc,
+                           const int32_t* kv_len, int Lmax, int topk, int B, int Hq, int Hkv, int d,
+                           int block, float scale, void* o, int32_t* idx, int32_t* cnt, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /*
  * Kernel timing, for measurement (not part of the pages' method; off by default).
  *

@@ -41,8 +41,11 @@ constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalis
 // its current block (they depend on kv_len, and paged on its page, only), then finds the
 // row's Top-K exactly as the selection kernel does (topk_cut / topk_walk, decode mode: the
 // valid scores are the row's first (kv_len - 1) / 64) while those copies are in flight,
-// and keeps the kept block indices, ascending, in LDS for the block list.
-template <int D, bool PAGED, bool EARLY, bool SEL>
+// and keeps the kept block indices, ascending, in LDS for the block list. SEL = 1 ranks
+// the row's score columns (column m is block m); SEL = 2 ranks candidate slots, each a
+// (score, block) pair with empty slots marked by block -1, the slots in ascending block
+// order (so a tie still goes to the lower block), as the candidates kernel writes them.
+template <int D, bool PAGED, bool EARLY, int SEL>
 __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   constexpr int HE = 32 * D;   // elements of a 32-row half tile
   __shared__ __attribute__((aligned(16))) uint16_t sk0[HE];
@@ -79,15 +82,22 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   // history ((Lmax - 1) / 64, at most kDecSelMaxCols, and the row holds s_ld >= that many),
   // so the loads need not wait for kv_len; the columns past the sequence's own history are
   // masked once it is known.
+  // (SEL = 2: the row's candidate slots, s_ld of them, and their blocks.)
   constexpr int PL = SEL ? kDecSelMaxCols / 64 : 1;
   float x[PL];
-  int nld = 0;
+  int xid[SEL == 2 ? PL : 1];
+  int ncol = 0;
   if constexpr (SEL) {
-    const int ncol = min(a.s_ld, (int)((a.Lmax - 1) / kBlock));
-    nld = (ncol + 63) >> 6;
+    ncol = SEL == 2 ? a.s_ld : min(a.s_ld, (int)((a.Lmax - 1) / kBlock));
+    const int nld = (ncol + 63) >> 6;
     const float* srow = a.s + bh * a.s_ld;
 #pragma unroll
     for (int i = 0; i < PL; ++i) x[i] = i < nld ? srow[min(lane + 64 * i, ncol - 1)] : -INFINITY;
+    if constexpr (SEL == 2) {
+      const int32_t* irow = a.s_id + bh * a.s_ld;
+#pragma unroll
+      for (int i = 0; i < PL; ++i) xid[i] = i < nld ? irow[min(lane + 64 * i, ncol - 1)] : -1;
+    }
   }
   const int L = min(max(a.kv_len[b], 1), (int)a.Lmax);
   const int cur = (L - 1) / kBlock;
@@ -117,8 +127,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
   int cnt = 0;
   bool early_cur = false;   // (SEL) the current block's copies were issued before the selection
   if constexpr (SEL) {
-    const int valid = cur;   // the row's history blocks (valid <= 64 nld)
-    const int k = min(a.topk, valid);
+    // positions ranked: the history columns (SEL = 1; cur <= ncol) or every candidate slot
+    const int valid = SEL == 2 ? ncol : cur;
+    const int k = min(a.topk, cur);   // (SEL = 2: at least min(K, cur) slots hold blocks)
     const int nreg = __builtin_amdgcn_readfirstlane((valid + 63) >> 6);
     // The scores (and q) are awaited before the current block's copies are issued: the
     // memory counter drains in issue order, so a wait for them after the copies would be a
@@ -129,9 +140,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
     for (int i = 0; i < PL; ++i) {
       float v = -INFINITY;
       if (i < nreg) v = x[i];
-      v = (lane + 64 * i < valid && v == v) ? v : -INFINITY;   // NaN ranks as -inf
-      v = v == 0.0f ? 0.0f : v;                                 // -0 -> +0
-      key[i] = lane + 64 * i < valid ? order_key(v) : 0u;
+      bool in = lane + 64 * i < valid;
+      if constexpr (SEL == 2) in = in && xid[i] >= 0 && xid[i] < cur;   // an empty slot is no block
+      v = (in && v == v) ? v : -INFINITY;   // NaN ranks as -inf
+      v = v == 0.0f ? 0.0f : v;             // -0 -> +0
+      key[i] = in ? order_key(v) : 0u;
     }
     if (t0 == 0) {
       // the current block's two halves into the first two ring slots, in flight during
@@ -168,11 +181,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       int need_eq;
       topk_cut<PL, true>(key, nreg, valid, k, T, need_eq);   // the wave has its SIMD to itself
       if (need_eq == 0) {   // no tie at the cut: every lane writes, the unkept ones to a spare slot
-        auto put = [&](int i, int pos, bool kept) { s_sel[kept ? pos : kDecSelMax] = lane + 64 * i; };
+        auto put = [&](int i, int pos, bool kept) {
+          s_sel[kept ? pos : kDecSelMax] = SEL == 2 ? xid[i] : lane + 64 * i;
+        };
         if (nreg <= PL / 2) topk_walk_gt<PL / 2>(key, T, put);
         else topk_walk_gt<PL>(key, T, put);
       } else {
-        topk_walk(key, nreg, T, need_eq, [&](int i, int pos) { s_sel[pos] = lane + 64 * i; });
+        topk_walk(key, nreg, T, need_eq, [&](int i, int pos) { s_sel[pos] = SEL == 2 ? xid[i] : lane + 64 * i; });
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");   // the list, for every lane
@@ -490,19 +505,23 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   a.wg = wg_order(grid);
   {
     const bool paged = a.page_table != nullptr, early = a.order != nullptr, sel = a.s != nullptr;
-    ProfScope prof(early ? "decode_early_stop" : paged ? (sel ? "decode_paged_topk" : "decode_paged") : sel ? "decode_topk" : "decode", st);
+    ProfScope prof(early ? "decode_early_stop"
+                   : paged ? (sel ? "decode_paged_topk" : "decode_paged")
+                   : sel ? (a.s_id != nullptr ? "decode_candidates_topk" : "decode_topk") : "decode", st);
     if (a.d == 128) {
-      if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true, false>), dim3(grid), dim3(64), 0, st, a);
-      else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<128, true, false, true>), dim3(grid), dim3(64), 0, st, a);
-      else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false, false>), dim3(grid), dim3(64), 0, st, a);
-      else if (sel) hipLaunchKernelGGL((decode_split_kernel<128, false, false, true>), dim3(grid), dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((decode_split_kernel<128, false, false, false>), dim3(grid), dim3(64), 0, st, a);
+      if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true, 0>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<128, true, false, 1>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false, 0>), dim3(grid), dim3(64), 0, st, a);
+      else if (sel && a.s_id != nullptr) hipLaunchKernelGGL((decode_split_kernel<128, false, false, 2>), dim3(grid), dim3(64), 0, st, a);
+      else if (sel) hipLaunchKernelGGL((decode_split_kernel<128, false, false, 1>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<128, false, false, 0>), dim3(grid), dim3(64), 0, st, a);
     } else {
-      if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true, false>), dim3(grid), dim3(64), 0, st, a);
-      else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<64, true, false, true>), dim3(grid), dim3(64), 0, st, a);
-      else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false, false>), dim3(grid), dim3(64), 0, st, a);
-      else if (sel) hipLaunchKernelGGL((decode_split_kernel<64, false, false, true>), dim3(grid), dim3(64), 0, st, a);
-      else hipLaunchKernelGGL((decode_split_kernel<64, false, false, false>), dim3(grid), dim3(64), 0, st, a);
+      if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true, 0>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<64, true, false, 1>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false, 0>), dim3(grid), dim3(64), 0, st, a);
+      else if (sel && a.s_id != nullptr) hipLaunchKernelGGL((decode_split_kernel<64, false, false, 2>), dim3(grid), dim3(64), 0, st, a);
+      else if (sel) hipLaunchKernelGGL((decode_split_kernel<64, false, false, 1>), dim3(grid), dim3(64), 0, st, a);
+      else hipLaunchKernelGGL((decode_split_kernel<64, false, false, 0>), dim3(grid), dim3(64), 0, st, a);
     }
   }
   if (a.nchunk > 1) {

@@ -259,48 +259,142 @@ hipError_t launch_pool(const PoolArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Block scores. Grid: rows x chunks of CH blocks. Each wave reads 64 lanes x 16 bytes =
-// BPW pooled keys per load (LPB lanes per key, fully coalesced), NIT loads in flight per
-// lane, and reduces each key's partial dot products across its LPB lanes.
+// Block scores of one wave: NIT loads of 64 lanes x 16 bytes = BPW pooled keys each (LPB
+// lanes per key, fully coalesced, all NIT in flight), each key's partial dot products
+// reduced across its LPB lanes. f(m, score) is called, on one lane per key, for the wave's
+// blocks m0 .. m0 + NIT * BPW - 1 below hist.
+template <int D>
+struct WaveScores {
+  static constexpr int LPB = D / 8, BPW = 64 / LPB, NIT = 8, PER_WAVE = NIT * BPW;
+  float qb[8];   // mean of the group's queries (this lane's 8-element slice), times scale / G
+  __device__ __forceinline__ WaveScores(const DecSelArgs& a, int b, int h) {
+    const int sub = (threadIdx.x & 63) % LPB;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qb[i] = 0.0f;
+    const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)h * a.G) * D + 8 * sub;
+    for (int g = 0; g < a.G; ++g) {
+      const u16x8 v = ld16(qp + (size_t)g * D);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qb[i] += bf2f(v[i]);
+    }
+  }
+  template <class F>
+  __device__ __forceinline__ void run(const DecSelArgs& a, long long row, int m0, int hist, F&& f) const {
+    const int lane = threadIdx.x & 63, sub = lane % LPB, bsel = lane / LPB;
+    const float qs = a.scale / (float)a.G;
+    const uint16_t* kp = a.kbar + ((size_t)row * a.C) * D + 8 * sub;
+    u16x8 kv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int m = m0 + it * BPW + bsel;
+      kv[it] = m < hist ? ld16(kp + (size_t)m * D) : u16x8{};
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot += qb[i] * bf2f(kv[it][i]);
+#pragma unroll
+      for (int o = 1; o < LPB; o <<= 1) dot += __shfl_xor(dot, o, 64);
+      const int m = m0 + it * BPW + bsel;
+      if (sub == 0 && m < hist) f(m, dot * qs);
+    }
+  }
+};
+
+// Block scores. Grid: rows x chunks of 4 waves x PER_WAVE blocks.
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(const DecSelArgs a) {
-  constexpr int LPB = D / 8, BPW = 64 / LPB, NIT = 8;
-  constexpr int CH = 4 * NIT * BPW;
+  using W = WaveScores<D>;
+  constexpr int CH = 4 * W::PER_WAVE;
   const int nch = (a.C + CH - 1) / CH;
   const long long row = blockIdx.x / nch;      // (b, h)
   const int chunk = (int)(blockIdx.x % nch);
   const int b = (int)(row / a.Hkv), h = (int)(row % a.Hkv);
   const int hist = min(max((a.kv_len[b] - 1) / kBlock, 0), a.C);
-  const int m0 = chunk * CH + (threadIdx.x >> 6) * NIT * BPW;
+  const int m0 = chunk * CH + (threadIdx.x >> 6) * W::PER_WAVE;
   if (m0 >= hist) return;   // uniform per wave
-  const int lane = threadIdx.x & 63, sub = lane % LPB, bsel = lane / LPB;
-  // mean of the group's queries, this lane's 8-element slice
-  float qb[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  const uint16_t* qp = a.q + ((size_t)b * a.Hq + (size_t)h * a.G) * D + 8 * sub;
-  for (int g = 0; g < a.G; ++g) {
-    const u16x8 v = ld16(qp + (size_t)g * D);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qb[i] += bf2f(v[i]);
-  }
-  const float qs = a.scale / (float)a.G;
-  const uint16_t* kp = a.kbar + ((size_t)row * a.C) * D + 8 * sub;
-  u16x8 kv[NIT];
-#pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    const int m = m0 + it * BPW + bsel;
-    kv[it] = m < hist ? ld16(kp + (size_t)m * D) : u16x8{};
-  }
+  const W ws(a, b, h);
   float* srow = a.s + (size_t)row * a.C;
+  ws.run(a, row, m0, hist, [&](int m, float v) { srow[m] = v; });
+}
+
+// Candidates: the scores of a chunk of CH = R x 4 x PER_WAVE blocks (each wave R runs of
+// the scoring above) go to LDS, and one wave keeps the chunk's min(K, blocks) best by the
+// selection's own search and walk (order keys: NaN as -inf, -0 as +0; ties to the lower
+// block). Every block of the row's global Top-K is among its chunk's K best, so the Top-K
+// of the candidates is the Top-K of the row; the slots keep ascending block order, so a
+// tie between candidates still goes to the lower block. Every slot of the chunk is
+// written (empty ones: block -1, score 0), also for chunks past the row's history.
+template <int D, int R>
+__global__ __launch_bounds__(256) void cand_kernel(const DecSelArgs a) {
+  using W = WaveScores<D>;
+  constexpr int CH = R * 4 * W::PER_WAVE, PL = CH / 64;
+  __shared__ float sc[CH];
+  const int nch = (a.C + CH - 1) / CH;
+  const long long row = blockIdx.x / nch;
+  const int chunk = (int)(blockIdx.x % nch);
+  const int b = (int)(row / a.Hkv), h = (int)(row % a.Hkv);
+  const int hist = min(max((a.kv_len[b] - 1) / kBlock, 0), a.C);
+  const int base = chunk * CH;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (base < hist) {
+    const W ws(a, b, h);
 #pragma unroll
-  for (int it = 0; it < NIT; ++it) {
-    float dot = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dot += qb[i] * bf2f(kv[it][i]);
-#pragma unroll
-    for (int o = 1; o < LPB; o <<= 1) dot += __shfl_xor(dot, o, 64);
-    const int m = m0 + it * BPW + bsel;
-    if (sub == 0 && m < hist) srow[m] = dot * qs;
+    for (int r = 0; r < R; ++r) {
+      const int m0 = base + (r * 4 + wv) * W::PER_WAVE;
+      if (m0 < hist) ws.run(a, row, m0, hist, [&](int m, float v) { sc[m - base] = v; });
+    }
   }
+  __syncthreads();
+  if (wv != 0) return;
+  const int valid = min(max(hist - base, 0), CH);   // the chunk's history blocks (uniform)
+  const int k = min(a.topk, valid);
+  float* cs = a.cs + (size_t)row * a.cld + (size_t)chunk * a.topk;
+  int32_t* ci = a.ci + (size_t)row * a.cld + (size_t)chunk * a.topk;
+  for (int p = k + lane; p < a.topk; p += 64) { cs[p] = 0.0f; ci[p] = -1; }
+  if (k == 0) return;
+  const int nreg = (valid + 63) >> 6;
+  uint32_t key[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    float v = lane + 64 * i < valid ? sc[lane + 64 * i] : 0.0f;
+    v = v == v ? v : -INFINITY;   // NaN ranks as -inf
+    v = v == 0.0f ? 0.0f : v;     // -0 equals +0
+    key[i] = lane + 64 * i < valid ? sas::order_key(v) : 0u;
+  }
+  uint32_t T;
+  int need_eq;
+  topk_cut(key, nreg, valid, k, T, need_eq);
+  topk_walk(key, nreg, T, need_eq, [&](int i, int pos) {
+    cs[pos] = sc[lane + 64 * i];
+    ci[pos] = base + lane + 64 * i;
+  });
+}
+
+int decode_cand_chunk(int C, int topk, int d) {
+  const int per = 4 * (d == 128 ? WaveScores<128>::PER_WAVE : WaveScores<64>::PER_WAVE);
+  for (int ch = per; ch <= 1024; ch *= 2)   // (a chunk is ranked by one wave, <= 16 keys a lane)
+    if ((long long)((C + ch - 1) / ch) * topk <= kDecSelMaxCols) return ch;
+  return 0;   // more slots than one decode row ranks
+}
+
+hipError_t launch_decode_candidates(const DecSelArgs& a, hipStream_t st) {
+  const long long rows = (long long)a.B * a.Hkv;
+  const dim3 grid((unsigned)(rows * ((a.C + a.cch - 1) / a.cch)));
+  const int r = a.cch / (4 * (a.d == 128 ? WaveScores<128>::PER_WAVE : WaveScores<64>::PER_WAVE));
+  ProfScope prof("decode_candidates", st);
+  if (a.d == 128) {
+    if (r == 1) hipLaunchKernelGGL((cand_kernel<128, 1>), grid, dim3(256), 0, st, a);
+    else if (r == 2) hipLaunchKernelGGL((cand_kernel<128, 2>), grid, dim3(256), 0, st, a);
+    else if (r == 4) hipLaunchKernelGGL((cand_kernel<128, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((cand_kernel<128, 8>), grid, dim3(256), 0, st, a);
+  } else {
+    if (r == 1) hipLaunchKernelGGL((cand_kernel<64, 1>), grid, dim3(256), 0, st, a);
+    else if (r == 2) hipLaunchKernelGGL((cand_kernel<64, 2>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((cand_kernel<64, 4>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(const DecSelArgs a) {
@@ -311,7 +405,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_rows_kernel(const DecSelArgs
 hipError_t launch_decode_select(const DecSelArgs& a, hipStream_t st) {
   const long long rows = (long long)a.B * a.Hkv;
   {
-    const int ch = a.d == 128 ? 4 * 8 * 4 : 4 * 8 * 8;
+    const int ch = 4 * (a.d == 128 ? WaveScores<128>::PER_WAVE : WaveScores<64>::PER_WAVE);
     const long long nch = (a.C + ch - 1) / ch;
     ProfScope prof("block_scores", st);
     if (a.d == 128) hipLaunchKernelGGL(score_kernel<128>, dim3((unsigned)(rows * nch)), dim3(256), 0, st, a);

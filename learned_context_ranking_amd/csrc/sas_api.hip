@@ -490,4 +490,71 @@ sas_status sas_decode_select(const void* q, const void* kbar, int B, int Hq, int
   return hip_result(sas::launch_decode_select(a, (hipStream_t)stream), "sas_decode_select launch");
 }
 
+// Workspace of sas_decode_long: the decode's partial states, then the candidate slots
+// (scores, then blocks), each part 256-byte aligned. 0 on invalid sizes.
+static size_t decode_long_layout(int B, int Hq, int Hkv, int d, int C, int topk, int* cch, int* cld,
+                                 size_t* cand_off) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || (d != 64 && d != 128) || C <= 0 || C > 8192 || topk < 1 ||
+      topk > sas::kDecSelMax)
+    return 0;
+  const int ch = sas::decode_cand_chunk(C, topk, d);
+  if (ch == 0) return 0;
+  const int ld = (C + ch - 1) / ch * topk;
+  const size_t part = (sas::decode_workspace_bytes(B, Hq, Hkv, d, topk) + 255) / 256 * 256;
+  const size_t slots = (size_t)B * Hkv * ld;
+  if (cch) *cch = ch;
+  if (cld) *cld = ld;
+  if (cand_off) *cand_off = part;
+  return part + (slots * 4 + 255) / 256 * 256 + slots * 4;
+}
+
+size_t sas_decode_long_workspace_size(int B, int Hq, int Hkv, int d, int C, int topk) {
+  return decode_long_layout(B, Hq, Hkv, d, C, topk, nullptr, nullptr, nullptr);
+}
+
+sas_status sas_decode_long(const void* q, const void* kbar, int C, const void* Kc, const void* Vc,
+                           const int32_t* kv_len, int Lmax, int topk, int B, int Hq, int Hkv, int d,
+                           int block, float scale, void* o, int32_t* idx, int32_t* cnt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  REQUIRE(kbar != nullptr, SAS_ERR_INVALID_ARG, "kbar must be non-NULL");
+  REQUIRE((idx == nullptr) == (cnt == nullptr), SAS_ERR_INVALID_ARG, "idx and cnt must both be given or both NULL");
+  REQUIRE(topk >= 1, SAS_ERR_INVALID_ARG, "topk=%d must be >= 1", topk);
+  REQUIRE(topk <= sas::kDecSelMax, SAS_ERR_UNSUPPORTED,
+          "topk=%d above %d: use sas_decode_select and sas_decode", topk, sas::kDecSelMax);
+  REQUIRE(C >= 1 && C <= 8192, SAS_ERR_UNSUPPORTED, "C=%d out of [1, 8192] pooled blocks", C);
+  REQUIRE(Lmax > 0 && (Lmax - 1) / 64 <= C, SAS_ERR_INVALID_ARG,
+          "C=%d pooled blocks cannot hold the %d history blocks of Lmax=%d", C, (Lmax - 1) / 64, Lmax);
+  REQUIRE(aligned16(kbar), SAS_ERR_INVALID_ARG, "kbar must be 16-byte aligned");
+  // cnt is an output here: check_decode's input checks are met with a stand-in pointer
+  const int32_t dummy = 0;
+  const sas_status chk = check_decode(q, Kc, Vc, kv_len, Lmax, &dummy, &dummy, B, Hq, Hkv, d, block, topk, scale, o);
+  if (chk != SAS_OK) return chk;
+  int cch = 0, cld = 0;
+  size_t cand_off = 0;
+  const size_t need = decode_long_layout(B, Hq, Hkv, d, C, topk, &cch, &cld, &cand_off);
+  REQUIRE(need > 0, SAS_ERR_UNSUPPORTED, "no candidate layout for C=%d, topk=%d", C, topk);
+  REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
+  REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  const size_t slots = (size_t)B * Hkv * cld;
+  float* cs = (float*)((char*)ws + cand_off);
+  int32_t* ci = (int32_t*)((char*)ws + cand_off + (slots * 4 + 255) / 256 * 256);
+
+  sas::DecSelArgs sa{};
+  sa.q = (const uint16_t*)q; sa.kbar = (const uint16_t*)kbar; sa.B = B; sa.Hq = Hq; sa.Hkv = Hkv;
+  sa.G = Hq / Hkv; sa.d = d; sa.C = C; sa.kv_len = kv_len; sa.scale = scale; sa.topk = topk;
+  sa.cs = cs; sa.ci = ci; sa.cch = cch; sa.cld = cld;
+  const sas_status st = hip_result(sas::launch_decode_candidates(sa, (hipStream_t)stream),
+                                   "sas_decode_long candidates launch");
+  if (st != SAS_OK) return st;
+  sas::DecodeArgs a = decode_args(q, Kc, Vc, kv_len, Lmax, nullptr, nullptr, nullptr, B, Hq, Hkv, d, topk, scale, o);
+  a.part = (float*)ws;
+  a.s = cs;
+  a.s_ld = cld;
+  a.s_id = ci;
+  a.topk = topk;
+  a.idx_out = idx;
+  a.cnt_out = cnt;
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_long launch");
+}
+
 }  // extern "C"

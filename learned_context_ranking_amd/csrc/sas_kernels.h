@@ -93,8 +93,18 @@ struct DecSelArgs {
   int32_t* cnt;         // [B][Hkv]
   float* lse;           // [B][Hkv] or null
   float* logg;          // [B][Hkv][kcap] or null
+  // candidates (launch_decode_candidates): per chunk of cch blocks its min(topk, blocks)
+  // best, as (score, block) in topk slots, ascending block, empty slots block -1;
+  // cs / ci are [B][Hkv][cld], cld = ceil(C / cch) * topk
+  float* cs;
+  int32_t* ci;
+  int cch, cld;
 };
 hipError_t launch_decode_select(const DecSelArgs& a, hipStream_t st);
+// Candidate chunk size in blocks for rows of C blocks and K = topk: the smallest
+// (4 waves x blocks per wave) x 2^r that leaves at most kDecSelMaxCols slots per row.
+int decode_cand_chunk(int C, int topk, int d);
+hipError_t launch_decode_candidates(const DecSelArgs& a, hipStream_t st);
 
 struct AttnArgs {
   const uint16_t* Q;
@@ -162,6 +172,9 @@ struct DecodeArgs {
   int s_ld, topk;
   int32_t* idx_out;
   int32_t* cnt_out;
+  // (candidates) block of each score slot [B][Hkv][s_ld], -1 for an empty slot; slots in
+  // ascending block order. With s_id == null slot m is block m.
+  const int32_t* s_id;
   WgOrder wg;            // workgroup order of the decode launch (set by the launcher)
 };
 constexpr int kDecSelMax = 64;        // largest K of the decode with its own selection

@@ -39,7 +39,7 @@ KERNELS = {
     "dkv": ("dkv_kernel<128, false>", ["attn_bwd.hip", "sas_common.h"]),
     "dq": ("dq_kernel<128, false>", ["attn_bwd.hip", "sas_common.h"]),
     "fwd": ("fwd_kernel<128, 1, 4, false>", ["attn_fwd.hip", "sas_common.h"]),
-    "decode": ("decode_split_kernel<128, false, false, false>", ["decode.hip", "sas_common.h"]),
+    "decode": ("decode_split_kernel<128, false, false, 0>", ["decode.hip", "sas_common.h"]),
     "select": ("select_kernel<8, 0>", ["select.hip", "sas_common.h"]),
 }
 CALIB_BYTES = 256 << 20

@@ -52,6 +52,8 @@ SIGNATURES = {
     "sas_decode_topk": ([_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
     "sas_decode_paged_topk": ([_P, _P, _P, _I, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
                                _P], _I),
+    "sas_decode_long_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "sas_decode_long": ([_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
     "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
@@ -369,6 +371,38 @@ def sas_decode_paged_topk(q, Kpool, Vpool, page_table, kv_len, s, topk, scale, w
                                        _ptr(kv_len), _ptr(s), ld, int(topk), B, Hq, Hkv, d, BLOCK, float(scale),
                                        _ptr(o), _ptr(idx), _ptr(cnt), _ptr(ws), ws.numel() * ws.element_size(),
                                        _stream(dev)))
+    return (o, idx, cnt) if want_idx else o
+
+
+def decode_long_workspace(B, Hq, Hkv, d, C, topk, device):
+    n = lib().sas_decode_long_workspace_size(B, Hq, Hkv, d, C, int(topk))
+    if n == 0:
+        raise ValueError(f"no decode_long layout for B={B} Hq={Hq} Hkv={Hkv} d={d} C={C} topk={topk}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def sas_decode_long(q, kbar, Kc, Vc, kv_len, topk, scale, ws=None, out=None, want_idx=False):
+    """One long-context decode step (block scores over the pooled keys, Top-K, decode) in two
+    launches. q bf16 [B, Hq, d]; kbar bf16 [B, Hkv, C, d] from sas_pool_keys; Kc/Vc bf16
+    [B, Hkv, Lmax, d]; kv_len int32 [B]. Returns o bf16 [B, Hq, d], and with want_idx also
+    idx int32 [B, Hkv, topk] and cnt int32 [B, Hkv]."""
+    for t, nm in ((q, "q"), (kbar, "kbar"), (Kc, "Kc"), (Vc, "Vc")):
+        _need(t, torch.bfloat16, nm)
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hq, d = q.shape
+    Hkv, Lmax = Kc.shape[1], Kc.shape[2]
+    C = kbar.shape[2]
+    dev = q.device
+    if ws is None:
+        ws = decode_long_workspace(B, Hq, Hkv, d, C, topk, dev)
+    o = torch.empty_like(q) if out is None else out
+    idx = cnt = None
+    if want_idx:
+        idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _check(lib().sas_decode_long(_ptr(q), _ptr(kbar), C, _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, int(topk), B, Hq,
+                                 Hkv, d, BLOCK, float(scale), _ptr(o), _ptr(idx), _ptr(cnt), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(dev)))
     return (o, idx, cnt) if want_idx else o
 
 
