@@ -277,6 +277,33 @@ def test_decode_paged_topk_rejects():
     assert L.sas_decode_paged_topk(*ok) == sas.SAS_ERR_INVALID_ARG
 
 
+def test_decode_long_rejects():
+    """The two-launch long-context decode checks its sizes before any HIP call, and its
+    workspace query is 0 for the sizes it rejects."""
+    L = sas.lib()
+    assert L.sas_decode_long_workspace_size(2, 8, 2, 128, 8192, 16) > 0
+    for bad in ((2, 8, 2, 128, 8193, 16), (2, 8, 2, 128, 512, 65), (2, 8, 2, 128, 512, 0),
+                (2, 8, 3, 128, 512, 16), (2, 8, 2, 96, 512, 16), (0, 8, 2, 128, 512, 16)):
+        assert L.sas_decode_long_workspace_size(*bad) == 0, bad
+    need = L.sas_decode_long_workspace_size(2, 8, 2, 128, 512, 16)
+    # q, kbar, C, Kc, Vc, kv_len, Lmax, topk, B, Hq, Hkv, d, block, scale, o, idx, cnt, ws, ws_bytes, stream
+    args = [FAKE, FAKE, 512, FAKE, FAKE, FAKE, 32768, 16, 2, 8, 2, 128, 64, 0.1, FAKE, NULL, NULL, FAKE, need, NULL]
+    for i, v, code in ((1, NULL, sas.SAS_ERR_INVALID_ARG),          # no pooled keys
+                       (1, MIS, sas.SAS_ERR_INVALID_ARG),           # misaligned pooled keys
+                       (7, 0, sas.SAS_ERR_INVALID_ARG),             # K = 0
+                       (7, 65, sas.SAS_ERR_UNSUPPORTED),            # K above 64
+                       (2, 8193, sas.SAS_ERR_UNSUPPORTED),          # more than 8192 pooled blocks
+                       (6, 32834, sas.SAS_ERR_INVALID_ARG),         # 513 history blocks, C = 512
+                       (15, FAKE, sas.SAS_ERR_INVALID_ARG),         # idx without cnt
+                       (0, NULL, sas.SAS_ERR_INVALID_ARG),          # no q
+                       (12, 32, sas.SAS_ERR_UNSUPPORTED),           # block != 64
+                       (18, need - 1, sas.SAS_ERR_WORKSPACE)):      # workspace too small
+        bad = list(args); bad[i] = v
+        assert L.sas_decode_long(*bad) == code, (i, v)
+    ok = list(args); ok[6] = 32832; ok[0] = NULL     # 512 history blocks fit C = 512 (then the
+    assert L.sas_decode_long(*ok) == sas.SAS_ERR_INVALID_ARG   # missing q stops it, before any HIP call)
+
+
 def test_decode_early_stop_rejects():
     L = sas.lib()
     # q, Kc, Vc, kv_len, Lmax, idx, cnt, order, B, Hq, Hkv, d, block, kcap, scale, tau, o, used, stream
