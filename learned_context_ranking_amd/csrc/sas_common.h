@@ -213,9 +213,11 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 //  * BALLOT = false: per-lane counts on the vector ALUs and one DPP wave reduction per bit,
 //    for kernels that keep several waves on each SIMD (a ballot and a scalar popcount per
 //    register would queue them all on the CU's single scalar unit);
+// Either way the registers past the row's keys (i >= nreg) must hold 0: the counts run
+// over a compile-time number of registers, the smallest listed step >= nreg.
 //  * BALLOT = true: one compare mask per register, summed by scalar popcounts, for a wave
 //    that has its SIMD to itself (no reduction chain: the latency of each bit is a few
-//    issue slots). The registers past nreg must hold 0.
+//    issue slots).
 template <int PL, bool BALLOT = false>
 __device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
                                          int& need_eq);
@@ -312,14 +314,15 @@ __device__ __forceinline__ float dpp_max(float v) {
                                    [](int x, int y) { return __float_as_int(fmaxf(__int_as_float(x), __int_as_float(y))); }));
 }
 
-// Number of keys >= c (GE) or > c over the wave's registers i < nreg: per-lane counts on
-// the vector ALUs and one DPP wave reduction.
-template <int PL, bool GE>
-__device__ __forceinline__ int topk_count_dpp(const uint32_t (&key)[PL], int nreg, uint32_t c) {
+// Number of keys >= c (GE) or > c over the wave's first NR registers: per-lane counts on
+// the vector ALUs (a compare and an add each; no guard per register, whose lane-mask
+// combination would cost two more instructions) and one DPP wave reduction. Registers
+// past the row's keys must hold 0.
+template <int NR, int PL, bool GE>
+__device__ __forceinline__ int topk_count_dpp(const uint32_t (&key)[PL], uint32_t c) {
   int cl = 0;
 #pragma clang loop unroll(full)
-  for (int i = 0; i < PL; ++i)
-    if (i < nreg) cl += (GE ? key[i] >= c : key[i] > c) ? 1 : 0;
+  for (int i = 0; i < NR; ++i) cl += (GE ? key[i] >= c : key[i] > c) ? 1 : 0;
   return dpp_sum_i(cl);
 }
 // The same over the first NR registers, each compare's lane mask (v_cmp into a scalar
@@ -340,7 +343,7 @@ __device__ __forceinline__ void topk_cut_n(const uint32_t (&key)[PL], int nreg, 
                                            int& need_eq) {
   auto count = [&](uint32_t c, auto ge) {
     if constexpr (BALLOT) return topk_count_mask<NR, PL, decltype(ge)::value>(key, c);
-    else return topk_count_dpp<PL, decltype(ge)::value>(key, nreg, c);
+    else return topk_count_dpp<NR, PL, decltype(ge)::value>(key, c);
   };
   T = 0;
   if (k < valid) {
@@ -360,9 +363,16 @@ __device__ __forceinline__ void topk_cut_n(const uint32_t (&key)[PL], int nreg, 
 template <int PL, bool BALLOT>
 __device__ __forceinline__ void topk_cut(const uint32_t (&key)[PL], int nreg, int valid, int k, uint32_t& T,
                                          int& need_eq) {
-  if constexpr (BALLOT && PL >= 2) {   // count over half the registers when the rest are padding
+  // count over the smallest compile-time number of registers that holds the row's keys
+  // (a half or all of them with mask counts, a quarter steps with per-lane counts)
+  if constexpr (BALLOT && PL >= 2) {
     if (nreg <= PL / 2) topk_cut_n<PL, PL / 2, true>(key, nreg, valid, k, T, need_eq);
     else topk_cut_n<PL, PL, true>(key, nreg, valid, k, T, need_eq);
+  } else if constexpr (!BALLOT && PL >= 8) {
+    if (nreg <= PL / 4) topk_cut_n<PL, PL / 4, false>(key, nreg, valid, k, T, need_eq);
+    else if (nreg <= PL / 2) topk_cut_n<PL, PL / 2, false>(key, nreg, valid, k, T, need_eq);
+    else if (nreg <= 3 * PL / 4) topk_cut_n<PL, 3 * PL / 4, false>(key, nreg, valid, k, T, need_eq);
+    else topk_cut_n<PL, PL, false>(key, nreg, valid, k, T, need_eq);
   } else {
     topk_cut_n<PL, PL, BALLOT>(key, nreg, valid, k, T, need_eq);
   }
