@@ -444,6 +444,39 @@ sas_status sas_decode_long(const void* q, const void* kbar, int C, const void* K
                            size_t ws_bytes, void* stream);
 
 /*
+ * sas_pool_keys_paged - sas_pool_keys over a paged key cache (the layout of
+ * sas_decode_paged): kbar[b][h][m] is the mean of the 64 keys of page page_table[b][m],
+ * summed in the same order (so equal, bit for bit, to sas_pool_keys on the same keys laid
+ * out contiguously). A page id outside [0, num_pages) pools to zero.
+ *
+ *   Kpool       bf16 [num_pages][Hkv][64][d], device, 16-byte aligned.
+ *   page_table  int32 [B][max_pages], device.   max_pages <= 8192; C = max_pages.
+ *   kv_len, first_block, d: as for sas_pool_keys.
+ *   kbar        bf16 [B][Hkv][max_pages][d], device, 16-byte aligned, out; other blocks untouched.
+ */
+sas_status sas_pool_keys_paged(const void* Kpool, int num_pages, const int32_t* page_table, int max_pages,
+                               int B, int Hkv, int d, const int32_t* kv_len, int first_block, void* kbar,
+                               void* stream);
+
+/*
+ * sas_decode_long_paged - sas_decode_long over a paged KV cache: the same candidates
+ * launch on kbar (from sas_pool_keys_paged, C = max_pages), then the paged decode ranking
+ * them. Kept blocks and o are identical to sas_decode_select (kcap = topk) followed by
+ * sas_decode_paged.
+ *
+ *   Kpool, Vpool, num_pages, page_table, max_pages, kv_len: as for sas_decode_paged
+ *   (max_pages <= 8192).
+ *   kbar     bf16 [B][Hkv][max_pages][d], 16-byte aligned.
+ *   q, topk, B, Hq, Hkv, d, block, scale, o, idx, cnt: as for sas_decode_long.
+ *   ws       workspace of sas_decode_long_workspace_size(B, Hq, Hkv, d, max_pages, topk) bytes.
+ */
+sas_status sas_decode_long_paged(const void* q, const void* kbar, const void* Kpool, const void* Vpool,
+                                 int num_pages, const int32_t* page_table, int max_pages,
+                                 const int32_t* kv_len, int topk, int B, int Hq, int Hkv, int d, int block,
+                                 float scale, void* o, int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
  * Kernel timing, for measurement (not part of the pages' method; off by default).
  *
  * sas_profile_enable(on): while on, every kernel the library launches is bracketed by two

@@ -506,10 +506,12 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
   {
     const bool paged = a.page_table != nullptr, early = a.order != nullptr, sel = a.s != nullptr;
     ProfScope prof(early ? "decode_early_stop"
-                   : paged ? (sel ? "decode_paged_topk" : "decode_paged")
+                   : paged ? (sel ? (a.s_id != nullptr ? "decode_paged_candidates_topk" : "decode_paged_topk")
+                                  : "decode_paged")
                    : sel ? (a.s_id != nullptr ? "decode_candidates_topk" : "decode_topk") : "decode", st);
     if (a.d == 128) {
       if (early) hipLaunchKernelGGL((decode_split_kernel<128, false, true, 0>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged && sel && a.s_id != nullptr) hipLaunchKernelGGL((decode_split_kernel<128, true, false, 2>), dim3(grid), dim3(64), 0, st, a);
       else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<128, true, false, 1>), dim3(grid), dim3(64), 0, st, a);
       else if (paged) hipLaunchKernelGGL((decode_split_kernel<128, true, false, 0>), dim3(grid), dim3(64), 0, st, a);
       else if (sel && a.s_id != nullptr) hipLaunchKernelGGL((decode_split_kernel<128, false, false, 2>), dim3(grid), dim3(64), 0, st, a);
@@ -517,6 +519,7 @@ hipError_t launch_decode(DecodeArgs a, hipStream_t st) {
       else hipLaunchKernelGGL((decode_split_kernel<128, false, false, 0>), dim3(grid), dim3(64), 0, st, a);
     } else {
       if (early) hipLaunchKernelGGL((decode_split_kernel<64, false, true, 0>), dim3(grid), dim3(64), 0, st, a);
+      else if (paged && sel && a.s_id != nullptr) hipLaunchKernelGGL((decode_split_kernel<64, true, false, 2>), dim3(grid), dim3(64), 0, st, a);
       else if (paged && sel) hipLaunchKernelGGL((decode_split_kernel<64, true, false, 1>), dim3(grid), dim3(64), 0, st, a);
       else if (paged) hipLaunchKernelGGL((decode_split_kernel<64, true, false, 0>), dim3(grid), dim3(64), 0, st, a);
       else if (sel && a.s_id != nullptr) hipLaunchKernelGGL((decode_split_kernel<64, false, false, 2>), dim3(grid), dim3(64), 0, st, a);

@@ -41,13 +41,23 @@ __global__ __launch_bounds__(256) void pool_kernel(const PoolArgs a) {
   const int b = (int)(bh / a.Hkv);
   if ((m + 1) * kBlock > a.kv_len[b] || m >= a.C) return;   // uniform per workgroup
   const int t = threadIdx.x, c = t % LPR, rg = t / LPR;
-  const uint16_t* src = a.K + ((size_t)bh * a.Lmax + (size_t)m * kBlock) * D + 8 * c;
+  const uint16_t* src;
+  bool live = true;
+  if (a.page_table != nullptr) {   // (uniform per workgroup)
+    const int pg = a.page_table[(size_t)b * a.C + m];
+    live = pg >= 0 && pg < a.num_pages;
+    src = a.K + ((size_t)(live ? pg : 0) * a.Hkv + (size_t)(bh % a.Hkv)) * kBlock * D + 8 * c;
+  } else {
+    src = a.K + ((size_t)bh * a.Lmax + (size_t)m * kBlock) * D + 8 * c;
+  }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (live) {
 #pragma unroll
-  for (int r = rg; r < kBlock; r += RG) {
-    const u16x8 v = ld16(src + (size_t)r * D);
+    for (int r = rg; r < kBlock; r += RG) {
+      const u16x8 v = ld16(src + (size_t)r * D);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += bf2f(v[i]);
+      for (int i = 0; i < 8; ++i) acc[i] += bf2f(v[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[rg][8 * c + i] = acc[i];

@@ -512,41 +512,27 @@ size_t sas_decode_long_workspace_size(int B, int Hq, int Hkv, int d, int C, int 
   return decode_long_layout(B, Hq, Hkv, d, C, topk, nullptr, nullptr, nullptr);
 }
 
-sas_status sas_decode_long(const void* q, const void* kbar, int C, const void* Kc, const void* Vc,
-                           const int32_t* kv_len, int Lmax, int topk, int B, int Hq, int Hkv, int d,
-                           int block, float scale, void* o, int32_t* idx, int32_t* cnt, void* ws,
-                           size_t ws_bytes, void* stream) {
-  REQUIRE(kbar != nullptr, SAS_ERR_INVALID_ARG, "kbar must be non-NULL");
-  REQUIRE((idx == nullptr) == (cnt == nullptr), SAS_ERR_INVALID_ARG, "idx and cnt must both be given or both NULL");
-  REQUIRE(topk >= 1, SAS_ERR_INVALID_ARG, "topk=%d must be >= 1", topk);
-  REQUIRE(topk <= sas::kDecSelMax, SAS_ERR_UNSUPPORTED,
-          "topk=%d above %d: use sas_decode_select and sas_decode", topk, sas::kDecSelMax);
-  REQUIRE(C >= 1 && C <= 8192, SAS_ERR_UNSUPPORTED, "C=%d out of [1, 8192] pooled blocks", C);
-  REQUIRE(Lmax > 0 && (Lmax - 1) / 64 <= C, SAS_ERR_INVALID_ARG,
-          "C=%d pooled blocks cannot hold the %d history blocks of Lmax=%d", C, (Lmax - 1) / 64, Lmax);
-  REQUIRE(aligned16(kbar), SAS_ERR_INVALID_ARG, "kbar must be 16-byte aligned");
-  // cnt is an output here: check_decode's input checks are met with a stand-in pointer
-  const int32_t dummy = 0;
-  const sas_status chk = check_decode(q, Kc, Vc, kv_len, Lmax, &dummy, &dummy, B, Hq, Hkv, d, block, topk, scale, o);
-  if (chk != SAS_OK) return chk;
+// The two launches of a long-context decode step (candidates, then the decode ranking them)
+// for a decode already described by `a` (caches, paging, sizes, scale, o): checks of kbar,
+// topk, C and the workspace, then the launches.
+static sas_status decode_long_launch(sas::DecodeArgs a, const void* kbar, int C, int topk, int32_t* idx,
+                                     int32_t* cnt, void* ws, size_t ws_bytes, void* stream, const char* what) {
   int cch = 0, cld = 0;
   size_t cand_off = 0;
-  const size_t need = decode_long_layout(B, Hq, Hkv, d, C, topk, &cch, &cld, &cand_off);
+  const size_t need = decode_long_layout(a.B, a.Hq, a.Hkv, a.d, C, topk, &cch, &cld, &cand_off);
   REQUIRE(need > 0, SAS_ERR_UNSUPPORTED, "no candidate layout for C=%d, topk=%d", C, topk);
   REQUIRE(ws != nullptr && ws_bytes >= need, SAS_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, ws_bytes);
   REQUIRE(aligned16(ws), SAS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  const size_t slots = (size_t)B * Hkv * cld;
+  const size_t slots = (size_t)a.B * a.Hkv * cld;
   float* cs = (float*)((char*)ws + cand_off);
   int32_t* ci = (int32_t*)((char*)ws + cand_off + (slots * 4 + 255) / 256 * 256);
 
   sas::DecSelArgs sa{};
-  sa.q = (const uint16_t*)q; sa.kbar = (const uint16_t*)kbar; sa.B = B; sa.Hq = Hq; sa.Hkv = Hkv;
-  sa.G = Hq / Hkv; sa.d = d; sa.C = C; sa.kv_len = kv_len; sa.scale = scale; sa.topk = topk;
+  sa.q = a.q; sa.kbar = (const uint16_t*)kbar; sa.B = a.B; sa.Hq = a.Hq; sa.Hkv = a.Hkv;
+  sa.G = a.Hq / a.Hkv; sa.d = a.d; sa.C = C; sa.kv_len = a.kv_len; sa.scale = a.scale; sa.topk = topk;
   sa.cs = cs; sa.ci = ci; sa.cch = cch; sa.cld = cld;
-  const sas_status st = hip_result(sas::launch_decode_candidates(sa, (hipStream_t)stream),
-                                   "sas_decode_long candidates launch");
+  const sas_status st = hip_result(sas::launch_decode_candidates(sa, (hipStream_t)stream), what);
   if (st != SAS_OK) return st;
-  sas::DecodeArgs a = decode_args(q, Kc, Vc, kv_len, Lmax, nullptr, nullptr, nullptr, B, Hq, Hkv, d, topk, scale, o);
   a.part = (float*)ws;
   a.s = cs;
   a.s_ld = cld;
@@ -554,7 +540,72 @@ sas_status sas_decode_long(const void* q, const void* kbar, int C, const void* K
   a.topk = topk;
   a.idx_out = idx;
   a.cnt_out = cnt;
-  return hip_result(sas::launch_decode(a, (hipStream_t)stream), "sas_decode_long launch");
+  return hip_result(sas::launch_decode(a, (hipStream_t)stream), what);
+}
+
+static sas_status check_decode_long(const void* kbar, int C, int topk, int hist_max, const int32_t* idx,
+                                    const int32_t* cnt) {
+  REQUIRE(kbar != nullptr, SAS_ERR_INVALID_ARG, "kbar must be non-NULL");
+  REQUIRE((idx == nullptr) == (cnt == nullptr), SAS_ERR_INVALID_ARG, "idx and cnt must both be given or both NULL");
+  REQUIRE(topk >= 1, SAS_ERR_INVALID_ARG, "topk=%d must be >= 1", topk);
+  REQUIRE(topk <= sas::kDecSelMax, SAS_ERR_UNSUPPORTED,
+          "topk=%d above %d: use sas_decode_select and sas_decode", topk, sas::kDecSelMax);
+  REQUIRE(C >= 1 && C <= 8192, SAS_ERR_UNSUPPORTED, "C=%d out of [1, 8192] pooled blocks", C);
+  REQUIRE(hist_max <= C, SAS_ERR_INVALID_ARG, "C=%d pooled blocks cannot hold %d history blocks", C, hist_max);
+  REQUIRE(aligned16(kbar), SAS_ERR_INVALID_ARG, "kbar must be 16-byte aligned");
+  return SAS_OK;
+}
+
+sas_status sas_decode_long(const void* q, const void* kbar, int C, const void* Kc, const void* Vc,
+                           const int32_t* kv_len, int Lmax, int topk, int B, int Hq, int Hkv, int d,
+                           int block, float scale, void* o, int32_t* idx, int32_t* cnt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  REQUIRE(Lmax > 0, SAS_ERR_INVALID_ARG, "Lmax must be > 0");
+  const sas_status lc = check_decode_long(kbar, C, topk, (Lmax - 1) / 64, idx, cnt);
+  if (lc != SAS_OK) return lc;
+  // cnt is an output here: check_decode's input checks are met with a stand-in pointer
+  const int32_t dummy = 0;
+  const sas_status chk = check_decode(q, Kc, Vc, kv_len, Lmax, &dummy, &dummy, B, Hq, Hkv, d, block, topk, scale, o);
+  if (chk != SAS_OK) return chk;
+  const sas::DecodeArgs a = decode_args(q, Kc, Vc, kv_len, Lmax, nullptr, nullptr, nullptr, B, Hq, Hkv, d, topk,
+                                        scale, o);
+  return decode_long_launch(a, kbar, C, topk, idx, cnt, ws, ws_bytes, stream, "sas_decode_long launch");
+}
+
+sas_status sas_decode_long_paged(const void* q, const void* kbar, const void* Kpool, const void* Vpool,
+                                 int num_pages, const int32_t* page_table, int max_pages,
+                                 const int32_t* kv_len, int topk, int B, int Hq, int Hkv, int d, int block,
+                                 float scale, void* o, int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  const sas_status lc = check_decode_long(kbar, max_pages, topk, max_pages - 1, idx, cnt);
+  if (lc != SAS_OK) return lc;
+  const int32_t dummy = 0;
+  const sas_status chk = check_decode_paged(q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, &dummy,
+                                            &dummy, B, Hq, Hkv, d, block, topk, scale, o);
+  if (chk != SAS_OK) return chk;
+  const sas::DecodeArgs a = decode_paged_args(q, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, nullptr,
+                                              nullptr, nullptr, B, Hq, Hkv, d, topk, scale, o, nullptr);
+  return decode_long_launch(a, kbar, max_pages, topk, idx, cnt, ws, ws_bytes, stream,
+                            "sas_decode_long_paged launch");
+}
+
+sas_status sas_pool_keys_paged(const void* Kpool, int num_pages, const int32_t* page_table, int max_pages,
+                               int B, int Hkv, int d, const int32_t* kv_len, int first_block, void* kbar,
+                               void* stream) {
+  REQUIRE(Kpool && page_table && kv_len && kbar, SAS_ERR_INVALID_ARG,
+          "Kpool, page_table, kv_len and kbar must be non-NULL");
+  REQUIRE(B > 0 && Hkv > 0 && num_pages > 0 && max_pages > 0, SAS_ERR_INVALID_ARG,
+          "B, Hkv, num_pages, max_pages must be > 0");
+  REQUIRE(d == 64 || d == 128, SAS_ERR_UNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  REQUIRE(max_pages <= 8192, SAS_ERR_UNSUPPORTED, "max_pages=%d above 8192", max_pages);
+  REQUIRE(first_block >= 0 && first_block <= max_pages, SAS_ERR_INVALID_ARG, "first_block=%d out of [0, %d]",
+          first_block, max_pages);
+  REQUIRE(aligned16(Kpool) && aligned16(kbar), SAS_ERR_INVALID_ARG, "Kpool and kbar must be 16-byte aligned");
+  sas::PoolArgs a{};
+  a.K = (const uint16_t*)Kpool; a.B = B; a.Hkv = Hkv; a.Lmax = max_pages * 64; a.C = max_pages; a.d = d;
+  a.kv_len = kv_len; a.first_block = first_block; a.nblk = max_pages - first_block; a.kbar = (uint16_t*)kbar;
+  a.page_table = page_table; a.num_pages = num_pages;
+  return hip_result(sas::launch_pool(a, (hipStream_t)stream), "sas_pool_keys_paged launch");
 }
 
 }  // extern "C"

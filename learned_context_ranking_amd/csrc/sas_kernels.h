@@ -73,11 +73,15 @@ struct GatesBwdArgs {
 hipError_t launch_gates_bwd(const GatesBwdArgs& a, hipStream_t st);
 
 struct PoolArgs {
-  const uint16_t* K;    // [B][Hkv][Lmax][d] bf16
+  const uint16_t* K;    // [B][Hkv][Lmax][d] bf16, or with page_table a pool [num_pages][Hkv][64][d]
   int B, Hkv, Lmax, C, d;
   const int32_t* kv_len;
   int first_block, nblk;   // blocks first_block .. first_block + nblk - 1
   uint16_t* kbar;       // [B][Hkv][C][d] bf16
+  // paged cache (page_table != null): block m of sequence b is page page_table[b * C + m];
+  // a page id outside [0, num_pages) pools to zero
+  const int32_t* page_table;
+  int num_pages;
 };
 hipError_t launch_pool(const PoolArgs& a, hipStream_t st);
 

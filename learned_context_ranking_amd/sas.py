@@ -54,6 +54,9 @@ SIGNATURES = {
                                _P], _I),
     "sas_decode_long_workspace_size": ([_I, _I, _I, _I, _I, _I], _SZ),
     "sas_decode_long": ([_P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P], _I),
+    "sas_pool_keys_paged": ([_P, _I, _P, _I, _I, _I, _I, _P, _I, _P, _P], _I),
+    "sas_decode_long_paged": ([_P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
+                               _P], _I),
     "sas_profile_enable": ([_I], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
     "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
@@ -403,6 +406,49 @@ def sas_decode_long(q, kbar, Kc, Vc, kv_len, topk, scale, ws=None, out=None, wan
     _check(lib().sas_decode_long(_ptr(q), _ptr(kbar), C, _ptr(Kc), _ptr(Vc), _ptr(kv_len), Lmax, int(topk), B, Hq,
                                  Hkv, d, BLOCK, float(scale), _ptr(o), _ptr(idx), _ptr(cnt), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(dev)))
+    return (o, idx, cnt) if want_idx else o
+
+
+def sas_pool_keys_paged(Kpool, page_table, kv_len, first_block=0, out=None):
+    """Kpool bf16 [num_pages, Hkv, 64, d]; page_table int32 [B, max_pages]; kv_len int32
+    [B]. Returns kbar bf16 [B, Hkv, max_pages, d] (as sas_pool_keys)."""
+    _need(Kpool, torch.bfloat16, "Kpool")
+    _need(page_table, torch.int32, "page_table")
+    _need(kv_len, torch.int32, "kv_len")
+    num_pages, Hkv, _, d = Kpool.shape
+    B, max_pages = page_table.shape
+    if out is None:
+        out = torch.zeros((B, Hkv, max_pages, d), dtype=torch.bfloat16, device=Kpool.device)
+    _need(out, torch.bfloat16, "out")
+    _check(lib().sas_pool_keys_paged(_ptr(Kpool), num_pages, _ptr(page_table), max_pages, B, Hkv, d, _ptr(kv_len),
+                                     int(first_block), _ptr(out), _stream(Kpool.device)))
+    return out
+
+
+def sas_decode_long_paged(q, kbar, Kpool, Vpool, page_table, kv_len, topk, scale, ws=None, out=None,
+                          want_idx=False):
+    """sas_decode_long over a paged cache. q bf16 [B, Hq, d]; kbar bf16 [B, Hkv, max_pages, d]
+    (sas_pool_keys_paged); Kpool/Vpool bf16 [num_pages, Hkv, 64, d]; page_table int32
+    [B, max_pages]; kv_len int32 [B]. Returns o, and with want_idx also idx and cnt."""
+    for t, nm in ((q, "q"), (kbar, "kbar"), (Kpool, "Kpool"), (Vpool, "Vpool")):
+        _need(t, torch.bfloat16, nm)
+    _need(page_table, torch.int32, "page_table")
+    _need(kv_len, torch.int32, "kv_len")
+    B, Hq, d = q.shape
+    num_pages, Hkv = Kpool.shape[0], Kpool.shape[1]
+    max_pages = page_table.shape[1]
+    dev = q.device
+    if ws is None:
+        ws = decode_long_workspace(B, Hq, Hkv, d, max_pages, topk, dev)
+    o = torch.empty_like(q) if out is None else out
+    idx = cnt = None
+    if want_idx:
+        idx = torch.empty((B, Hkv, topk), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+    _check(lib().sas_decode_long_paged(_ptr(q), _ptr(kbar), _ptr(Kpool), _ptr(Vpool), num_pages, _ptr(page_table),
+                                       max_pages, _ptr(kv_len), int(topk), B, Hq, Hkv, d, BLOCK, float(scale),
+                                       _ptr(o), _ptr(idx), _ptr(cnt), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(dev)))
     return (o, idx, cnt) if want_idx else o
 
 

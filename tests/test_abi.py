@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 28, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -302,6 +302,27 @@ def test_decode_long_rejects():
         assert L.sas_decode_long(*bad) == code, (i, v)
     ok = list(args); ok[6] = 32832; ok[0] = NULL     # 512 history blocks fit C = 512 (then the
     assert L.sas_decode_long(*ok) == sas.SAS_ERR_INVALID_ARG   # missing q stops it, before any HIP call)
+
+
+def test_paged_long_decode_rejects():
+    L = sas.lib()
+    need = L.sas_decode_long_workspace_size(2, 8, 2, 128, 512, 16)
+    # q, kbar, Kpool, Vpool, num_pages, page_table, max_pages, kv_len, topk, B, Hq, Hkv, d, block,
+    # scale, o, idx, cnt, ws, ws_bytes, stream
+    args = [FAKE, FAKE, FAKE, FAKE, 100, FAKE, 512, FAKE, 16, 2, 8, 2, 128, 64, 0.1, FAKE, NULL, NULL, FAKE, need, NULL]
+    for i, v, code in ((1, NULL, sas.SAS_ERR_INVALID_ARG), (8, 65, sas.SAS_ERR_UNSUPPORTED),
+                       (6, 8193, sas.SAS_ERR_UNSUPPORTED), (5, NULL, sas.SAS_ERR_INVALID_ARG),
+                       (4, 0, sas.SAS_ERR_INVALID_ARG), (16, FAKE, sas.SAS_ERR_INVALID_ARG),
+                       (13, 32, sas.SAS_ERR_UNSUPPORTED), (19, need - 1, sas.SAS_ERR_WORKSPACE)):
+        bad = list(args); bad[i] = v
+        assert L.sas_decode_long_paged(*bad) == code, (i, v)
+    # Kpool, num_pages, page_table, max_pages, B, Hkv, d, kv_len, first_block, kbar, stream
+    pargs = [FAKE, 100, FAKE, 512, 2, 2, 128, FAKE, 0, FAKE, NULL]
+    for i, v, code in ((2, NULL, sas.SAS_ERR_INVALID_ARG), (1, 0, sas.SAS_ERR_INVALID_ARG),
+                       (6, 96, sas.SAS_ERR_UNSUPPORTED), (3, 8193, sas.SAS_ERR_UNSUPPORTED),
+                       (8, 513, sas.SAS_ERR_INVALID_ARG), (9, MIS, sas.SAS_ERR_INVALID_ARG)):
+        bad = list(pargs); bad[i] = v
+        assert L.sas_pool_keys_paged(*bad) == code, (i, v)
 
 
 def test_decode_early_stop_rejects():

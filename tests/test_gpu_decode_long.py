@@ -9,6 +9,9 @@ keys, Top-K, decode; [SAS-ja] "仕組み" Algorithm 2 with the block score of [P
 * Exact integer keys and queries repeating with a short period: every score is exact in
   fp32 and in the oracle's float64 and the K-th score of each row is tied, so the kept
   blocks equal the oracle's decode_select bit for bit and the output the oracle's decode.
+* Paged caches (sas_pool_keys_paged, sas_decode_long_paged) with pages in random order:
+  pooled keys, kept blocks and output equal to the contiguous path bit for bit; an
+  out-of-range page id pools to zero.
 """
 import math
 
@@ -98,3 +101,62 @@ def test_decode_long_exact_ties_against_oracle(Hq, Hkv, d, period, topk):
     assert np.array_equal(host(idx), idx_r) and np.array_equal(host(cnt), cnt_r)
     ref = oracle.decode(qf, kf, synth.bf16_bits_to_f32(vb), kv_len, idx_r, cnt_r, scale)
     assert_close("o", host(o), ref)
+
+
+def _paged(Kc, Vc, seed):
+    """The caches as a pool of 64-token pages in random order plus a page table."""
+    B, Hkv, Lmax, d = Kc.shape
+    C = Lmax // 64
+    perm = torch.randperm(B * C, generator=torch.Generator().manual_seed(seed)).to(Kc.device)
+    Kp = Kc.reshape(B, Hkv, C, 64, d).permute(0, 2, 1, 3, 4).reshape(B * C, Hkv, 64, d)[perm].contiguous()
+    Vp = Vc.reshape(B, Hkv, C, 64, d).permute(0, 2, 1, 3, 4).reshape(B * C, Hkv, 64, d)[perm].contiguous()
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(B * C, device=perm.device)
+    return Kp, Vp, inv.reshape(B, C).to(torch.int32).contiguous()
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,Lmax,topk", [
+    (3, 8, 2, 128, 65536, 16),
+    (2, 10, 2, 64, 32768, 64),
+], ids=["64K-K16", "32K-d64-G5-K64"])
+def test_decode_long_paged_matches_contiguous(B, Hq, Hkv, d, Lmax, topk):
+    """Pages in random order: pooled keys equal to sas_pool_keys on the contiguous cache, and
+    kept blocks and output equal to sas_decode_long on it (so to sas_decode_select +
+    sas_decode_paged), bit for bit."""
+    log(f"decode_long_paged B={B} Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} K={topk}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(Lmax + d)
+    Kc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    kv_len = dev(np.array([Lmax, Lmax // 2 + 7, 200][:B], np.int32))
+    Kp, Vp, pt = _paged(Kc, Vc, 21)
+    scale = 1.0 / math.sqrt(d)
+    kbar = sas.sas_pool_keys(Kc, kv_len)
+    kbar_p = sas.sas_pool_keys_paged(Kp, pt, kv_len)
+    o, idx, cnt = sas.sas_decode_long(q, kbar, Kc, Vc, kv_len, topk, scale, want_idx=True)
+    op, idxp, cntp = sas.sas_decode_long_paged(q, kbar_p, Kp, Vp, pt, kv_len, topk, scale, want_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(kbar_p, kbar), "paged pooled keys differ"
+    assert torch.equal(idxp, idx) and torch.equal(cntp, cnt)
+    assert torch.equal(op, o), "paged and contiguous long decode differ"
+
+
+def test_pool_keys_paged_bad_page():
+    """A page id outside the pool pools to zero; the other blocks are unchanged."""
+    B, Hkv, d, Lmax = 2, 2, 128, 4096
+    log(f"pool_keys_paged bad page B={B} Hkv={Hkv} d={d} Lmax={Lmax}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    Kc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    Kp, _, pt = _paged(Kc, Kc, 6)
+    kv_len = dev(np.array([Lmax, Lmax], np.int32))
+    pt[0, 3] = -1
+    pt[1, 10] = Kp.shape[0]
+    kbar = sas.sas_pool_keys(Kc, kv_len)
+    kbar_p = sas.sas_pool_keys_paged(Kp, pt, kv_len)
+    torch.cuda.synchronize()
+    assert torch.all(kbar_p[0, :, 3] == 0) and torch.all(kbar_p[1, :, 10] == 0)
+    kbar[0, :, 3] = 0
+    kbar[1, :, 10] = 0
+    assert torch.equal(kbar_p, kbar)
