@@ -774,3 +774,28 @@ def test_pn_early_stop_closed_form_masses():
         assert used[0, 0] == expected(tau), (tau, used, expected(tau))
     # 0.29 separates "compared with the mass before the block" (3) from "after it" (2)
     assert [expected(t) for t in (0.05, 0.1, 0.29, 0.3, 5.0)] == [4, 3, 3, 2, 1]
+
+
+@pytest.mark.parametrize("chunk", [3, 16, 128])
+def test_po_topk_of_chunk_candidates_is_row_topk(chunk):
+    """P-o. The two-stage long-context selection rests on one property of Top-K with ties
+    to the lowest index: each block of a row's Top-K is among the Top-K of its own chunk
+    (at most K - 1 blocks of the row, so of its chunk, rank above it), so ranking only the
+    chunks' Top-K blocks, kept in block order so that a tie still goes to the lower block,
+    gives the row's Top-K. Checked with the oracle's row_topk on rows with heavy ties,
+    NaN, -inf, -0 and rows shorter than K."""
+    rng = np.random.default_rng(chunk)
+    for trial in range(300):
+        n = int(rng.integers(1, 600))
+        k = int(rng.integers(1, 70))
+        s = np.round(rng.normal(size=n) * 2) / 2          # few distinct values: many ties
+        for v, frac in ((np.nan, 0.03), (-np.inf, 0.03), (-0.0, 0.05), (0.0, 0.05)):
+            s[rng.random(n) < frac] = v
+        full = oracle.row_topk(s, k)
+        cand = []
+        for c0 in range(0, n, chunk):
+            cand.extend(c0 + oracle.row_topk(s[c0:c0 + chunk], k))
+        cand = np.asarray(cand)
+        assert np.all(np.diff(cand) > 0)                   # block order
+        two_stage = cand[oracle.row_topk(s[cand], k)]
+        assert np.array_equal(two_stage, full), (trial, n, k)
