@@ -113,3 +113,30 @@ def test_decode_topk_graph_replay(B, Hkv, Lmax):
     with torch.cuda.graph(g):
         out = step()
     _replays(g, out, ref)
+
+
+def test_decode_long_graph_replay():
+    """The two-launch long-context decode (candidates in the workspace, then the decode
+    ranking them), captured and replayed."""
+    B, Hq, Hkv, d, Lmax, topk = 2, 8, 2, 128, 65536, 16
+    log(f"graph: decode_long B={B} Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} K={topk}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    Kc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    kv_len = dev(np.array([Lmax, 20000], np.int32))
+    kbar = sas.sas_pool_keys(Kc, kv_len)
+    ws = sas.decode_long_workspace(B, Hq, Hkv, d, Lmax // 64, topk, q.device)
+    scale = 1.0 / math.sqrt(d)
+
+    def step():
+        o, idx, cnt = sas.sas_decode_long(q, kbar, Kc, Vc, kv_len, topk, scale, ws=ws, want_idx=True)
+        return dict(idx=idx, cnt=cnt, o=o)
+
+    ref = {k: v.clone() for k, v in step().items()}
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        out = step()
+    _replays(gr, out, ref)
