@@ -345,7 +345,8 @@ __global__ __launch_bounds__(256) void cand_kernel(const DecSelArgs a) {
   const long long row = blockIdx.x / nch;
   const int chunk = (int)(blockIdx.x % nch);
   const int b = (int)(row / a.Hkv), h = (int)(row % a.Hkv);
-  const int hist = min(max((a.kv_len[b] - 1) / kBlock, 0), a.C);
+  // (kv_len is clamped to the cache as the decode clamps it, so both see the same history)
+  const int hist = min(max((a.kv_len[b] - 1) / kBlock, 0), min(a.C, a.hist_cap));
   const int base = chunk * CH;
   const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   if (base < hist) {

@@ -531,6 +531,7 @@ static sas_status decode_long_launch(sas::DecodeArgs a, const void* kbar, int C,
   sa.q = a.q; sa.kbar = (const uint16_t*)kbar; sa.B = a.B; sa.Hq = a.Hq; sa.Hkv = a.Hkv;
   sa.G = a.Hq / a.Hkv; sa.d = a.d; sa.C = C; sa.kv_len = a.kv_len; sa.scale = a.scale; sa.topk = topk;
   sa.cs = cs; sa.ci = ci; sa.cch = cch; sa.cld = cld;
+  sa.hist_cap = (int)((a.Lmax - 1) / 64);   // kv_len past the cache is clamped, as in the decode
   const sas_status st = hip_result(sas::launch_decode_candidates(sa, (hipStream_t)stream), what);
   if (st != SAS_OK) return st;
   a.part = (float*)ws;

@@ -103,6 +103,7 @@ struct DecSelArgs {
   float* cs;
   int32_t* ci;
   int cch, cld;
+  int hist_cap;         // (candidates) history blocks of a row at most: the decode's, (Lmax - 1) / 64
 };
 hipError_t launch_decode_select(const DecSelArgs& a, hipStream_t st);
 // Candidate chunk size in blocks for rows of C blocks and K = topk: the smallest

@@ -160,3 +160,24 @@ def test_pool_keys_paged_bad_page():
     kbar[0, :, 3] = 0
     kbar[1, :, 10] = 0
     assert torch.equal(kbar_p, kbar)
+
+
+def test_decode_long_kv_len_past_cache_is_clamped():
+    """kv_len above Lmax reads as Lmax (the documented clamp) in both launches: kept blocks,
+    counts and output equal those of kv_len = Lmax, and no kept block is the current one."""
+    B, Hq, Hkv, d, Lmax, topk = 2, 8, 2, 128, 4096, 16
+    log(f"decode_long kv_len past the cache B={B} Lmax={Lmax} K={topk}")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(33)
+    Kc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    Vc = torch.randn((B, Hkv, Lmax, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    full = dev(np.array([Lmax, Lmax], np.int32))
+    kbar = sas.sas_pool_keys(Kc, full)              # every block pooled, the last one too
+    scale = 1.0 / math.sqrt(d)
+    o, idx, cnt = sas.sas_decode_long(q, kbar, Kc, Vc, full, topk, scale, want_idx=True)
+    o2, idx2, cnt2 = sas.sas_decode_long(q, kbar, Kc, Vc, dev(np.array([Lmax + 1000, 1 << 30], np.int32)), topk,
+                                         scale, want_idx=True)
+    torch.cuda.synchronize()
+    assert int(idx.max()) < (Lmax - 1) // 64
+    assert torch.equal(idx2, idx) and torch.equal(cnt2, cnt) and torch.equal(o2, o)
