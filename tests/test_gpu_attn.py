@@ -31,6 +31,7 @@ CASES = [
     (1, 4, 1, 512, 128, 0, "sparse", True, "normal"),       # budget 0: the causal current block only
     (1, 8, 2, 4096, 64, 8, "sparse", True, "zipf"),         # popular key blocks: split key-major lists
     (1, 5, 1, 4096, 128, 8, "sparse", True, "zipf"),        # the same with G = 5
+    (1, 16, 1, 512, 64, 3, "sparse", True, "normal"),       # G = 16 (eight workgroups of 2 heads)
 ]
 
 

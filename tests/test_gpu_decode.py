@@ -49,7 +49,8 @@ def test_decode_gated_variant():
     _decode_case(3, 8, 2, 128, 2048, [2048, 777, 130], 6, gated=True)
 
 
-@pytest.mark.parametrize("Hq,Hkv,d", [(5, 1, 64), (8, 8, 64), (16, 2, 128), (10, 2, 128)])
+@pytest.mark.parametrize("Hq,Hkv,d", [(5, 1, 64), (8, 8, 64), (16, 2, 128), (10, 2, 128), (32, 1, 128),
+                                      (64, 2, 64)])
 def test_decode_groups(Hq, Hkv, d):
     _decode_case(3, Hq, Hkv, d, 1536, [1536, 900, 64], 5, seed=Hq)
 

@@ -45,7 +45,8 @@ def _compare_paths(q, Kc, Vc, kbar, kv_len, topk, scale):
     (1, 32, 8, 128, 131072, 64),
     (3, 10, 2, 64, 65536, 32),
     (8, 32, 8, 128, 32768, 16),
-], ids=["8K", "128K-K16", "128K-K64", "64K-d64-G5", "32K-B8"])
+    (2, 64, 2, 64, 16384, 16),
+], ids=["8K", "128K-K16", "128K-K64", "64K-d64-G5", "32K-B8", "16K-d64-G32"])
 def test_decode_long_matches_select_then_decode(B, Hq, Hkv, d, Lmax, topk):
     log(f"decode_long B={B} Hq={Hq} Hkv={Hkv} d={d} Lmax={Lmax} K={topk}")
     g = torch.Generator(device="cuda")

@@ -81,6 +81,11 @@ def test_decode_topk_group_of_five():
     _case(3, 10, 2, 128, 2048, [2048, 1500, 700], 12, seed=3)
 
 
+def test_decode_topk_group_of_32():
+    """The largest group: 32 query heads per KV head fill the 32 query columns of the tile."""
+    _case(3, 32, 1, 128, 4096, [4096, 2500, 300], 16, seed=7)
+
+
 def test_decode_topk_ties_nan():
     """Scores on a half-integer grid (ties at the cut broken toward the lower index), NaN and
     -inf ranked lowest, -0 equal to +0."""
