@@ -786,6 +786,10 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, tr["host"], tr["cnt"], args.cpu_seconds)
+    props = torch.cuda.get_device_properties(0)
+    out["versions"] = {"library": sas.version(), "torch": torch.__version__, "hip": torch.version.hip,
+                       "device": props.name, "arch": getattr(props, "gcnArchName", None),
+                       "compute_units": props.multi_processor_count}
     print(json.dumps(out), flush=True)
 
 
