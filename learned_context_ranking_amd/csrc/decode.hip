@@ -163,9 +163,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
           const size_t off = ((size_t)max(pg, 0) * a.Hkv + h) * (size_t)(kBlock * D) + (size_t)(32 * u) * D;
           const int pbytes = pg < 0 ? 0 : min(max(L - cur * kBlock - 32 * u, 0), 32) * D * 2;
 #pragma unroll
-          for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Kc + off, pbytes, kb + 512 * i, voff[i], 0u);
+          for (int i = 0; i < NWIN; ++i) buffer_load_lds16_u(a.Kc + off, pbytes, kb + 512 * i, voff[i]);
 #pragma unroll
-          for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Vc + off, pbytes, vb + 512 * i, voff[i], 0u);
+          for (int i = 0; i < NWIN; ++i) buffer_load_lds16_u(a.Vc + off, pbytes, vb + 512 * i, voff[i]);
         } else {
           const uint32_t so = ((uint32_t)cur * kBlock + 32u * u) * (uint32_t)(D * 2);
 #pragma unroll
@@ -266,9 +266,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(const DecodeArgs a) {
       const size_t off = ((size_t)max(m, 0) * a.Hkv + h) * (size_t)(kBlock * D) + (size_t)(32 * (uu & 1)) * D;
       const int bytes = m < 0 ? 0 : half_keys(uu) * D * 2;
 #pragma unroll
-      for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Kc + off, bytes, kb + 512 * i, voff[i], 0u);
+      for (int i = 0; i < NWIN; ++i) buffer_load_lds16_u(a.Kc + off, bytes, kb + 512 * i, voff[i]);
 #pragma unroll
-      for (int i = 0; i < NWIN; ++i) buffer_load_lds16(a.Vc + off, bytes, vb + 512 * i, voff[i], 0u);
+      for (int i = 0; i < NWIN; ++i) buffer_load_lds16_u(a.Vc + off, bytes, vb + 512 * i, voff[i]);
     } else {
       const uint32_t so = ((uint32_t)m * kBlock + 32u * (uu & 1)) * (uint32_t)(D * 2);
 #pragma unroll
