@@ -21,6 +21,20 @@ namespace sas {
 
 constexpr float kDecRescaleThreshold = 8.0f;   // log2 of the largest unnormalised exponential
 
+// The same copy from a base address and range that are equal in every lane but that the
+// compiler cannot prove uniform (a page's address, computed from a page id read out of a
+// lane-held list): both are moved to scalar registers first. Otherwise the compiler wraps
+// each copy in a loop over the distinct resources of the wave's lanes (four
+// v_readfirstlane, two compares and an exec-mask loop per copy), which stalls the issue of
+// the copies behind it.
+__device__ __forceinline__ void buffer_load_lds16_u(const void* base, int bytes, void* lds, uint32_t voffset) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  buffer_load_lds16(reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo), __builtin_amdgcn_readfirstlane(bytes),
+                    lds, voffset, 0u);
+}
+
 // 32-key half blocks through a ring of 4 LDS buffer sets: half block u+3 is copied in
 // while u is computed, so about three half blocks (48 KB) are in flight per wave.
 //
