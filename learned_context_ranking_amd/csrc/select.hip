@@ -33,34 +33,26 @@ __device__ __forceinline__ float log_gate(int gate, float x, float norm) {
 // carries only its own code path: the per-register walks below are fully unrolled)
 constexpr int kStageCap = 256;   // rows with kcap up to this stage their output in LDS
 
-template <int PL, int GATE>
-__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
-  // kept (index, log g) of each wave's row, written out with coalesced stores at the end
-  __shared__ int s_idx[4][kStageCap];
-  __shared__ float s_lg[4][kStageCap];
+// One wave's row with its valid scores in the first NR registers of each lane (NR is the
+// smallest quarter step of PL that holds them): loads, LSE, search and walk run over NR
+// registers only, so the short rows of a prefill (row j has j valid scores) do not pay
+// for the longest. PL is the register count of the widest row (the gate output is
+// written over all of it).
+template <int NR, int PL, int GATE>
+__device__ __forceinline__ void select_row(const SelectArgs& a, long long row, int valid, int* s_idx,
+                                           float* s_lg) {
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.R) return;  // uniform per wave
-  int valid;
-  if (a.mode == 0) {
-    valid = (int)(row % a.rows);
-  } else {
-    const long long b = row / ((long long)a.H * a.rows);
-    valid = a.row_valid[b];
-  }
-  valid = min(max(valid, 0), a.cols);
   const float* srow = a.s + row * a.ld;
 
   // Loads without branches (the index clamped into the valid columns, which are the only
-  // ones read), so all PL loads are in flight together; masks are applied afterwards.
-  float x[PL];
+  // ones read), so all NR loads are in flight together; masks are applied afterwards.
+  float x[NR];
   if (valid > 0) {
 #pragma unroll
-    for (int i = 0; i < PL; ++i) x[i] = srow[min(lane + 64 * i, valid - 1)];
+    for (int i = 0; i < NR; ++i) x[i] = srow[min(lane + 64 * i, valid - 1)];
   }
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
+  for (int i = 0; i < NR; ++i) {
     float v = valid > 0 ? x[i] : -INFINITY;
     v = (lane + 64 * i < valid && v == v) ? v : -INFINITY;   // NaN ranks as -inf
     x[i] = v == 0.0f ? 0.0f : v;                             // -0 -> +0
@@ -69,7 +61,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   // LSE over the valid scores.
   float mx = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) mx = fmaxf(mx, x[i]);
+  for (int i = 0; i < NR; ++i) mx = fmaxf(mx, x[i]);
   mx = dpp_max(mx);
   float lse = -INFINITY;
   if (mx != -INFINITY) {
@@ -79,7 +71,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     const float mxl = mx * kLog2e;
     float sum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mxl));
+    for (int i = 0; i < NR; ++i) sum += __builtin_amdgcn_exp2f(fmaf(x[i], kLog2e, -mxl));
     sum = dpp_sum(sum);
     lse = mx + logf(sum);
   }
@@ -89,7 +81,7 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
       const int m = lane + 64 * i;
-      if (m < a.cols) grow[m] = (m < valid && lse != -INFINITY) ? expf(x[i] - lse) : 0.0f;
+      if (m < a.cols) grow[m] = (i < NR && m < valid && lse != -INFINITY) ? expf(x[i < NR ? i : 0] - lse) : 0.0f;
     }
   }
   if (!a.do_select) return;
@@ -99,9 +91,9 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   float* lg_row = a.logg != nullptr ? a.logg + row * a.kcap : nullptr;
   if (k > 0) {
     const int nreg = (valid + 63) >> 6;   // registers holding valid scores (uniform)
-    uint32_t key[PL];
+    uint32_t key[NR];
 #pragma unroll
-    for (int i = 0; i < PL; ++i) key[i] = (lane + 64 * i < valid) ? order_key(x[i]) : 0u;
+    for (int i = 0; i < NR; ++i) key[i] = (lane + 64 * i < valid) ? order_key(x[i]) : 0u;
     uint32_t T;
     int need_eq;
     topk_cut(key, nreg, valid, k, T, need_eq);
@@ -126,8 +118,8 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     if (a.kcap <= kStageCap) {
       // a row's kept entries are few per register (one or two lanes): gather them in LDS
       walk([&](int i, int pos) {
-        s_idx[wv][pos] = lane + 64 * i;
-        s_lg[wv][pos] = log_gate(GATE, key_score(key[i]), norm);
+        s_idx[pos] = lane + 64 * i;
+        s_lg[pos] = log_gate(GATE, key_score(key[i]), norm);
       });
     } else {
       walk([&](int i, int pos) {
@@ -146,8 +138,8 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     for (int p = lane; p < a.kcap; p += 64) {
       const bool kept = p < k;
-      idx_row[p] = kept ? s_idx[wv][p] : -1;
-      if (lg_row != nullptr) lg_row[p] = kept ? s_lg[wv][p] : 0.0f;
+      idx_row[p] = kept ? s_idx[p] : -1;
+      if (lg_row != nullptr) lg_row[p] = kept ? s_lg[p] : 0.0f;
     }
   } else {
     for (int p = k + lane; p < a.kcap; p += 64) {
@@ -156,6 +148,33 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
     }
   }
   if (lane == 0) a.cnt[row] = k;
+}
+
+template <int PL, int GATE>
+__global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
+  // kept (index, log g) of each wave's row, written out with coalesced stores at the end
+  __shared__ int s_idx[4][kStageCap];
+  __shared__ float s_lg[4][kStageCap];
+  const int wv = threadIdx.x >> 6;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.R) return;  // uniform per wave
+  int valid;
+  if (a.mode == 0) {
+    valid = (int)(row % a.rows);
+  } else {
+    const long long b = row / ((long long)a.H * a.rows);
+    valid = a.row_valid[b];
+  }
+  valid = __builtin_amdgcn_readfirstlane(min(max(valid, 0), a.cols));
+  const int nreg = (valid + 63) >> 6;
+  if constexpr (PL >= 4) {
+    if (nreg <= PL / 4) select_row<PL / 4, PL, GATE>(a, row, valid, s_idx[wv], s_lg[wv]);
+    else if (nreg <= PL / 2) select_row<PL / 2, PL, GATE>(a, row, valid, s_idx[wv], s_lg[wv]);
+    else if (nreg <= 3 * PL / 4) select_row<3 * PL / 4, PL, GATE>(a, row, valid, s_idx[wv], s_lg[wv]);
+    else select_row<PL, PL, GATE>(a, row, valid, s_idx[wv], s_lg[wv]);
+  } else {
+    select_row<PL, PL, GATE>(a, row, valid, s_idx[wv], s_lg[wv]);
+  }
 }
 
 template <int PL>
