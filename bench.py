@@ -530,7 +530,10 @@ def run_long_decode(torch, reps=20):
                         "select_share": round(ms_sel / (ms_sel + ms_att), 3),
                         "select_gbs": round(sel_bytes / ms_sel / 1e6, 1),
                         "step_us": round(ms_two * 1e3, 2),
-                        "decode_long_us": round(ms_long * 1e3, 2)})
+                        "decode_long_us": round(ms_long * 1e3, 2),
+                        # the selection's share of the two-launch step: what the step spends
+                        # beyond the attention alone (the same decode, event to event)
+                        "decode_long_select_share": round(max(ms_long - ms_att, 0.0) / ms_long, 3)})
             log(f"[bench]   B={B} L={L}: select {ms_sel * 1e3:.1f} us, attention {ms_att * 1e3:.1f} us, "
                 f"step {ms_two * 1e3:.1f} us; sas_decode_long {ms_long * 1e3:.1f} us")
     del Kc, Vc, kbar
