@@ -156,8 +156,10 @@ __global__ __launch_bounds__(256) void select_kernel(const SelectArgs a) {
   __shared__ int s_idx[4][kStageCap];
   __shared__ float s_lg[4][kStageCap];
   const int wv = threadIdx.x >> 6;
-  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.R) return;  // uniform per wave
+  // Rows in reverse order: a prefill's rows grow with j within each (batch, head), so the
+  // longest rows start early and the launch ends on short ones.
+  const long long row = a.R - 1 - ((long long)blockIdx.x * 4 + (threadIdx.x >> 6));
+  if (row < 0) return;  // uniform per wave
   int valid;
   if (a.mode == 0) {
     valid = (int)(row % a.rows);
