@@ -497,6 +497,15 @@ sas_status sas_profile_enable(int on);
 int sas_profile_collect(int max, char* names, int name_len, int* launches, double* total_ms);
 
 /*
+ * sas_profile_only(name): while timing is on, bracket only the kernels of this name (one of
+ * the names listed above; NULL or "" brackets every kernel again). Each bracketed launch
+ * adds two event records to its stream; timing one kernel of a multi-kernel step keeps the
+ * others free of them. The name is copied (at most 31 characters). Returns SAS_OK, or
+ * SAS_ERR_INVALID_ARG for a longer name.
+ */
+sas_status sas_profile_only(const char* name);
+
+/*
  * sas_profile_collect_launches: like sas_profile_collect, but one entry per recorded launch
  * in launch order (names as above, ms[i] its event time), for medians and percentiles. At
  * most `max` entries are written; the record is cleared either way. Returns the count, or

@@ -25,6 +25,7 @@ struct Rec {
 
 std::atomic<bool> g_on{false};
 std::mutex g_mu;
+char g_only[32] = "";             // kernel name to bracket alone ("" = every kernel)
 std::vector<Rec> g_recs;          // launches recorded since the last collect
 std::vector<hipEvent_t> g_pool;   // events ready for reuse
 
@@ -44,6 +45,7 @@ hipEvent_t take_event() {
 ProfScope::ProfScope(const char* name, hipStream_t st) : name_(name), st_(st), a_(nullptr) {
   if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);
+  if (g_only[0] != '\0' && strcmp(g_only, name) != 0) return;
   a_ = take_event();
   if (a_ != nullptr && hipEventRecord((hipEvent_t)a_, st) != hipSuccess) {
     g_pool.push_back((hipEvent_t)a_);
@@ -104,6 +106,15 @@ sas_status sas_debug_workgroup_order(unsigned long long seed) {
 
 sas_status sas_profile_enable(int on) {
   sas::g_on.store(on != 0, std::memory_order_relaxed);
+  return SAS_OK;
+}
+
+sas_status sas_profile_only(const char* name) {
+  using namespace sas;
+  if (name != nullptr && strlen(name) >= sizeof(g_only)) return SAS_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (name == nullptr) g_only[0] = '\0';
+  else strcpy(g_only, name);
   return SAS_OK;
 }
 

@@ -58,6 +58,7 @@ SIGNATURES = {
     "sas_decode_long_paged": ([_P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P, _P, _SZ,
                                _P], _I),
     "sas_profile_enable": ([_I], _I),
+    "sas_profile_only": ([ctypes.c_char_p], _I),
     "sas_profile_collect": ([_I, ctypes.c_char_p, _I, _P, _P], _I),
     "sas_profile_collect_launches": ([_I, ctypes.c_char_p, _I, _P], _I),
     "sas_debug_workgroup_order": ([ctypes.c_ulonglong], _I),
@@ -493,6 +494,11 @@ def sas_decode_select(q, kbar, kv_len, scale, topk, kcap=None, want_lse=False, w
 def profile_enable(on: bool = True):
     """Turn the library's per-kernel event timing on or off (measurement only)."""
     _check(lib().sas_profile_enable(1 if on else 0))
+
+
+def profile_only(name: str | None = None):
+    """While timing is on, bracket only the kernels called `name` (None: every kernel)."""
+    _check(lib().sas_profile_only(None if name is None else name.encode()))
 
 
 def profile_collect(max_kernels: int = 32, name_len: int = 32):

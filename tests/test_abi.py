@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     L = ctypes.CDLL(sas.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -343,3 +343,12 @@ def test_profile_toggle_without_gpu():
     assert L.sas_profile_enable(1) == sas.SAS_OK
     assert sas.profile_collect() == {}
     assert L.sas_profile_enable(0) == sas.SAS_OK
+
+
+def test_profile_only_names():
+    """The one-kernel filter takes a name of up to 31 characters; NULL clears it."""
+    L = sas.lib()
+    assert L.sas_profile_only(b"dkv") == sas.SAS_OK
+    assert L.sas_profile_only(b"x" * 31) == sas.SAS_OK
+    assert L.sas_profile_only(b"x" * 32) == sas.SAS_ERR_INVALID_ARG
+    assert L.sas_profile_only(None) == sas.SAS_OK

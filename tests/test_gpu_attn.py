@@ -163,6 +163,21 @@ def test_kernel_timing_records_each_launch():
     assert sas.profile_collect() == {}
 
 
+def test_kernel_timing_one_kernel():
+    """With the one-kernel filter only that kernel's launches are recorded."""
+    case = (1, 8, 2, 512, 128, 4, "sparse", True, "normal")
+    sas.profile_enable(True)
+    sas.profile_only("dkv")
+    try:
+        sas.profile_collect()
+        _run(case)
+        prof = sas.profile_collect()
+    finally:
+        sas.profile_only(None)
+        sas.profile_enable(False)
+    assert list(prof) == ["dkv"] and prof["dkv"][0] == 1 and prof["dkv"][1] > 0.0, prof
+
+
 def _full_size(B, Hq, Hkv, n, d, topk, scores, nsample_j=6, nsample_m=3, backward=True, most_used=False):
     log(f"full size B={B} Hq={Hq} Hkv={Hkv} n={n} d={d} K={topk} scores={scores}")
     P = Prefill(B, Hq, Hkv, n, d, seed=0, scores=scores, backward=backward)
