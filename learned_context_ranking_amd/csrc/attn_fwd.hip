@@ -331,6 +331,250 @@ static hipError_t launch_fwd_t(const AttnArgs& a, int nsplit, int hpw, hipStream
   return launch_fwd_o<D, NTILE, NW, false>(a, nsplit, hpw, st);
 }
 
+// The same forward (32 rows per wave, two query heads per workgroup) at three waves per
+// SIMD instead of two. Measured with rocprofv3's SQ counters, the two-wave kernel's waves
+// spend ~43 % of their cycles waiting on instruction dependencies (LDS operands, matrix
+// results) and the matrix cores overlap vector work in only ~39 % of their busy cycles; a
+// third wave per SIMD covers more of those waits. That takes at most 168 registers per lane
+// and 53 KB of LDS per workgroup: K stays double-buffered, V gets one buffer (48 KB in
+// all), and the V^T operands are read just before their products (no register copy held
+// across the softmax; 162 registers). Per step t:
+//   copy V(t) into the V buffer and K(t+1) into the other K buffer;
+//   S(t) from K(t); softmax(t);
+//   wait for V(t) (K(t+1) may still be in flight), barrier; P V(t);
+//   wait for K(t+1), barrier (every wave is done with V(t) and K(t) before they are refilled).
+// The arithmetic and its order are those of fwd_kernel, so the outputs are identical.
+template <int D, bool OUT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void fwd3_kernel(const AttnArgs a, int nsplit, int hpw) {
+  constexpr int NW = 4;
+  constexpr int WPH = 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sk0[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sk1[Tile<D>::ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[Tile<D>::ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ql = lane & 31;
+  const int NB = a.n / kBlock, G = a.Hq / a.Hkv;
+  const int BH = a.B * a.Hkv;
+  const int per_j = BH * nsplit;
+  const unsigned bid = wg_index(a.wg);
+  const int j = NB - 1 - (int)(bid / per_j);
+  const int r = bid % per_j;
+  const int split = r / BH;
+  const int h = (r % BH) % a.Hkv, b = (r % BH) / a.Hkv;
+  const int head0 = split * hpw;
+  const int nheads = min(hpw, G - head0);
+  const int whead = wave / WPH;
+  const int wrow0 = (wave % WPH) * 32;
+  const bool active = whead < nheads;
+  const int hq = h * G + head0 + (active ? whead : 0);
+  const size_t kv_off = ((size_t)(b * a.Hkv + h) * a.n) * D;
+  const uint16_t* Kh = a.K + kv_off;
+  const uint16_t* Vh = a.V + kv_off;
+  const size_t q_off = ((size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock + wrow0) * D;
+  const size_t sel_row = (size_t)(b * a.Hkv + h) * NB + j;
+  const int cnt_j = min(max(a.cnt[sel_row], 0), min(a.kcap, j));
+  const int32_t* idx_row = a.idx + sel_row * a.kcap;
+  const float* lg_row = a.logg != nullptr ? a.logg + sel_row * a.kcap : nullptr;
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = as_bf16x8(ld16(a.Q + q_off + ql * D + 16 * ks + 8 * hl));
+  auto load_sel = [&](int i, int& v, float& g) {
+    v = i < cnt_j ? idx_row[i] : 0;
+    g = (i < cnt_j && lg_row != nullptr) ? lg_row[i] * kLog2e : 0.0f;
+  };
+  LaneList sel_c, sel_k, sel_v;
+  int tc = 0, tk = 0, tv = 0;
+  constexpr int NWIN = Tile<D>::CPR / NW;
+  uint32_t voff[NWIN];
+#pragma unroll
+  for (int i = 0; i < NWIN; ++i) {
+    const int sidx = 64 * (wave + NW * i) + lane;
+    const int rr = sidx / Tile<D>::CPR, c = sidx % Tile<D>::CPR;
+    voff[i] = (uint32_t)(rr * D + ((c ^ Tile<D>::swz(rr)) << 3)) * 2u;
+  }
+  const int kvbytes = a.n * D * 2;
+  auto block_of = [&](LaneList& L, int t) {
+    int mb = j;
+    if (t > 0) {
+      L.ensure(t - 1, lane, load_sel);
+      mb = L.at(t - 1);
+      if (mb < 0 || mb >= j) mb = 0;
+    }
+    return (uint32_t)mb * (uint32_t)(kBlock * D * 2);
+  };
+  auto fetch_k = [&](uint16_t* kb) {
+    const uint32_t so = block_of(sel_k, tk);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Kh, kvbytes, kb + 512 * (wave + NW * i), voff[i], so);
+    if (tk < cnt_j) ++tk;
+  };
+  auto fetch_v = [&]() {
+    const uint32_t so = block_of(sel_v, tv);
+#pragma unroll
+    for (int i = 0; i < NWIN; ++i) buffer_load_lds16(Vh, kvbytes, sv + 512 * (wave + NW * i), voff[i], so);
+    if (tv < cnt_j) ++tv;
+  };
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.0f;
+  float mref = -INFINITY, lrow = 0.0f;
+  const float c2 = a.scale * kLog2e;
+  const int g16 = lane >> 4, lp = lane & 15;
+  const int tr_row = 4 * (g16 >> 1) + (lp >> 2), tr_d = 16 * (g16 & 1) + 4 * (lp & 3);
+  const int rx0 = ql * D + ((hl ^ Tile<D>::swz(ql)) << 3);
+  const int tx0 = tr_row * D + ((((tr_d >> 3) ^ Tile<D>::swz(tr_row))) << 3) + (tr_d & 7);
+
+  auto step = [&](auto diag_c, const uint16_t* kc, uint16_t* kn) {
+    constexpr bool DIAG = decltype(diag_c)::value;
+    const int t = tc;
+    float lg2 = 0.0f;
+    bool ok = true;
+    if (!DIAG) {
+      sel_c.ensure(t - 1, lane, load_sel);
+      const int mb = sel_c.at(t - 1);
+      lg2 = sel_c.gat(t - 1);
+      if (mb < 0 || mb >= j) { lg2 = -INFINITY; ok = false; }
+    }
+    const float gmul = OUT ? fast_exp2(lg2) : 1.0f;
+    if (OUT) lg2 = ok ? 0.0f : -INFINITY;
+    ++tc;
+    fetch_v();        // V of this block (single buffer: every wave is done with the last one)
+    fetch_k(kn);      // K of the next block (its buffer held block t - 1)
+    int rx = rx0, tx = tx0;
+    asm volatile("" : "+v"(rx), "+v"(tx));
+    f32x16 st[2];
+    if (active) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[mt][i] = 0.0f;
+#pragma unroll
+      for (int k0 = 0; k0 < D / 16; k0 += 4) {
+        bf16x8 kr[4][2];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) kr[u][mt] = as_bf16x8(ld16(&kc[32 * mt * D + (rx ^ ((k0 + u) << 4))]));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) st[mt] = mfma32(kr[u][mt], qf[k0 + u], st[mt]);
+      }
+      if (DIAG) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = 32 * mt + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (key > wrow0 + ql) st[mt][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[mt][i]);
+      mx = half_max(mx);
+      const float bmax = mx * c2 + lg2;
+      if (__any(bmax > mref + kRescaleThreshold)) {
+        const float mnew = fmaxf(mref, bmax);
+        const float alpha = fast_exp2(mref - mnew);
+        mref = mnew;
+        lrow *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      }
+    }
+    bf16x8 pf[2][2];
+    if (active) {
+      const float off = lg2 - mref;
+      float ls = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(st[mt][i] * c2 + off);
+          st[mt][i] = OUT ? p * gmul : p;
+          ls += p;
+        }
+      lrow += ls;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int o = 8 * hh;
+          pf[mt][hh] = pack8(st[mt][o], st[mt][o + 1], st[mt][o + 2], st[mt][o + 3],
+                             st[mt][o + 4], st[mt][o + 5], st[mt][o + 6], st[mt][o + 7]);
+        }
+    }
+    wait_vm_n<NWIN>();   // V of this block has landed (the K copy behind it may not have)
+    barrier_lds();
+    if (active) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r0 = 32 * mt + 16 * hh;
+            const bf16x8 v = join_tr16(lds_tr16(&sv[r0 * D + (tx ^ ((4 * dt) << 3))]),
+                                       lds_tr16(&sv[(r0 + 8) * D + (tx ^ ((4 * dt ^ 2) << 3))]));
+            oacc[dt] = mfma32(v, pf[mt][hh], oacc[dt]);
+          }
+    }
+    wait_vm();        // K of the next block has landed
+    barrier_lds();    // ... for every wave, and every wave is done with sv and kc
+  };
+  const std::integral_constant<bool, true> diag_step;
+  const std::integral_constant<bool, false> plain_step;
+  fetch_k(sk0);
+  wait_vm();
+  barrier_lds();
+  step(diag_step, sk0, sk1);
+  const int nrest = cnt_j;
+  const int nfull = nrest & ~1;
+  for (int it = 0; it < nfull; it += 2) {
+    step(plain_step, sk1, sk0);
+    step(plain_step, sk0, sk1);
+  }
+  if (nfull < nrest) step(plain_step, sk1, sk0);
+  wait_vm();
+  if (!active) return;
+  const size_t lse_off = (size_t)(b * a.Hq + hq) * a.n + (size_t)j * kBlock + wrow0;
+  const float l = half_sum(lrow);
+  const float inv = 1.0f / l;
+  if (hl == 0) a.lse_rows[lse_off + ql] = (mref + log2f(l)) * kLn2;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d0 = 32 * dt + 8 * g4 + 4 * hl;
+      bf16x4 v;
+      v[0] = (__bf16)(oacc[dt][4 * g4 + 0] * inv);
+      v[1] = (__bf16)(oacc[dt][4 * g4 + 1] * inv);
+      v[2] = (__bf16)(oacc[dt][4 * g4 + 2] * inv);
+      v[3] = (__bf16)(oacc[dt][4 * g4 + 3] * inv);
+      *reinterpret_cast<bf16x4*>(a.Oout + q_off + ql * D + d0) = v;
+    }
+}
+
+template <int D, bool OUT>
+static hipError_t launch_fwd3_o(const AttnArgs& a, int nsplit, int hpw, hipStream_t st) {
+  const int NB = a.n / kBlock;
+  const unsigned grid = (unsigned)(NB * a.B * a.Hkv * nsplit);
+  AttnArgs b = a;
+  b.wg = wg_order(grid);
+  ProfScope prof("fwd", st);
+  hipLaunchKernelGGL((fwd3_kernel<D, OUT>), dim3(grid), dim3(256), 0, st, b, nsplit, hpw);
+  return hipGetLastError();
+}
+
 // Heads of a KV group per workgroup: at most 4 waves of 64 rows; larger groups are split
 // evenly across workgroups.
 void head_split(int G, int* nsplit, int* hpw, int* nw) {
@@ -347,7 +591,8 @@ hipError_t launch_fwd(const AttnArgs& a, hipStream_t st) {
     // 32 rows per wave (two waves per head), two heads per workgroup (split evenly)
     nsplit = (G + 1) / 2;
     hpw = (G + nsplit - 1) / nsplit;
-    if (a.d == 128) return launch_fwd_t<128, 1, 4>(a, nsplit, hpw, st);
+    if (a.d == 128) return a.gate_out ? launch_fwd3_o<128, true>(a, nsplit, hpw, st)
+                                      : launch_fwd3_o<128, false>(a, nsplit, hpw, st);
     return launch_fwd_t<64, 1, 4>(a, nsplit, hpw, st);
   }
   if (a.d == 128) {

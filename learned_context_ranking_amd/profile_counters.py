@@ -22,6 +22,11 @@ bench's workloads (each begins with its input generation, torch's random-number 
 and the library's kernels listed per workload:
 
     python3 -m learned_context_ranking_amd.profile_counters --trace DB TITLE "COMMAND" [--by-workload NAME ...]
+
+SQ counters (waits, instruction activity, matrix/vector co-execution) collected in several
+runs are summarised per attention kernel with:
+
+    python3 -m learned_context_ranking_amd.profile_counters --sq OUT_FILE "COMMAND" DIR [DIR ...]
 """
 from __future__ import annotations
 
@@ -38,7 +43,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNELS = {
     "dkv": ("dkv_kernel<128, false>", ["attn_bwd.hip", "sas_common.h"]),
     "dq": ("dq_kernel<128, false>", ["attn_bwd.hip", "sas_common.h"]),
-    "fwd": ("fwd_kernel<128, 1, 4, false>", ["attn_fwd.hip", "sas_common.h"]),
+    "fwd": ("fwd3_kernel<128, false>", ["attn_fwd.hip", "sas_common.h"]),
     "decode": ("decode_split_kernel<128, false, false, 0>", ["decode.hip", "sas_common.h"]),
     "select": ("select_kernel<8, 0>", ["select.hip", "sas_common.h"]),
 }
@@ -250,9 +255,54 @@ def main_trace(argv):
             print(f"| `{_short(n)}` | {g} | {len(ds)} | {sum(ds) / len(ds) / 1e3:.1f} | {min(ds) / 1e3:.1f} |")
 
 
+SQ_RATIOS = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_ANY",
+             "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS")
+
+
+def main_sq(argv):
+    """Per-launch means of SQ counters of the attention kernels over several counter runs
+    (one directory each), with each wait / activity counter as a fraction of the waves'
+    resident cycles (SQ_WAVE_CYCLES) and the matrix cores' co-execution fraction
+    (SQ_VALU_MFMA_COEXEC_CYCLES over SQ_VALU_MFMA_BUSY_CYCLES)."""
+    out_path, command, dirs = argv[0], argv[1], argv[2:]
+    vals = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path, newline="") as fh:
+                for row in csv.DictReader(fh):
+                    for short in ("fwd", "dq", "dkv"):
+                        if KERNELS[short][0] in row["Kernel_Name"]:
+                            vals[short][row["Counter_Name"]].append(float(row["Counter_Value"]))
+    with open(out_path, "w") as fh:
+        fh.write("# SQ counters of the attention kernels per launch (mean over dispatches), from rocprofv3\n")
+        fh.write("# counter runs of (one run per group of counters):\n")
+        fh.write(f"#   {command}\n")
+        fh.write("# *_frac = counter / SQ_WAVE_CYCLES (share of the waves' resident cycles);\n")
+        fh.write("# coexec_frac = SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES (share of the\n")
+        fh.write("# matrix cores' busy cycles with vector instructions executing beside them).\n")
+        for short in ("fwd", "dq", "dkv"):
+            cs = vals.get(short)
+            if not cs:
+                continue
+            avg = {c: sum(v) / len(v) for c, v in cs.items()}
+            fh.write(f"[{short}] {KERNELS[short][0]}\n")
+            for c in sorted(avg):
+                fh.write(f"{c} = {avg[c]:.6g}\n")
+            if avg.get("SQ_WAVE_CYCLES"):
+                for c in SQ_RATIOS:
+                    if c in avg:
+                        fh.write(f"{c}_frac = {avg[c] / avg['SQ_WAVE_CYCLES']:.3f}\n")
+            if avg.get("SQ_VALU_MFMA_BUSY_CYCLES") and "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+                fh.write(f"coexec_frac = {avg['SQ_VALU_MFMA_COEXEC_CYCLES'] / avg['SQ_VALU_MFMA_BUSY_CYCLES']:.3f}\n")
+            fh.write(f"source_sha256 = {source_digest(short)}\n")
+    print("->", out_path)
+
+
 def main(argv):
     if argv[1] == "--mfma":
         return main_mfma(argv[2:])
+    if argv[1] == "--sq":
+        return main_sq(argv[2:])
     if argv[1] == "--trace":
         return main_trace(argv[2:])
     fetch_dir, write_dir, out_dir, command = argv[1], argv[2], argv[3], argv[4]
