@@ -32,6 +32,8 @@ CASES = [
     (1, 8, 2, 4096, 64, 8, "sparse", True, "zipf"),         # popular key blocks: split key-major lists
     (1, 5, 1, 4096, 128, 8, "sparse", True, "zipf"),        # the same with G = 5
     (1, 16, 1, 512, 64, 3, "sparse", True, "normal"),       # G = 16 (eight workgroups of 2 heads)
+    (1, 8, 1, 512, 128, 5, "sparse", True, "planted"),      # the d = 128 forward at G = 8
+    (1, 6, 2, 768, 128, 5, "sparse", True, "zipf"),         # G = 3 at d = 128 (a split with one head)
 ]
 
 
@@ -112,6 +114,14 @@ def test_key_major_small_budget():
     # reference reaches |dK| ~ 9, |dV| ~ 15 (bf16 operands give ~0.3 % of that); the
     # gradients take the bound relative to their magnitude here
     test_fwd_bwd_parity(case, grad_scale_aware=True)
+
+
+def test_fwd_bwd_group_16_d128():
+    """G = 16 at d = 128 (the forward's head split: eight workgroups of two heads). Each key
+    block's dV sums 16 heads x 64 rows per item, so the reference reaches |dV| ~ 10 and the
+    gradients take the bound relative to their magnitude (bf16 operands give ~0.2 % of it);
+    O and LSE keep the fixed bound."""
+    test_fwd_bwd_parity((1, 16, 1, 512, 128, 3, "sparse", True, "normal"), grad_scale_aware=True)
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.02])
