@@ -15,8 +15,11 @@
 // O^T += V^T P^T. V stays in its natural row-major layout in LDS and the V^T operand is
 // read with the transposing ds_read_b64_tr_b16, in the key order the accumulator uses.
 //
-// Pipeline: the next block's K/V tiles are copied from global memory straight into the
-// other LDS buffer (buffer loads into LDS with a scalar per-block offset, swizzled tiles)
+// Two kernels share this structure: fwd3_kernel (d = 128, two or more query heads per KV
+// head; three waves per SIMD, see its comment) and fwd_kernel (the other shapes).
+//
+// Pipeline of fwd_kernel: the next block's K/V tiles are copied from global memory straight
+// into the other LDS buffer (buffer loads into LDS with a scalar per-block offset, swizzled tiles)
 // while the current block is computed; one barrier per block. The copy is issued on every
 // step (past the end of the list it repeats the last block) and the steps run in whole
 // rounds of two, so the compiler's tracking of the copies in flight stays exact and it
